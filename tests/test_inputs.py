@@ -1,0 +1,74 @@
+"""The seeded workload generator: determinism, sizes, distributions, Zipf load."""
+import hashlib
+
+import numpy as np
+import pytest
+
+import moe_inputs as mi
+
+
+def _sha(layer, x):
+    h = hashlib.sha256()
+    for k in sorted(layer):
+        h.update(layer[k].tobytes())
+    h.update(x.tobytes())
+    return h.hexdigest()
+
+
+def test_tiny_is_deterministic_and_seed_dependent():
+    a = _sha(*mi.workload_inputs("tiny"))
+    b = _sha(*mi.workload_inputs("tiny"))
+    assert a == b
+    l2 = mi.make_layer(mi.TINY, seed=1)
+    assert _sha(l2, mi.make_tokens(mi.TINY, 1, 4)) != a
+
+
+def test_sizes_match_the_layer():
+    shp = mi.QWEN35_MOE
+    # one expert: gate 589,824 B + up 589,824 B + down 720,896 B
+    assert shp.I * shp.H // 256 * mi.Q4K_SB_BYTES == 589_824
+    assert shp.H * shp.I // 256 * mi.Q5K_SB_BYTES == 720_896
+    layer = mi.make_layer(mi.TINY, 0)
+    assert layer["gate"].shape == (8, 128 * 256 // 256 * 144)
+    assert layer["down"].shape == (8, 256 * 128 // 256 * 176)
+    assert layer["router_w"].dtype == np.float32 and layer["router_w"].shape == (256, 8)
+
+
+def test_scale_fields_in_range():
+    rng = mi._rng(0, 99)
+    blob = mi.kquant_blob(rng, 4096, 4).reshape(4096, 144)
+    d = blob[:, 0:2].copy().view("<f2").astype(np.float64).ravel()
+    dm = blob[:, 2:4].copy().view("<f2").astype(np.float64).ravel()
+    for v in (d, dm):
+        # fp16 rounding moves the ends by at most half an ulp (2^-19 at 4e-3)
+        assert v.min() >= 1e-3 - 2 ** -21 and v.max() <= 4e-3 + 2 ** -19
+        assert abs(v.mean() - 2.5e-3) < 0.05e-3
+    body = blob[:, 4:]
+    # uniform bytes: every byte value appears, mean ~127.5
+    assert abs(body.mean() - 127.5) < 1.0 and len(np.unique(body)) == 256
+
+
+def test_token_rows_standard_normal():
+    x = mi.make_tokens(mi.QWEN35_MOE, 4, 256)
+    assert x.dtype == np.float32 and x.shape == (256, 2048)
+    assert abs(x.mean()) < 0.01 and abs(x.std() - 1) < 0.01
+
+
+def test_zipf_load_slope():
+    """Realised per-expert slot counts at T=512 follow a log-log slope of -1 +- 0.1."""
+    import oracle
+    w = mi.WORKLOADS["prefill512_zipf"]
+    layer = mi.make_layer(w.shape, w.seed, zipf=True)
+    x = mi.make_tokens(w.shape, w.seed, w.T, zipf=True)
+    idx, _, _, _ = oracle.router(x, layer["router_w"], w.shape.k)
+    c = np.sort(np.bincount(idx.ravel(), minlength=w.shape.E))[::-1]
+    nz = c > 0
+    r = np.arange(1, w.shape.E + 1)
+    slope = np.polyfit(np.log(r[nz]), np.log(c[nz]), 1)[0]
+    assert -1.1 <= slope <= -0.9, slope
+    # the uniform workload keeps nearly every expert busy
+    u = mi.WORKLOADS["prefill4096"]
+    lu = mi.make_layer(u.shape, u.seed)
+    xu = mi.make_tokens(u.shape, u.seed, 512)
+    iu, _, _, _ = oracle.router(xu, lu["router_w"], u.shape.k)
+    assert len(np.unique(iu)) >= 250
