@@ -1,0 +1,358 @@
+#!/usr/bin/env python3
+"""Throughput of the routed MoE layer on one MI355X.
+
+Headline (``value``): decode, T = 1 token row per step, on the
+Qwen3.5-35B-A3B-shaped layer (H=2048, 256 experts, top-8, I=512, a shared
+expert of I=512; Q4_K gate/up, Q5_K down; seeded synthetic weights and tokens).
+One step = one moe_layer_forward call (router + top-k + gate/up/SwiGLU + down +
+slot-order combine).  Steps cycle through a pool of 64 token rows and through
+several copies of the weights at different addresses, so that a step's 19.2 MB
+of weights is not served from the 256 MB last-level cache left warm by the step
+before.  Steps are replayed from a HIP graph (one graph of 16 steps).
+
+Secondary (``prefill``): T = 4096 token rows per step, same layer shape (seed
+4, uniform router), grouped-GEMM path.
+
+Per-kernel durations come from HIP events recorded at the library's phase
+boundaries (moe_opts.phase_events) in an eager pass over the same workload,
+enqueued behind a long matmul so that the events bracket back-to-back kernels.
+
+Run: python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("MoE-layer tokens/s at T=1 and T=4096; % peak HBM BW (decode) / % MFMA (prefill)")
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
+FP16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak
+
+
+class HipEvents:
+    """hipEvent_t handles from libamdhip64 (torch's events only see torch's own
+    stream bookkeeping; these are passed into the library call)."""
+
+    def __init__(self, n):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.ev = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.ev.append(e.value)
+
+    def array(self, i0, n):
+        return (ctypes.c_void_p * n)(*self.ev[i0:i0 + n])
+
+    def ms(self, a, b):
+        f = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(f), ctypes.c_void_p(self.ev[a]),
+                                        ctypes.c_void_p(self.ev[b])) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return f.value
+
+    def close(self):
+        for e in self.ev:
+            self.hip.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def keep_gpu_busy(torch, ms_target=60.0):
+    """Enqueue ~ms_target of matmul so the host can run ahead of the GPU."""
+    a = torch.randn(8192, 8192, device="cuda")
+    torch.cuda.synchronize()
+    for _ in range(max(1, int(ms_target / 8))):
+        a = a @ a
+        a = a * (1.0 / 8192 ** 0.5)
+    return a
+
+
+def phase_profile(torch, qm, call, n_steps, n_events):
+    """Average duration (ms) of each phase over n_steps eager calls."""
+    ev = HipEvents(n_steps * n_events)
+    _ = keep_gpu_busy(torch)
+    for i in range(n_steps):
+        call(i, ev.array(i * n_events, n_events))
+    torch.cuda.synchronize()
+    per = np.zeros((n_steps, n_events - 1))
+    for i in range(n_steps):
+        for p in range(n_events - 1):
+            per[i, p] = ev.ms(i * n_events + p, i * n_events + p + 1)
+    ev.close()
+    return per.mean(axis=0), per
+
+
+def time_steps(torch, run_step, K):
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        run_step(i)
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
+def bench_decode(args, torch, qm, mi, DeviceLayer):
+    shp = mi.QWEN35_MOE
+    w = mi.WORKLOADS["decode"]
+    layer = mi.make_layer(shp, w.seed)
+    base = DeviceLayer.from_shape(layer, shp)
+    copies = [base] + [base.clone_weights() for _ in range(args.copies - 1)]
+    pool = torch.from_numpy(mi.make_tokens(shp, w.seed, 64, stream=101)).cuda()
+    T = 1
+    ws = base.workspace(T)
+    out = torch.empty((T, shp.H), device="cuda")
+    used = []
+
+    def step(i, events=None):
+        c = copies[i % len(copies)]
+        used.append(qm.moe_layer_forward(c.desc, pool[i % 64:i % 64 + 1], T, out, ws,
+                                         events=events))
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    assert set(used) == {qm.MOE_PATH_GEMV}, used
+
+    # eager throughput
+    eager_s = time_steps(torch, step, args.steps)
+
+    # graph replay: one graph of G consecutive steps (tokens and copies cycle)
+    G = 16
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in range(G):
+            step(i)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graphs = []
+    for gi in range(64 // G):          # 4 graphs cover the 64-token pool
+        gg = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gg):
+            for i in range(gi * G, gi * G + G):
+                step(i)
+        graphs.append(gg)
+    torch.cuda.synchronize()
+    for gg in graphs:
+        gg.replay()
+    torch.cuda.synchronize()
+    n_rep = args.steps // G
+    rest = args.steps - n_rep * G
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for r in range(n_rep):
+        graphs[r % len(graphs)].replay()
+    for i in range(rest):
+        step(i)
+    torch.cuda.synchronize()
+    graph_s = time.perf_counter() - t0
+    del g
+
+    # per-kernel phases: 0 start, 1 routed, 2 gate/up done, 3 down+combine done
+    nprof = min(args.steps, 256)
+    mean_ms, _ = phase_profile(torch, qm, lambda i, e: step(i, e), nprof, 4)
+    router_ms, gateup_ms, down_ms = (float(v) for v in mean_ms)
+
+    E_bytes_gu = 2 * (shp.I * shp.H // 256) * mi.Q4K_SB_BYTES          # gate + up of one expert
+    E_bytes_d = (shp.H * shp.I // 256) * mi.Q5K_SB_BYTES
+    n_inst = shp.k + 1                                                   # 8 routed + shared
+    gateup_bytes = n_inst * E_bytes_gu + shp.H * 4 + n_inst * shp.I * 4  # weights + x + h
+    layer_bytes = n_inst * (E_bytes_gu + E_bytes_d) + shp.H * shp.E * 4  # 19,202,048 B
+    ms_graph = graph_s / args.steps * 1e3
+    res = {
+        "value": T * args.steps / graph_s,
+        "ms_per_step": ms_graph,
+        "eager_tokens_per_s": T * args.steps / eager_s,
+        "eager_ms_per_step": eager_s / args.steps * 1e3,
+        "phase_ms": {"router_topk": router_ms, "gateup_gemv": gateup_ms,
+                     "down_gemv_combine": down_ms},
+        "layer_algorithmic_bytes": layer_bytes,
+        "layer_hbm_frac_graph": layer_bytes / (ms_graph * 1e-3) / (HBM_PEAK_GBS * 1e9),
+        "layer_hbm_frac_kernels": layer_bytes / (sum(mean_ms) * 1e-3) / (HBM_PEAK_GBS * 1e9),
+        "roofline": {
+            "kernel": "gateup_gemv_kernel<64,1>",
+            "bound": "hbm",
+            "achieved": gateup_bytes / (gateup_ms * 1e-3) / 1e9,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": gateup_bytes / (gateup_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "traffic": None,
+            "algorithmic_bytes_per_launch": gateup_bytes,
+            "avg_launch_ms": gateup_ms,
+        },
+    }
+    return res, layer, pool.cpu().numpy()
+
+
+def bench_prefill(args, torch, qm, mi, DeviceLayer):
+    shp = mi.QWEN35_MOE
+    w = mi.WORKLOADS["prefill4096"]
+    layer = mi.make_layer(shp, w.seed)
+    base = DeviceLayer.from_shape(layer, shp)
+    copies = [base, base.clone_weights()]
+    T = w.T
+    x_host = mi.make_tokens(shp, w.seed, T)
+    x = torch.from_numpy(x_host).cuda()
+    ws = base.workspace(T)
+    out = torch.empty((T, shp.H), device="cuda")
+    used = []
+
+    def step(i, events=None):
+        c = copies[i % len(copies)]
+        used.append(qm.moe_layer_forward(c.desc, x, T, out, ws, events=events))
+
+    K, W = args.prefill_steps, args.prefill_warmup
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+    assert set(used) == {qm.MOE_PATH_MFMA}, used
+    secs = time_steps(torch, step, K)
+    mean_ms, _ = phase_profile(torch, qm, lambda i, e: step(i, e), K, 6)
+    names = ["router_topk", "convert_bucket", "gemm_gateup", "gemm_down", "combine"]
+    slots = T * shp.k + T
+    flops_gu = 2.0 * 2 * shp.H * shp.I * slots
+    flops_d = 2.0 * shp.I * shp.H * slots
+    gu_ms = float(mean_ms[2])
+    d_ms = float(mean_ms[3])
+    res = {
+        "workload": ("prefill T=4096: same layer shape, seed 4, uniform router, "
+                     "grouped fp16-MFMA path, 2 rotating weight copies"),
+        "value": T * K / secs,
+        "unit": "tokens/s",
+        "ms_per_step": secs / K * 1e3,
+        "steps": K,
+        "warmup": W,
+        "dtype": "fp16 operands, fp32 accumulate (router fp32)",
+        "phase_ms": {n: float(v) for n, v in zip(names, mean_ms)},
+        "expert_gflop": (flops_gu + flops_d) / 1e9,
+        "expert_mfma_frac": (flops_gu + flops_d) / ((gu_ms + d_ms) * 1e-3) / (FP16_MFMA_PEAK_TFLOPS * 1e12),
+        "roofline": {
+            "kernel": "gemm_gateup_kernel",
+            "bound": "mfma",
+            "achieved": flops_gu / (gu_ms * 1e-3) / 1e12,
+            "peak": FP16_MFMA_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": flops_gu / (gu_ms * 1e-3) / 1e12 / FP16_MFMA_PEAK_TFLOPS,
+            "traffic": None,
+            "algorithmic_flops_per_launch": flops_gu,
+            "avg_launch_ms": gu_ms,
+        },
+    }
+    return res, layer, x_host
+
+
+def cpu_baseline_decode(layer, pool, budget_s):
+    import moe_inputs as mi
+    import oracle
+    ol = oracle.Layer.from_shape(layer, mi.QWEN35_MOE)
+    n = 0
+    t0 = time.perf_counter()
+    while n < pool.shape[0] and (time.perf_counter() - t0) < budget_s:
+        oracle.forward(ol, pool[n:n + 1])
+        n += 1
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "tokens/s", "cores": oracle.max_threads(), "kind": "oracle",
+            "sample": f"{n} decode tokens, one T=1 oracle call each (routing, decode of the 9 "
+                      f"touched experts, fp64 FFN), {dt:.1f} s"}
+
+
+def cpu_baseline_prefill(layer, x, rows):
+    import moe_inputs as mi
+    import oracle
+    ol = oracle.Layer.from_shape(layer, mi.QWEN35_MOE)
+    t0 = time.perf_counter()
+    oracle.forward(ol, x[:rows])
+    dt = time.perf_counter() - t0
+    return {"value": rows / dt, "unit": "tokens/s", "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": f"first {rows} of the 4096 prefill rows in one oracle call (routing, decode "
+                      f"of every touched expert, fp64 FFN), {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=800)
+    ap.add_argument("--warmup", type=int, default=64)
+    ap.add_argument("--copies", type=int, default=4, help="weight copies cycled by decode steps")
+    ap.add_argument("--prefill-steps", type=int, default=20)
+    ap.add_argument("--prefill-warmup", type=int, default=3)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle decode work")
+    ap.add_argument("--cpu-prefill-rows", type=int, default=192)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}): "
+              "this build has no multi-GPU path; the layer's shards run on one device.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import moe_inputs as mi
+    import quantized_moe_transformer_amd as qm
+    from quantized_moe_transformer_amd.layer import DeviceLayer
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    print("[bench] decode T=1 ...", file=sys.stderr, flush=True)
+    dec, dec_layer, pool = bench_decode(args, torch, qm, mi, DeviceLayer)
+    pre = None
+    if not args.no_prefill:
+        print("[bench] prefill T=4096 ...", file=sys.stderr, flush=True)
+        pre, pre_layer, x_pre = bench_prefill(args, torch, qm, mi, DeviceLayer)
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] oracle on the host ...", file=sys.stderr, flush=True)
+        cpu = cpu_baseline_decode(dec_layer, pool, args.cpu_budget)
+        if pre is not None:
+            pre["cpu_baseline"] = cpu_baseline_prefill(pre_layer, x_pre, args.cpu_prefill_rows)
+
+    line = {
+        "metric": METRIC,
+        "value": dec["value"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": dec["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32 (Q4_K/Q5_K weights decoded in registers, fp32 accumulate)",
+        "data": "synthetic",
+        "config": {
+            "workload": ("decode T=1: Qwen3.5-35B-A3B-shaped routed MoE layer, H=2048, 256 "
+                         "experts, top-8, I=512, shared expert I=512, Q4_K gate/up, Q5_K down, "
+                         "seed 1, 64-token pool, 4 rotating weight copies, HIP-graph replay"),
+            "T": 1,
+            "path": "gemv",
+            "parallelism": "single GPU",
+        },
+        "roofline": dec["roofline"],
+        "cpu_baseline": cpu,
+        "decode": {k: v for k, v in dec.items() if k not in ("value", "ms_per_step", "roofline")},
+        "prefill": pre,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,210 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) routed Mixture-of-Experts layer library
+ *          (libmoe_hip.so).
+ *
+ * One routed MoE layer shaped like the Qwen3.5-35B-A3B layer of the page
+ * "CKE Zip: From Splitting Tokens To Splitting Qwen3.5 Weights":
+ *   - an fp32 router, softmax and top-k of E experts (section "What PR #382
+ *     Now Splits": 256 routed experts, eight selected per token);
+ *   - per selected expert a 4-bit K-quant (Q4_K) gate/up projection, SwiGLU
+ *     and a 5-bit K-quant (Q5_K) down projection, scaled by the routing
+ *     weight and merged in selected-slot order (section "A Separate Decode
+ *     Result Shows Why Axis Choice Matters");
+ *   - an always-on shared expert (section "What The First Prototype Split":
+ *     the remote runs "the routed and shared SwiGLU branches");
+ *   - a sharded mode in which the intermediate dimension of every routed and
+ *     of the shared expert is split into shards, each yielding a hidden-sized
+ *     partial; the partials add up to the whole (section "What PR #382 Now
+ *     Splits"; page "Distributed CPU: Zip Fusion Beyond Tensor Parallelism",
+ *     section "What Must Cross the Fabric: The Reduction Algebra").
+ *
+ * Conventions for every entry point
+ *   - Tensor pointers are DEVICE pointers unless stated otherwise; `stream`
+ *     is a hipStream_t (NULL = the default stream).  All work is enqueued on
+ *     `stream`; nothing synchronises the host.  Results are valid once the
+ *     caller has synchronised the stream.
+ *   - The caller owns every buffer, including the workspace.  The library
+ *     allocates and frees nothing and keeps no pointer after returning.
+ *   - Every argument is checked before anything is enqueued: on an error
+ *     nothing runs and outputs are untouched.  Device faults surface at the
+ *     caller's next synchronisation.  No exceptions cross the ABI.
+ *   - T = 0 is valid and enqueues nothing.  Outputs are overwritten, never
+ *     accumulated into.  Inputs must not alias outputs.
+ *   - Identical inputs give bit-identical outputs (fixed reduction orders, no
+ *     floating-point atomics).  The library keeps no mutable global state;
+ *     calls on different streams with different workspaces may overlap.
+ *
+ * Weight format (a reading: the pages name Q4_K/Q5_K but print no layout)
+ *   A superblock holds 256 weights, in 8 sub-blocks of 32:
+ *     Q4_K, 144 bytes: fp16 d | fp16 dmin | 12 bytes scales | 128 bytes qs
+ *     Q5_K, 176 bytes: fp16 d | fp16 dmin | 12 bytes scales | 32 bytes qh | 128 bytes qs
+ *   Sub-block j has a 6-bit scale sc_j and min m_j: for j < 4 the low six
+ *   bits of scales[j] and scales[j+4]; for j >= 4 the low/high nibble of
+ *   scales[j+4] with the top two bits of scales[j-4] / scales[j] above them.
+ *   Element 64c+l (c < 4, l < 32) is the low nibble of qs[32c+l], element
+ *   64c+32+l its high nibble; Q5_K adds 16 * bit (2c) resp. (2c+1) of qh[l].
+ *   w = d*sc_j*q - dmin*m_j.
+ *   A matrix is stored one row per output feature with the reduction
+ *   dimension K contiguous, its flat row-major array cut into superblocks
+ *   (a superblock may hold several rows when K < 256).
+ */
+#ifndef MOE_HIP_H
+#define MOE_HIP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+/* Status codes returned by every entry point. */
+#define MOE_OK 0
+#define MOE_EINVAL (-1)        /* null pointer, negative size, k not in [1, min(E,16)], shard not in [0,n) */
+#define MOE_EUNSUPPORTED (-2)  /* shape or alignment outside what the kernels handle (see below) */
+#define MOE_EWORKSPACE (-3)    /* workspace smaller than moe_workspace_bytes() */
+#define MOE_ELAUNCH (-4)       /* a kernel launch failed (hipGetLastError) */
+#define MOE_ENODEVICE (-5)     /* no gfx950 device is current */
+
+/* Compute paths (moe_opts.path). */
+#define MOE_PATH_AUTO 0        /* GEMV for T <= 32, grouped MFMA GEMM above */
+#define MOE_PATH_GEMV 1        /* fp32 dequant-GEMV, fp32 accumulation */
+#define MOE_PATH_MFMA 2        /* fp16-operand MFMA grouped GEMM, fp32 accumulation */
+
+/*
+ * Layer description: plain values and device pointers, read during the call
+ * only.
+ *   hidden        H, a multiple of 256 with H/256 in {1, 2, 4} or H in {2048, 4096}
+ *   n_experts     E, 1..1024
+ *   top_k         k, 1..min(E, 16)
+ *   inter         I, intermediate width of each routed expert, a multiple of 64
+ *   shared_inter  Is, 0 (no shared expert) or equal to I
+ *   shared_weight weight of the shared expert's output (1 in the Qwen3.5 layer)
+ *   router_w      fp32 [H][E] row-major: logits = x . router_w
+ *   gate_q, up_q  Q4_K, E consecutive matrices of [I rows][H] (I*H/256 superblocks each)
+ *   down_q        Q5_K, E consecutive matrices of [H rows][I] (H*I/256 superblocks each)
+ *   sh_gate_q, sh_up_q, sh_down_q  the shared expert, same formats, width Is
+ *                 (may be NULL when Is = 0)
+ * Every weight pointer must be 16-byte aligned; router_w and token buffers
+ * 16-byte aligned as well.
+ */
+typedef struct moe_layer_desc {
+    int32_t hidden, n_experts, top_k, inter, shared_inter;
+    float shared_weight;
+    const float *router_w;
+    const uint8_t *gate_q, *up_q, *down_q;
+    const uint8_t *sh_gate_q, *sh_up_q, *sh_down_q;
+} moe_layer_desc;
+
+/* Options.  `path` forces a compute path (MOE_PATH_*); `path_used`, a HOST
+ * pointer that may be NULL, receives the path that ran.
+ * `phase_events` (HOST array of n_phase_events hipEvent_t created by the
+ * caller, may be NULL) lets a caller time the kernels of a call per region:
+ * event i is recorded on the call's stream at phase boundary i, for
+ * i < n_phase_events.  Boundaries:
+ *   GEMV path: 0 start, 1 after routing, 2 after gate/up+SwiGLU, 3 after down+combine
+ *   MFMA path: 0 start, 1 after routing, 2 after fp16 conversion and bucketing,
+ *              3 after the gate/up GEMM, 4 after the down GEMM, 5 after the combine
+ * (moe_layer_forward_shard has no routing phase: boundary 1 is recorded
+ * right after boundary 0). */
+typedef struct moe_opts {
+    int32_t path;
+    int32_t *path_used;
+    void **phase_events;
+    int32_t n_phase_events;
+} moe_opts;
+
+/* Bytes of device workspace that router_topk, moe_layer_forward and
+ * moe_layer_forward_shard need for T token rows split into num_shards shards
+ * (any path).  Host-only; needs no device.  Returns 0 for an invalid
+ * description. */
+size_t moe_workspace_bytes(const moe_layer_desc *desc, int32_t T, int32_t num_shards);
+
+/*
+ * Router: logits[t][e] = sum_h x[t][h] * router_w[h][e] in fp32; the k largest
+ * logits in descending order (ties to the lower expert index) become slots
+ * 0..k-1 of topk_idx; topk_w[t][j] = softmax over all E logits of expert
+ * topk_idx[t][j], renormalised over the k selected -- equal to the softmax of
+ * the k selected logits alone.  (Page "CKE Zip ...", sections "What The First
+ * Prototype Split" and "What PR #382 Now Splits": the top-k indices and their
+ * routing weights are what the coordinator ships with each row, and the
+ * synchronised router decision is what both shards consume.)
+ *   x         fp32 [T][H]
+ *   topk_idx  int32 [T][k] (output)
+ *   topk_w    fp32 [T][k] (output)
+ *   ws        device workspace of at least moe_workspace_bytes(desc, T, 1) bytes
+ */
+int router_topk(const moe_layer_desc *desc, const float *x, int32_t T,
+                int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * The whole layer: routing, then
+ *   out[t] = sum_{j<k} topk_w[t][j] * FFN_{topk_idx[t][j]}(x[t]) + shared_weight * FFN_shared(x[t])
+ * with FFN(x) = W_down (silu(W_gate x) * (W_up x)), summed in slot order and
+ * the shared expert last.
+ *   x    fp32 [T][H];  out fp32 [T][H]
+ *   opts may be NULL (automatic path).
+ */
+int moe_layer_forward(const moe_layer_desc *desc, const float *x, int32_t T, float *out,
+                      const moe_opts *opts, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Shard `shard` of `num_shards` of the layer, with the routing given (the
+ * synchronised router decision, e.g. from router_topk): the same sum as
+ * moe_layer_forward restricted to intermediate rows
+ * [shard*I/num_shards, (shard+1)*I/num_shards) of every routed expert and
+ * [shard*Is/num_shards, (shard+1)*Is/num_shards) of the shared one.  The
+ * partials of all shards add up to the unsplit output (moe_reduce_partials).
+ * Requires (I/num_shards) % 64 == 0.
+ *   topk_idx int32 [T][k], topk_w fp32 [T][k] (device);  partial fp32 [T][H]
+ */
+int moe_layer_forward_shard(const moe_layer_desc *desc, const float *x, int32_t T,
+                            const int32_t *topk_idx, const float *topk_w,
+                            int32_t shard, int32_t num_shards, float *partial,
+                            const moe_opts *opts, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * out[i] = sum over s = 0, 1, ..., num_shards-1 (ascending, fp32) of partials[s][i].
+ * `partials` is a HOST array of num_shards (1..16) device pointers.  The hub's
+ * sum of shard partials in a fixed, declared order (page "Distributed CPU
+ * ...", sections "What Must Cross the Fabric: The Reduction Algebra" and
+ * "Communication Must Be Measured").
+ */
+int moe_reduce_partials(const float *const *partials, int32_t num_shards, int64_t n_elems,
+                        float *out, void *stream);
+
+/*
+ * Test hook: decode n_sb superblocks (bits = 4: Q4_K, 5: Q5_K) into
+ * n_sb*256 values in flat order.  out_dtype 0: fp32 (exactly the
+ * round-to-nearest-even fp32 value of d*sc*q - dmin*m); 1: bf16 and 2: fp16,
+ * each the round-to-nearest-even conversion of that fp32 value.
+ */
+int moe_dequant(const uint8_t *sbs, int32_t bits, int64_t n_sb, int32_t out_dtype,
+                void *out, void *stream);
+
+/*
+ * Test hook: the token->expert bucketing of the grouped-GEMM path.
+ *   counts[e]   number of slots (t, j) with topk_idx[t][j] == e          (int32 [E])
+ *   offsets[e]  exclusive prefix sum of counts, offsets[E] = T*k          (int32 [E+1])
+ *   perm[p]     slot ids s = t*k + j sorted by expert, ascending s within
+ *               an expert (a stable counting sort)                         (int32 [T*k])
+ *   ws          workspace of at least moe_workspace_bytes(desc, T, 1) bytes
+ * Entries of topk_idx outside [0, E) are a caller error (not checked on the device).
+ */
+int moe_route_bucket(const moe_layer_desc *desc, const int32_t *topk_idx, int32_t T,
+                     int32_t *counts, int32_t *offsets, int32_t *perm,
+                     void *ws, size_t ws_bytes, void *stream);
+
+/* Text for a status code (static storage). */
+const char *moe_status_str(int status);
+
+/* MOE_ABI_VERSION of the built library. */
+int moe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_HIP_H */

@@ -186,20 +186,27 @@ int oracle_router(const float *x, int T, int H, const float *Wr, int E, int k,
 {
     if (T < 0 || H <= 0 || E <= 0 || k < 1 || k > E || (T && (!x || !Wr || !idx)))
         return ORC_EINVAL;
-    double *l = malloc(sizeof(double) * E);
-    double *wd = malloc(sizeof(double) * k);
-    if (!l || !wd) { free(l); free(wd); return ORC_ENOMEM; }
-    for (int t = 0; t < T; ++t) {
-        route_token(x + (int64_t)t * H, H, Wr, E, k, l, idx + (int64_t)t * k, wd);
-        if (logits) memcpy(logits + (int64_t)t * E, l, sizeof(double) * E);
-        for (int j = 0; j < k; ++j) {
-            if (w) w[(int64_t)t * k + j] = (float)wd[j];
-            if (w_d) w_d[(int64_t)t * k + j] = wd[j];
+    int fail = 0;
+    /* token rows are independent: each is routed by the same code on any thread */
+#pragma omp parallel reduction(|:fail)
+    {
+        double *l = malloc(sizeof(double) * E);
+        double *wd = malloc(sizeof(double) * k);
+        if (!l || !wd) fail = 1;
+#pragma omp for schedule(static)
+        for (int t = 0; t < T; ++t) {
+            if (!l || !wd) continue;
+            route_token(x + (int64_t)t * H, H, Wr, E, k, l, idx + (int64_t)t * k, wd);
+            if (logits) memcpy(logits + (int64_t)t * E, l, sizeof(double) * E);
+            for (int j = 0; j < k; ++j) {
+                if (w) w[(int64_t)t * k + j] = (float)wd[j];
+                if (w_d) w_d[(int64_t)t * k + j] = wd[j];
+            }
         }
+        free(l);
+        free(wd);
     }
-    free(l);
-    free(wd);
-    return ORC_OK;
+    return fail ? ORC_ENOMEM : ORC_OK;
 }
 
 /* ------------------------------------------------------------------------ */

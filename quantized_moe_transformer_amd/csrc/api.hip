@@ -1,0 +1,335 @@
+// api.hip -- the C ABI of libmoe_hip.so: argument checks, workspace layout,
+// path choice and kernel launches.  The entry points are declared (with their
+// contracts) in include/moe.h.
+#include <string.h>
+
+#include "moe_internal.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// small kernels: dequant test hook and shard-partial reduction
+// ---------------------------------------------------------------------------
+
+// One workgroup (256 threads) per superblock, thread i decodes element i:
+// element 64c+l is the low nibble of qs[32c+l], 64c+32+l its high nibble;
+// the 5-bit format adds 16 * bit (2c or 2c+1) of qh[l].
+__global__ void __launch_bounds__(256)
+dequant_kernel(const uint8_t* __restrict__ sbs, int bits, int64_t n_sb, int out_dtype,
+               void* __restrict__ out) {
+    const int i = threadIdx.x;
+    const int c = i >> 6, r = i & 63, l = r & 31, upper = r >> 5;
+    const int sbb = bits == 4 ? kQ4Bytes : kQ5Bytes;
+    for (int64_t b = blockIdx.x; b < n_sb; b += gridDim.x) {
+        const uint8_t* sb = sbs + b * sbb;
+        const SbHead hd = load_head(sb);
+        float sc, m;
+        sub_scale_min(hd, i >> 5, sc, m);
+        const uint8_t* qs = sb + (bits == 4 ? 16 : 48);
+        const uint32_t byte = qs[32 * c + l];
+        uint32_t q = upper ? (byte >> 4) : (byte & 15u);
+        if (bits == 5) q |= ((uint32_t)(sb[16 + l] >> (2 * c + upper)) & 1u) << 4;
+        const float wv = kq_weight(hd.d * sc, hd.dmin * m, (float)q);
+        const int64_t o = b * kSbWeights + i;
+        if (out_dtype == 0)
+            reinterpret_cast<float*>(out)[o] = wv;
+        else if (out_dtype == 1)
+            reinterpret_cast<uint16_t*>(out)[o] = f32_to_bf16_rne(wv);
+        else
+            reinterpret_cast<_Float16*>(out)[o] = (_Float16)wv;
+    }
+}
+
+struct PartialPtrs {
+    const float* p[16];
+};
+
+// out = ((p0 + p1) + p2) + ...: ascending shard order, fp32.
+__global__ void __launch_bounds__(256)
+reduce4_kernel(PartialPtrs ps, int n, size_t n4, float* __restrict__ out) {
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n4) return;
+    float4 acc = reinterpret_cast<const float4*>(ps.p[0])[i];
+    for (int s = 1; s < n; ++s) {
+        const float4 v = reinterpret_cast<const float4*>(ps.p[s])[i];
+        acc.x += v.x;
+        acc.y += v.y;
+        acc.z += v.z;
+        acc.w += v.w;
+    }
+    reinterpret_cast<float4*>(out)[i] = acc;
+}
+
+__global__ void __launch_bounds__(256)
+reduce1_kernel(PartialPtrs ps, int n, size_t count, float* __restrict__ out) {
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= count) return;
+    float acc = ps.p[0][i];
+    for (int s = 1; s < n; ++s) acc += ps.p[s][i];
+    out[i] = acc;
+}
+
+hipError_t launch_reduce(const float* const* partials, int n, int64_t count, float* out,
+                         hipStream_t s) {
+    PartialPtrs ps = {};
+    bool vec = (count % 4) == 0 && ((uintptr_t)out & 15) == 0;
+    for (int i = 0; i < n; ++i) {
+        ps.p[i] = partials[i];
+        vec = vec && (((uintptr_t)partials[i] & 15) == 0);
+    }
+    if (vec) {
+        const size_t n4 = (size_t)count / 4;
+        reduce4_kernel<<<(unsigned)((n4 + 255) / 256), 256, 0, s>>>(ps, n, n4, out);
+    } else {
+        reduce1_kernel<<<(unsigned)((count + 255) / 256), 256, 0, s>>>(ps, n, (size_t)count, out);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_dequant(const uint8_t* sbs, int bits, int64_t n_sb, int out_dtype, void* out,
+                          hipStream_t s) {
+    const int64_t blocks = n_sb < 65536 ? n_sb : 65536;
+    dequant_kernel<<<(unsigned)blocks, 256, 0, s>>>(sbs, bits, n_sb, out_dtype, out);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// workspace layout
+// ---------------------------------------------------------------------------
+
+static inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+WsLayout ws_layout(const moe_layer_desc& d, int T, int num_shards) {
+    WsLayout L = {};
+    const size_t H = d.hidden, E = d.n_experts, k = d.top_k;
+    const size_t Tz = T;
+    const size_t Iloc = (size_t)(d.inter / num_shards);
+    const size_t nslot = k + (d.shared_inter > 0 ? 1 : 0);
+    size_t off = 0;
+    L.router_ks = router_splits(T, d.hidden);
+    L.router_part = off;  off = align256(off + (size_t)L.router_ks * Tz * E * 4);
+    L.idx = off;          off = align256(off + Tz * k * 4);
+    L.w = off;            off = align256(off + Tz * k * 4);
+    const size_t base = off;
+    L.hbuf = base;
+    const size_t gemv_end = align256(base + Tz * nslot * Iloc * 4);
+    off = base;
+    L.x16 = off;          off = align256(off + Tz * H * 2);
+    L.bhist = off;        off = align256(off + (size_t)bucket_blocks(T, (int)k) * E * 4);
+    L.counts = off;       off = align256(off + (E + 1) * 4);
+    L.offsets = off;      off = align256(off + (E + 2) * 4);
+    L.tile_off = off;     off = align256(off + (E + 3) * 4);
+    L.perm = off;         off = align256(off + Tz * k * 4);
+    L.h16 = off;          off = align256(off + (Tz * k + Tz) * Iloc * 2);
+    L.y = off;            off = align256(off + Tz * k * H * 4);
+    L.ysh = off;          off = align256(off + Tz * H * 4);
+    L.total = gemv_end > off ? gemv_end : off;
+    return L;
+}
+
+// ---------------------------------------------------------------------------
+// checks
+// ---------------------------------------------------------------------------
+
+static inline bool al16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+static int check_desc(const moe_layer_desc* d) {
+    if (!d) return MOE_EINVAL;
+    if (d->hidden <= 0 || d->n_experts <= 0 || d->top_k < 1 || d->inter <= 0 || d->shared_inter < 0)
+        return MOE_EINVAL;
+    if (d->n_experts > 1024) return MOE_EUNSUPPORTED;
+    if (d->top_k > 16 || d->top_k > d->n_experts) return MOE_EINVAL;
+    if (!d->router_w || !d->gate_q || !d->up_q || !d->down_q) return MOE_EINVAL;
+    if (d->shared_inter > 0 && (!d->sh_gate_q || !d->sh_up_q || !d->sh_down_q)) return MOE_EINVAL;
+    const int nsb = d->hidden / kSbWeights;
+    if (d->hidden % kSbWeights || !(nsb == 1 || nsb == 2 || nsb == 4 || nsb == 8 || nsb == 16))
+        return MOE_EUNSUPPORTED;
+    if (d->inter % 64) return MOE_EUNSUPPORTED;
+    if (d->shared_inter != 0 && d->shared_inter != d->inter) return MOE_EUNSUPPORTED;
+    if (!al16(d->router_w) || !al16(d->gate_q) || !al16(d->up_q) || !al16(d->down_q))
+        return MOE_EUNSUPPORTED;
+    if (d->shared_inter > 0 && (!al16(d->sh_gate_q) || !al16(d->sh_up_q) || !al16(d->sh_down_q)))
+        return MOE_EUNSUPPORTED;
+    return MOE_OK;
+}
+
+static bool gemv_supports(const moe_layer_desc* d, int nshards) {
+    const int iloc = d->inter / nshards;
+    return iloc >= 64 && iloc <= 2048 && (iloc & (iloc - 1)) == 0;
+}
+
+static int choose_path(const moe_layer_desc* d, int T, int nshards, const moe_opts* o, int* path) {
+    const int req = o ? o->path : MOE_PATH_AUTO;
+    if (req == MOE_PATH_GEMV) {
+        if (!gemv_supports(d, nshards)) return MOE_EUNSUPPORTED;
+        *path = MOE_PATH_GEMV;
+    } else if (req == MOE_PATH_MFMA) {
+        *path = MOE_PATH_MFMA;
+    } else if (req == MOE_PATH_AUTO) {
+        *path = (T <= kGemvMaxT && gemv_supports(d, nshards)) ? MOE_PATH_GEMV : MOE_PATH_MFMA;
+    } else {
+        return MOE_EINVAL;
+    }
+    return MOE_OK;
+}
+
+// gfx950 check of the current device, cached per device ordinal.
+static int check_device() {
+    static int cache[64];   // 0 unknown, 1 gfx950, 2 not (value races are benign: same result)
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return MOE_ENODEVICE;
+    if (dev >= 0 && dev < 64 && cache[dev]) return cache[dev] == 1 ? MOE_OK : MOE_ENODEVICE;
+    hipDeviceProp_t p;
+    if (hipGetDeviceProperties(&p, dev) != hipSuccess) return MOE_ENODEVICE;
+    const bool ok = strncmp(p.gcnArchName, "gfx950", 6) == 0;
+    if (dev >= 0 && dev < 64) cache[dev] = ok ? 1 : 2;
+    return ok ? MOE_OK : MOE_ENODEVICE;
+}
+
+static int launched(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ELAUNCH; }
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_status_str(int status) {
+    switch (status) {
+        case MOE_OK: return "ok";
+        case MOE_EINVAL: return "invalid argument";
+        case MOE_EUNSUPPORTED: return "unsupported shape or alignment";
+        case MOE_EWORKSPACE: return "workspace too small";
+        case MOE_ELAUNCH: return "kernel launch failed";
+        case MOE_ENODEVICE: return "no gfx950 device";
+        default: return "unknown status";
+    }
+}
+
+size_t moe_workspace_bytes(const moe_layer_desc* desc, int32_t T, int32_t num_shards) {
+    if (check_desc(desc) != MOE_OK || T < 0 || num_shards < 1 || num_shards > 16) return 0;
+    if (desc->inter % num_shards) return 0;
+    return ws_layout(*desc, T, num_shards).total;
+}
+
+int router_topk(const moe_layer_desc* desc, const float* x, int32_t T, int32_t* topk_idx,
+                float* topk_w, void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_desc(desc);
+    if (rc) return rc;
+    if (T < 0) return MOE_EINVAL;
+    if (T == 0) return MOE_OK;
+    if (!x || !topk_idx || !topk_w || !ws) return MOE_EINVAL;
+    const WsLayout L = ws_layout(*desc, T, 1);
+    if (ws_bytes < L.total) return MOE_EWORKSPACE;
+    if ((rc = check_device())) return rc;
+    return launched(launch_router(*desc, x, T, topk_idx, topk_w, (char*)ws, L, (hipStream_t)stream));
+}
+
+static int forward_common(const moe_layer_desc* desc, const float* x, int32_t T,
+                          const int32_t* idx, const float* w, int32_t shard, int32_t nshards,
+                          float* out, const moe_opts* opts, void* ws, size_t ws_bytes,
+                          void* stream, bool route) {
+    int rc = check_desc(desc);
+    if (rc) return rc;
+    if (T < 0 || nshards < 1 || nshards > 16 || shard < 0 || shard >= nshards) return MOE_EINVAL;
+    if (desc->inter % nshards || (desc->inter / nshards) % 64) return MOE_EUNSUPPORTED;
+    int path = 0;
+    if ((rc = choose_path(desc, T, nshards, opts, &path))) return rc;
+    if (opts && opts->path_used) *opts->path_used = path;
+    if (T == 0) return MOE_OK;
+    if (!x || !out || !ws || (!route && (!idx || !w))) return MOE_EINVAL;
+    if (!al16(x) || !al16(out) || ((uintptr_t)ws & 255)) return MOE_EUNSUPPORTED;
+    const WsLayout L = ws_layout(*desc, T, nshards);
+    if (ws_bytes < L.total) return MOE_EWORKSPACE;
+    if ((rc = check_device())) return rc;
+    hipStream_t s = (hipStream_t)stream;
+    char* wsp = (char*)ws;
+    PhaseMarks pm;
+    if (opts && opts->phase_events && opts->n_phase_events > 0) {
+        pm.ev = opts->phase_events;
+        pm.n = opts->n_phase_events;
+        pm.s = s;
+    }
+    pm.mark(0);
+    if (route) {
+        int32_t* ridx = reinterpret_cast<int32_t*>(wsp + L.idx);
+        float* rw = reinterpret_cast<float*>(wsp + L.w);
+        if (launch_router(*desc, x, T, ridx, rw, wsp, L, s) != hipSuccess) return MOE_ELAUNCH;
+        idx = ridx;
+        w = rw;
+    }
+    pm.mark(1);
+    hipError_t e = path == MOE_PATH_GEMV
+                       ? launch_gemv(*desc, x, T, idx, w, shard, nshards, out, wsp, L, s, pm)
+                       : launch_mfma(*desc, x, T, idx, w, shard, nshards, out, wsp, L, s, pm);
+    return launched(e);
+}
+
+int moe_layer_forward(const moe_layer_desc* desc, const float* x, int32_t T, float* out,
+                      const moe_opts* opts, void* ws, size_t ws_bytes, void* stream) {
+    return forward_common(desc, x, T, nullptr, nullptr, 0, 1, out, opts, ws, ws_bytes, stream,
+                          true);
+}
+
+int moe_layer_forward_shard(const moe_layer_desc* desc, const float* x, int32_t T,
+                            const int32_t* topk_idx, const float* topk_w, int32_t shard,
+                            int32_t num_shards, float* partial, const moe_opts* opts, void* ws,
+                            size_t ws_bytes, void* stream) {
+    return forward_common(desc, x, T, topk_idx, topk_w, shard, num_shards, partial, opts, ws,
+                          ws_bytes, stream, false);
+}
+
+int moe_reduce_partials(const float* const* partials, int32_t num_shards, int64_t n_elems,
+                        float* out, void* stream) {
+    if (!partials || num_shards < 1 || num_shards > 16 || n_elems < 0) return MOE_EINVAL;
+    if (n_elems == 0) return MOE_OK;
+    if (!out) return MOE_EINVAL;
+    for (int i = 0; i < num_shards; ++i)
+        if (!partials[i]) return MOE_EINVAL;
+    int rc = check_device();
+    if (rc) return rc;
+    return launched(launch_reduce(partials, num_shards, n_elems, out, (hipStream_t)stream));
+}
+
+int moe_dequant(const uint8_t* sbs, int32_t bits, int64_t n_sb, int32_t out_dtype, void* out,
+                void* stream) {
+    if ((bits != 4 && bits != 5) || n_sb < 0 || out_dtype < 0 || out_dtype > 2) return MOE_EINVAL;
+    if (n_sb == 0) return MOE_OK;
+    if (!sbs || !out) return MOE_EINVAL;
+    if (!al16(sbs)) return MOE_EUNSUPPORTED;
+    int rc = check_device();
+    if (rc) return rc;
+    return launched(launch_dequant(sbs, bits, n_sb, out_dtype, out, (hipStream_t)stream));
+}
+
+int moe_route_bucket(const moe_layer_desc* desc, const int32_t* topk_idx, int32_t T,
+                     int32_t* counts, int32_t* offsets, int32_t* perm, void* ws, size_t ws_bytes,
+                     void* stream) {
+    int rc = check_desc(desc);
+    if (rc) return rc;
+    if (T < 0) return MOE_EINVAL;
+    if (T == 0) return MOE_OK;
+    if (!topk_idx || !counts || !offsets || !perm || !ws) return MOE_EINVAL;
+    if ((uintptr_t)ws & 255) return MOE_EUNSUPPORTED;
+    const WsLayout L = ws_layout(*desc, T, 1);
+    if (ws_bytes < L.total) return MOE_EWORKSPACE;
+    if ((rc = check_device())) return rc;
+    hipStream_t s = (hipStream_t)stream;
+    char* wsp = (char*)ws;
+    int32_t* wc = reinterpret_cast<int32_t*>(wsp + L.counts);
+    int32_t* wo = reinterpret_cast<int32_t*>(wsp + L.offsets);
+    int32_t* wt = reinterpret_cast<int32_t*>(wsp + L.tile_off);
+    int32_t* bh = reinterpret_cast<int32_t*>(wsp + L.bhist);
+    if (launch_bucket(topk_idx, T, desc->top_k, desc->n_experts, desc->shared_inter > 0, wc, wo,
+                      wt, perm, bh, s) != hipSuccess)
+        return MOE_ELAUNCH;
+    const size_t E = desc->n_experts;
+    if (hipMemcpyAsync(counts, wc, E * 4, hipMemcpyDeviceToDevice, s) != hipSuccess ||
+        hipMemcpyAsync(offsets, wo, (E + 1) * 4, hipMemcpyDeviceToDevice, s) != hipSuccess)
+        return MOE_ELAUNCH;
+    return MOE_OK;
+}
+
+}  // extern "C"

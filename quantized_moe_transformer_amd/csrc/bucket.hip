@@ -1,0 +1,132 @@
+// bucket.hip -- token -> expert bucketing for the grouped-GEMM path.
+//
+// Rows are independent through the MoE region (page "CKE Zip: From Splitting
+// Tokens To Splitting Qwen3.5 Weights", section "What The First Prototype
+// Split"), so the slots (t, j) can be regrouped by expert and every expert's
+// weights streamed once for all of its rows.  The regrouping is a stable
+// counting sort of the slot ids s = t*k + j by expert:
+//   bucket_hist     per 1024-slot block, per-expert counts (LDS integer adds);
+//   bucket_scan     one workgroup: counts, exclusive scan over experts
+//                   (offsets), per-block bases, and the grouped-GEMM tile list
+//                   (tiles of kTileM rows per expert, the shared expert last as
+//                   group E with all T rows);
+//   bucket_scatter  per block: per-wave histograms -> per-wave bases, the rank
+//                   of a slot among equal experts inside its wave by a
+//                   64-step lane scan, perm[base + rank] = s.
+// Integer counts are order-independent and the ranks are positional, so the
+// result is deterministic.
+#include "moe_internal.h"
+
+namespace moe {
+
+constexpr int kBucketBlock = 1024;   // slots (= threads) per block
+constexpr int kBucketWaves = kBucketBlock / 64;
+
+__global__ void __launch_bounds__(kBucketBlock)
+bucket_hist_kernel(const int32_t* __restrict__ idx, int n, int E, int32_t* __restrict__ bhist) {
+    extern __shared__ int32_t hist[];   // [E]
+    for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
+    __syncthreads();
+    const int s = blockIdx.x * kBucketBlock + threadIdx.x;
+    if (s < n) {
+        const int e = idx[s];
+        if ((unsigned)e < (unsigned)E) atomicAdd(&hist[e], 1);
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += blockDim.x) bhist[(size_t)blockIdx.x * E + e] = hist[e];
+}
+
+// Single workgroup of 1024 threads; E <= 1024.
+__global__ void __launch_bounds__(1024)
+bucket_scan_kernel(int nblk, int E, int T, int shared, int32_t* __restrict__ bhist,
+                   int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                   int32_t* __restrict__ tile_off) {
+    __shared__ int32_t sc[1024];
+    __shared__ int32_t st[1024];
+    const int e = threadIdx.x;
+    int c = 0;
+    if (e < E)
+        for (int b = 0; b < nblk; ++b) c += bhist[(size_t)b * E + e];
+    const int tiles = (c + kTileM - 1) / kTileM;
+    sc[e] = e < E ? c : 0;
+    st[e] = e < E ? tiles : 0;
+    __syncthreads();
+    // Hillis-Steele inclusive scans of counts and tiles
+    for (int off = 1; off < 1024; off <<= 1) {
+        const int a = e >= off ? sc[e - off] : 0;
+        const int b = e >= off ? st[e - off] : 0;
+        __syncthreads();
+        sc[e] += a;
+        st[e] += b;
+        __syncthreads();
+    }
+    if (e < E) {
+        const int excl = sc[e] - c;
+        counts[e] = c;
+        offsets[e] = excl;
+        tile_off[e] = st[e] - tiles;
+        // per-block bases for the scatter, in place
+        int base = excl;
+        for (int b = 0; b < nblk; ++b) {
+            const int h = bhist[(size_t)b * E + e];
+            bhist[(size_t)b * E + e] = base;
+            base += h;
+        }
+    }
+    if (e == E - 1) {
+        offsets[E] = sc[e];
+        offsets[E + 1] = sc[e] + (shared ? T : 0);
+        tile_off[E] = st[e];
+        tile_off[E + 1] = st[e] + (shared ? (T + kTileM - 1) / kTileM : 0);
+        counts[E] = shared ? T : 0;
+    }
+}
+
+__global__ void __launch_bounds__(kBucketBlock)
+bucket_scatter_kernel(const int32_t* __restrict__ idx, int n, int E,
+                      const int32_t* __restrict__ bbase, int32_t* __restrict__ perm) {
+    extern __shared__ int32_t wh[];   // [kBucketWaves][E]
+    for (int i = threadIdx.x; i < kBucketWaves * E; i += blockDim.x) wh[i] = 0;
+    __syncthreads();
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int s = blockIdx.x * kBucketBlock + threadIdx.x;
+    int e = -1;
+    if (s < n) {
+        e = idx[s];
+        if ((unsigned)e >= (unsigned)E) e = -1;
+    }
+    if (e >= 0) atomicAdd(&wh[wave * E + e], 1);
+    __syncthreads();
+    // exclusive scan over waves, per expert
+    for (int x = threadIdx.x; x < E; x += blockDim.x) {
+        int run = bbase[(size_t)blockIdx.x * E + x];
+        for (int w = 0; w < kBucketWaves; ++w) {
+            const int h = wh[w * E + x];
+            wh[w * E + x] = run;
+            run += h;
+        }
+    }
+    __syncthreads();
+    // rank among earlier lanes of this wave with the same expert
+    int rank = 0;
+    for (int l = 0; l < 64; ++l) {
+        const int el = __shfl(e, l, 64);
+        rank += (l < lane && el == e) ? 1 : 0;
+    }
+    if (e >= 0) perm[wh[wave * E + e] + rank] = s;
+}
+
+hipError_t launch_bucket(const int32_t* idx, int T, int k, int E, bool shared, int32_t* counts,
+                         int32_t* offsets, int32_t* tile_off, int32_t* perm, int32_t* bhist,
+                         hipStream_t s) {
+    const int n = T * k;
+    const int nblk = bucket_blocks(T, k);
+    bucket_hist_kernel<<<nblk, kBucketBlock, E * sizeof(int32_t), s>>>(idx, n, E, bhist);
+    bucket_scan_kernel<<<1, 1024, 0, s>>>(nblk, E, T, shared ? 1 : 0, bhist, counts, offsets,
+                                          tile_off);
+    bucket_scatter_kernel<<<nblk, kBucketBlock, kBucketWaves * E * sizeof(int32_t), s>>>(
+        idx, n, E, bhist, perm);
+    return hipGetLastError();
+}
+
+}  // namespace moe

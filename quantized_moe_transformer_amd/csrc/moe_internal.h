@@ -1,0 +1,171 @@
+// moe_internal.h -- shared device helpers and kernel launchers of libmoe_hip.so.
+//
+// Everything here is gfx950 (CDNA4) code: 64-lane wavefronts, MFMA matrix
+// cores, 160 KB of LDS per CU.  Nothing in this directory is shared with the
+// CPU oracle.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+constexpr int kWave = 64;
+constexpr int kQ4Bytes = 144;   // 4-bit K-quant superblock
+constexpr int kQ5Bytes = 176;   // 5-bit K-quant superblock
+constexpr int kSbWeights = 256;
+constexpr int kGemvMaxT = 32;   // automatic path: GEMV up to this many rows
+constexpr int kTileM = 64;      // grouped-GEMM rows (slots) per tile
+// h is carried into the down projection as fp16 scaled by 2^-4: the SwiGLU
+// output of the Qwen3.5-shaped layer reaches ~2e4, the scale keeps a 50x
+// margin to fp16's 65504 at no cost in relative precision.
+constexpr float kHScale = 0.0625f;
+constexpr float kHUnscale = 16.0f;
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float float16v __attribute__((ext_vector_type(16)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// K-quant field decoding (device)
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t bits16) {
+    union { uint16_t u; _Float16 h; } cv;
+    cv.u = (uint16_t)bits16;
+    return (float)cv.h;
+}
+
+// The 16-byte head of a superblock: d, dmin and the 12 scale bytes as words.
+struct SbHead {
+    float d, dmin;
+    uint32_t s0, s1, s2;
+};
+
+__device__ __forceinline__ SbHead load_head(const uint8_t* sb) {
+    uint4 v = *reinterpret_cast<const uint4*>(sb);
+    SbHead h;
+    h.d = f16_bits_to_f32(v.x & 0xffffu);
+    h.dmin = f16_bits_to_f32(v.x >> 16);
+    h.s0 = v.y;
+    h.s1 = v.z;
+    h.s2 = v.w;
+    return h;
+}
+
+// 6-bit scale and min of sub-block j.  Bytes 0..3 (word s0) carry the scales
+// of sub-blocks 0..3 in their low six bits and the top two bits of the scales
+// of sub-blocks 4..7; bytes 4..7 (s1) do the same for the mins; bytes 8..11
+// (s2) carry the low nibbles of scale (low half) and min (high half) of
+// sub-blocks 4..7.
+__device__ __forceinline__ void sub_scale_min(const SbHead& h, int j, float& sc, float& m) {
+    uint32_t isc, im;
+    if (j < 4) {
+        isc = (h.s0 >> (8 * j)) & 63u;
+        im = (h.s1 >> (8 * j)) & 63u;
+    } else {
+        const int jj = j - 4;
+        isc = ((h.s2 >> (8 * jj)) & 15u) | (((h.s0 >> (8 * jj + 6)) & 3u) << 4);
+        im = ((h.s2 >> (8 * jj + 4)) & 15u) | (((h.s1 >> (8 * jj + 6)) & 3u) << 4);
+    }
+    sc = (float)isc;
+    m = (float)im;
+}
+
+// One weight: w = d*sc*q - dmin*m.  d*sc (<= 17 significant bits) and dmin*m
+// are exact in fp32, and the fused multiply-add rounds the exact value once,
+// so the result is the round-to-nearest-even fp32 of the real weight.
+__device__ __forceinline__ float kq_weight(float dsc, float dmm, float q) {
+    return __builtin_fmaf(q, dsc, -dmm);
+}
+
+// Code of byte b (0..15) of a 16-byte piece held as 4 words: low nibble.
+__device__ __forceinline__ uint32_t piece_byte(const uint4& v, int b) {
+    const uint32_t w = b < 4 ? v.x : b < 8 ? v.y : b < 12 ? v.z : v.w;
+    return (w >> (8 * (b & 3))) & 0xffu;
+}
+
+// ---------------------------------------------------------------------------
+// Wave reductions (64 lanes), fixed butterfly order: deterministic
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float wave_sum_group(float v, int group) {
+    // sum over aligned groups of `group` lanes (group a power of two <= 64)
+    for (int off = group >> 1; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+__device__ __forceinline__ float silu_f(float z) {
+    // z * sigmoid(z); expf(-z) overflows to +inf for very negative z, giving -0
+    return z / (1.0f + __expf(-z));
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);  // quiet NaN
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// ---------------------------------------------------------------------------
+// Workspace layout
+// ---------------------------------------------------------------------------
+
+struct WsLayout {
+    // shared by both paths
+    size_t router_part;   // float [ks][T][E]
+    size_t idx, w;        // int32 / float [T][k] (routing computed inside the forward call)
+    // GEMV path
+    size_t hbuf;          // float [T*(k+1)][I_loc]
+    // grouped-GEMM path (overlays the GEMV region)
+    size_t x16;           // fp16 [T][H]
+    size_t bhist;         // int32 [nblk][E]
+    size_t counts;        // int32 [E+1]
+    size_t offsets;       // int32 [E+2]
+    size_t tile_off;      // int32 [E+3]
+    size_t perm;          // int32 [T*k]
+    size_t h16;           // fp16 [T*k + T][I_loc]
+    size_t y;             // float [T*k][H]
+    size_t ysh;           // float [T][H]
+    size_t total;
+    int router_ks;        // router K-splits
+};
+
+int router_splits(int T, int H);
+WsLayout ws_layout(const moe_layer_desc& d, int T, int num_shards);
+inline int bucket_blocks(int T, int k) { return (T * k + 1023) / 1024; }
+
+// ---------------------------------------------------------------------------
+// Launchers (enqueue only; arguments already validated)
+// ---------------------------------------------------------------------------
+
+// Records caller-owned timing events at phase boundaries (see moe_opts).
+struct PhaseMarks {
+    void** ev = nullptr;
+    int n = 0;
+    hipStream_t s = nullptr;
+    void mark(int i) const {
+        if (i < n && ev && ev[i]) (void)hipEventRecord((hipEvent_t)ev[i], s);
+    }
+};
+
+hipError_t launch_router(const moe_layer_desc& d, const float* x, int T, int32_t* idx, float* w,
+                         char* ws, const WsLayout& L, hipStream_t s);
+hipError_t launch_gemv(const moe_layer_desc& d, const float* x, int T, const int32_t* idx,
+                       const float* w, int shard, int nshards, float* out, char* ws,
+                       const WsLayout& L, hipStream_t s, const PhaseMarks& pm);
+hipError_t launch_bucket(const int32_t* idx, int T, int k, int E, bool shared, int32_t* counts,
+                         int32_t* offsets, int32_t* tile_off, int32_t* perm, int32_t* bhist,
+                         hipStream_t s);
+hipError_t launch_mfma(const moe_layer_desc& d, const float* x, int T, const int32_t* idx,
+                       const float* w, int shard, int nshards, float* out, char* ws,
+                       const WsLayout& L, hipStream_t s, const PhaseMarks& pm);
+hipError_t launch_reduce(const float* const* partials, int n, int64_t count, float* out,
+                         hipStream_t s);
+hipError_t launch_dequant(const uint8_t* sbs, int bits, int64_t n_sb, int out_dtype, void* out,
+                          hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,45 @@
+"""Comparison helpers shared by the GPU parity tests and the smoke check."""
+import functools
+
+import numpy as np
+
+# Tolerances, max|gpu - ref| / RMS(ref) over every compared output of a call:
+GEMV_TOL = 1e-4      # fp32 dequant-GEMV path
+MFMA_TOL = 1e-2      # fp16-operand MFMA path (fp32 accumulation)
+TOPK_GAP = 1e-5      # top-k may differ only between experts whose logits are closer than this
+
+
+def rel_err(got, ref):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    rms = np.sqrt(np.mean(ref ** 2))
+    return float(np.abs(got - ref).max() / rms) if ref.size else 0.0
+
+
+def topk_check(gpu_idx, ora_idx, ora_logits, gap=TOPK_GAP):
+    """Classify rows: exact match, exempt (every differing slot is a swap
+    between experts whose oracle logits differ by < gap), or wrong.
+    Returns (exact_rows, exempt_rows, wrong_rows) as index arrays."""
+    gpu_idx = np.asarray(gpu_idx)
+    ora_idx = np.asarray(ora_idx)
+    exact, exempt, wrong = [], [], []
+    for t in range(gpu_idx.shape[0]):
+        g, o = gpu_idx[t], ora_idx[t]
+        if np.array_equal(g, o):
+            exact.append(t)
+            continue
+        ok = len(set(g.tolist())) == len(g) and all(0 <= e < ora_logits.shape[1] for e in g)
+        for j in range(len(g)):
+            if g[j] != o[j] and abs(ora_logits[t, g[j]] - ora_logits[t, o[j]]) >= gap:
+                ok = False
+        (exempt if ok else wrong).append(t)
+    return np.array(exact, int), np.array(exempt, int), np.array(wrong, int)
+
+
+@functools.lru_cache(maxsize=4)
+def workload(name):
+    """Host arrays of a named workload (cached per process)."""
+    import moe_inputs as mi
+    w = mi.WORKLOADS[name]
+    layer = mi.make_layer(w.shape, w.seed, zipf=w.zipf)
+    return w, layer

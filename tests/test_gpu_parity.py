@@ -1,0 +1,333 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bars: dequantised weights and bucketing bit-exact; top-k exact except swaps
+between experts whose oracle logits are closer than 1e-5; layer outputs within
+max|err|/RMS <= 1e-4 on the fp32 GEMV path and <= 1e-2 on the fp16 MFMA path.
+Rows whose routing legitimately differs (exempt near-ties) are compared again
+under the oracle's routing through moe_layer_forward_shard(0 of 1).
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+import moe_inputs as mi  # noqa: E402
+import oracle  # noqa: E402
+from kquant_pack import pack_sb, read_fixture  # noqa: E402
+from parity_util import GEMV_TOL, MFMA_TOL, rel_err, topk_check, workload  # noqa: E402
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import quantized_moe_transformer_amd as qm  # noqa: E402
+from quantized_moe_transformer_amd.layer import DeviceLayer  # noqa: E402
+
+DEV = "cuda"
+_layers = {}
+
+
+def say(msg):
+    print(f"[parity] {msg}", flush=True)
+
+
+def dev_layer(name):
+    if name not in _layers:
+        w, layer = workload(name)
+        _layers[name] = (w, layer, DeviceLayer.from_shape(layer, w.shape),
+                         oracle.Layer.from_shape(layer, w.shape))
+    return _layers[name]
+
+
+def gpu(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def run_forward(dl, x, path=qm.MOE_PATH_AUTO):
+    T = x.shape[0]
+    xd = gpu(x)
+    out = torch.full((T, dl.H), float("nan"), device=DEV)
+    ws = dl.workspace(T)
+    used = qm.moe_layer_forward(dl.desc, xd, T, out, ws, path=path)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), used
+
+
+def run_router(dl, x):
+    T = x.shape[0]
+    idx = torch.empty((T, dl.k), dtype=torch.int32, device=DEV)
+    w = torch.empty((T, dl.k), dtype=torch.float32, device=DEV)
+    qm.router_topk(dl.desc, gpu(x), T, idx, w, dl.workspace(T))
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), w.cpu().numpy()
+
+
+def run_shard(dl, x, idx, w, shard, n, path=qm.MOE_PATH_AUTO):
+    T = x.shape[0]
+    part = torch.full((T, dl.H), float("nan"), device=DEV)
+    used = qm.moe_layer_forward_shard(dl.desc, gpu(x), T, gpu(idx), gpu(w), shard, n, part,
+                                      dl.workspace(T, n), path=path)
+    torch.cuda.synchronize()
+    return part, used
+
+
+# ---------------------------------------------------------------------------
+# dequantisation: bit-exact
+# ---------------------------------------------------------------------------
+
+def gpu_dequant(blob, bits, dtype):
+    b = gpu(np.ascontiguousarray(blob).reshape(-1))
+    n_sb = b.numel() // (144 if bits == 4 else 176)
+    tdt = {0: torch.float32, 1: torch.bfloat16, 2: torch.float16}[dtype]
+    out = torch.empty(n_sb * 256, dtype=tdt, device=DEV)
+    qm.moe_dequant(b, bits, n_sb, dtype, out)
+    torch.cuda.synchronize()
+    return out.cpu()
+
+
+def check_dequant_bitwise(blob, bits):
+    ref = oracle.dequant(blob, bits)
+    got = gpu_dequant(blob, bits, 0).numpy()
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+    ref16 = ref.astype(np.float16)                     # RNE
+    got16 = gpu_dequant(blob, bits, 2).numpy()
+    assert np.array_equal(got16.view(np.uint16), ref16.view(np.uint16))
+    refbf = torch.from_numpy(ref).to(torch.bfloat16)   # RNE
+    gotbf = gpu_dequant(blob, bits, 1)
+    assert torch.equal(gotbf.view(torch.int16), refbf.view(torch.int16))
+
+
+def test_dequant_handworked_and_sweep():
+    fx = read_fixture(os.path.join(os.path.dirname(__file__), "golden", "kquant_handworked.txt"))
+    head = bytes([0x00, 0x1C, 0x00, 0x18]) + fx["scales"]
+    sb4 = np.frombuffer(head + fx["q4_qs"], np.uint8)
+    sb5 = np.frombuffer(head + fx["q5_qh"] + fx["q5_qs"], np.uint8)
+    w4 = gpu_dequant(sb4, 4, 0).numpy()
+    w5 = gpu_dequant(sb5, 5, 0).numpy()
+    for i, n in fx["q4_w512"].items():
+        assert w4[i] == np.float32(n / 512)
+    for i, n in fx["q5_w512"].items():
+        assert w5[i] == np.float32(n / 512)
+    # every (scale, min) pair with every code, several (d, dmin)
+    rng = np.random.default_rng(5)
+    for bits in (4, 5):
+        nq = 16 if bits == 4 else 32
+        for d, dm in [(0x1C00, 0x1800), (0x3C00, 0x0001), (0x7BFF, 0x0400), (0x1234, 0x2345)]:
+            blobs = []
+            pairs = [(s, m) for s in range(64) for m in range(64)]
+            for b in range(0, len(pairs), 8):
+                sc = [p[0] for p in pairs[b:b + 8]]
+                mm = [p[1] for p in pairs[b:b + 8]]
+                q = [int(v) for j in range(8) for v in rng.permutation(np.tile(np.arange(nq), 32 // nq))]
+                blobs.append(pack_sb(d, dm, sc, mm, q, bits))
+            check_dequant_bitwise(np.concatenate(blobs), bits)
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode"])
+def test_dequant_layer_matrices(name):
+    w, layer = workload(name)
+    experts = range(w.shape.E) if w.shape.E <= 8 else [0, 1, 137, w.shape.E - 1]
+    for e in experts:
+        say(f"dequant {name} expert {e}")
+        check_dequant_bitwise(layer["gate"][e], 4)
+        check_dequant_bitwise(layer["up"][e], 4)
+        check_dequant_bitwise(layer["down"][e], 5)
+    check_dequant_bitwise(layer["sh_gate"], 4)
+    check_dequant_bitwise(layer["sh_down"], 5)
+
+
+# ---------------------------------------------------------------------------
+# router: top-k exact except near-ties; weights
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name,T,stream", [("tiny", 4, None), ("decode", 64, 7),
+                                           ("decode_batched", 32, None),
+                                           ("prefill512_zipf", 512, None),
+                                           ("prefill4096", 4096, None), ("prefill4096", 333, 3)])
+def test_router_topk(name, T, stream):
+    w, layer, dl, ol = dev_layer(name)
+    x = mi.make_tokens(w.shape, w.seed, T, stream=w.x_stream if stream is None else stream,
+                       zipf=w.zipf)
+    say(f"router {name} T={T}")
+    gi, gw = run_router(dl, x)
+    oi, ow, owd, logits = oracle.router(x, layer["router_w"], w.shape.k)
+    exact, exempt, wrong = topk_check(gi, oi, logits)
+    assert len(wrong) == 0, (wrong[:5], gi[wrong[:5]], oi[wrong[:5]])
+    assert len(exact) >= T - 2
+    assert np.allclose(gw[exact], owd[exact], rtol=2e-6, atol=1e-7)
+    assert np.allclose(gw.sum(1), 1.0, atol=1e-6)
+
+
+# ---------------------------------------------------------------------------
+# bucketing: bit-exact against the oracle's stable counting sort
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name,T", [("tiny", 4), ("prefill512_zipf", 512), ("prefill4096", 4096),
+                                    ("prefill4096", 1500)])
+def test_bucket_bit_exact(name, T):
+    w, layer, dl, ol = dev_layer(name)
+    x = mi.make_tokens(w.shape, w.seed, T, zipf=w.zipf)
+    oi, _, _, _ = oracle.router(x, layer["router_w"], w.shape.k)
+    say(f"bucket {name} T={T}")
+    E = w.shape.E
+    counts = torch.empty(E, dtype=torch.int32, device=DEV)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=DEV)
+    perm = torch.empty(T * w.shape.k, dtype=torch.int32, device=DEV)
+    qm.moe_route_bucket(dl.desc, gpu(oi), T, counts, offsets, perm, dl.workspace(T))
+    torch.cuda.synchronize()
+    rc, ro, rp, _ = oracle.bucket(oi, E)
+    assert np.array_equal(counts.cpu().numpy(), rc)
+    assert np.array_equal(offsets.cpu().numpy(), ro)
+    assert np.array_equal(perm.cpu().numpy(), rp)
+
+
+# ---------------------------------------------------------------------------
+# whole layer
+# ---------------------------------------------------------------------------
+
+def check_layer(name, T, path, tol, stream=None, rows=None):
+    w, layer, dl, ol = dev_layer(name)
+    x = mi.make_tokens(w.shape, w.seed, T, stream=w.x_stream if stream is None else stream,
+                       zipf=w.zipf)
+    say(f"forward {name} T={T} path={path}")
+    got, used = run_forward(dl, x, path)
+    if path != qm.MOE_PATH_AUTO:
+        assert used == path
+    sel = np.arange(T) if rows is None else np.asarray(rows)
+    xs = x[sel]
+    oi, ow, _, logits = oracle.router(xs, layer["router_w"], w.shape.k)
+    gi, gw = run_router(dl, x)
+    exact, exempt, wrong = topk_check(gi[sel], oi, logits)
+    assert len(wrong) == 0
+    ref = oracle.forward(ol, xs)
+    err = rel_err(got[sel][exact], ref[exact])
+    say(f"  max|err|/RMS = {err:.3e} over {len(exact)} rows ({len(exempt)} exempt)")
+    assert err <= tol
+    # every row again under the oracle's own routing (covers exempt rows)
+    part, _ = run_shard(dl, x[sel], oi, ow, 0, 1, path)
+    err2 = rel_err(part.cpu().numpy(), ref)
+    assert err2 <= tol
+    return got, used
+
+
+def test_gemv_tiny():
+    check_layer("tiny", 4, qm.MOE_PATH_GEMV, GEMV_TOL)
+
+
+def test_gemv_decode_tokens():
+    for s in range(4):
+        _, used = check_layer("decode", 1, qm.MOE_PATH_AUTO, GEMV_TOL, stream=s)
+        assert used == qm.MOE_PATH_GEMV
+
+
+def test_gemv_batched_decode():
+    check_layer("decode_batched", 32, qm.MOE_PATH_AUTO, GEMV_TOL)
+    check_layer("decode_batched", 7, qm.MOE_PATH_GEMV, GEMV_TOL, stream=5)
+
+
+def test_mfma_tiny_and_ragged():
+    check_layer("tiny", 4, qm.MOE_PATH_MFMA, MFMA_TOL)
+    check_layer("tiny", 131, qm.MOE_PATH_MFMA, MFMA_TOL, stream=3)
+    check_layer("decode", 1, qm.MOE_PATH_MFMA, MFMA_TOL)
+    check_layer("decode", 67, qm.MOE_PATH_MFMA, MFMA_TOL, stream=9)
+
+
+def test_mfma_zipf_512():
+    _, used = check_layer("prefill512_zipf", 512, qm.MOE_PATH_AUTO, MFMA_TOL)
+    assert used == qm.MOE_PATH_MFMA
+
+
+def test_mfma_prefill_4096_sampled():
+    rows = np.unique(np.concatenate([np.arange(0, 4096, 37), [4095, 1, 2, 3]]))
+    check_layer("prefill4096", 4096, qm.MOE_PATH_AUTO, MFMA_TOL, rows=rows)
+
+
+# ---------------------------------------------------------------------------
+# shard mode: partials per shard and their on-device reduction
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name,T,path,tol", [
+    ("tiny", 4, qm.MOE_PATH_GEMV, GEMV_TOL),
+    ("tiny", 4, qm.MOE_PATH_MFMA, MFMA_TOL),
+    ("decode_sharded", 1, qm.MOE_PATH_AUTO, GEMV_TOL),
+    ("decode_batched", 32, qm.MOE_PATH_AUTO, GEMV_TOL),
+    ("prefill4096", 512, qm.MOE_PATH_MFMA, MFMA_TOL),
+])
+def test_shard_partials_and_reduce(name, T, path, tol):
+    w, layer, dl, ol = dev_layer(name)
+    x = mi.make_tokens(w.shape, w.seed, T, stream=w.x_stream, zipf=w.zipf)
+    n = 2
+    say(f"shards {name} T={T} path={path}")
+    # the synchronised router decision, computed once on the device
+    gi, gw = run_router(dl, x)
+    oi, ow, _, logits = oracle.router(x, layer["router_w"], w.shape.k)
+    exact, exempt, wrong = topk_check(gi, oi, logits)
+    assert len(wrong) == 0
+    parts = [run_shard(dl, x, oi, ow, s, n, path)[0] for s in range(n)]
+    full = oracle.forward(ol, x, oi, ow)
+    for s in range(n):
+        ref_s = oracle.forward(ol, x, oi, ow, s, n)
+        assert rel_err(parts[s].cpu().numpy(), ref_s) <= tol * rel_scale(ref_s, full)
+    out = torch.empty((T, dl.H), device=DEV)
+    qm.moe_reduce_partials(parts, T * dl.H, out)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    assert rel_err(o, full) <= tol
+    # the reduction is the plain ascending fp32 sum of the partials
+    p = [q.cpu().numpy() for q in parts]
+    assert np.array_equal(o, p[0] + p[1])
+
+
+def rel_scale(part, full):
+    # a partial's own RMS is smaller than the layer's; measure both against the layer's RMS
+    return float(np.sqrt(np.mean(np.asarray(full, np.float64) ** 2)) /
+                 np.sqrt(np.mean(np.asarray(part, np.float64) ** 2)))
+
+
+# ---------------------------------------------------------------------------
+# determinism and edge cases
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name,T,path", [("decode", 1, qm.MOE_PATH_GEMV),
+                                         ("decode_batched", 32, qm.MOE_PATH_GEMV),
+                                         ("prefill4096", 4096, qm.MOE_PATH_MFMA)])
+def test_bit_identical_reruns(name, T, path):
+    w, layer, dl, ol = dev_layer(name)
+    x = mi.make_tokens(w.shape, w.seed, T, stream=w.x_stream, zipf=w.zipf)
+    say(f"determinism {name} T={T}")
+    a, _ = run_forward(dl, x, path)
+    b, _ = run_forward(dl, x, path)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    assert np.isfinite(a).all()
+
+
+def test_empty_batch_leaves_output_untouched():
+    w, layer, dl, ol = dev_layer("tiny")
+    out = torch.full((1, dl.H), 7.0, device=DEV)
+    x = torch.zeros((1, dl.H), device=DEV)
+    for path in (qm.MOE_PATH_GEMV, qm.MOE_PATH_MFMA):
+        qm.moe_layer_forward(dl.desc, x, 0, out, dl.workspace(1), path=path)
+    torch.cuda.synchronize()
+    assert torch.all(out == 7.0)
+
+
+@pytest.mark.parametrize("E,k,Is", [(8, 8, 128), (1, 1, 0), (4, 3, 0)])
+@pytest.mark.parametrize("path,tol", [(qm.MOE_PATH_GEMV, GEMV_TOL), (qm.MOE_PATH_MFMA, MFMA_TOL)])
+def test_degenerate_layers(E, k, Is, path, tol):
+    """k = E (full softmax mixture), a single dense expert, no shared expert."""
+    shp = mi.LayerShape(H=256, E=E, k=k, I=128, Is=Is)
+    layer = mi.make_layer(shp, seed=21)
+    x = mi.make_tokens(shp, 21, 70)
+    dl = DeviceLayer.from_shape(layer, shp)
+    ol = oracle.Layer.from_shape(layer, shp)
+    say(f"degenerate E={E} k={k} Is={Is} path={path}")
+    got, _ = run_forward(dl, x, path)
+    oi, ow, _, logits = oracle.router(x, layer["router_w"], k)
+    gi, gw = run_router(dl, x)
+    exact, exempt, wrong = topk_check(gi, oi, logits)
+    assert len(wrong) == 0
+    ref = oracle.forward(ol, x)
+    assert rel_err(got[exact], ref[exact]) <= tol
