@@ -13,9 +13,9 @@ before.  Steps are replayed from a HIP graph (one graph of 16 steps).
 Secondary (``prefill``): T = 4096 token rows per step, same layer shape (seed
 4, uniform router), grouped-GEMM path.
 
-Per-kernel durations come from HIP events recorded at the library's phase
-boundaries (moe_opts.phase_events) in an eager pass over the same workload,
-enqueued behind a long matmul so that the events bracket back-to-back kernels.
+Per-kernel durations come from start/stop HIP events that the library attaches
+to each kernel launch (moe_opts.kernel_events, hipExtLaunchKernel) in an eager
+pass over the same workload.
 
 Run: python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -70,29 +70,23 @@ class HipEvents:
             self.hip.hipEventDestroy(ctypes.c_void_p(e))
 
 
-def keep_gpu_busy(torch, ms_target=60.0):
-    """Enqueue ~ms_target of matmul so the host can run ahead of the GPU."""
-    a = torch.randn(8192, 8192, device="cuda")
-    torch.cuda.synchronize()
-    for _ in range(max(1, int(ms_target / 8))):
-        a = a @ a
-        a = a * (1.0 / 8192 ** 0.5)
-    return a
-
-
-def phase_profile(torch, qm, call, n_steps, n_events):
-    """Average duration (ms) of each phase over n_steps eager calls."""
-    ev = HipEvents(n_steps * n_events)
-    _ = keep_gpu_busy(torch)
+def kernel_profile(torch, qm, call, n_steps, names):
+    """Average duration (ms) of each named kernel over n_steps eager calls, from
+    start/stop events the library attaches to those launches (hipExtLaunchKernel
+    records the dispatch's own begin/end)."""
+    from quantized_moe_transformer_amd._lib import KERNEL_IDS, N_KERNEL_IDS
+    per_step = 2 * N_KERNEL_IDS
+    ev = HipEvents(n_steps * per_step)
     for i in range(n_steps):
-        call(i, ev.array(i * n_events, n_events))
+        call(i, ev.array(i * per_step, per_step))
     torch.cuda.synchronize()
-    per = np.zeros((n_steps, n_events - 1))
-    for i in range(n_steps):
-        for p in range(n_events - 1):
-            per[i, p] = ev.ms(i * n_events + p, i * n_events + p + 1)
+    out = {}
+    for n in names:
+        kid = KERNEL_IDS[n]
+        out[n] = float(np.mean([ev.ms(i * per_step + 2 * kid, i * per_step + 2 * kid + 1)
+                                for i in range(n_steps)]))
     ev.close()
-    return per.mean(axis=0), per
+    return out
 
 
 def time_steps(torch, run_step, K):
@@ -162,15 +156,17 @@ def bench_decode(args, torch, qm, mi, DeviceLayer):
     graph_s = time.perf_counter() - t0
     del g
 
-    # per-kernel phases: 0 start, 1 routed, 2 gate/up done, 3 down+combine done
+    # per-kernel durations of the same calls
     nprof = min(args.steps, 256)
-    mean_ms, _ = phase_profile(torch, qm, lambda i, e: step(i, e), nprof, 4)
-    router_ms, gateup_ms, down_ms = (float(v) for v in mean_ms)
+    kms = kernel_profile(torch, qm, lambda i, e: step(i, e), nprof,
+                         ["gemv_front", "gateup_gemv", "down_gemv"])
+    gateup_ms = kms["gateup_gemv"]
 
     E_bytes_gu = 2 * (shp.I * shp.H // 256) * mi.Q4K_SB_BYTES          # gate + up of one expert
     E_bytes_d = (shp.H * shp.I // 256) * mi.Q5K_SB_BYTES
     n_inst = shp.k + 1                                                   # 8 routed + shared
-    gateup_bytes = n_inst * E_bytes_gu + shp.H * 4 + n_inst * shp.I * 4  # weights + x + h
+    # the routed gate/up kernel: 8 experts' gate+up bytes, x, and h written
+    gateup_bytes = shp.k * E_bytes_gu + shp.H * 4 + shp.k * shp.I * 4
     layer_bytes = n_inst * (E_bytes_gu + E_bytes_d) + shp.H * shp.E * 4  # 19,202,048 B
     ms_graph = graph_s / args.steps * 1e3
     res = {
@@ -178,13 +174,12 @@ def bench_decode(args, torch, qm, mi, DeviceLayer):
         "ms_per_step": ms_graph,
         "eager_tokens_per_s": T * args.steps / eager_s,
         "eager_ms_per_step": eager_s / args.steps * 1e3,
-        "phase_ms": {"router_topk": router_ms, "gateup_gemv": gateup_ms,
-                     "down_gemv_combine": down_ms},
+        "kernel_ms": kms,
         "layer_algorithmic_bytes": layer_bytes,
         "layer_hbm_frac_graph": layer_bytes / (ms_graph * 1e-3) / (HBM_PEAK_GBS * 1e9),
-        "layer_hbm_frac_kernels": layer_bytes / (sum(mean_ms) * 1e-3) / (HBM_PEAK_GBS * 1e9),
+        "layer_hbm_frac_kernels": layer_bytes / (sum(kms.values()) * 1e-3) / (HBM_PEAK_GBS * 1e9),
         "roofline": {
-            "kernel": "gateup_gemv_kernel<64,1>",
+            "kernel": "gemv_gateup_kernel<64,1> (8 routed experts)",
             "bound": "hbm",
             "achieved": gateup_bytes / (gateup_ms * 1e-3) / 1e9,
             "peak": HBM_PEAK_GBS,
@@ -221,13 +216,14 @@ def bench_prefill(args, torch, qm, mi, DeviceLayer):
     torch.cuda.synchronize()
     assert set(used) == {qm.MOE_PATH_MFMA}, used
     secs = time_steps(torch, step, K)
-    mean_ms, _ = phase_profile(torch, qm, lambda i, e: step(i, e), K, 6)
-    names = ["router_topk", "convert_bucket", "gemm_gateup", "gemm_down", "combine"]
+    names = ["router_mfma", "router_topk", "x_f16", "bucket_hist", "bucket_scan",
+             "bucket_scatter", "gemm_gateup", "gemm_down", "combine"]
+    kms = kernel_profile(torch, qm, lambda i, e: step(i, e), K, names)
     slots = T * shp.k + T
     flops_gu = 2.0 * 2 * shp.H * shp.I * slots
     flops_d = 2.0 * shp.I * shp.H * slots
-    gu_ms = float(mean_ms[2])
-    d_ms = float(mean_ms[3])
+    gu_ms = kms["gemm_gateup"]
+    d_ms = kms["gemm_down"]
     res = {
         "workload": ("prefill T=4096: same layer shape, seed 4, uniform router, "
                      "grouped fp16-MFMA path, 2 rotating weight copies"),
@@ -237,7 +233,7 @@ def bench_prefill(args, torch, qm, mi, DeviceLayer):
         "steps": K,
         "warmup": W,
         "dtype": "fp16 operands, fp32 accumulate (router fp32)",
-        "phase_ms": {n: float(v) for n, v in zip(names, mean_ms)},
+        "kernel_ms": kms,
         "expert_gflop": (flops_gu + flops_d) / 1e9,
         "expert_mfma_frac": (flops_gu + flops_d) / ((gu_ms + d_ms) * 1e-3) / (FP16_MFMA_PEAK_TFLOPS * 1e12),
         "roofline": {
@@ -261,12 +257,13 @@ def cpu_baseline_decode(layer, pool, budget_s):
     ol = oracle.Layer.from_shape(layer, mi.QWEN35_MOE)
     n = 0
     t0 = time.perf_counter()
-    while n < pool.shape[0] and (time.perf_counter() - t0) < budget_s:
-        oracle.forward(ol, pool[n:n + 1])
+    while (time.perf_counter() - t0) < budget_s:
+        i = n % pool.shape[0]
+        oracle.forward(ol, pool[i:i + 1])
         n += 1
     dt = time.perf_counter() - t0
     return {"value": n / dt, "unit": "tokens/s", "cores": oracle.max_threads(), "kind": "oracle",
-            "sample": f"{n} decode tokens, one T=1 oracle call each (routing, decode of the 9 "
+            "sample": f"{n} decode tokens (cycling a 64-token pool), one T=1 oracle call each (routing, decode of the 9 "
                       f"touched experts, fp64 FFN), {dt:.1f} s"}
 
 
@@ -293,8 +290,8 @@ def main():
     ap.add_argument("--prefill-warmup", type=int, default=3)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle decode work")
-    ap.add_argument("--cpu-prefill-rows", type=int, default=192)
+    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle decode work")
+    ap.add_argument("--cpu-prefill-rows", type=int, default=2048)
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

@@ -100,26 +100,37 @@ typedef struct moe_layer_desc {
 
 /* Options.  `path` forces a compute path (MOE_PATH_*); `path_used`, a HOST
  * pointer that may be NULL, receives the path that ran.
- * `phase_events` (HOST array of n_phase_events hipEvent_t created by the
- * caller, may be NULL) lets a caller time the kernels of a call per region:
- * event i is recorded on the call's stream at phase boundary i, for
- * i < n_phase_events.  Boundaries:
- *   GEMV path: 0 start, 1 after routing, 2 after gate/up+SwiGLU, 3 after down+combine
- *   MFMA path: 0 start, 1 after routing, 2 after fp16 conversion and bucketing,
- *              3 after the gate/up GEMM, 4 after the down GEMM, 5 after the combine
- * (moe_layer_forward_shard has no routing phase: boundary 1 is recorded
- * right after boundary 0). */
+ * `kernel_events` (HOST array of n_kernel_events hipEvent_t created by the
+ * caller, may be NULL) times the kernels of a call: kernel id i (MOE_K_*) is
+ * launched with hipExtLaunchKernel and events 2i / 2i+1 as its start / stop
+ * events, so hipEventElapsedTime(ev[2i], ev[2i+1]) is that launch's own
+ * duration.  Events of kernels the call does not launch are left untouched. */
 typedef struct moe_opts {
     int32_t path;
     int32_t *path_used;
-    void **phase_events;
-    int32_t n_phase_events;
+    void **kernel_events;
+    int32_t n_kernel_events;
 } moe_opts;
+
+/* Kernel ids for moe_opts.kernel_events. */
+#define MOE_K_GEMV_FRONT 0       /* T <= 32: router partial logits; shared-expert gate/up */
+#define MOE_K_ROUTER_MFMA 1      /* fp32-MFMA router logits (large T) */
+#define MOE_K_ROUTER_TOPK 2      /* top-k + weights */
+#define MOE_K_GATEUP_GEMV 3      /* decode: top-k (when routing) + routed gate/up + SwiGLU */
+#define MOE_K_DOWN_GEMV 4        /* decode: down + slot-order combine */
+#define MOE_K_X_F16 5            /* prefill: tokens to fp16 */
+#define MOE_K_BUCKET_HIST 6
+#define MOE_K_BUCKET_SCAN 7
+#define MOE_K_BUCKET_SCATTER 8
+#define MOE_K_GEMM_GATEUP 9      /* prefill: grouped GEMM gate/up + SwiGLU */
+#define MOE_K_GEMM_DOWN 10       /* prefill: grouped GEMM down */
+#define MOE_K_COMBINE 11         /* prefill: slot-order combine */
+#define MOE_K_COUNT 12
 
 /* Bytes of device workspace that router_topk, moe_layer_forward and
  * moe_layer_forward_shard need for T token rows split into num_shards shards
  * (any path).  Host-only; needs no device.  Returns 0 for an invalid
- * description. */
+ * description.  Calls that share one workspace must not overlap in time. */
 size_t moe_workspace_bytes(const moe_layer_desc *desc, int32_t T, int32_t num_shards);
 
 /*
@@ -134,7 +145,8 @@ size_t moe_workspace_bytes(const moe_layer_desc *desc, int32_t T, int32_t num_sh
  *   x         fp32 [T][H]
  *   topk_idx  int32 [T][k] (output)
  *   topk_w    fp32 [T][k] (output)
- *   ws        device workspace of at least moe_workspace_bytes(desc, T, 1) bytes
+ *   ws        device workspace of at least moe_workspace_bytes(desc, T, 1) bytes,
+ *             256-byte aligned
  */
 int router_topk(const moe_layer_desc *desc, const float *x, int32_t T,
                 int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes, void *stream);

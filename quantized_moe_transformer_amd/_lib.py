@@ -17,6 +17,11 @@ LIB_PATH = os.path.join(HERE, "libmoe_hip.so")
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_ELAUNCH, MOE_ENODEVICE = 0, -1, -2, -3, -4, -5
 MOE_PATH_AUTO, MOE_PATH_GEMV, MOE_PATH_MFMA = 0, 1, 2
+# kernel ids for moe_opts.kernel_events (include/moe.h MOE_K_*)
+KERNEL_IDS = {"gemv_front": 0, "router_mfma": 1, "router_topk": 2, "gateup_gemv": 3,
+              "down_gemv": 4, "x_f16": 5, "bucket_hist": 6, "bucket_scan": 7, "bucket_scatter": 8,
+              "gemm_gateup": 9, "gemm_down": 10, "combine": 11}
+N_KERNEL_IDS = 12
 
 
 class MoeError(RuntimeError):
@@ -37,7 +42,7 @@ class moe_layer_desc(ctypes.Structure):
 
 class moe_opts(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("path_used", ctypes.POINTER(ctypes.c_int32)),
-                ("phase_events", ctypes.POINTER(ctypes.c_void_p)), ("n_phase_events", ctypes.c_int32)]
+                ("kernel_events", ctypes.POINTER(ctypes.c_void_p)), ("n_kernel_events", ctypes.c_int32)]
 
 
 def _load():
@@ -123,8 +128,8 @@ def _opts(path: int, events=None):
 
 def moe_layer_forward(desc, x, T, out, ws, path: int = MOE_PATH_AUTO, stream=None,
                       events=None) -> int:
-    """Returns the path that ran.  `events`: optional ctypes array of hipEvent_t
-    recorded at the phase boundaries (see moe_opts in include/moe.h)."""
+    """Returns the path that ran.  `events`: optional ctypes array of hipEvent_t,
+    start/stop pairs per kernel id (moe_opts.kernel_events in include/moe.h)."""
     o, used = _opts(path, events)
     _check("moe_layer_forward", lib.moe_layer_forward(ctypes.byref(desc), _ptr(x), T, _ptr(out),
                                                       ctypes.byref(o), _ptr(ws), _nbytes(ws),

@@ -223,8 +223,11 @@ int router_topk(const moe_layer_desc* desc, const float* x, int32_t T, int32_t* 
     if (!x || !topk_idx || !topk_w || !ws) return MOE_EINVAL;
     const WsLayout L = ws_layout(*desc, T, 1);
     if (ws_bytes < L.total) return MOE_EWORKSPACE;
+    if ((uintptr_t)ws & 255) return MOE_EUNSUPPORTED;
     if ((rc = check_device())) return rc;
-    return launched(launch_router(*desc, x, T, topk_idx, topk_w, (char*)ws, L, (hipStream_t)stream));
+    Ctx c;
+    c.s = (hipStream_t)stream;
+    return launched(launch_router(*desc, x, T, topk_idx, topk_w, (char*)ws, L, c));
 }
 
 static int forward_common(const moe_layer_desc* desc, const float* x, int32_t T,
@@ -244,27 +247,23 @@ static int forward_common(const moe_layer_desc* desc, const float* x, int32_t T,
     const WsLayout L = ws_layout(*desc, T, nshards);
     if (ws_bytes < L.total) return MOE_EWORKSPACE;
     if ((rc = check_device())) return rc;
-    hipStream_t s = (hipStream_t)stream;
     char* wsp = (char*)ws;
-    PhaseMarks pm;
-    if (opts && opts->phase_events && opts->n_phase_events > 0) {
-        pm.ev = opts->phase_events;
-        pm.n = opts->n_phase_events;
-        pm.s = s;
+    Ctx c;
+    c.s = (hipStream_t)stream;
+    if (opts && opts->kernel_events && opts->n_kernel_events > 0) {
+        c.ev = opts->kernel_events;
+        c.n_ev = opts->n_kernel_events;
     }
-    pm.mark(0);
+    if (path == MOE_PATH_GEMV)
+        return launched(launch_gemv(*desc, x, T, idx, w, shard, nshards, out, wsp, L, c, route));
     if (route) {
         int32_t* ridx = reinterpret_cast<int32_t*>(wsp + L.idx);
         float* rw = reinterpret_cast<float*>(wsp + L.w);
-        if (launch_router(*desc, x, T, ridx, rw, wsp, L, s) != hipSuccess) return MOE_ELAUNCH;
+        if (launch_router(*desc, x, T, ridx, rw, wsp, L, c) != hipSuccess) return MOE_ELAUNCH;
         idx = ridx;
         w = rw;
     }
-    pm.mark(1);
-    hipError_t e = path == MOE_PATH_GEMV
-                       ? launch_gemv(*desc, x, T, idx, w, shard, nshards, out, wsp, L, s, pm)
-                       : launch_mfma(*desc, x, T, idx, w, shard, nshards, out, wsp, L, s, pm);
-    return launched(e);
+    return launched(launch_mfma(*desc, x, T, idx, w, shard, nshards, out, wsp, L, c));
 }
 
 int moe_layer_forward(const moe_layer_desc* desc, const float* x, int32_t T, float* out,
@@ -317,13 +316,15 @@ int moe_route_bucket(const moe_layer_desc* desc, const int32_t* topk_idx, int32_
     if (ws_bytes < L.total) return MOE_EWORKSPACE;
     if ((rc = check_device())) return rc;
     hipStream_t s = (hipStream_t)stream;
+    Ctx c;
+    c.s = s;
     char* wsp = (char*)ws;
     int32_t* wc = reinterpret_cast<int32_t*>(wsp + L.counts);
     int32_t* wo = reinterpret_cast<int32_t*>(wsp + L.offsets);
     int32_t* wt = reinterpret_cast<int32_t*>(wsp + L.tile_off);
     int32_t* bh = reinterpret_cast<int32_t*>(wsp + L.bhist);
     if (launch_bucket(topk_idx, T, desc->top_k, desc->n_experts, desc->shared_inter > 0, wc, wo,
-                      wt, perm, bh, s) != hipSuccess)
+                      wt, perm, bh, c) != hipSuccess)
         return MOE_ELAUNCH;
     const size_t E = desc->n_experts;
     if (hipMemcpyAsync(counts, wc, E * 4, hipMemcpyDeviceToDevice, s) != hipSuccess ||

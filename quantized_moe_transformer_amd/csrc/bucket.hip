@@ -118,14 +118,15 @@ bucket_scatter_kernel(const int32_t* __restrict__ idx, int n, int E,
 
 hipError_t launch_bucket(const int32_t* idx, int T, int k, int E, bool shared, int32_t* counts,
                          int32_t* offsets, int32_t* tile_off, int32_t* perm, int32_t* bhist,
-                         hipStream_t s) {
+                         const Ctx& c) {
     const int n = T * k;
     const int nblk = bucket_blocks(T, k);
-    bucket_hist_kernel<<<nblk, kBucketBlock, E * sizeof(int32_t), s>>>(idx, n, E, bhist);
-    bucket_scan_kernel<<<1, 1024, 0, s>>>(nblk, E, T, shared ? 1 : 0, bhist, counts, offsets,
-                                          tile_off);
-    bucket_scatter_kernel<<<nblk, kBucketBlock, kBucketWaves * E * sizeof(int32_t), s>>>(
-        idx, n, E, bhist, perm);
+    launch_k(c, MOE_K_BUCKET_HIST, bucket_hist_kernel, dim3(nblk), dim3(kBucketBlock),
+             (uint32_t)(E * sizeof(int32_t)), idx, n, E, bhist);
+    launch_k(c, MOE_K_BUCKET_SCAN, bucket_scan_kernel, dim3(1), dim3(1024), 0, nblk, E, T,
+             shared ? 1 : 0, bhist, counts, offsets, tile_off);
+    launch_k(c, MOE_K_BUCKET_SCATTER, bucket_scatter_kernel, dim3(nblk), dim3(kBucketBlock),
+             (uint32_t)(kBucketWaves * E * sizeof(int32_t)), idx, n, E, bhist, perm);
     return hipGetLastError();
 }
 

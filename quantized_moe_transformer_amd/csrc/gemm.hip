@@ -324,7 +324,7 @@ combine_kernel(const float* __restrict__ y, const float* __restrict__ ysh,
 
 hipError_t launch_mfma(const moe_layer_desc& d, const float* x, int T, const int32_t* idx,
                        const float* w, int shard, int nshards, float* out, char* ws,
-                       const WsLayout& L, hipStream_t s, const PhaseMarks& pm) {
+                       const WsLayout& L, const Ctx& c) {
     const int H = d.hidden, E = d.n_experts, k = d.top_k;
     const bool shared = d.shared_inter > 0;
     const int Iloc = d.inter / nshards;
@@ -339,27 +339,22 @@ hipError_t launch_mfma(const moe_layer_desc& d, const float* x, int T, const int
     float* ysh = reinterpret_cast<float*>(ws + L.ysh);
 
     const size_t n4 = (size_t)T * H / 4;
-    x_to_f16_kernel<<<(unsigned)((n4 + 255) / 256), 256, 0, s>>>(x, x16, n4);
-    hipError_t err = launch_bucket(idx, T, k, E, shared, counts, offsets, tile_off, perm, bhist, s);
+    launch_k(c, MOE_K_X_F16, x_to_f16_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, x,
+             x16, n4);
+    hipError_t err = launch_bucket(idx, T, k, E, shared, counts, offsets, tile_off, perm, bhist, c);
     if (err != hipSuccess) return err;
-    pm.mark(2);
     // an upper bound on the number of tiles; blocks past the real count exit
     const int max_tiles = (T * k + kTileM - 1) / kTileM + E + (shared ? (T + kTileM - 1) / kTileM : 0);
     const int Imax = (d.inter > d.shared_inter ? d.inter : d.shared_inter) / nshards;
-    dim3 g1(max_tiles, (Imax + 63) / 64);
-    gemm_gateup_kernel<<<g1, 256, 0, s>>>(x16, T, H, perm, offsets, tile_off, E, k, d.gate_q,
-                                          d.up_q, d.sh_gate_q, d.sh_up_q, d.inter,
-                                          d.shared_inter, shard, nshards, h16, Iloc);
-    pm.mark(3);
-    dim3 g2(max_tiles, (H + 127) / 128);
-    gemm_down_kernel<<<g2, 256, 0, s>>>(h16, Iloc, T, H, perm, offsets, tile_off, E, k, d.down_q,
-                                        d.sh_down_q, d.inter, d.shared_inter, shard, nshards, w,
-                                        d.shared_weight, y, ysh);
-    pm.mark(4);
+    launch_k(c, MOE_K_GEMM_GATEUP, gemm_gateup_kernel, dim3(max_tiles, (Imax + 63) / 64), dim3(256),
+             0, x16, T, H, perm, offsets, tile_off, E, k, d.gate_q, d.up_q, d.sh_gate_q, d.sh_up_q,
+             d.inter, d.shared_inter, shard, nshards, h16, Iloc);
+    launch_k(c, MOE_K_GEMM_DOWN, gemm_down_kernel, dim3(max_tiles, (H + 127) / 128), dim3(256), 0,
+             h16, Iloc, T, H, perm, offsets, tile_off, E, k, d.down_q, d.sh_down_q, d.inter,
+             d.shared_inter, shard, nshards, w, d.shared_weight, y, ysh);
     const size_t nc = (size_t)T * H / 4;
-    combine_kernel<<<(unsigned)((nc + 255) / 256), 256, 0, s>>>(y, ysh, idx, T, H, E, k,
-                                                               shared ? 1 : 0, out);
-    pm.mark(5);
+    launch_k(c, MOE_K_COMBINE, combine_kernel, dim3((unsigned)((nc + 255) / 256)), dim3(256), 0, y,
+             ysh, idx, T, H, E, k, shared ? 1 : 0, out);
     return hipGetLastError();
 }
 

@@ -3,10 +3,19 @@
 // At one (or a few) token rows the layer is a stream of packed weight bytes:
 // each byte is read once and used once, so the work is bound by HBM
 // bandwidth (page "Distributed CPU: Zip Fusion Beyond Tensor Parallelism",
-// section "Decode vs Prefill: Same Weights, Different Bottlenecks").  The
-// kernels stream the superblocks of the selected experts with 16-byte loads,
-// unpack the 6-bit scales/mins and the codes in registers and reduce across
-// lanes of the wavefront.
+// section "Decode vs Prefill: Same Weights, Different Bottlenecks").  On this
+// chip every dependent kernel adds a fixed ~2 us to a step, so the layer runs
+// as three kernels, each streaming its share of the bytes:
+//
+//   front   the router's split-K partial logits and, side by side in the same
+//           grid, the shared expert's gate/up + SwiGLU, which needs no routing;
+//   gateup  every workgroup first sums its token's partial logits in a fixed
+//           order and runs the top-k (one wave, identical in every workgroup of
+//           the token), then gate/up + SwiGLU of its routed expert's rows;
+//   down    down projections, one wave per slot, slot results added in the
+//           selected-slot order with the shared expert last (page "CKE Zip:
+//           From Splitting Tokens To Splitting Qwen3.5 Weights", section "A
+//           Separate Decode Result Shows Why Axis Choice Matters").
 //
 // Work unit of a lane: a 16-byte piece of a superblock's codes -- 32 weights,
 // 16 from sub-block 2c and 16 from sub-block 2c+1 -- plus the superblock's
@@ -14,38 +23,42 @@
 // lanes cover one superblock, so the lanes of a wave read one contiguous run
 // of a row.  The per-sub-block scale factors out of the dot product:
 //   sum_i w_i x_i = d*sc_a*sum(q x)_a + d*sc_b*sum(q x)_b - dmin*(m_a sum x_a + m_b sum x_b)
-//
-//   gateup_gemv  h[p][r] = silu(Wg[r] . x) * (Wu[r] . x) for every selected
-//                expert instance p = (token, slot) and the shared expert
-//   down_gemv    out[t][o] = sum_j w_j (Wd_j[o] . h_j) + sw (Wd_sh[o] . h_sh),
-//                slots in selected-slot order, shared expert last (page "CKE
-//                Zip ...", section "A Separate Decode Result Shows Why Axis
-//                Choice Matters": routes merged in the original slot order)
+// Every weight load of a wave is issued before the first one is consumed.
 #include "moe_internal.h"
+#include "topk.h"
 
 namespace moe {
 
+// ---------------------------------------------------------------------------
+// lane-level pieces
+// ---------------------------------------------------------------------------
+
 // Partial dot product of one lane's piece.  xl/xh: the 16 activations under
 // the low / high nibbles; sl/sh their sums.  qh: the 16 high-bit bytes of the
-// piece (5-bit format) or nullptr-equivalent (HIGH = false).
+// piece (5-bit format only).  Codes are unpacked four at a time from masked
+// words (one byte-convert per code).
 template <bool HIGH>
 __device__ __forceinline__ float piece_dot(const SbHead& h, const uint4& qs, const uint4& qh, int c,
                                            const float* xl, const float* xh, float sl, float sh) {
     float sca, ma, scb, mb;
     sub_scale_min(h, 2 * c, sca, ma);
     sub_scale_min(h, 2 * c + 1, scb, mb);
+    const uint32_t qw[4] = {qs.x, qs.y, qs.z, qs.w};
+    const uint32_t hw[4] = {qh.x, qh.y, qh.z, qh.w};
     float dl = 0.f, dh = 0.f;
 #pragma unroll
-    for (int b = 0; b < 16; ++b) {
-        const uint32_t byte = piece_byte(qs, b);
-        uint32_t ql = byte & 15u, qq = byte >> 4;
+    for (int wi = 0; wi < 4; ++wi) {
+        uint32_t lo = qw[wi] & 0x0f0f0f0fu;
+        uint32_t hi = (qw[wi] >> 4) & 0x0f0f0f0fu;
         if (HIGH) {
-            const uint32_t hb = piece_byte(qh, b);
-            ql |= ((hb >> (2 * c)) & 1u) << 4;
-            qq |= ((hb >> (2 * c + 1)) & 1u) << 4;
+            lo |= ((hw[wi] >> (2 * c)) & 0x01010101u) << 4;
+            hi |= ((hw[wi] >> (2 * c + 1)) & 0x01010101u) << 4;
         }
-        dl = __builtin_fmaf((float)ql, xl[b], dl);
-        dh = __builtin_fmaf((float)qq, xh[b], dh);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            dl = __builtin_fmaf((float)((lo >> (8 * b)) & 0xffu), xl[4 * wi + b], dl);
+            dh = __builtin_fmaf((float)((hi >> (8 * b)) & 0xffu), xh[4 * wi + b], dh);
+        }
     }
     return h.d * (sca * dl + scb * dh) - h.dmin * (ma * sl + mb * sh);
 }
@@ -61,179 +74,488 @@ __device__ __forceinline__ void load16(const float* p, float* v) {
     }
 }
 
+// 16-byte load of streamed-once weight bytes, marked non-temporal.
+__device__ __forceinline__ uint4 stream_load(const uint8_t* p) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// Sum of each of 8 values over the 64 lanes of a wave, by exchanging halves
+// (values 0-3 stay on lanes with bit 5 clear, 4-7 on the others, and so on):
+// 11 cross-lane moves instead of 48.  Lane l ends with the sum of value
+// 4*b5 + 2*b4 + b3 (b = bits of l).  Fixed order: deterministic.
+__device__ __forceinline__ float wave_sum8(float v[8]) {
+    const int lane = threadIdx.x & 63;
+    float a[4], b[2];
+    const bool u5 = lane & 32, u4 = lane & 16, u3 = lane & 8;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float keep = u5 ? v[4 + i] : v[i];
+        const float give = u5 ? v[i] : v[4 + i];
+        a[i] = keep + __shfl_xor(give, 32, 64);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const float keep = u4 ? a[2 + i] : a[i];
+        const float give = u4 ? a[i] : a[2 + i];
+        b[i] = keep + __shfl_xor(give, 16, 64);
+    }
+    float s = (u3 ? b[1] : b[0]) + __shfl_xor(u3 ? b[0] : b[1], 8, 64);
+    s += __shfl_xor(s, 4, 64);
+    s += __shfl_xor(s, 2, 64);
+    s += __shfl_xor(s, 1, 64);
+    return s;
+}
+
+// ---------------------------------------------------------------------------
+// gate/up + SwiGLU for a group of rows of one expert instance
+// ---------------------------------------------------------------------------
+
+constexpr int kGuWaves = 2;   // waves per gate/up workgroup
+constexpr int kGuSteps = 4;   // row steps per wave (each step: gate row + up row)
+
+// The activations under one lane's pieces (they do not depend on the expert).
+template <int LPR, int NSBL>
+struct XRegs {
+    float xl[NSBL][16], xh[NSBL][16], sl[NSBL], sh[NSBL];
+
+    __device__ __forceinline__ void load(const float* __restrict__ xt) {
+        const int task = (threadIdx.x & 63) % LPR;
+        const int sbi = task >> 3, piece = task & 7, c = piece >> 1, hh = piece & 1;
+#pragma unroll
+        for (int it = 0; it < NSBL; ++it) {
+            const int sb = sbi + (LPR / 8) * it;
+            const float* xp = xt + sb * kSbWeights + 64 * c + 16 * hh;
+            load16(xp, xl[it]);
+            load16(xp + 32, xh[it]);
+        }
+    }
+    __device__ __forceinline__ void sums() {
+#pragma unroll
+        for (int it = 0; it < NSBL; ++it) {
+            float a = 0.f, b = 0.f;
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                a += xl[it][q];
+                b += xh[it][q];
+            }
+            sl[it] = a;
+            sh[it] = b;
+        }
+    }
+};
+
 // LPR: lanes per row (8 * superblocks per row, capped at 64); NSBL:
 // superblocks per lane per row (H / 2048 when LPR = 64, else 1).
+// Rows [rbase, rbase + kGuSteps * 64/LPR) of the instance, h written to hrow.
 template <int LPR, int NSBL>
-__global__ void __launch_bounds__(256)
-gateup_gemv_kernel(const uint8_t* __restrict__ gate, const uint8_t* __restrict__ up,
-                   const uint8_t* __restrict__ sh_gate, const uint8_t* __restrict__ sh_up,
-                   const float* __restrict__ x, const int32_t* __restrict__ idx, int H, int E,
-                   int k, int I, int Is, int shard, int nshards, int nslot,
-                   float* __restrict__ hbuf, int hstride) {
+__device__ __forceinline__ void gateup_rows(const uint8_t* __restrict__ G,
+                                            const uint8_t* __restrict__ U, int H, int Iloc,
+                                            int i0, XRegs<LPR, NSBL>& X, int rbase,
+                                            float* __restrict__ hrow) {
     constexpr int RS = 64 / LPR;   // rows side by side in a wave
-    constexpr int RPW = 2;         // row steps per wave
-    const int p = blockIdx.y;
-    const int t = p / nslot, j = p % nslot;
-    const uint8_t *G, *U;
-    int Iexp;
-    if (j < k) {
-        const int e = idx[(size_t)t * k + j];
-        if ((unsigned)e >= (unsigned)E) return;
-        const size_t mat = (size_t)I * H / kSbWeights * kQ4Bytes;
-        G = gate + (size_t)e * mat;
-        U = up + (size_t)e * mat;
-        Iexp = I;
-    } else {
-        G = sh_gate;
-        U = sh_up;
-        Iexp = Is;
-    }
-    const int Iloc = Iexp / nshards, i0 = shard * Iloc;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int lane = threadIdx.x & 63;
     const int rslot = lane / LPR, task = lane % LPR;
     const int sbi = task >> 3, piece = task & 7, c = piece >> 1, hh = piece & 1;
     const int nsb_row = H / kSbWeights;
 
-    const float* xt = x + (size_t)t * H;
-    float xl[NSBL][16], xh[NSBL][16], sl[NSBL], sh[NSBL];
+    SbHead hg[kGuSteps][NSBL], hu[kGuSteps][NSBL];
+    uint4 qg[kGuSteps][NSBL], qu[kGuSteps][NSBL];
 #pragma unroll
-    for (int it = 0; it < NSBL; ++it) {
-        const int sb = sbi + (LPR / 8) * it;
-        const float* xp = xt + sb * kSbWeights + 64 * c + 16 * hh;
-        load16(xp, xl[it]);
-        load16(xp + 32, xh[it]);
-        float a = 0.f, b = 0.f;
+    for (int st = 0; st < kGuSteps; ++st) {
+        const int r = min(rbase + st * RS + rslot, Iloc - 1);   // tail rows clamped, discarded
+        const size_t row = (size_t)(i0 + r) * nsb_row;
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            a += xl[it][q];
-            b += xh[it][q];
+        for (int it = 0; it < NSBL; ++it) {
+            const int sb = sbi + (LPR / 8) * it;
+            const uint8_t* gs = G + (row + sb) * kQ4Bytes;
+            const uint8_t* us = U + (row + sb) * kQ4Bytes;
+            qg[st][it] = stream_load(gs + 16 + 32 * c + 16 * hh);
+            qu[st][it] = stream_load(us + 16 + 32 * c + 16 * hh);
+            hg[st][it] = load_head(gs);
+            hu[st][it] = load_head(us);
         }
-        sl[it] = a;
-        sh[it] = b;
     }
-
-    const int rbase = (blockIdx.x * 4 + wave) * RPW * RS;
-    float g[RPW], u[RPW];
+    X.sums();
+    float (&xl)[NSBL][16] = X.xl;
+    float (&xh)[NSBL][16] = X.xh;
+    float (&sl)[NSBL] = X.sl;
+    float (&sh)[NSBL] = X.sh;
+    float v[2 * kGuSteps];
 #pragma unroll
-    for (int st = 0; st < RPW; ++st) {
-        const int r = rbase + st * RS + rslot;
+    for (int st = 0; st < kGuSteps; ++st) {
         float pg = 0.f, pu = 0.f;
-        if (r < Iloc) {
-            const size_t row = (size_t)(i0 + r) * nsb_row;
 #pragma unroll
-            for (int it = 0; it < NSBL; ++it) {
-                const int sb = sbi + (LPR / 8) * it;
-                const uint8_t* gs = G + (row + sb) * kQ4Bytes;
-                const uint8_t* us = U + (row + sb) * kQ4Bytes;
-                const SbHead hg = load_head(gs);
-                const SbHead hu = load_head(us);
-                const uint4 qg = *reinterpret_cast<const uint4*>(gs + 16 + 32 * c + 16 * hh);
-                const uint4 qu = *reinterpret_cast<const uint4*>(us + 16 + 32 * c + 16 * hh);
-                pg += piece_dot<false>(hg, qg, qg, c, xl[it], xh[it], sl[it], sh[it]);
-                pu += piece_dot<false>(hu, qu, qu, c, xl[it], xh[it], sl[it], sh[it]);
-            }
+        for (int it = 0; it < NSBL; ++it) {
+            pg += piece_dot<false>(hg[st][it], qg[st][it], qg[st][it], c, xl[it], xh[it], sl[it], sh[it]);
+            pu += piece_dot<false>(hu[st][it], qu[st][it], qu[st][it], c, xl[it], xh[it], sl[it], sh[it]);
         }
-        g[st] = pg;
-        u[st] = pu;
+        v[2 * st] = pg;
+        v[2 * st + 1] = pu;
     }
+    if (LPR == 64) {
+        // one row per step: value 2*st (+1 for up) ends on lanes with
+        // bits (5,4,3) = (st>>1, st&1, 0 gate / 1 up)
+        const float s = wave_sum8(v);
+        const float other = __shfl_xor(s, 8, 64);
+        const int st = ((lane >> 5) << 1) | ((lane >> 4) & 1);
+        const int r = rbase + st;
+        if ((lane & 15) == 0 && r < Iloc) hrow[r] = silu_f(s) * other;
+    } else {
 #pragma unroll
-    for (int st = 0; st < RPW; ++st) {
-        const float gs = wave_sum_group(g[st], LPR);
-        const float us = wave_sum_group(u[st], LPR);
-        const int r = rbase + st * RS + rslot;
-        if (task == 0 && r < Iloc) hbuf[(size_t)p * hstride + r] = silu_f(gs) * us;
+        for (int st = 0; st < kGuSteps; ++st) {
+            const float gs = wave_sum_group(v[2 * st], LPR);
+            const float us = wave_sum_group(v[2 * st + 1], LPR);
+            const int r = rbase + st * RS + rslot;
+            if (task == 0 && r < Iloc) hrow[r] = silu_f(gs) * us;
+        }
     }
 }
 
-// One wave per RSd = 64 / LPRd output rows of one token; LPRd = I_loc / 32.
-__global__ void __launch_bounds__(64)
-down_gemv_kernel(const uint8_t* __restrict__ down, const uint8_t* __restrict__ sh_down,
-                 const float* __restrict__ hbuf, int hstride, const int32_t* __restrict__ idx,
-                 const float* __restrict__ w, float sw, int H, int E, int k, int I, int Is,
-                 int shard, int nshards, int nslot, int lprd, float* __restrict__ out) {
+// ---------------------------------------------------------------------------
+// kernel arguments
+// ---------------------------------------------------------------------------
+
+struct GemvArgs {
+    const uint8_t *gate, *up, *down, *sh_gate, *sh_up, *sh_down;
+    const float* router_w;
+    const float* x;
+    int T, H, E, k, I, Is, shard, nshards, nslot;
+    float sw;
+    const int32_t* idx;   // routing read by gateup (when given) and by down
+    const float* w;
+    float* hbuf;          // [T*nslot][Iloc]
+    int hstride;
+    float* part;          // [T][E][ks] router partial logits
+    int route;            // gateup computes the top-k from `part` ...
+    int32_t* idx_out;     // ... and its first workgroup per token writes it here
+    float* w_out;
+    int n_router_blocks;  // front kernel: router workgroups (0: none)
+    int shared_rows_blocks;
+    float* out;
+};
+
+constexpr int kRtE = 32;       // experts per router workgroup
+constexpr int kRtMaxRows = 512;   // rows of H per split (H / kRouterSplits) at most
+
+// ---------------------------------------------------------------------------
+// front: router partial logits and the shared expert's gate/up
+// ---------------------------------------------------------------------------
+
+// Partial logits of TT tokens x kRtE experts over H / kRouterSplits rows of
+// H: eight row groups of 32 lanes (one lane per expert, 128-byte rows of the
+// router matrix), summed in a fixed order in LDS.
+template <int TT>
+__device__ __forceinline__ void router_role(const GemvArgs& a, int rb) {
+    __shared__ float xs[TT][kRtMaxRows];
+    __shared__ float red[8][TT][kRtE];
+    constexpr int KS = kRouterSplits;
+    const int n_ec = (a.E + kRtE - 1) / kRtE;
+    const int tb = rb / (n_ec * KS);
+    const int rem = rb % (n_ec * KS);
+    const int ec = rem / KS, ks = rem % KS;
+    const int t0 = tb * TT;
+    const int nt = min(TT, a.T - t0);
+    const int rows = a.H / KS;            // a multiple of 32
+    const int h0 = ks * rows;
+    const int tid = threadIdx.x;
+    for (int i = tid; i < TT * rows; i += blockDim.x) {
+        const int tt = i / rows, hh = i % rows;
+        xs[tt][hh] = tt < nt ? a.x[(size_t)(t0 + tt) * a.H + h0 + hh] : 0.f;
+    }
+    __syncthreads();
+    const int el = tid & 31, g = tid >> 5;   // expert within chunk, row group (8)
+    const int e = min(ec * kRtE + el, a.E - 1);
+    float acc[TT];
+#pragma unroll
+    for (int i = 0; i < TT; ++i) acc[i] = 0.f;
+    for (int r0 = 0; r0 < rows; r0 += 32) {   // 4 rows per row group per pass
+        float wv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wv[i] = a.router_w[(size_t)(h0 + r0 + g + 8 * i) * a.E + e];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int tt = 0; tt < TT; ++tt)
+                acc[tt] = __builtin_fmaf(xs[tt][r0 + g + 8 * i], wv[i], acc[tt]);
+    }
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) red[g][tt][el] = acc[tt];
+    __syncthreads();
+    if (tid < TT * kRtE) {
+        const int tt = tid / kRtE, ee = tid % kRtE;
+        const int eg = ec * kRtE + ee;
+        if (tt < nt && eg < a.E) {
+            float s = red[0][tt][ee];
+#pragma unroll
+            for (int q = 1; q < 8; ++q) s += red[q][tt][ee];
+            a.part[((size_t)(t0 + tt) * a.E + eg) * KS + ks] = s;
+        }
+    }
+}
+
+template <int LPR, int NSBL, int TT>
+__global__ void __launch_bounds__(256)
+gemv_front_kernel(GemvArgs a) {
+    const int b = blockIdx.x;
+    if (b < a.n_router_blocks) {
+        router_role<TT>(a, b);
+        return;
+    }
+    // shared expert: blocks per token = shared_rows_blocks, 4 waves each
+    const int sb = b - a.n_router_blocks;
+    const int t = sb / a.shared_rows_blocks;
+    const int rblk = sb % a.shared_rows_blocks;
+    const int Iloc = a.Is / a.nshards, i0 = a.shard * Iloc;
+    const int wave = threadIdx.x >> 6;
+    constexpr int rows_per_wave = kGuSteps * (64 / LPR);
+    const int rbase = (rblk * 4 + wave) * rows_per_wave;
+    if (rbase >= Iloc) return;
+    const int p = t * a.nslot + a.k;
+    XRegs<LPR, NSBL> X;
+    X.load(a.x + (size_t)t * a.H);
+    gateup_rows<LPR, NSBL>(a.sh_gate, a.sh_up, a.H, Iloc, i0, X, rbase,
+                           a.hbuf + (size_t)p * a.hstride);
+}
+
+// routed experts: grid (row blocks, T*k)
+template <int LPR, int NSBL>
+__global__ void __launch_bounds__(64 * kGuWaves)
+gemv_gateup_kernel(GemvArgs a) {
+    __shared__ int32_t s_idx[16];
+    __shared__ float s_w[16];
+    const int q = blockIdx.y;
+    const int t = q / a.k, j = q % a.k;
+    XRegs<LPR, NSBL> X;
+    X.load(a.x + (size_t)t * a.H);   // independent of the routing: in flight during the top-k
+    int e;
+    if (a.route) {
+        if (threadIdx.x < 64) wave_topk<4, kRouterSplits>(a.part, a.E, a.k, t, s_idx, s_w);   // E <= 256
+        __syncthreads();
+        e = s_idx[j];
+        if (blockIdx.x == 0 && j == 0 && threadIdx.x < a.k) {
+            a.idx_out[(size_t)t * a.k + threadIdx.x] = s_idx[threadIdx.x];
+            a.w_out[(size_t)t * a.k + threadIdx.x] = s_w[threadIdx.x];
+        }
+    } else {
+        e = a.idx[(size_t)t * a.k + j];
+    }
+    if ((unsigned)e >= (unsigned)a.E) return;
+    const size_t mat = (size_t)a.I * a.H / kSbWeights * kQ4Bytes;
+    const int Iloc = a.I / a.nshards, i0 = a.shard * Iloc;
+    const int wave = threadIdx.x >> 6;
+    constexpr int rows_per_wave = kGuSteps * (64 / LPR);
+    const int rbase = (blockIdx.x * kGuWaves + wave) * rows_per_wave;
+    if (rbase >= Iloc) return;
+    const int p = t * a.nslot + j;
+    gateup_rows<LPR, NSBL>(a.gate + (size_t)e * mat, a.up + (size_t)e * mat, a.H, Iloc, i0, X,
+                           rbase, a.hbuf + (size_t)p * a.hstride);
+}
+
+// ---------------------------------------------------------------------------
+// down + slot-order combine
+// ---------------------------------------------------------------------------
+
+constexpr int kDnPasses = 2;   // row passes per wave in the down kernel
+
+// Block: one wave per slot (nw = min(nslot, 16) waves, slot j on wave j % nw),
+// kDnPasses * (64 / lprd) output rows of one token; lprd = I_loc / 32.
+__global__ void __launch_bounds__(1024)
+gemv_down_kernel(GemvArgs a, int lprd) {
+    __shared__ float ys[17][kDnPasses * 64];
     const int t = blockIdx.y;
-    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int nw = blockDim.x >> 6;
+    const int rs = 64 / lprd;                     // rows per pass
     const int rslot = lane / lprd, task = lane % lprd;
     const int cg = task >> 1, hh = task & 1;
-    const int o = blockIdx.x * (64 / lprd) + rslot;
-    float acc = 0.f;
-    for (int j = 0; j < nslot; ++j) {
+    const int obase = blockIdx.x * kDnPasses * rs;
+    const int H = a.H;
+    for (int j = wave; j < a.nslot; j += nw) {
         const uint8_t* D;
-        float wj;
         int Iexp;
-        if (j < k) {
-            const int e = idx[(size_t)t * k + j];
-            if ((unsigned)e >= (unsigned)E) continue;
-            D = down + (size_t)e * ((size_t)H * I / kSbWeights * kQ5Bytes);
-            wj = w[(size_t)t * k + j];
-            Iexp = I;
+        bool valid = true;
+        if (j < a.k) {
+            const int e = a.idx[(size_t)t * a.k + j];
+            valid = (unsigned)e < (unsigned)a.E;
+            D = a.down + (size_t)(valid ? e : 0) * ((size_t)H * a.I / kSbWeights * kQ5Bytes);
+            Iexp = a.I;
         } else {
-            D = sh_down;
-            wj = sw;
-            Iexp = Is;
+            D = a.sh_down;
+            Iexp = a.Is;
         }
-        const int Iloc = Iexp / nshards, i0 = shard * Iloc;
-        float part = 0.f;
-        if (o < H) {
-            const size_t base = (size_t)o * Iexp + i0 + 64 * cg;
-            const int c = (int)((base & 255) >> 6);
-            const uint8_t* sb = D + (base >> 8) * kQ5Bytes;
-            const SbHead hd = load_head(sb);
-            const uint4 qh = *reinterpret_cast<const uint4*>(sb + 16 + 16 * hh);
-            const uint4 qs = *reinterpret_cast<const uint4*>(sb + 48 + 32 * c + 16 * hh);
-            const float* hp = hbuf + (size_t)(t * nslot + j) * hstride + 64 * cg + 16 * hh;
-            float hl[16], hu[16];
-            load16(hp, hl);
-            load16(hp + 32, hu);
-            float a = 0.f, b = 0.f;
+        const int Iloc = Iexp / a.nshards, i0 = a.shard * Iloc;
+        SbHead hd[kDnPasses];
+        uint4 qh[kDnPasses], qs[kDnPasses];
+        int cc[kDnPasses];
 #pragma unroll
-            for (int q = 0; q < 16; ++q) {
-                a += hl[q];
-                b += hu[q];
-            }
-            part = piece_dot<true>(hd, qs, qh, c, hl, hu, a, b);
+        for (int ps = 0; ps < kDnPasses; ++ps) {
+            const int o = min(obase + ps * rs + rslot, H - 1);
+            const size_t base = (size_t)o * Iexp + i0 + 64 * cg;
+            cc[ps] = (int)((base & 255) >> 6);
+            const uint8_t* sb = D + (base >> 8) * kQ5Bytes;
+            qs[ps] = stream_load(sb + 48 + 32 * cc[ps] + 16 * hh);
+            qh[ps] = stream_load(sb + 16 + 16 * hh);
+            hd[ps] = load_head(sb);
         }
-        const float y = wave_sum_group(part, lprd);
-        acc = __builtin_fmaf(wj, y, acc);
+        const float* hp = a.hbuf + (size_t)(t * a.nslot + j) * a.hstride + 64 * cg + 16 * hh;
+        float hl[16], hu[16];
+        load16(hp, hl);
+        load16(hp + 32, hu);
+        float sa = 0.f, sb2 = 0.f;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            sa += hl[q];
+            sb2 += hu[q];
+        }
+#pragma unroll
+        for (int ps = 0; ps < kDnPasses; ++ps) {
+            const float part = piece_dot<true>(hd[ps], qs[ps], qh[ps], cc[ps], hl, hu, sa, sb2);
+            const float y = wave_sum_group(part, lprd);
+            if (task == 0) ys[j][ps * rs + rslot] = valid ? y : 0.f;
+        }
     }
-    if (task == 0 && o < H) out[(size_t)t * H + o] = acc;
+    __syncthreads();
+    if (threadIdx.x < kDnPasses * rs) {
+        const int r = threadIdx.x;
+        const int o = obase + r;
+        if (o < H) {
+            float acc = 0.f;
+            for (int j = 0; j < a.nslot; ++j) {
+                float wj;
+                if (j < a.k) {
+                    const int e = a.idx[(size_t)t * a.k + j];
+                    wj = (unsigned)e < (unsigned)a.E ? a.w[(size_t)t * a.k + j] : 0.f;
+                } else {
+                    wj = a.sw;
+                }
+                acc = __builtin_fmaf(wj, ys[j][r], acc);
+            }
+            a.out[(size_t)t * H + o] = acc;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+
+static GemvArgs base_args(const moe_layer_desc& d, const float* x, int T, int shard, int nshards) {
+    GemvArgs a = {};
+    a.gate = d.gate_q;
+    a.up = d.up_q;
+    a.down = d.down_q;
+    a.sh_gate = d.sh_gate_q;
+    a.sh_up = d.sh_up_q;
+    a.sh_down = d.sh_down_q;
+    a.router_w = d.router_w;
+    a.x = x;
+    a.T = T;
+    a.H = d.hidden;
+    a.E = d.n_experts;
+    a.k = d.top_k;
+    a.I = d.inter;
+    a.Is = d.shared_inter;
+    a.shard = shard;
+    a.nshards = nshards;
+    a.nslot = d.top_k + (d.shared_inter > 0 ? 1 : 0);
+    a.sw = d.shared_weight;
+    return a;
 }
 
 template <int LPR, int NSBL>
-static void launch_gateup(const moe_layer_desc& d, const float* x, int T, const int32_t* idx,
-                          int shard, int nshards, int nslot, float* hbuf, int hstride,
-                          hipStream_t s) {
-    constexpr int rows_per_block = 4 * 2 * (64 / LPR);
-    const int Imax = (d.inter > d.shared_inter ? d.inter : d.shared_inter) / nshards;
-    dim3 grid((Imax + rows_per_block - 1) / rows_per_block, T * nslot);
-    gateup_gemv_kernel<LPR, NSBL><<<grid, 256, 0, s>>>(
-        d.gate_q, d.up_q, d.sh_gate_q, d.sh_up_q, x, idx, d.hidden, d.n_experts, d.top_k,
-        d.inter, d.shared_inter, shard, nshards, nslot, hbuf, hstride);
+static void launch_front_t(const GemvArgs& a, int n_shared_blocks, const Ctx& c) {
+    const dim3 grid(a.n_router_blocks + n_shared_blocks);
+    if (a.T == 1)
+        launch_k(c, MOE_K_GEMV_FRONT, gemv_front_kernel<LPR, NSBL, 1>, grid, dim3(256), 0, a);
+    else
+        launch_k(c, MOE_K_GEMV_FRONT, gemv_front_kernel<LPR, NSBL, 4>, grid, dim3(256), 0, a);
 }
+
+template <int LPR, int NSBL>
+static void launch_gateup_t(const GemvArgs& a, const Ctx& c) {
+    constexpr int rows_per_block = kGuWaves * kGuSteps * (64 / LPR);
+    const int Iloc = a.I / a.nshards;
+    const dim3 grid((Iloc + rows_per_block - 1) / rows_per_block, a.T * a.k);
+    launch_k(c, MOE_K_GATEUP_GEMV, gemv_gateup_kernel<LPR, NSBL>, grid, dim3(64 * kGuWaves), 0, a);
+}
+
+#define MOE_DISPATCH_H(nsb, F, ...)                                  \
+    switch (nsb) {                                                   \
+        case 1: F<8, 1>(__VA_ARGS__); break;                         \
+        case 2: F<16, 1>(__VA_ARGS__); break;                        \
+        case 4: F<32, 1>(__VA_ARGS__); break;                        \
+        case 8: F<64, 1>(__VA_ARGS__); break;                        \
+        case 16: F<64, 2>(__VA_ARGS__); break;                       \
+        default: return hipErrorInvalidValue;                        \
+    }
+
+static int lanes_per_row(int nsb) { return nsb >= 8 ? 64 : 8 * nsb; }
+
+// Front kernel: router partials (T <= kGemvMaxT) and/or the shared expert's gate/up.
+static hipError_t launch_front(GemvArgs& a, bool route, bool shared, const WsLayout& L, char* ws,
+                               const Ctx& c) {
+    const int nsb = a.H / kSbWeights;
+    a.part = reinterpret_cast<float*>(ws + L.router_part);
+    const int TT = a.T == 1 ? 1 : 4;
+    const int n_ec = (a.E + kRtE - 1) / kRtE;
+    a.n_router_blocks = route ? ((a.T + TT - 1) / TT) * n_ec * kRouterSplits : 0;
+    int n_shared = 0;
+    if (shared) {
+        const int rows_per_block = 4 * kGuSteps * (64 / lanes_per_row(nsb));
+        const int Iloc = a.Is / a.nshards;
+        a.shared_rows_blocks = (Iloc + rows_per_block - 1) / rows_per_block;
+        n_shared = a.shared_rows_blocks * a.T;
+    }
+    if (a.n_router_blocks + n_shared == 0) return hipSuccess;
+    MOE_DISPATCH_H(nsb, launch_front_t, a, n_shared, c);
+    return hipGetLastError();
+}
+
+// Router partial logits only (router_topk at T <= kGemvMaxT).
+hipError_t launch_router_small(const moe_layer_desc& d, const float* x, int T, char* ws,
+                               const WsLayout& L, const Ctx& c) {
+    GemvArgs a = base_args(d, x, T, 0, 1);
+    return launch_front(a, true, false, L, ws, c);
+}
+
+hipError_t launch_router(const moe_layer_desc& d, const float* x, int T, int32_t* idx, float* w,
+                         char* ws, const WsLayout& L, const Ctx& c);   // router.hip
 
 hipError_t launch_gemv(const moe_layer_desc& d, const float* x, int T, const int32_t* idx,
                        const float* w, int shard, int nshards, float* out, char* ws,
-                       const WsLayout& L, hipStream_t s, const PhaseMarks& pm) {
-    const int nslot = d.top_k + (d.shared_inter > 0 ? 1 : 0);
+                       const WsLayout& L, const Ctx& c, bool route) {
+    GemvArgs a = base_args(d, x, T, shard, nshards);
     const int Iloc = d.inter / nshards;
-    float* hbuf = reinterpret_cast<float*>(ws + L.hbuf);
-    const int nsb_row = d.hidden / kSbWeights;
-    switch (nsb_row) {
-        case 1: launch_gateup<8, 1>(d, x, T, idx, shard, nshards, nslot, hbuf, Iloc, s); break;
-        case 2: launch_gateup<16, 1>(d, x, T, idx, shard, nshards, nslot, hbuf, Iloc, s); break;
-        case 4: launch_gateup<32, 1>(d, x, T, idx, shard, nshards, nslot, hbuf, Iloc, s); break;
-        case 8: launch_gateup<64, 1>(d, x, T, idx, shard, nshards, nslot, hbuf, Iloc, s); break;
-        case 16: launch_gateup<64, 2>(d, x, T, idx, shard, nshards, nslot, hbuf, Iloc, s); break;
-        default: return hipErrorInvalidValue;
+    a.hbuf = reinterpret_cast<float*>(ws + L.hbuf);
+    a.hstride = Iloc;
+    a.out = out;
+    // small T: partials in the front kernel, top-k inside the gate/up kernel;
+    // otherwise the matrix-core router runs first
+    const bool fused_route = route && T <= kGemvMaxT && d.n_experts <= 256;
+    if (route) {
+        a.idx_out = reinterpret_cast<int32_t*>(ws + L.idx);
+        a.w_out = reinterpret_cast<float*>(ws + L.w);
+        if (!fused_route) {
+            hipError_t e = launch_router(d, x, T, a.idx_out, a.w_out, ws, L, c);
+            if (e != hipSuccess) return e;
+        }
+        idx = a.idx_out;
+        w = a.w_out;
     }
-    pm.mark(2);
+    hipError_t e = launch_front(a, fused_route, d.shared_inter > 0, L, ws, c);
+    if (e != hipSuccess) return e;
+    a.route = fused_route ? 1 : 0;
+    a.idx = idx;
+    a.w = w;
+    const int nsb = d.hidden / kSbWeights;
+    MOE_DISPATCH_H(nsb, launch_gateup_t, a, c);
     const int lprd = Iloc / 32;
-    dim3 grid2((d.hidden + (64 / lprd) - 1) / (64 / lprd), T);
-    down_gemv_kernel<<<grid2, 64, 0, s>>>(d.down_q, d.sh_down_q, hbuf, Iloc, idx, w,
-                                          d.shared_weight, d.hidden, d.n_experts, d.top_k,
-                                          d.inter, d.shared_inter, shard, nshards, nslot, lprd,
-                                          out);
-    pm.mark(3);
+    const int rows_per_block = kDnPasses * (64 / lprd);
+    const int nw = a.nslot < 16 ? a.nslot : 16;
+    const dim3 grid2((d.hidden + rows_per_block - 1) / rows_per_block, T);
+    launch_k(c, MOE_K_DOWN_GEMV, gemv_down_kernel, grid2, dim3(64 * nw), 0, a, lprd);
     return hipGetLastError();
 }
 

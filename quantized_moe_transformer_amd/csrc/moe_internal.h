@@ -5,6 +5,7 @@
 // CPU oracle.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -19,6 +20,7 @@ constexpr int kQ5Bytes = 176;   // 5-bit K-quant superblock
 constexpr int kSbWeights = 256;
 constexpr int kGemvMaxT = 32;   // automatic path: GEMV up to this many rows
 constexpr int kTileM = 64;      // grouped-GEMM rows (slots) per tile
+constexpr int kRouterSplits = 8;   // split-K partial logits per expert at small T
 // h is carried into the down projection as fp16 scaled by 2^-4: the SwiGLU
 // output of the Qwen3.5-shaped layer reaches ~2e4, the scale keeps a 50x
 // margin to fp16's 65504 at no cost in relative precision.
@@ -116,7 +118,7 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 
 struct WsLayout {
     // shared by both paths
-    size_t router_part;   // float [ks][T][E]
+    size_t router_part;   // float [T][E][ks]
     size_t idx, w;        // int32 / float [T][k] (routing computed inside the forward call)
     // GEMV path
     size_t hbuf;          // float [T*(k+1)][I_loc]
@@ -142,27 +144,39 @@ inline int bucket_blocks(int T, int k) { return (T * k + 1023) / 1024; }
 // Launchers (enqueue only; arguments already validated)
 // ---------------------------------------------------------------------------
 
-// Records caller-owned timing events at phase boundaries (see moe_opts).
-struct PhaseMarks {
-    void** ev = nullptr;
-    int n = 0;
+// Launch context: the stream, and (optionally) caller-owned start/stop events
+// per kernel id (moe_opts.kernel_events).  A timed kernel is launched with
+// hipExtLaunchKernel, whose events carry the dispatch's own timestamps.
+struct Ctx {
     hipStream_t s = nullptr;
-    void mark(int i) const {
-        if (i < n && ev && ev[i]) (void)hipEventRecord((hipEvent_t)ev[i], s);
-    }
+    void** ev = nullptr;
+    int n_ev = 0;
+    hipEvent_t start(int id) const { return (ev && 2 * id + 1 < n_ev) ? (hipEvent_t)ev[2 * id] : nullptr; }
+    hipEvent_t stop(int id) const { return (ev && 2 * id + 1 < n_ev) ? (hipEvent_t)ev[2 * id + 1] : nullptr; }
 };
 
+template <typename... KArgs, typename... Args>
+inline void launch_k(const Ctx& c, int id, void (*kern)(KArgs...), dim3 grid, dim3 block,
+                     uint32_t shm, Args... args) {
+    const hipEvent_t a = c.start(id), z = c.stop(id);
+    if (a || z)
+        hipExtLaunchKernelGGL(kern, grid, block, shm, c.s, a, z, 0, static_cast<KArgs>(args)...);
+    else
+        kern<<<grid, block, shm, c.s>>>(static_cast<KArgs>(args)...);
+}
+
 hipError_t launch_router(const moe_layer_desc& d, const float* x, int T, int32_t* idx, float* w,
-                         char* ws, const WsLayout& L, hipStream_t s);
+                         char* ws, const WsLayout& L, const Ctx& c);
+// route: run the router (and top-k) in the front kernel, writing L.idx / L.w
 hipError_t launch_gemv(const moe_layer_desc& d, const float* x, int T, const int32_t* idx,
                        const float* w, int shard, int nshards, float* out, char* ws,
-                       const WsLayout& L, hipStream_t s, const PhaseMarks& pm);
+                       const WsLayout& L, const Ctx& c, bool route);
 hipError_t launch_bucket(const int32_t* idx, int T, int k, int E, bool shared, int32_t* counts,
                          int32_t* offsets, int32_t* tile_off, int32_t* perm, int32_t* bhist,
-                         hipStream_t s);
+                         const Ctx& c);
 hipError_t launch_mfma(const moe_layer_desc& d, const float* x, int T, const int32_t* idx,
                        const float* w, int shard, int nshards, float* out, char* ws,
-                       const WsLayout& L, hipStream_t s, const PhaseMarks& pm);
+                       const WsLayout& L, const Ctx& c);
 hipError_t launch_reduce(const float* const* partials, int n, int64_t count, float* out,
                          hipStream_t s);
 hipError_t launch_dequant(const uint8_t* sbs, int bits, int64_t n_sb, int out_dtype, void* out,

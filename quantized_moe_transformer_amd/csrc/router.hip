@@ -1,4 +1,4 @@
-// router.hip -- fp32 router GEMM, top-k and renormalised routing weights.
+// router.hip -- fp32 router logits, top-k and renormalised routing weights.
 //
 // Page "CKE Zip: From Splitting Tokens To Splitting Qwen3.5 Weights", sections
 // "What The First Prototype Split" (the selected top-k expert indices and
@@ -6,139 +6,124 @@
 // Splits" (eight of 256 experts per token; one synchronised router decision
 // feeds every shard).
 //
-// Two kernels:
-//   router_partial  logits partial sums over a slice of H for a tile of tokens
-//                   (split-K across many workgroups so that a single decode
-//                   token still spreads the 2 MiB router matrix over the chip);
-//   router_topk     per token (one wave): sum the partials in ascending split
-//                   order, k rounds of a wave-wide arg-max (ties to the lower
-//                   expert index), softmax of the k selected logits.
+// Logits stay fp32 throughout (the top-k must be exact up to near-ties).
+// Few token rows (<= 32): split-K partial logits from the decode front
+// kernel (gemv.hip), then router_topk.  Many rows use:
+//   router_mfma     a dense [T x H] x [H x E] product on the fp32 matrix cores
+//                   (v_mfma_f32_16x16x4_f32);
+//   router_topk     one wave per token (topk.h).
 #include "moe_internal.h"
+#include "topk.h"
 
 namespace moe {
 
-constexpr int kRouterTT = 16;      // tokens per workgroup
-constexpr int kRouterChunk = 128;  // rows of H staged in LDS at a time
+int router_splits(int T, int H) { return T <= kGemvMaxT ? kRouterSplits : 1; }
 
-int router_splits(int T, int H) {
-    // enough workgroups to cover the chip; each split handles >= 16 rows of H
-    const int tblocks = (T + kRouterTT - 1) / kRouterTT;
-    int ks = 512 / (tblocks > 0 ? tblocks : 1);
-    const int kmax = H / 16;
-    if (ks > kmax) ks = kmax;
-    if (ks < 1) ks = 1;
-    return ks;
-}
+// grid (ceil(T/16), ceil(E/256)); block 512 threads = 8 waves; the block owns
+// 16 tokens x 256 experts, wave w the experts [32w, 32w+32) as two 16x16 tiles.
+// K advances 32 at a time; the next step's operands are fetched into
+// registers while the current step runs on the matrix cores.
+constexpr int kRmT = 16, kRmE = 256, kRmK = 32;
 
-__global__ void __launch_bounds__(256)
-router_partial_kernel(const float* __restrict__ x, const float* __restrict__ wr, int T, int H,
-                      int E, int rows_per_split, float* __restrict__ part) {
-    __shared__ float xs[kRouterTT][kRouterChunk];
-    const int t0 = blockIdx.x * kRouterTT;
-    const int ks = blockIdx.y;
-    const int h0 = ks * rows_per_split;
-    const int h1 = min(H, h0 + rows_per_split);
-    const int nt = min(kRouterTT, T - t0);
-
-    for (int e0 = 0; e0 < E; e0 += blockDim.x) {
-        const int e = e0 + threadIdx.x;
-        float acc[kRouterTT];
+__global__ void __launch_bounds__(512)
+router_mfma_kernel(const float* __restrict__ x, const float* __restrict__ wr, int T, int H, int E,
+                   float* __restrict__ logits) {
+    __shared__ float xs[kRmT][kRmK + 1];
+    __shared__ float ws[kRmK][kRmE + 4];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int t0 = blockIdx.x * kRmT, e0 = blockIdx.y * kRmE;
+    // loaders: x one float per thread; Wr four float4 per thread
+    const int xt = tid >> 5, xk = tid & 31;
+    const bool xok = t0 + xt < T;
+    float xr;
+    float4 wv[4];
+    auto fetch = [&](int k0) {
+        xr = xok ? x[(size_t)(t0 + xt) * H + k0 + xk] : 0.f;
 #pragma unroll
-        for (int i = 0; i < kRouterTT; ++i) acc[i] = 0.f;
-        for (int hc = h0; hc < h1; hc += kRouterChunk) {
-            const int hn = min(kRouterChunk, h1 - hc);
-            __syncthreads();
-            for (int i = threadIdx.x; i < kRouterTT * kRouterChunk; i += blockDim.x) {
-                const int tt = i / kRouterChunk, hh = i % kRouterChunk;
-                xs[tt][hh] = (tt < nt && hh < hn) ? x[(size_t)(t0 + tt) * H + hc + hh] : 0.f;
-            }
-            __syncthreads();
-            if (e < E) {
-                for (int hh = 0; hh < hn; ++hh) {
-                    const float wv = wr[(size_t)(hc + hh) * E + e];
-#pragma unroll
-                    for (int i = 0; i < kRouterTT; ++i) acc[i] = __builtin_fmaf(xs[i][hh], wv, acc[i]);
-                }
+        for (int q = 0; q < 4; ++q) {
+            const int f = tid + 512 * q;
+            const int r = f >> 6, c4 = (f & 63) * 4;
+            const int e = e0 + c4;
+            const float* row = wr + (size_t)(k0 + r) * E;
+            if ((E & 3) == 0 && e + 3 < E) {
+                wv[q] = *reinterpret_cast<const float4*>(row + e);
+            } else {
+                wv[q].x = e < E ? row[e] : 0.f;
+                wv[q].y = e + 1 < E ? row[e + 1] : 0.f;
+                wv[q].z = e + 2 < E ? row[e + 2] : 0.f;
+                wv[q].w = e + 3 < E ? row[e + 3] : 0.f;
             }
         }
-        if (e < E) {
-            for (int i = 0; i < nt; ++i) part[((size_t)ks * T + t0 + i) * E + e] = acc[i];
+    };
+    fetch(0);
+    float4v acc[2] = {};
+    for (int k0 = 0; k0 < H; k0 += kRmK) {
+        __syncthreads();
+        xs[xt][xk] = xr;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int f = tid + 512 * q;
+            *reinterpret_cast<float4*>(&ws[f >> 6][(f & 63) * 4]) = wv[q];
+        }
+        __syncthreads();
+        if (k0 + kRmK < H) fetch(k0 + kRmK);
+#pragma unroll
+        for (int ks = 0; ks < kRmK / 4; ++ks) {
+            const float a = xs[lane & 15][ks * 4 + (lane >> 4)];
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                const float bv = ws[ks * 4 + (lane >> 4)][wave * 32 + b * 16 + (lane & 15)];
+                acc[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bv, acc[b], 0, 0, 0);
+            }
+        }
+    }
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        const int e = e0 + wave * 32 + b * 16 + (lane & 15);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = t0 + 4 * (lane >> 4) + i;
+            if (t < T && e < E) logits[(size_t)t * E + e] = acc[b][i];
         }
     }
 }
 
-// One wave per token.  Lane l holds experts l, l+64, ... (E <= 1024).
+// Four tokens per workgroup, one wave each.
 __global__ void __launch_bounds__(256)
 router_topk_kernel(const float* __restrict__ part, int ks_n, int T, int E, int k,
                    int32_t* __restrict__ idx, float* __restrict__ w) {
-    const int lane = threadIdx.x & 63;
-    const int t = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
-    float l[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int e = lane + 64 * i;
-        float s = -INFINITY;
-        if (e < E) {
-            s = 0.f;
-            for (int ks = 0; ks < ks_n; ++ks) s += part[((size_t)ks * T + t) * E + e];
-            if (s != s) s = -INFINITY;  // a NaN logit is never preferred
-        }
-        l[i] = s;
-    }
-    uint32_t taken = 0;
-    float sel_l[16];
-    int sel_e[16];
-    for (int j = 0; j < k; ++j) {
-        float bv = -INFINITY;
-        int be = 0x7fffffff;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int e = lane + 64 * i;
-            if (e < E && !((taken >> i) & 1u) && (l[i] > bv || (l[i] == bv && e < be))) {
-                bv = l[i];
-                be = e;
-            }
-        }
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-            const float ov = __shfl_xor(bv, off, 64);
-            const int oe = __shfl_xor(be, off, 64);
-            if (ov > bv || (ov == bv && oe < be)) {
-                bv = ov;
-                be = oe;
-            }
-        }
-        if ((be & 63) == lane) taken |= 1u << (be >> 6);
-        sel_l[j] = bv;
-        sel_e[j] = be;
-    }
-    if (lane == 0) {
-        const float mx = sel_l[0];
-        float ex[16];
-        float z = 0.f;
-        for (int j = 0; j < k; ++j) {
-            ex[j] = expf(sel_l[j] - mx);
-            z += ex[j];
-        }
-        const float inv = 1.0f / z;
-        for (int j = 0; j < k; ++j) {
-            idx[(size_t)t * k + j] = sel_e[j];
-            w[(size_t)t * k + j] = ex[j] * inv;
-        }
+    int32_t* ir = idx + (size_t)t * k;
+    float* wr = w + (size_t)t * k;
+    if (ks_n == 1) {
+        if (E <= 256) wave_topk<4, 1>(part, E, k, t, ir, wr);
+        else wave_topk<16, 1>(part, E, k, t, ir, wr);
+    } else {
+        if (E <= 256) wave_topk<4, kRouterSplits>(part, E, k, t, ir, wr);
+        else wave_topk<16, kRouterSplits>(part, E, k, t, ir, wr);
     }
 }
 
+hipError_t launch_router_small(const moe_layer_desc& d, const float* x, int T, char* ws,
+                               const WsLayout& L, const Ctx& c);   // gemv.hip: partials only
+
 hipError_t launch_router(const moe_layer_desc& d, const float* x, int T, int32_t* idx, float* w,
-                         char* ws, const WsLayout& L, hipStream_t s) {
+                         char* ws, const WsLayout& L, const Ctx& c) {
     const int H = d.hidden, E = d.n_experts;
-    const int ks = L.router_ks;
-    const int rows = (H + ks - 1) / ks;
     float* part = reinterpret_cast<float*>(ws + L.router_part);
-    dim3 g1((T + kRouterTT - 1) / kRouterTT, ks);
-    const int threads = E < 256 ? ((E + 63) / 64) * 64 : 256;
-    router_partial_kernel<<<g1, threads, 0, s>>>(x, d.router_w, T, H, E, rows, part);
-    router_topk_kernel<<<(T + 3) / 4, 256, 0, s>>>(part, ks, T, E, d.top_k, idx, w);
+    if (T <= kGemvMaxT) {
+        hipError_t e = launch_router_small(d, x, T, ws, L, c);
+        if (e != hipSuccess) return e;
+        launch_k(c, MOE_K_ROUTER_TOPK, router_topk_kernel, dim3((T + 3) / 4), dim3(256), 0, part,
+                 L.router_ks, T, E, d.top_k, idx, w);
+        return hipGetLastError();
+    }
+    dim3 g((T + kRmT - 1) / kRmT, (E + kRmE - 1) / kRmE);
+    launch_k(c, MOE_K_ROUTER_MFMA, router_mfma_kernel, g, dim3(512), 0, x, d.router_w, T, H, E,
+             part);
+    launch_k(c, MOE_K_ROUTER_TOPK, router_topk_kernel, dim3((T + 3) / 4), dim3(256), 0, part, 1,
+             T, E, d.top_k, idx, w);
     return hipGetLastError();
 }
 

@@ -41,8 +41,9 @@ class DeviceLayer:
         return other
 
     def workspace(self, T: int, num_shards: int = 1):
+        """A zero-filled workspace (its leading counters must start at zero)."""
         import torch
         nbytes = _lib.moe_workspace_bytes(self.desc, T, num_shards)
         if nbytes == 0 and T > 0:
             raise ValueError("invalid layer description")
-        return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+        return torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=self.device)
