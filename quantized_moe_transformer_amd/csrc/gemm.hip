@@ -12,25 +12,46 @@
 // exceeds a 1e-2 max-error/RMS bound while fp16 stays near 3e-3; gfx950 runs
 // both at the same rate.
 //
-//   gemm_gateup  per (expert, 64-row tile, 64 intermediate columns): the
-//                rows' tokens gathered from x16, gate and up superblocks
-//                dequantised into LDS as fp16, two accumulators; epilogue
-//                h = silu(g) * u, stored fp16 (scaled by 2^-4) in expert-
-//                sorted row order.
-//   gemm_down    per (expert, 64-row tile, 128 outputs): h rows x dequantised
-//                5-bit down weights; epilogue scales by the routing weight and
-//                writes the row's slot of the per-slot output buffer (the
-//                shared expert writes its own buffer, times its weight).
-//   combine      out[t] = sum over slots in selected-slot order, then the
-//                shared expert (page "CKE Zip ...", section "A Separate Decode
-//                Result Shows Why Axis Choice Matters").
+// One kernel template serves both projections.  A workgroup owns one tile:
+// up to 160 rows of one expert's group (a whole routed expert at T = 4096, so
+// its weights are dequantised once per column tile) times 256 weight rows, and
+// walks K in steps of 64 (one pair of K-quant sub-blocks).  Its 8 waves are
+//   4 consumer waves: MFMA only, from one LDS stage; wave w owns two 32-wide
+//     column blocks times every 32-row block the tile has (up to 5), so each
+//     fragment read from LDS feeds several MFMAs;
+//   4 producer waves: gather the next step's rows (fp16) into the other LDS
+//     stage and dequantise the next step's packed weights there, with the
+//     weight loads issued 2-3 steps ahead into a register ring;
+// so dequantisation (VALU) and matrix work (MFMA) run side by side.
+//
+//   gateup (MODE 0): A = token rows of x16 gathered through the expert-sorted
+//     slot list, B = 128 gate rows + the matching 128 up rows (4-bit); each
+//     consumer wave holds a gate block and the matching up block, so the
+//     epilogue writes h = silu(g) * u (fp16, scaled by 2^-4) straight from
+//     registers, in sorted row order.
+//   down (MODE 1): A = h rows (contiguous per expert), B = 256 down rows
+//     (5-bit); the epilogue scales by the routing weight (and 2^4) and writes
+//     the slot's row of the per-slot buffer (the shared expert: its own
+//     buffer, times its weight).
+//   combine: out[t] = sum over slots in selected-slot order, then the shared
+//     expert (page "CKE Zip: From Splitting Tokens To Splitting Qwen3.5
+//     Weights", section "A Separate Decode Result Shows Why Axis Choice
+//     Matters").
 #include "moe_internal.h"
 
 namespace moe {
 
-constexpr int kBK = 64;           // K per LDS stage (one pair of sub-blocks)
-constexpr int kLdsPad = 8;        // halves of padding per LDS row
-constexpr int kLdsRow = kBK + kLdsPad;
+constexpr int kBK = 64;                 // K per step (one pair of sub-blocks)
+constexpr int kLdsRow = kBK + 8;        // halves per LDS row (8 halves of padding)
+constexpr int kTM = kTileM;             // rows per tile (up to 5 blocks of 32)
+constexpr int kTN = 256;                // weight rows per tile
+// weight-load prefetch distance (steps): 3 for the 4-bit gate/up stream, 2
+// for the 5-bit down stream (its pieces carry high bits too: more registers)
+template <int MODE> struct PrefetchDistance { static constexpr int v = MODE == 0 ? 3 : 2; };
+constexpr int kConsumers = 4;           // consumer waves (two 32-column blocks each)
+constexpr int kProducers = 4;           // producer waves
+constexpr int kGemmThreads = 64 * (kConsumers + kProducers);
+constexpr int kBTasks = kTN * 2 / (64 * kProducers);   // 16-byte code pieces per producer thread
 
 __device__ __forceinline__ int find_group(const int32_t* __restrict__ tile_off, int ngroups,
                                           int tile) {
@@ -55,18 +76,23 @@ __device__ __forceinline__ void dequant_piece_to_lds(const SbHead& hd, const uin
     sub_scale_min(hd, 2 * c + 1, scb, mb);
     const float dsa = hd.d * sca, dma = hd.dmin * ma;
     const float dsb = hd.d * scb, dmb = hd.dmin * mb;
+    const uint32_t qw[4] = {qs.x, qs.y, qs.z, qs.w};
+    const uint32_t hw[4] = {qh.x, qh.y, qh.z, qh.w};
     half8 lo[2], hi[2];
 #pragma unroll
-    for (int b = 0; b < 16; ++b) {
-        const uint32_t byte = piece_byte(qs, b);
-        uint32_t ql = byte & 15u, qq = byte >> 4;
+    for (int wi = 0; wi < 4; ++wi) {
+        uint32_t l4 = qw[wi] & 0x0f0f0f0fu;
+        uint32_t h4 = (qw[wi] >> 4) & 0x0f0f0f0fu;
         if (HIGH) {
-            const uint32_t hb = piece_byte(qh, b);
-            ql |= ((hb >> (2 * c)) & 1u) << 4;
-            qq |= ((hb >> (2 * c + 1)) & 1u) << 4;
+            l4 |= ((hw[wi] >> (2 * c)) & 0x01010101u) << 4;
+            h4 |= ((hw[wi] >> (2 * c + 1)) & 0x01010101u) << 4;
         }
-        lo[b >> 3][b & 7] = (_Float16)kq_weight(dsa, dma, (float)ql);
-        hi[b >> 3][b & 7] = (_Float16)kq_weight(dsb, dmb, (float)qq);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int i = 4 * wi + b;
+            lo[i >> 3][i & 7] = (_Float16)kq_weight(dsa, dma, (float)((l4 >> (8 * b)) & 0xffu));
+            hi[i >> 3][i & 7] = (_Float16)kq_weight(dsb, dmb, (float)((h4 >> (8 * b)) & 0xffu));
+        }
     }
     *reinterpret_cast<half8*>(row + 16 * hh) = lo[0];
     *reinterpret_cast<half8*>(row + 16 * hh + 8) = lo[1];
@@ -74,207 +100,287 @@ __device__ __forceinline__ void dequant_piece_to_lds(const SbHead& hd, const uin
     *reinterpret_cast<half8*>(row + 32 + 16 * hh + 8) = hi[1];
 }
 
-__global__ void __launch_bounds__(256)
-gemm_gateup_kernel(const _Float16* __restrict__ x16, int T, int H,
-                   const int32_t* __restrict__ perm, const int32_t* __restrict__ offsets,
-                   const int32_t* __restrict__ tile_off, int E, int k,
-                   const uint8_t* __restrict__ gate, const uint8_t* __restrict__ up,
-                   const uint8_t* __restrict__ sh_gate, const uint8_t* __restrict__ sh_up,
-                   int I, int Is, int shard, int nshards, _Float16* __restrict__ h16,
-                   int hstride) {
-    __shared__ _Float16 As[kTileM][kLdsRow];
-    __shared__ _Float16 Bs[128][kLdsRow];
-    const int tile = blockIdx.x;
-    const int ngroups = E + 1;
-    if (tile >= tile_off[ngroups]) return;
-    const int g = find_group(tile_off, ngroups, tile);
-    const bool is_sh = g == E;
-    const int m0 = (tile - tile_off[g]) * kTileM;
-    const int rows = is_sh ? T : offsets[g + 1] - offsets[g];
-    const int mcount = min(kTileM, rows - m0);
-    const int hrow0 = offsets[g] + m0;
-    const uint8_t *G, *U;
-    int Iexp;
-    if (!is_sh) {
-        const size_t mat = (size_t)I * H / kSbWeights * kQ4Bytes;
-        G = gate + (size_t)g * mat;
-        U = up + (size_t)g * mat;
-        Iexp = I;
-    } else {
-        G = sh_gate;
-        U = sh_up;
-        Iexp = Is;
-    }
-    const int Iloc = Iexp / nshards, i0 = shard * Iloc;
-    const int n0 = blockIdx.y * 64;
-    if (n0 >= Iloc) return;
+struct GemmArgs {
+    const _Float16* a_src;          // MODE 0: x16 [T][H]; MODE 1: h16 [T*k + T][Iloc]
+    int a_stride;                   // halves per A row
+    const int32_t* perm;            // expert-sorted slot ids
+    const int32_t* offsets;         // [E+2]: group row starts (group E = shared expert)
+    const int32_t* tile_off;        // [E+2]: group tile starts
+    int T, H, E, k, I, Is, shard, nshards;
+    const uint8_t *w_routed, *w_routed2, *w_shared, *w_shared2;   // MODE 0: gate, up
+    const float* route_w;           // [T*k] routing weights
+    float sw;
+    int n_ntiles;                   // weight-row tiles per group
+    int nk;                         // K steps
+    _Float16* h_out;                // MODE 0
+    int h_stride;
+    float* y;                       // MODE 1: [T*k][H]
+    float* ysh;                     // MODE 1: [T][H]
+};
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    // A loader: rows tid/8 and tid/8 + 32, 16-byte chunk tid%8
-    const int ac = tid & 7;
-    int tokA[2];
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int m = (tid >> 3) + 32 * q;
-        tokA[q] = -1;
-        if (m < mcount) tokA[q] = is_sh ? (m0 + m) : perm[offsets[g] + m0 + m] / k;
-    }
-    // B loader: weight row tid/2 (first 64 gate, next 64 up), piece half tid%2
-    const int br = tid >> 1, bhh = tid & 1;
-    const int bcol = br & 63;
-    const bool bvalid = n0 + bcol < Iloc;
-    const int nsb_row = H / kSbWeights;
-    const uint8_t* brow = (br < 64 ? G : U) + (size_t)(i0 + n0 + bcol) * nsb_row * kQ4Bytes;
+// Packed weights of one producer task (weight row, 16-byte half) for one step.
+struct BRegs {
+    uint4 head, qs, qh;
+};
 
-    const int wm = wave & 1, wn = wave >> 1;
-    float16v accG = {}, accU = {};
-    const int nk = H / kBK;
-    for (int kk = 0; kk < nk; ++kk) {
-        uint4 av[2];
+struct __align__(16) GemmLds {
+    _Float16 a[2][kTM][kLdsRow];
+    _Float16 b[2][kTN][kLdsRow];
+};
+
+// Everything a workgroup knows about its tile.
+struct TileInfo {
+    int g, m0, mcount, grow0, Iexp, Iloc, i0, n0;
+    bool is_sh;
+};
+
+// The tile's K loop and epilogue for exactly MB 32-row blocks (straight-line
+// code: the fragment reads of a 16-wide K slice are issued before its MFMAs).
+template <int MODE, int MB>
+__device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileInfo& ti, GemmLds& lds,
+                                          const int32_t* row_src, const float* row_w) {
+    constexpr int kPD = PrefetchDistance<MODE>::v;
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int g = ti.g, m0 = ti.m0, mcount = ti.mcount, grow0 = ti.grow0;
+    const int Iexp = ti.Iexp, Iloc = ti.Iloc, i0 = ti.i0, n0 = ti.n0;
+    const bool is_sh = ti.is_sh;
+    (void)m0;
+
+    if (wave >= kConsumers) {
+        // ------------------------------- producers -------------------------------
+        const int pt = tid - 64 * kConsumers;
+        const uint8_t* wsrc[kBTasks];   // MODE 0: the row's superblocks; MODE 1: matrix base
+        size_t eoff[kBTasks];           // MODE 1: element offset of the row's range
+        int bhh[kBTasks], brr[kBTasks];
+        bool bok[kBTasks];
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            av[q] = make_uint4(0, 0, 0, 0);
-            if (tokA[q] >= 0)
-                av[q] = *reinterpret_cast<const uint4*>(x16 + (size_t)tokA[q] * H + kk * kBK + ac * 8);
+        for (int q = 0; q < kBTasks; ++q) {
+            const int task = pt + 64 * kProducers * q;
+            const int r = task >> 1;
+            bhh[q] = task & 1;
+            brr[q] = r;
+            eoff[q] = 0;
+            if (MODE == 0) {
+                const int col = r & (kTN / 2 - 1);
+                bok[q] = n0 + col < Iloc;
+                const size_t mat = (size_t)a.I * a.H / kSbWeights * kQ4Bytes;
+                const uint8_t* m = is_sh ? (r < kTN / 2 ? a.w_shared : a.w_shared2)
+                                         : (r < kTN / 2 ? a.w_routed : a.w_routed2) + (size_t)g * mat;
+                wsrc[q] = m + (size_t)(i0 + n0 + col) * (a.H / kSbWeights) * kQ4Bytes;
+            } else {
+                const int o = n0 + r;
+                bok[q] = o < a.H;
+                wsrc[q] = is_sh ? a.w_shared
+                                : a.w_routed + (size_t)g * ((size_t)a.H * a.I / kSbWeights * kQ5Bytes);
+                eoff[q] = (size_t)o * Iexp + i0;
+            }
         }
-        SbHead hd = {};
-        uint4 qs = make_uint4(0, 0, 0, 0);
-        const int c = kk & 3;
-        if (bvalid) {
-            const uint8_t* sb = brow + (kk >> 2) * kQ4Bytes;
-            hd = load_head(sb);
-            qs = *reinterpret_cast<const uint4*>(sb + 16 + 32 * c + 16 * bhh);
-        }
-        __syncthreads();
+        auto load_b = [&](int kk, BRegs* rg) {
 #pragma unroll
-        for (int q = 0; q < 2; ++q)
-            *reinterpret_cast<uint4*>(&As[(tid >> 3) + 32 * q][ac * 8]) = av[q];
-        dequant_piece_to_lds<false>(hd, qs, qs, c, bhh, &Bs[br][0]);
-        __syncthreads();
+            for (int q = 0; q < kBTasks; ++q) {
+                rg[q].head = make_uint4(0, 0, 0, 0);
+                rg[q].qs = make_uint4(0, 0, 0, 0);
+                rg[q].qh = make_uint4(0, 0, 0, 0);
+                if (!bok[q]) continue;
+                if (MODE == 0) {
+                    const uint8_t* sb = wsrc[q] + (kk >> 2) * kQ4Bytes;
+                    rg[q].head = *reinterpret_cast<const uint4*>(sb);
+                    rg[q].qs = *reinterpret_cast<const uint4*>(sb + 16 + 32 * (kk & 3) + 16 * bhh[q]);
+                } else {
+                    const size_t base = eoff[q] + (size_t)kk * kBK;
+                    const int c = (int)((base & 255) >> 6);
+                    const uint8_t* sb = wsrc[q] + (base >> 8) * kQ5Bytes;
+                    rg[q].head = *reinterpret_cast<const uint4*>(sb);
+                    rg[q].qh = *reinterpret_cast<const uint4*>(sb + 16 + 16 * bhh[q]);
+                    rg[q].qs = *reinterpret_cast<const uint4*>(sb + 48 + 32 * c + 16 * bhh[q]);
+                }
+            }
+        };
+        auto store_b = [&](int kk, const BRegs* rg, int stage) {
+#pragma unroll
+            for (int q = 0; q < kBTasks; ++q) {
+                SbHead hd;
+                hd.d = f16_bits_to_f32(rg[q].head.x & 0xffffu);
+                hd.dmin = f16_bits_to_f32(rg[q].head.x >> 16);
+                hd.s0 = rg[q].head.y;
+                hd.s1 = rg[q].head.z;
+                hd.s2 = rg[q].head.w;
+                const int c = MODE == 0 ? (kk & 3)
+                                        : (int)(((eoff[q] + (size_t)kk * kBK) & 255) >> 6);
+                dequant_piece_to_lds<MODE == 1>(hd, rg[q].qs, rg[q].qh, c, bhh[q],
+                                                &lds.b[stage][brr[q]][0]);
+            }
+        };
+        // A: MB*32 rows x 8 chunks of 16 bytes; chunk task = pt + 256 i
+        size_t asrc[MB];
+        bool aok[MB];
+#pragma unroll
+        for (int i = 0; i < MB; ++i) {
+            const int task = pt + 256 * i;
+            const int r = task >> 3, c8 = task & 7;
+            const int src = row_src[r];
+            aok[i] = src >= 0;
+            asrc[i] = (MODE == 0 ? (size_t)max(src, 0) : (size_t)(grow0 + r)) * a.a_stride + c8 * 8;
+        }
+        uint4 areg[MB];
+        auto load_a = [&](int kk) {
+#pragma unroll
+            for (int i = 0; i < MB; ++i) {
+                areg[i] = make_uint4(0, 0, 0, 0);
+                if (aok[i]) areg[i] = *reinterpret_cast<const uint4*>(a.a_src + asrc[i] + kk * kBK);
+            }
+        };
+        auto store_a = [&](int stage) {
+#pragma unroll
+            for (int i = 0; i < MB; ++i) {
+                const int task = pt + 256 * i;
+                *reinterpret_cast<uint4*>(&lds.a[stage][task >> 3][(task & 7) * 8]) = areg[i];
+            }
+        };
+
+        BRegs ring[kPD][kBTasks];
+#pragma unroll
+        for (int s = 0; s < kPD; ++s)
+            if (s < a.nk) load_b(s, ring[s]);
+        load_a(0);
+        store_a(0);
+        if (a.nk > 1) load_a(1);
+        store_b(0, ring[0], 0);
+        if (kPD < a.nk) load_b(kPD, ring[0]);
+        __syncthreads();   // stage 0 ready
+        for (int kk0 = 0; kk0 < a.nk; kk0 += kPD) {
+#pragma unroll
+            for (int u = 0; u < kPD; ++u) {
+                const int kk = kk0 + u;
+                if (kk >= a.nk) break;
+                // while the consumers work on step kk: step kk+1 into the other stage
+                const int nxt = kk + 1;
+                if (nxt < a.nk) {
+                    store_a(nxt & 1);
+                    if (nxt + 1 < a.nk) load_a(nxt + 1);
+                    store_b(nxt, ring[(u + 1) % kPD], nxt & 1);
+                    if (nxt + kPD < a.nk) load_b(nxt + kPD, ring[(u + 1) % kPD]);
+                }
+                __syncthreads();
+            }
+        }
+        return;
+    }
+
+    // ------------------------------- consumers -------------------------------
+    float16v acc[MB][2];
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+        acc[i][0] = float16v{};
+        acc[i][1] = float16v{};
+    }
+    // this wave's two 32-row blocks of B: gate block w and up block w (MODE 0),
+    // or output blocks 2w and 2w+1 (MODE 1)
+    const int bc0 = MODE == 0 ? 32 * wave : 64 * wave;
+    const int bc1 = MODE == 0 ? kTN / 2 + 32 * wave : 64 * wave + 32;
+    __syncthreads();              // stage 0 ready
+    for (int kk = 0; kk < a.nk; ++kk) {
+        const int st = kk & 1;
 #pragma unroll
         for (int ks = 0; ks < kBK / 16; ++ks) {
             const int kof = ks * 16 + 8 * (lane >> 5);
-            const half8 a = *reinterpret_cast<const half8*>(&As[wm * 32 + (lane & 31)][kof]);
-            const half8 bg = *reinterpret_cast<const half8*>(&Bs[wn * 32 + (lane & 31)][kof]);
-            const half8 bu = *reinterpret_cast<const half8*>(&Bs[64 + wn * 32 + (lane & 31)][kof]);
-            accG = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bg, accG, 0, 0, 0);
-            accU = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bu, accU, 0, 0, 0);
-        }
-    }
-    const int n = n0 + wn * 32 + (lane & 31);
+            const half8 b0 = *reinterpret_cast<const half8*>(&lds.b[st][bc0 + (lane & 31)][kof]);
+            const half8 b1 = *reinterpret_cast<const half8*>(&lds.b[st][bc1 + (lane & 31)][kof]);
+            half8 av[MB];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-        const int m = wm * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if (m < mcount && n < Iloc) {
-            const float h = silu_f(accG[v]) * accU[v] * kHScale;
-            h16[(size_t)(hrow0 + m) * hstride + n] = (_Float16)h;
+            for (int i = 0; i < MB; ++i)
+                av[i] = *reinterpret_cast<const half8*>(&lds.a[st][32 * i + (lane & 31)][kof]);
+#pragma unroll
+            for (int i = 0; i < MB; ++i) {
+                acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], b0, acc[i][0], 0, 0, 0);
+                acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], b1, acc[i][1], 0, 0, 0);
+            }
         }
+        __syncthreads();
+    }
+
+    if (MODE == 0) {
+        const int n = n0 + 32 * wave + (lane & 31);
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int m = 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                if (m < mcount && n < Iloc) {
+                    const float h = silu_f(acc[i][0][v]) * acc[i][1][v] * kHScale;
+                    a.h_out[(size_t)(grow0 + m) * a.h_stride + n] = (_Float16)h;
+                }
+            }
+    } else {
+        const int oa = n0 + 64 * wave + (lane & 31);
+        float* dst = is_sh ? a.ysh : a.y;
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int m = 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                if (m < mcount) {
+                    const float sc = row_w[m];
+                    float* drow = dst + (size_t)row_src[m] * a.H;
+                    if (oa < a.H) drow[oa] = acc[i][0][v] * sc;
+                    if (oa + 32 < a.H) drow[oa + 32] = acc[i][1][v] * sc;
+                }
+            }
     }
 }
 
-__global__ void __launch_bounds__(256)
-gemm_down_kernel(const _Float16* __restrict__ h16, int hstride, int T, int H,
-                 const int32_t* __restrict__ perm, const int32_t* __restrict__ offsets,
-                 const int32_t* __restrict__ tile_off, int E, int k,
-                 const uint8_t* __restrict__ down, const uint8_t* __restrict__ sh_down, int I,
-                 int Is, int shard, int nshards, const float* __restrict__ w, float sw,
-                 float* __restrict__ y, float* __restrict__ ysh) {
-    __shared__ _Float16 As[kTileM][kLdsRow];
-    __shared__ _Float16 Bs[128][kLdsRow];
-    __shared__ int32_t slot_s[kTileM];
-    __shared__ float slot_w[kTileM];
-    const int tile = blockIdx.x;
-    const int ngroups = E + 1;
-    if (tile >= tile_off[ngroups]) return;
-    const int g = find_group(tile_off, ngroups, tile);
-    const bool is_sh = g == E;
-    const int m0 = (tile - tile_off[g]) * kTileM;
-    const int rows = is_sh ? T : offsets[g + 1] - offsets[g];
-    const int mcount = min(kTileM, rows - m0);
-    const int hrow0 = offsets[g] + m0;
-    const uint8_t* D;
-    int Iexp;
-    if (!is_sh) {
-        D = down + (size_t)g * ((size_t)H * I / kSbWeights * kQ5Bytes);
-        Iexp = I;
-    } else {
-        D = sh_down;
-        Iexp = Is;
-    }
-    const int Iloc = Iexp / nshards, i0 = shard * Iloc;
-    const int n0 = blockIdx.y * 128;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    if (tid < kTileM) {
-        int s = -1;
-        float ws = 0.f;
-        if (tid < mcount) {
-            if (is_sh) {
-                s = m0 + tid;
-                ws = sw * kHUnscale;
+template <int MODE>
+__global__ void __launch_bounds__(kGemmThreads)
+gemm_grouped_kernel(GemmArgs a) {
+    __shared__ GemmLds lds;
+    __shared__ int32_t row_src[kTM];     // MODE 0: token of each row; MODE 1: slot id
+    __shared__ float row_w[kTM];         // MODE 1: routing weight * 2^4 of each row
+
+    const int ngroups = a.E + 1;
+    const int ntiles = a.tile_off[ngroups];
+    // block -> (row tile, column tile): the column tiles of one row tile run
+    // on one XCD (blocks 8 apart), so its gathered rows are reused in L2; row
+    // tiles are taken in reverse (the shared expert's, the largest, first)
+    const int b = blockIdx.x;
+    const int nt = a.n_ntiles;
+    const int tile_raw = (b / (8 * nt)) * 8 + (b & 7);
+    const int ntile = (b >> 3) % nt;
+    if (tile_raw >= ntiles) return;
+    const int tile = ntiles - 1 - tile_raw;
+    TileInfo ti;
+    ti.g = find_group(a.tile_off, ngroups, tile);
+    ti.is_sh = ti.g == a.E;
+    ti.m0 = (tile - a.tile_off[ti.g]) * kTM;
+    const int rows = ti.is_sh ? a.T : a.offsets[ti.g + 1] - a.offsets[ti.g];
+    ti.mcount = min(kTM, rows - ti.m0);
+    ti.grow0 = a.offsets[ti.g] + ti.m0;   // first row of the tile in sorted order
+    ti.Iexp = ti.is_sh ? a.Is : a.I;
+    ti.Iloc = ti.Iexp / a.nshards;
+    ti.i0 = a.shard * ti.Iloc;
+    ti.n0 = ntile * (MODE == 0 ? kTN / 2 : kTN);
+    const int tid = threadIdx.x;
+    if (tid < kTM) {
+        int src = -1;
+        float rw = 0.f;
+        if (tid < ti.mcount) {
+            if (MODE == 0) {
+                src = ti.is_sh ? (ti.m0 + tid) : a.perm[ti.grow0 + tid] / a.k;
             } else {
-                s = perm[hrow0 + tid];
-                ws = w[s] * kHUnscale;
+                src = ti.is_sh ? (ti.m0 + tid) : a.perm[ti.grow0 + tid];
+                rw = (ti.is_sh ? a.sw : a.route_w[src]) * kHUnscale;
             }
         }
-        slot_s[tid] = s;
-        slot_w[tid] = ws;
-    }
-    const int ac = tid & 7;
-    const int br = tid >> 1, bhh = tid & 1;
-    const int o = n0 + br;
-    const bool bvalid = o < H;
-    const int wm = wave & 1, wn = wave >> 1;
-    float16v acc0 = {}, acc1 = {};
-    const int nk = Iloc / kBK;
-    for (int kk = 0; kk < nk; ++kk) {
-        uint4 av[2];
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int m = (tid >> 3) + 32 * q;
-            av[q] = make_uint4(0, 0, 0, 0);
-            if (m < mcount)
-                av[q] = *reinterpret_cast<const uint4*>(h16 + (size_t)(hrow0 + m) * hstride +
-                                                        kk * kBK + ac * 8);
-        }
-        SbHead hd = {};
-        uint4 qs = make_uint4(0, 0, 0, 0), qh = make_uint4(0, 0, 0, 0);
-        int c = 0;
-        if (bvalid) {
-            const size_t base = (size_t)o * Iexp + i0 + kk * kBK;
-            c = (int)((base & 255) >> 6);
-            const uint8_t* sb = D + (base >> 8) * kQ5Bytes;
-            hd = load_head(sb);
-            qh = *reinterpret_cast<const uint4*>(sb + 16 + 16 * bhh);
-            qs = *reinterpret_cast<const uint4*>(sb + 48 + 32 * c + 16 * bhh);
-        }
-        __syncthreads();
-#pragma unroll
-        for (int q = 0; q < 2; ++q)
-            *reinterpret_cast<uint4*>(&As[(tid >> 3) + 32 * q][ac * 8]) = av[q];
-        dequant_piece_to_lds<true>(hd, qs, qh, c, bhh, &Bs[br][0]);
-        __syncthreads();
-#pragma unroll
-        for (int ks = 0; ks < kBK / 16; ++ks) {
-            const int kof = ks * 16 + 8 * (lane >> 5);
-            const half8 a = *reinterpret_cast<const half8*>(&As[wm * 32 + (lane & 31)][kof]);
-            const half8 b0 = *reinterpret_cast<const half8*>(&Bs[wn * 64 + (lane & 31)][kof]);
-            const half8 b1 = *reinterpret_cast<const half8*>(&Bs[wn * 64 + 32 + (lane & 31)][kof]);
-            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b0, acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b1, acc1, 0, 0, 0);
-        }
+        row_src[tid] = src;
+        row_w[tid] = rw;
     }
     __syncthreads();
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-        const int m = wm * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if (m < mcount) {
-            const int s = slot_s[m];
-            const float sc = slot_w[m];
-            float* dst = is_sh ? ysh : y;
-            const int oa = n0 + wn * 64 + (lane & 31);
-            if (oa < H) dst[(size_t)s * H + oa] = acc0[v] * sc;
-            if (oa + 32 < H) dst[(size_t)s * H + oa + 32] = acc1[v] * sc;
-        }
+    switch ((ti.mcount + 31) >> 5) {
+        case 1: gemm_tile<MODE, 1>(a, ti, lds, row_src, row_w); break;
+        case 2: gemm_tile<MODE, 2>(a, ti, lds, row_src, row_w); break;
+        case 3: gemm_tile<MODE, 3>(a, ti, lds, row_src, row_w); break;
+        case 4: gemm_tile<MODE, 4>(a, ti, lds, row_src, row_w); break;
+        default: gemm_tile<MODE, 5>(a, ti, lds, row_src, row_w); break;
     }
 }
 
@@ -343,15 +449,51 @@ hipError_t launch_mfma(const moe_layer_desc& d, const float* x, int T, const int
              x16, n4);
     hipError_t err = launch_bucket(idx, T, k, E, shared, counts, offsets, tile_off, perm, bhist, c);
     if (err != hipSuccess) return err;
-    // an upper bound on the number of tiles; blocks past the real count exit
-    const int max_tiles = (T * k + kTileM - 1) / kTileM + E + (shared ? (T + kTileM - 1) / kTileM : 0);
-    const int Imax = (d.inter > d.shared_inter ? d.inter : d.shared_inter) / nshards;
-    launch_k(c, MOE_K_GEMM_GATEUP, gemm_gateup_kernel, dim3(max_tiles, (Imax + 63) / 64), dim3(256),
-             0, x16, T, H, perm, offsets, tile_off, E, k, d.gate_q, d.up_q, d.sh_gate_q, d.sh_up_q,
-             d.inter, d.shared_inter, shard, nshards, h16, Iloc);
-    launch_k(c, MOE_K_GEMM_DOWN, gemm_down_kernel, dim3(max_tiles, (H + 127) / 128), dim3(256), 0,
-             h16, Iloc, T, H, perm, offsets, tile_off, E, k, d.down_q, d.sh_down_q, d.inter,
-             d.shared_inter, shard, nshards, w, d.shared_weight, y, ysh);
+    // an upper bound on the number of row tiles; blocks past the real count exit
+    const int max_tiles = (T * k + kTM - 1) / kTM + E + (shared ? (T + kTM - 1) / kTM : 0);
+    const int max_tiles8 = (max_tiles + 7) / 8 * 8;
+
+    GemmArgs a = {};
+    a.perm = perm;
+    a.offsets = offsets;
+    a.tile_off = tile_off;
+    a.T = T;
+    a.H = H;
+    a.E = E;
+    a.k = k;
+    a.I = d.inter;
+    a.Is = d.shared_inter;
+    a.shard = shard;
+    a.nshards = nshards;
+    a.route_w = w;
+    a.sw = d.shared_weight;
+
+    GemmArgs g1 = a;
+    g1.a_src = x16;
+    g1.a_stride = H;
+    g1.w_routed = d.gate_q;
+    g1.w_routed2 = d.up_q;
+    g1.w_shared = d.sh_gate_q;
+    g1.w_shared2 = d.sh_up_q;
+    g1.n_ntiles = (Iloc + kTN / 2 - 1) / (kTN / 2);
+    g1.nk = H / kBK;
+    g1.h_out = h16;
+    g1.h_stride = Iloc;
+    launch_k(c, MOE_K_GEMM_GATEUP, gemm_grouped_kernel<0>, dim3(max_tiles8 * g1.n_ntiles),
+             dim3(kGemmThreads), 0, g1);
+
+    GemmArgs g2 = a;
+    g2.a_src = h16;
+    g2.a_stride = Iloc;
+    g2.w_routed = d.down_q;
+    g2.w_shared = d.sh_down_q;
+    g2.n_ntiles = (H + kTN - 1) / kTN;
+    g2.nk = Iloc / kBK;
+    g2.y = y;
+    g2.ysh = ysh;
+    launch_k(c, MOE_K_GEMM_DOWN, gemm_grouped_kernel<1>, dim3(max_tiles8 * g2.n_ntiles),
+             dim3(kGemmThreads), 0, g2);
+
     const size_t nc = (size_t)T * H / 4;
     launch_k(c, MOE_K_COMBINE, combine_kernel, dim3((unsigned)((nc + 255) / 256)), dim3(256), 0, y,
              ysh, idx, T, H, E, k, shared ? 1 : 0, out);

@@ -19,7 +19,7 @@ constexpr int kQ4Bytes = 144;   // 4-bit K-quant superblock
 constexpr int kQ5Bytes = 176;   // 5-bit K-quant superblock
 constexpr int kSbWeights = 256;
 constexpr int kGemvMaxT = 32;   // automatic path: GEMV up to this many rows
-constexpr int kTileM = 64;      // grouped-GEMM rows (slots) per tile
+constexpr int kTileM = 160;     // grouped-GEMM rows (slots) per tile (5 blocks of 32)
 constexpr int kRouterSplits = 8;   // split-K partial logits per expert at small T
 // h is carried into the down projection as fp16 scaled by 2^-4: the SwiGLU
 // output of the Qwen3.5-shaped layer reaches ~2e4, the scale keeps a 50x
