@@ -216,7 +216,7 @@ def bench_prefill(args, torch, qm, mi, DeviceLayer):
     torch.cuda.synchronize()
     assert set(used) == {qm.MOE_PATH_MFMA}, used
     secs = time_steps(torch, step, K)
-    names = ["router_mfma", "router_topk", "x_f16", "bucket_hist", "bucket_scan",
+    names = ["x_f16", "router_split", "router_mfma", "router_topk", "bucket_hist", "bucket_scan",
              "bucket_scatter", "gemm_gateup", "gemm_down", "combine"]
     kms = kernel_profile(torch, qm, lambda i, e: step(i, e), K, names)
     slots = T * shp.k + T

@@ -114,18 +114,19 @@ typedef struct moe_opts {
 
 /* Kernel ids for moe_opts.kernel_events. */
 #define MOE_K_GEMV_FRONT 0       /* T <= 32: router partial logits; shared-expert gate/up */
-#define MOE_K_ROUTER_MFMA 1      /* fp32-MFMA router logits (large T) */
+#define MOE_K_ROUTER_MFMA 1      /* T > 32: router logits on the matrix cores (split fp16, fp32-accurate) */
 #define MOE_K_ROUTER_TOPK 2      /* top-k + weights */
 #define MOE_K_GATEUP_GEMV 3      /* decode: top-k (when routing) + routed gate/up + SwiGLU */
 #define MOE_K_DOWN_GEMV 4        /* decode: down + slot-order combine */
-#define MOE_K_X_F16 5            /* prefill: tokens to fp16 */
+#define MOE_K_X_F16 5            /* T > 32: tokens to fp16 (hi and, for the router, lo parts) */
 #define MOE_K_BUCKET_HIST 6
 #define MOE_K_BUCKET_SCAN 7
 #define MOE_K_BUCKET_SCATTER 8
 #define MOE_K_GEMM_GATEUP 9      /* prefill: grouped GEMM gate/up + SwiGLU */
 #define MOE_K_GEMM_DOWN 10       /* prefill: grouped GEMM down */
 #define MOE_K_COMBINE 11         /* prefill: slot-order combine */
-#define MOE_K_COUNT 12
+#define MOE_K_ROUTER_SPLIT 12    /* T > 32: router matrix split into fp16 hi/lo parts */
+#define MOE_K_COUNT 13
 
 /* Bytes of device workspace that router_topk, moe_layer_forward and
  * moe_layer_forward_shard need for T token rows split into num_shards shards
@@ -134,7 +135,9 @@ typedef struct moe_opts {
 size_t moe_workspace_bytes(const moe_layer_desc *desc, int32_t T, int32_t num_shards);
 
 /*
- * Router: logits[t][e] = sum_h x[t][h] * router_w[h][e] in fp32; the k largest
+ * Router: logits[t][e] = sum_h x[t][h] * router_w[h][e] to fp32 accuracy (for
+ * T > 32 on the matrix cores with each operand split into two fp16 parts,
+ * which requires |x| < 65504 and |router_w| < 64); the k largest
  * logits in descending order (ties to the lower expert index) become slots
  * 0..k-1 of topk_idx; topk_w[t][j] = softmax over all E logits of expert
  * topk_idx[t][j], renormalised over the k selected -- equal to the softmax of

@@ -108,6 +108,10 @@ WsLayout ws_layout(const moe_layer_desc& d, int T, int num_shards) {
     size_t off = 0;
     L.router_ks = router_splits(T, d.hidden);
     L.router_part = off;  off = align256(off + (size_t)L.router_ks * Tz * E * 4);
+    const bool big = T > kGemvMaxT;
+    L.x_lo = off;         off = align256(off + (big ? Tz * H * 2 : 0));
+    L.w_hi = off;         off = align256(off + (big ? E * H * 2 : 0));
+    L.w_lo = off;         off = align256(off + (big ? E * H * 2 : 0));
     L.idx = off;          off = align256(off + Tz * k * 4);
     L.w = off;            off = align256(off + Tz * k * 4);
     const size_t base = off;
@@ -263,7 +267,8 @@ static int forward_common(const moe_layer_desc* desc, const float* x, int32_t T,
         idx = ridx;
         w = rw;
     }
-    return launched(launch_mfma(*desc, x, T, idx, w, shard, nshards, out, wsp, L, c));
+    return launched(launch_mfma(*desc, x, T, idx, w, shard, nshards, out, wsp, L, c,
+                                route && T > kGemvMaxT));
 }
 
 int moe_layer_forward(const moe_layer_desc* desc, const float* x, int32_t T, float* out,

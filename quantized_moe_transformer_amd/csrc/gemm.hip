@@ -384,20 +384,6 @@ gemm_grouped_kernel(GemmArgs a) {
     }
 }
 
-__global__ void __launch_bounds__(256)
-x_to_f16_kernel(const float* __restrict__ x, _Float16* __restrict__ x16, size_t n4) {
-    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= n4) return;
-    const float4 v = reinterpret_cast<const float4*>(x)[i];
-    typedef _Float16 half4 __attribute__((ext_vector_type(4)));
-    half4 h;
-    h[0] = (_Float16)v.x;
-    h[1] = (_Float16)v.y;
-    h[2] = (_Float16)v.z;
-    h[3] = (_Float16)v.w;
-    reinterpret_cast<half4*>(x16)[i] = h;
-}
-
 // out[t] = ((y[t,0] + y[t,1]) + ... + y[t,k-1]) + ysh[t]; y rows already carry
 // their routing weight, ysh the shared weight.  Slots whose expert index is
 // out of range contribute nothing.
@@ -430,7 +416,7 @@ combine_kernel(const float* __restrict__ y, const float* __restrict__ ysh,
 
 hipError_t launch_mfma(const moe_layer_desc& d, const float* x, int T, const int32_t* idx,
                        const float* w, int shard, int nshards, float* out, char* ws,
-                       const WsLayout& L, const Ctx& c) {
+                       const WsLayout& L, const Ctx& c, bool x16_ready) {
     const int H = d.hidden, E = d.n_experts, k = d.top_k;
     const bool shared = d.shared_inter > 0;
     const int Iloc = d.inter / nshards;
@@ -444,9 +430,10 @@ hipError_t launch_mfma(const moe_layer_desc& d, const float* x, int T, const int
     float* y = reinterpret_cast<float*>(ws + L.y);
     float* ysh = reinterpret_cast<float*>(ws + L.ysh);
 
-    const size_t n4 = (size_t)T * H / 4;
-    launch_k(c, MOE_K_X_F16, x_to_f16_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, x,
-             x16, n4);
+    if (!x16_ready) {
+        hipError_t e = launch_x16(x, T, H, ws, L, c);
+        if (e != hipSuccess) return e;
+    }
     hipError_t err = launch_bucket(idx, T, k, E, shared, counts, offsets, tile_off, perm, bhist, c);
     if (err != hipSuccess) return err;
     // an upper bound on the number of row tiles; blocks past the real count exit

@@ -119,6 +119,8 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 struct WsLayout {
     // shared by both paths
     size_t router_part;   // float [T][E][ks]
+    size_t x_lo;          // fp16 [T][H] low parts of x (router at large T)
+    size_t w_hi, w_lo;    // fp16 [E][H] split router matrix (router at large T)
     size_t idx, w;        // int32 / float [T][k] (routing computed inside the forward call)
     // GEMV path
     size_t hbuf;          // float [T*(k+1)][I_loc]
@@ -174,9 +176,11 @@ hipError_t launch_gemv(const moe_layer_desc& d, const float* x, int T, const int
 hipError_t launch_bucket(const int32_t* idx, int T, int k, int E, bool shared, int32_t* counts,
                          int32_t* offsets, int32_t* tile_off, int32_t* perm, int32_t* bhist,
                          const Ctx& c);
+// x16_ready: the router already wrote the fp16 tokens (L.x16)
 hipError_t launch_mfma(const moe_layer_desc& d, const float* x, int T, const int32_t* idx,
                        const float* w, int shard, int nshards, float* out, char* ws,
-                       const WsLayout& L, const Ctx& c);
+                       const WsLayout& L, const Ctx& c, bool x16_ready);
+hipError_t launch_x16(const float* x, int T, int H, char* ws, const WsLayout& L, const Ctx& c);
 hipError_t launch_reduce(const float* const* partials, int n, int64_t count, float* out,
                          hipStream_t s);
 hipError_t launch_dequant(const uint8_t* sbs, int bits, int64_t n_sb, int out_dtype, void* out,
