@@ -38,6 +38,57 @@ HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 FP16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak
 
 
+# HBM bytes per launch of the roofline kernels, from two rocprofv3 --pmc passes
+# (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch, averaged over the bench's
+# dispatches of that kernel), each multiplied by the calibration factor that the
+# same counter gives for a plain device copy of known size (bench.py
+# --copy-probe).  Keyed by the SHA-256 of the kernel's sources: when they change,
+# the counters no longer describe the kernel and traffic is reported as null.
+TRAFFIC = {
+    # decode T=1, 180 dispatches: FETCH 4760.5 KiB x 1.99980, WRITE 16.1 KiB x 1.0
+    "gemv_gateup": {"sources_sha256": "10eb62a1c6a78686e8526d0a0cfaf2b5e475d2394f18a09bb74f4ed2a461b314",
+                    "fetch_bytes": 9748452, "write_bytes": 16448},
+    # prefill T=4096, 5 dispatches: FETCH 223885.0 KiB x 1.99980, WRITE 36864.0 KiB x 1.0
+    "gemm_gateup": {"sources_sha256": "da7f0db95ea1262963b3db902c3856fb0e262d14324706cf3cdf7ea2f3472f67",
+                    "fetch_bytes": 458469725, "write_bytes": 37748736},
+}
+FETCH_SIZE_FACTOR = 1.99980   # plain 256 MiB copy: true bytes read / FETCH_SIZE bytes
+WRITE_SIZE_FACTOR = 1.0
+TRAFFIC_SOURCES = {
+    "gemv_gateup": ["gemv.hip", "topk.h", "moe_internal.h"],
+    "gemm_gateup": ["gemm.hip", "moe_internal.h"],
+}
+
+
+def sources_sha(kernel):
+    import hashlib
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "quantized_moe_transformer_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_for(kernel):
+    t = TRAFFIC.get(kernel)
+    if t is None or t["sources_sha256"] != sources_sha(kernel):
+        return None
+    return t["fetch_bytes"] + t["write_bytes"]
+
+
+def copy_probe(torch, mib):
+    """A plain device-to-device copy of known size, for calibrating the
+    FETCH_SIZE / WRITE_SIZE counters (one torch copy kernel per call)."""
+    n = mib * (1 << 20) // 4
+    src = torch.randn(n, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4,
+                      "dispatches": 5}), flush=True)
+
+
 class HipEvents:
     """hipEvent_t handles from libamdhip64 (torch's events only see torch's own
     stream bookkeeping; these are passed into the library call)."""
@@ -185,7 +236,7 @@ def bench_decode(args, torch, qm, mi, DeviceLayer):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": gateup_bytes / (gateup_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "traffic": None,
+            "traffic": traffic_for("gemv_gateup"),
             "algorithmic_bytes_per_launch": gateup_bytes,
             "avg_launch_ms": gateup_ms,
         },
@@ -243,7 +294,7 @@ def bench_prefill(args, torch, qm, mi, DeviceLayer):
             "peak": FP16_MFMA_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": flops_gu / (gu_ms * 1e-3) / 1e12 / FP16_MFMA_PEAK_TFLOPS,
-            "traffic": None,
+            "traffic": traffic_for("gemm_gateup"),
             "algorithmic_flops_per_launch": flops_gu,
             "avg_launch_ms": gu_ms,
         },
@@ -292,6 +343,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle decode work")
     ap.add_argument("--cpu-prefill-rows", type=int, default=2048)
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain MIB-MiB device copy five times (counter calibration)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -308,6 +361,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_probe:
+        copy_probe(torch, args.copy_probe)
+        return
 
     print("[bench] decode T=1 ...", file=sys.stderr, flush=True)
     dec, dec_layer, pool = bench_decode(args, torch, qm, mi, DeviceLayer)
