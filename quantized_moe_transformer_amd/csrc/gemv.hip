@@ -122,8 +122,10 @@ __device__ __forceinline__ float wave_sum8(float v[8]) {
 // gate/up + SwiGLU for a group of rows of one expert instance
 // ---------------------------------------------------------------------------
 
-constexpr int kGuWaves = 2;   // waves per gate/up workgroup
+constexpr int kGuWaves = 2;   // waves per routed gate/up workgroup
 constexpr int kGuSteps = 4;   // row steps per wave (each step: gate row + up row)
+constexpr int kShWaves = 4;   // waves per shared-expert gate/up workgroup (front kernel)
+constexpr int kShSteps = 1;   // their row steps per wave
 
 // The activations under one lane's pieces (they do not depend on the expert).
 template <int LPR, int NSBL>
@@ -158,8 +160,8 @@ struct XRegs {
 
 // LPR: lanes per row (8 * superblocks per row, capped at 64); NSBL:
 // superblocks per lane per row (H / 2048 when LPR = 64, else 1).
-// Rows [rbase, rbase + kGuSteps * 64/LPR) of the instance, h written to hrow.
-template <int LPR, int NSBL>
+// Rows [rbase, rbase + STEPS * 64/LPR) of the instance, h written to hrow.
+template <int LPR, int NSBL, int STEPS>
 __device__ __forceinline__ void gateup_rows(const uint8_t* __restrict__ G,
                                             const uint8_t* __restrict__ U, int H, int Iloc,
                                             int i0, XRegs<LPR, NSBL>& X, int rbase,
@@ -170,10 +172,10 @@ __device__ __forceinline__ void gateup_rows(const uint8_t* __restrict__ G,
     const int sbi = task >> 3, piece = task & 7, c = piece >> 1, hh = piece & 1;
     const int nsb_row = H / kSbWeights;
 
-    SbHead hg[kGuSteps][NSBL], hu[kGuSteps][NSBL];
-    uint4 qg[kGuSteps][NSBL], qu[kGuSteps][NSBL];
+    SbHead hg[STEPS][NSBL], hu[STEPS][NSBL];
+    uint4 qg[STEPS][NSBL], qu[STEPS][NSBL];
 #pragma unroll
-    for (int st = 0; st < kGuSteps; ++st) {
+    for (int st = 0; st < STEPS; ++st) {
         const int r = min(rbase + st * RS + rslot, Iloc - 1);   // tail rows clamped, discarded
         const size_t row = (size_t)(i0 + r) * nsb_row;
 #pragma unroll
@@ -192,9 +194,9 @@ __device__ __forceinline__ void gateup_rows(const uint8_t* __restrict__ G,
     float (&xh)[NSBL][16] = X.xh;
     float (&sl)[NSBL] = X.sl;
     float (&sh)[NSBL] = X.sh;
-    float v[2 * kGuSteps];
+    float v[2 * STEPS];
 #pragma unroll
-    for (int st = 0; st < kGuSteps; ++st) {
+    for (int st = 0; st < STEPS; ++st) {
         float pg = 0.f, pu = 0.f;
 #pragma unroll
         for (int it = 0; it < NSBL; ++it) {
@@ -204,7 +206,7 @@ __device__ __forceinline__ void gateup_rows(const uint8_t* __restrict__ G,
         v[2 * st] = pg;
         v[2 * st + 1] = pu;
     }
-    if (LPR == 64) {
+    if (LPR == 64 && STEPS == 4) {
         // one row per step: value 2*st (+1 for up) ends on lanes with
         // bits (5,4,3) = (st>>1, st&1, 0 gate / 1 up)
         const float s = wave_sum8(v);
@@ -214,7 +216,7 @@ __device__ __forceinline__ void gateup_rows(const uint8_t* __restrict__ G,
         if ((lane & 15) == 0 && r < Iloc) hrow[r] = silu_f(s) * other;
     } else {
 #pragma unroll
-        for (int st = 0; st < kGuSteps; ++st) {
+        for (int st = 0; st < STEPS; ++st) {
             const float gs = wave_sum_group(v[2 * st], LPR);
             const float us = wave_sum_group(v[2 * st + 1], LPR);
             const int r = rbase + st * RS + rslot;
@@ -247,51 +249,72 @@ struct GemvArgs {
 };
 
 constexpr int kRtE = 32;       // experts per router workgroup
-constexpr int kRtMaxRows = 512;   // rows of H per split (H / kRouterSplits) at most
 
 // ---------------------------------------------------------------------------
 // front: router partial logits and the shared expert's gate/up
 // ---------------------------------------------------------------------------
 
-// Partial logits of TT tokens x kRtE experts over H / kRouterSplits rows of
-// H: eight row groups of 32 lanes (one lane per expert, 128-byte rows of the
-// router matrix), summed in a fixed order in LDS.
-template <int TT>
+// Partial logits of TT tokens x kRtE experts over the H / kRouterSplits rows
+// of one split (NSB = H / 256, so 32 * NSB rows).  Thread (q, g): four
+// consecutive experts 4q..4q+3 (one 16-byte load per row when E % 4 == 0)
+// of rows g, g + 32, ...; all of its router loads are issued before the
+// tokens arrive in LDS.  The 32 row groups are summed in a fixed order.
+template <int TT, int NSB>
 __device__ __forceinline__ void router_role(const GemvArgs& a, int rb) {
-    __shared__ float xs[TT][kRtMaxRows];
-    __shared__ float red[8][TT][kRtE];
     constexpr int KS = kRouterSplits;
+    constexpr int ROWS = 32 * NSB;
+    __shared__ float xs[TT][ROWS];
+    __shared__ float red[32][TT][kRtE];
     const int n_ec = (a.E + kRtE - 1) / kRtE;
     const int tb = rb / (n_ec * KS);
     const int rem = rb % (n_ec * KS);
     const int ec = rem / KS, ks = rem % KS;
     const int t0 = tb * TT;
     const int nt = min(TT, a.T - t0);
-    const int rows = a.H / KS;            // a multiple of 32
-    const int h0 = ks * rows;
+    const int h0 = ks * ROWS;
     const int tid = threadIdx.x;
-    for (int i = tid; i < TT * rows; i += blockDim.x) {
-        const int tt = i / rows, hh = i % rows;
+    const int q = tid & 7, g = tid >> 3;
+    const int e0 = ec * kRtE + 4 * q;
+    float wv[NSB][4];
+    if ((a.E & 3) == 0 && e0 + 3 < a.E) {
+#pragma unroll
+        for (int r = 0; r < NSB; ++r) {
+            const float4 f =
+                *reinterpret_cast<const float4*>(a.router_w + (size_t)(h0 + g + 32 * r) * a.E + e0);
+            wv[r][0] = f.x;
+            wv[r][1] = f.y;
+            wv[r][2] = f.z;
+            wv[r][3] = f.w;
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < NSB; ++r)
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                wv[r][c] = a.router_w[(size_t)(h0 + g + 32 * r) * a.E + min(e0 + c, a.E - 1)];
+    }
+    for (int i = tid; i < TT * ROWS; i += blockDim.x) {
+        const int tt = i / ROWS, hh = i % ROWS;
         xs[tt][hh] = tt < nt ? a.x[(size_t)(t0 + tt) * a.H + h0 + hh] : 0.f;
     }
     __syncthreads();
-    const int el = tid & 31, g = tid >> 5;   // expert within chunk, row group (8)
-    const int e = min(ec * kRtE + el, a.E - 1);
-    float acc[TT];
+    float acc[TT][4];
 #pragma unroll
-    for (int i = 0; i < TT; ++i) acc[i] = 0.f;
-    for (int r0 = 0; r0 < rows; r0 += 32) {   // 4 rows per row group per pass
-        float wv[4];
+    for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) wv[i] = a.router_w[(size_t)(h0 + r0 + g + 8 * i) * a.E + e];
+        for (int c = 0; c < 4; ++c) acc[tt][c] = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+    for (int r = 0; r < NSB; ++r)
 #pragma unroll
-            for (int tt = 0; tt < TT; ++tt)
-                acc[tt] = __builtin_fmaf(xs[tt][r0 + g + 8 * i], wv[i], acc[tt]);
-    }
+        for (int tt = 0; tt < TT; ++tt) {
+            const float xv = xs[tt][g + 32 * r];
 #pragma unroll
-    for (int tt = 0; tt < TT; ++tt) red[g][tt][el] = acc[tt];
+            for (int c = 0; c < 4; ++c) acc[tt][c] = __builtin_fmaf(xv, wv[r][c], acc[tt][c]);
+        }
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) red[g][tt][4 * q + c] = acc[tt][c];
     __syncthreads();
     if (tid < TT * kRtE) {
         const int tt = tid / kRtE, ee = tid % kRtE;
@@ -299,7 +322,7 @@ __device__ __forceinline__ void router_role(const GemvArgs& a, int rb) {
         if (tt < nt && eg < a.E) {
             float s = red[0][tt][ee];
 #pragma unroll
-            for (int q = 1; q < 8; ++q) s += red[q][tt][ee];
+            for (int gg = 1; gg < 32; ++gg) s += red[gg][tt][ee];
             a.part[((size_t)(t0 + tt) * a.E + eg) * KS + ks] = s;
         }
     }
@@ -310,23 +333,24 @@ __global__ void __launch_bounds__(256)
 gemv_front_kernel(GemvArgs a) {
     const int b = blockIdx.x;
     if (b < a.n_router_blocks) {
-        router_role<TT>(a, b);
+        router_role<TT, (LPR / 8) * NSBL>(a, b);
         return;
     }
-    // shared expert: blocks per token = shared_rows_blocks, 4 waves each
+    // shared expert: blocks per token = shared_rows_blocks, kShWaves waves each
     const int sb = b - a.n_router_blocks;
     const int t = sb / a.shared_rows_blocks;
     const int rblk = sb % a.shared_rows_blocks;
     const int Iloc = a.Is / a.nshards, i0 = a.shard * Iloc;
     const int wave = threadIdx.x >> 6;
-    constexpr int rows_per_wave = kGuSteps * (64 / LPR);
-    const int rbase = (rblk * 4 + wave) * rows_per_wave;
+    if (wave >= kShWaves) return;
+    constexpr int rows_per_wave = kShSteps * (64 / LPR);
+    const int rbase = (rblk * kShWaves + wave) * rows_per_wave;
     if (rbase >= Iloc) return;
     const int p = t * a.nslot + a.k;
     XRegs<LPR, NSBL> X;
     X.load(a.x + (size_t)t * a.H);
-    gateup_rows<LPR, NSBL>(a.sh_gate, a.sh_up, a.H, Iloc, i0, X, rbase,
-                           a.hbuf + (size_t)p * a.hstride);
+    gateup_rows<LPR, NSBL, kShSteps>(a.sh_gate, a.sh_up, a.H, Iloc, i0, X, rbase,
+                                     a.hbuf + (size_t)p * a.hstride);
 }
 
 // routed experts: grid (row blocks, T*k)
@@ -359,8 +383,8 @@ gemv_gateup_kernel(GemvArgs a) {
     const int rbase = (blockIdx.x * kGuWaves + wave) * rows_per_wave;
     if (rbase >= Iloc) return;
     const int p = t * a.nslot + j;
-    gateup_rows<LPR, NSBL>(a.gate + (size_t)e * mat, a.up + (size_t)e * mat, a.H, Iloc, i0, X,
-                           rbase, a.hbuf + (size_t)p * a.hstride);
+    gateup_rows<LPR, NSBL, kGuSteps>(a.gate + (size_t)e * mat, a.up + (size_t)e * mat, a.H, Iloc,
+                                     i0, X, rbase, a.hbuf + (size_t)p * a.hstride);
 }
 
 // ---------------------------------------------------------------------------
@@ -374,6 +398,7 @@ constexpr int kDnPasses = 2;   // row passes per wave in the down kernel
 __global__ void __launch_bounds__(1024)
 gemv_down_kernel(GemvArgs a, int lprd) {
     __shared__ float ys[17][kDnPasses * 64];
+    __shared__ float s_wt[17];   // each slot's weight (0 for an invalid expert)
     const int t = blockIdx.y;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int nw = blockDim.x >> 6;
@@ -386,15 +411,19 @@ gemv_down_kernel(GemvArgs a, int lprd) {
         const uint8_t* D;
         int Iexp;
         bool valid = true;
+        float wj;
         if (j < a.k) {
             const int e = a.idx[(size_t)t * a.k + j];
+            wj = a.w[(size_t)t * a.k + j];
             valid = (unsigned)e < (unsigned)a.E;
             D = a.down + (size_t)(valid ? e : 0) * ((size_t)H * a.I / kSbWeights * kQ5Bytes);
             Iexp = a.I;
         } else {
+            wj = a.sw;
             D = a.sh_down;
             Iexp = a.Is;
         }
+        if (lane == 0) s_wt[j] = valid ? wj : 0.f;
         const int Iloc = Iexp / a.nshards, i0 = a.shard * Iloc;
         SbHead hd[kDnPasses];
         uint4 qh[kDnPasses], qs[kDnPasses];
@@ -432,16 +461,7 @@ gemv_down_kernel(GemvArgs a, int lprd) {
         const int o = obase + r;
         if (o < H) {
             float acc = 0.f;
-            for (int j = 0; j < a.nslot; ++j) {
-                float wj;
-                if (j < a.k) {
-                    const int e = a.idx[(size_t)t * a.k + j];
-                    wj = (unsigned)e < (unsigned)a.E ? a.w[(size_t)t * a.k + j] : 0.f;
-                } else {
-                    wj = a.sw;
-                }
-                acc = __builtin_fmaf(wj, ys[j][r], acc);
-            }
+            for (int j = 0; j < a.nslot; ++j) acc = __builtin_fmaf(s_wt[j], ys[j][r], acc);
             a.out[(size_t)t * H + o] = acc;
         }
     }
@@ -513,7 +533,7 @@ static hipError_t launch_front(GemvArgs& a, bool route, bool shared, const WsLay
     a.n_router_blocks = route ? ((a.T + TT - 1) / TT) * n_ec * kRouterSplits : 0;
     int n_shared = 0;
     if (shared) {
-        const int rows_per_block = 4 * kGuSteps * (64 / lanes_per_row(nsb));
+        const int rows_per_block = kShWaves * kShSteps * (64 / lanes_per_row(nsb));
         const int Iloc = a.Is / a.nshards;
         a.shared_rows_blocks = (Iloc + rows_per_block - 1) / rows_per_block;
         n_shared = a.shared_rows_blocks * a.T;

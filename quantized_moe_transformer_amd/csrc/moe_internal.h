@@ -94,9 +94,24 @@ __device__ __forceinline__ uint32_t piece_byte(const uint4& v, int b) {
 // Wave reductions (64 lanes), fixed butterfly order: deterministic
 // ---------------------------------------------------------------------------
 
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov_f(float v) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over aligned groups of `group` lanes (a power of two <= 64), the same
+// bits in every lane of a group.  Up to 16 lanes by DPP moves inside a row
+// (xor 1, xor 2, half-row mirror, row mirror: each step adds two equal
+// groups that mirror each other, and a + b == b + a), beyond that by lane
+// exchanges.
 __device__ __forceinline__ float wave_sum_group(float v, int group) {
-    // sum over aligned groups of `group` lanes (group a power of two <= 64)
-    for (int off = group >> 1; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    if (group >= 2) v += dpp_mov_f<0xB1>(v);    // quad_perm [1,0,3,2]
+    if (group >= 4) v += dpp_mov_f<0x4E>(v);    // quad_perm [2,3,0,1]
+    if (group >= 8) v += dpp_mov_f<0x141>(v);   // row_half_mirror
+    if (group >= 16) v += dpp_mov_f<0x140>(v);  // row_mirror
+    if (group >= 32) v += __shfl_xor(v, 16, 64);
+    if (group >= 64) v += __shfl_xor(v, 32, 64);
     return v;
 }
 

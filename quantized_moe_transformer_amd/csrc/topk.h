@@ -14,19 +14,14 @@ namespace moe {
 // Wave-wide maximum of v (every lane gets it): within each 16-lane row by DPP
 // moves (xor 1, xor 2, half-row mirror, row mirror), then across the four
 // rows through lane reads.  fmaxf ignores NaN operands.
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float v) {
-    return __builtin_bit_cast(
-        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
-}
 __device__ __forceinline__ float readlane_f(float v, int l) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
 }
 __device__ __forceinline__ float wave_max(float v) {
-    v = fmaxf(v, dpp_f<0xB1>(v));    // quad_perm [1,0,3,2]
-    v = fmaxf(v, dpp_f<0x4E>(v));    // quad_perm [2,3,0,1]
-    v = fmaxf(v, dpp_f<0x141>(v));   // row_half_mirror
-    v = fmaxf(v, dpp_f<0x140>(v));   // row_mirror
+    v = fmaxf(v, dpp_mov_f<0xB1>(v));    // quad_perm [1,0,3,2]
+    v = fmaxf(v, dpp_mov_f<0x4E>(v));    // quad_perm [2,3,0,1]
+    v = fmaxf(v, dpp_mov_f<0x141>(v));   // row_half_mirror
+    v = fmaxf(v, dpp_mov_f<0x140>(v));   // row_mirror
     return fmaxf(fmaxf(readlane_f(v, 0), readlane_f(v, 16)),
                  fmaxf(readlane_f(v, 32), readlane_f(v, 48)));
 }
@@ -34,10 +29,10 @@ __device__ __forceinline__ float wave_max(float v) {
 // Sum over lanes 0-15 (row 0), the same bits in each of them: each step adds
 // two equal-sized groups that mirror each other, and a + b == b + a.
 __device__ __forceinline__ float row_sum(float v) {
-    v += dpp_f<0xB1>(v);
-    v += dpp_f<0x4E>(v);
-    v += dpp_f<0x141>(v);
-    v += dpp_f<0x140>(v);
+    v += dpp_mov_f<0xB1>(v);
+    v += dpp_mov_f<0x4E>(v);
+    v += dpp_mov_f<0x141>(v);
+    v += dpp_mov_f<0x140>(v);
     return v;
 }
 
