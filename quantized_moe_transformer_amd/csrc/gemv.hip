@@ -91,39 +91,38 @@ __device__ __forceinline__ uint4 stream_load(const uint8_t* p) {
     return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
-// Sum of each of 8 values over the 64 lanes of a wave, by exchanging halves
-// (values 0-3 stay on lanes with bit 5 clear, 4-7 on the others, and so on):
-// 11 cross-lane moves instead of 48.  Lane l ends with the sum of value
-// 4*b5 + 2*b4 + b3 (b = bits of l).  Fixed order: deterministic.
-__device__ __forceinline__ float wave_sum8(float v[8]) {
+// Sum of each of N values (N = 2, 4 or 8) over the 64 lanes of a wave, by
+// exchanging halves: values 0..N/2-1 stay on lanes with bit 5 clear, the rest
+// on the others, then bit 4, and so on (log2 N lane exchanges instead of
+// N * 6), and the rest of the sum inside groups of 64/N lanes.  Lane l ends
+// with the sum of value sum_s bit(5 - s, l) * N / 2^(s+1).  Fixed order:
+// deterministic.
+template <int N>
+__device__ __forceinline__ float wave_sum_n(const float* v) {
+    static_assert(N == 2 || N == 4 || N == 8, "2, 4 or 8 values");
     const int lane = threadIdx.x & 63;
-    float a[4], b[2];
-    const bool u5 = lane & 32, u4 = lane & 16, u3 = lane & 8;
+    float cur[N];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float keep = u5 ? v[4 + i] : v[i];
-        const float give = u5 ? v[i] : v[4 + i];
-        a[i] = keep + __shfl_xor(give, 32, 64);
-    }
+    for (int i = 0; i < N; ++i) cur[i] = v[i];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const float keep = u4 ? a[2 + i] : a[i];
-        const float give = u4 ? a[i] : a[2 + i];
-        b[i] = keep + __shfl_xor(give, 16, 64);
+    for (int n = N, off = 32; n > 1; n >>= 1, off >>= 1) {
+        const bool up = lane & off;
+#pragma unroll
+        for (int i = 0; i < n / 2; ++i) {
+            const float keep = up ? cur[n / 2 + i] : cur[i];
+            const float give = up ? cur[i] : cur[n / 2 + i];
+            cur[i] = keep + __shfl_xor(give, off, 64);
+        }
     }
-    float s = (u3 ? b[1] : b[0]) + __shfl_xor(u3 ? b[0] : b[1], 8, 64);
-    s += __shfl_xor(s, 4, 64);
-    s += __shfl_xor(s, 2, 64);
-    s += __shfl_xor(s, 1, 64);
-    return s;
+    return wave_sum_group(cur[0], 64 / N);
 }
 
 // ---------------------------------------------------------------------------
 // gate/up + SwiGLU for a group of rows of one expert instance
 // ---------------------------------------------------------------------------
 
-constexpr int kGuWaves = 2;   // waves per routed gate/up workgroup
-constexpr int kGuSteps = 4;   // row steps per wave (each step: gate row + up row)
+constexpr int kGuWaves = 4;   // waves per routed gate/up workgroup
+constexpr int kGuSteps = 2;   // row steps per wave (each step: gate row + up row)
 constexpr int kShWaves = 4;   // waves per shared-expert gate/up workgroup (front kernel)
 constexpr int kShSteps = 1;   // their row steps per wave
 
@@ -206,14 +205,15 @@ __device__ __forceinline__ void gateup_rows(const uint8_t* __restrict__ G,
         v[2 * st] = pg;
         v[2 * st + 1] = pu;
     }
-    if (LPR == 64 && STEPS == 4) {
-        // one row per step: value 2*st (+1 for up) ends on lanes with
-        // bits (5,4,3) = (st>>1, st&1, 0 gate / 1 up)
-        const float s = wave_sum8(v);
-        const float other = __shfl_xor(s, 8, 64);
-        const int st = ((lane >> 5) << 1) | ((lane >> 4) & 1);
-        const int r = rbase + st;
-        if ((lane & 15) == 0 && r < Iloc) hrow[r] = silu_f(s) * other;
+    if (LPR == 64 && (STEPS == 1 || STEPS == 2 || STEPS == 4)) {
+        // one row per step: value 2*st (+1 for up) ends on the lanes whose
+        // top log2(2*STEPS) bits spell it; gate and up of a step sit G lanes
+        // apart
+        constexpr int G = 32 / STEPS;
+        const float s = wave_sum_n<2 * STEPS>(v);
+        const float other = __shfl_xor(s, G, 64);
+        const int r = rbase + lane / (2 * G);
+        if ((lane & (2 * G - 1)) == 0 && r < Iloc) hrow[r] = silu_f(s) * other;
     } else {
 #pragma unroll
         for (int st = 0; st < STEPS; ++st) {

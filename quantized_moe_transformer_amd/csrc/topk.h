@@ -11,19 +11,38 @@
 
 namespace moe {
 
-// Wave-wide maximum of v (every lane gets it): within each 16-lane row by DPP
-// moves (xor 1, xor 2, half-row mirror, row mirror), then across the four
-// rows through lane reads.  fmaxf ignores NaN operands.
-__device__ __forceinline__ float readlane_f(float v, int l) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+// Logits are ranked as int32 keys with the same order as the floats: the
+// bits of a non-negative float, and for a negative one the bits with the
+// magnitude field flipped.  -0 is first made +0 (they compare equal), a NaN
+// logit ranks as -inf, and INT32_MIN (below -inf's key) marks an expert that
+// is taken or does not exist.
+__device__ __forceinline__ int logit_key(float f) {
+    if (f != f) f = -INFINITY;
+    const int i = __builtin_bit_cast(int, f + 0.0f);
+    return i < 0 ? i ^ 0x7fffffff : i;
 }
-__device__ __forceinline__ float wave_max(float v) {
-    v = fmaxf(v, dpp_mov_f<0xB1>(v));    // quad_perm [1,0,3,2]
-    v = fmaxf(v, dpp_mov_f<0x4E>(v));    // quad_perm [2,3,0,1]
-    v = fmaxf(v, dpp_mov_f<0x141>(v));   // row_half_mirror
-    v = fmaxf(v, dpp_mov_f<0x140>(v));   // row_mirror
-    return fmaxf(fmaxf(readlane_f(v, 0), readlane_f(v, 16)),
-                 fmaxf(readlane_f(v, 32), readlane_f(v, 48)));
+__device__ __forceinline__ float key_logit(int k) {
+    return __builtin_bit_cast(float, k < 0 ? k ^ 0x7fffffff : k);
+}
+constexpr int kKeyNone = (int)0x80000000;
+
+// Wave-wide maximum of int keys, returned wave-uniform: within each 16-lane
+// row by DPP moves (xor 1, xor 2, half-row mirror, row mirror), then row 0
+// into row 1 and row 2 into row 3 (row_bcast:15), rows 0-1 into rows 2-3
+// (row_bcast:31), and lane 63 read out.
+// Lanes that a step's row mask leaves out read INT32_MIN, the identity of max.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_max_step(int v) {
+    return max(v, __builtin_amdgcn_update_dpp(kKeyNone, v, CTRL, ROWS, 0xf, false));
+}
+__device__ __forceinline__ int wave_max_key(int v) {
+    v = dpp_max_step<0xB1, 0xf>(v);    // quad_perm [1,0,3,2]
+    v = dpp_max_step<0x4E, 0xf>(v);    // quad_perm [2,3,0,1]
+    v = dpp_max_step<0x141, 0xf>(v);   // row_half_mirror
+    v = dpp_max_step<0x140, 0xf>(v);   // row_mirror
+    v = dpp_max_step<0x142, 0xa>(v);   // row_bcast:15 into rows 1 and 3
+    v = dpp_max_step<0x143, 0xc>(v);   // row_bcast:31 into rows 2 and 3
+    return __builtin_amdgcn_readlane(v, 63);
 }
 
 // Sum over lanes 0-15 (row 0), the same bits in each of them: each step adds
@@ -41,11 +60,12 @@ __device__ __forceinline__ float row_sum(float v) {
 // ... (NE per lane: E <= 64*NE); every partial load is issued before any sum,
 // and each expert's partials are added in ascending split order.
 //
-// Each of the k rounds takes the wave maximum m of the remaining logits, then
-// the lowest expert index holding m (ballots of l == m, scanned from the
-// lowest expert block), so ties go to the lower index; the winner's logit is
-// replaced by NaN, which the maximum ignores and no compare matches.  A NaN
-// logit counts as -inf: never preferred over a number.  Lane j keeps slot j.
+// Each round takes the wave maximum m of the remaining keys and gives the
+// next slots to every expert holding m, in ascending expert index (ballots
+// of key == m, scanned from the lowest expert block), so ties go to the
+// lower index; a tie group larger than the slots left is cut at the lowest
+// indices.  Selected experts' keys become INT32_MIN.  A NaN logit counts as
+// -inf: never preferred over a number.  Lane j keeps slot j.
 template <int NE, int KS>
 __device__ __forceinline__ void wave_topk(const float* __restrict__ part, int E, int k, int t,
                                           int32_t* idx_row, float* w_row) {
@@ -70,41 +90,39 @@ __device__ __forceinline__ void wave_topk(const float* __restrict__ part, int E,
             }
         }
     }
-    const float qnan = __builtin_nanf("");
-    float l[NE];
+    int key[NE];
 #pragma unroll
     for (int i = 0; i < NE; ++i) {
         float s = pv[i][0];
 #pragma unroll
         for (int q = 1; q < KS; ++q) s += pv[i][q];
-        if (s != s) s = -INFINITY;
-        l[i] = lane + 64 * i < E ? s : qnan;
+        key[i] = lane + 64 * i < E ? logit_key(s) : kKeyNone;
     }
     float my_l = -INFINITY, top = 0.f;
     int my_e = 0;
-    for (int j = 0; j < k; ++j) {
-        float m = l[0];
+    int j = 0;   // slots filled (wave-uniform)
+    while (j < k) {
+        int m = key[0];
 #pragma unroll
-        for (int i = 1; i < NE; ++i) m = fmaxf(m, l[i]);
-        m = wave_max(m);
-        if (j == 0) top = m;
-        int wi = 0;
-        uint64_t wb = 0;
+        for (int i = 1; i < NE; ++i) m = max(m, key[i]);
+        m = wave_max_key(m);
+        if (m == kKeyNone) break;   // nothing left (cannot happen for k <= E)
+        const float ml = key_logit(m);
+        if (j == 0) top = ml;
 #pragma unroll
-        for (int i = NE - 1; i >= 0; --i) {
-            const uint64_t b = __builtin_amdgcn_ballot_w64(l[i] == m);
-            if (b) {
-                wi = i;
-                wb = b;
+        for (int i = 0; i < NE; ++i) {
+            const bool hit = key[i] == m;
+            uint64_t b = __builtin_amdgcn_ballot_w64(hit);
+            if (hit) key[i] = kKeyNone;
+            while (b != 0 && j < k) {
+                const int wl = (int)__builtin_ctzll(b);
+                b &= b - 1;
+                if (lane == j) {
+                    my_l = ml;
+                    my_e = wl + 64 * i;
+                }
+                ++j;
             }
-        }
-        const int wl = wb ? (int)__builtin_ctzll(wb) : 0;
-#pragma unroll
-        for (int i = 0; i < NE; ++i)
-            if (i == wi && lane == wl) l[i] = qnan;
-        if (lane == j) {
-            my_l = m;
-            my_e = wl + 64 * wi;
         }
     }
     // softmax of the selected logits (= the full softmax renormalised over

@@ -163,6 +163,40 @@ def test_router_topk(name, T, stream):
     assert np.allclose(gw.sum(1), 1.0, atol=1e-6)
 
 
+@pytest.mark.parametrize("dup", [4, 3])
+@pytest.mark.parametrize("T", [4, 64])
+def test_router_exact_ties(dup, T):
+    """Router columns repeated `dup` times give bit-identical logits, so every
+    selection is made of tie groups: ties go to the lower expert index, and a
+    group larger than the slots left (3 + 3 + 2 of 3 at k = 8) is cut at the
+    lowest indices."""
+    w, layer = workload("decode")
+    shp = w.shape
+    r = layer["router_w"].copy()
+    n = shp.E // dup
+    for q in range(1, dup):
+        r[:, q * n:(q + 1) * n] = r[:, :n]
+    lay = dict(layer, router_w=r)
+    dl = DeviceLayer.from_shape(lay, shp)
+    x = mi.make_tokens(shp, w.seed, T, stream=11)
+    oi, ow, owd, logits = oracle.router(x, r, shp.k)
+    assert all(len(set(logits[t, oi[t]].tolist())) < shp.k for t in range(T))
+    say(f"router ties dup={dup} T={T}")
+    gi, gw = run_router(dl, x)
+    if T <= 32:
+        # split-K fp32 sums in a fixed order: repeated columns tie exactly
+        assert np.array_equal(gi, oi), (gi[:2], oi[:2])
+        assert np.abs(gw - owd).max() <= 2e-5
+        ol = oracle.Layer.from_shape(lay, shp)
+        got, used = run_forward(dl, x)
+        assert used == qm.MOE_PATH_GEMV
+        assert rel_err(got, oracle.forward(ol, x)) <= GEMV_TOL
+    else:
+        exact, exempt, wrong = topk_check(gi, oi, logits)
+        assert len(wrong) == 0
+        assert np.abs(gw[exact] - owd[exact]).max() <= 2e-5
+
+
 # ---------------------------------------------------------------------------
 # bucketing: bit-exact against the oracle's stable counting sort
 # ---------------------------------------------------------------------------
