@@ -67,6 +67,33 @@ __device__ __forceinline__ int find_group(const int32_t* __restrict__ tile_off, 
 // Dequantise one 16-byte code piece (32 weights: sub-block 2c low nibbles and
 // sub-block 2c+1 high nibbles) to fp16 and store it into an LDS row at k
 // offsets 16*hh + [0,16) and 32 + 16*hh + [0,16).
+//
+// The fp16 bit pattern 0x6400 | q is the number 1024 + q (q < 1024), so one
+// and-or turns two code bytes of a word into two fp16 numbers, and
+//   w = d*sc*q - dmin*m = (1024 + q) * (d*sc) - (1024*d*sc + dmin*m)
+// is one mixed-precision fma per weight (fp16 operand, fp32 arithmetic,
+// fp16 result).  The constant 1024*d*sc + dmin*m is rounded to fp32 once
+// (relative 2^-24 of a value <= 1024 |d*sc| + |dmin*m|): far below the fp16
+// rounding of w itself.
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+
+// (x & m) | o in one v_and_or_b32 (the compiler splits it into an and and an
+// or when the constants are literals).
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t o) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(m), "v"(o));
+    return r;
+}
+
+// bytes 0 and 2 of `bytes` (codes, masked by m) as the fp16 numbers 1024 + code
+__device__ __forceinline__ half2v code_pair(uint32_t bytes, uint32_t m) {
+    return __builtin_bit_cast(half2v, and_or(bytes, m, 0x64006400u));
+}
+
+__device__ __forceinline__ _Float16 mix_fma(_Float16 q1024, float ds, float c) {
+    return (_Float16)__builtin_fmaf((float)q1024, ds, c);
+}
+
 template <bool HIGH>
 __device__ __forceinline__ void dequant_piece_to_lds(const SbHead& hd, const uint4& qs,
                                                      const uint4& qh, int c, int hh,
@@ -74,25 +101,40 @@ __device__ __forceinline__ void dequant_piece_to_lds(const SbHead& hd, const uin
     float sca, ma, scb, mb;
     sub_scale_min(hd, 2 * c, sca, ma);
     sub_scale_min(hd, 2 * c + 1, scb, mb);
-    const float dsa = hd.d * sca, dma = hd.dmin * ma;
-    const float dsb = hd.d * scb, dmb = hd.dmin * mb;
+    const float dsa = hd.d * sca, dsb = hd.d * scb;
+    const float ca = -__builtin_fmaf(1024.0f, dsa, hd.dmin * ma);
+    const float cb = -__builtin_fmaf(1024.0f, dsb, hd.dmin * mb);
     const uint32_t qw[4] = {qs.x, qs.y, qs.z, qs.w};
     const uint32_t hw[4] = {qh.x, qh.y, qh.z, qh.w};
     half8 lo[2], hi[2];
 #pragma unroll
     for (int wi = 0; wi < 4; ++wi) {
-        uint32_t l4 = qw[wi] & 0x0f0f0f0fu;
-        uint32_t h4 = (qw[wi] >> 4) & 0x0f0f0f0fu;
+        half2v la, lb, ha, hb;   // codes (0, 2) and (1, 3) of the low and high nibbles
         if (HIGH) {
-            l4 |= ((hw[wi] >> (2 * c)) & 0x01010101u) << 4;
-            h4 |= ((hw[wi] >> (2 * c + 1)) & 0x01010101u) << 4;
+            const uint32_t l5 = (qw[wi] & 0x0f0f0f0fu) | (((hw[wi] >> (2 * c)) & 0x01010101u) << 4);
+            const uint32_t h5 =
+                ((qw[wi] >> 4) & 0x0f0f0f0fu) | (((hw[wi] >> (2 * c + 1)) & 0x01010101u) << 4);
+            la = code_pair(l5, 0x00ff00ffu);
+            lb = code_pair(l5 >> 8, 0x00ff00ffu);
+            ha = code_pair(h5, 0x00ff00ffu);
+            hb = code_pair(h5 >> 8, 0x00ff00ffu);
+        } else {
+            la = code_pair(qw[wi], 0x000f000fu);
+            lb = code_pair(qw[wi] >> 8, 0x000f000fu);
+            ha = code_pair(qw[wi] >> 4, 0x000f000fu);
+            hb = code_pair(qw[wi] >> 12, 0x000f000fu);
         }
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const int i = 4 * wi + b;
-            lo[i >> 3][i & 7] = (_Float16)kq_weight(dsa, dma, (float)((l4 >> (8 * b)) & 0xffu));
-            hi[i >> 3][i & 7] = (_Float16)kq_weight(dsb, dmb, (float)((h4 >> (8 * b)) & 0xffu));
-        }
+        half8& L = lo[wi >> 1];
+        half8& Hh = hi[wi >> 1];
+        const int o = 4 * (wi & 1);
+        L[o + 0] = mix_fma(la[0], dsa, ca);
+        L[o + 1] = mix_fma(lb[0], dsa, ca);
+        L[o + 2] = mix_fma(la[1], dsa, ca);
+        L[o + 3] = mix_fma(lb[1], dsa, ca);
+        Hh[o + 0] = mix_fma(ha[0], dsb, cb);
+        Hh[o + 1] = mix_fma(hb[0], dsb, cb);
+        Hh[o + 2] = mix_fma(ha[1], dsb, cb);
+        Hh[o + 3] = mix_fma(hb[1], dsb, cb);
     }
     *reinterpret_cast<half8*>(row + 16 * hh) = lo[0];
     *reinterpret_cast<half8*>(row + 16 * hh + 8) = lo[1];
@@ -150,10 +192,97 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileInfo& ti,
     if (wave >= kConsumers) {
         // ------------------------------- producers -------------------------------
         const int pt = tid - 64 * kConsumers;
+        // A: MB*32 rows x 8 chunks of 16 bytes; chunk task = pt + 256 i
+        size_t asrc[MB];
+        bool aok[MB];
+#pragma unroll
+        for (int i = 0; i < MB; ++i) {
+            const int task = pt + 256 * i;
+            const int r = task >> 3, c8 = task & 7;
+            const int src = row_src[r];
+            aok[i] = src >= 0;
+            asrc[i] = (MODE == 0 ? (size_t)max(src, 0) : (size_t)(grow0 + r)) * a.a_stride + c8 * 8;
+        }
+        uint4 areg[MB];
+        auto load_a = [&](int kk) {
+#pragma unroll
+            for (int i = 0; i < MB; ++i) {
+                areg[i] = make_uint4(0, 0, 0, 0);
+                if (aok[i]) areg[i] = *reinterpret_cast<const uint4*>(a.a_src + asrc[i] + kk * kBK);
+            }
+        };
+        auto store_a = [&](int stage) {
+#pragma unroll
+            for (int i = 0; i < MB; ++i) {
+                const int task = pt + 256 * i;
+                *reinterpret_cast<uint4*>(&lds.a[stage][task >> 3][(task & 7) * 8]) = areg[i];
+            }
+        };
+
+        if constexpr (MODE == 0) {
+            // Producer thread pt owns weight row pt of the tile (gate rows
+            // 0-127, the matching up rows 128-255) and loads the row's whole
+            // 144-byte superblock -- nine 16-byte loads, contiguous -- once per
+            // four steps into a two-slot register ring, one superblock ahead;
+            // each step dequantises its 64 weights of the current one.
+            const int col = pt & (kTN / 2 - 1);
+            const int colc = n0 + col < Iloc ? col : 0;   // ragged tile: discarded columns
+            const size_t mat = (size_t)a.I * a.H / kSbWeights * kQ4Bytes;
+            const uint8_t* m = is_sh ? (pt < kTN / 2 ? a.w_shared : a.w_shared2)
+                                     : (pt < kTN / 2 ? a.w_routed : a.w_routed2) + (size_t)g * mat;
+            const int nsb = a.H / kSbWeights;
+            const uint8_t* rowp = m + (size_t)(i0 + n0 + colc) * nsb * kQ4Bytes;
+            uint4 sbr[2][kQ4Bytes / 16];
+            auto load_sb = [&](int p, uint4* r) {
+                const uint4* src =
+                    reinterpret_cast<const uint4*>(rowp + (size_t)min(p, nsb - 1) * kQ4Bytes);
+#pragma unroll
+                for (int i = 0; i < kQ4Bytes / 16; ++i) r[i] = src[i];
+            };
+            auto deq_step = [&](const uint4* r, int c, int stage) {
+                SbHead hd;
+                hd.d = f16_bits_to_f32(r[0].x & 0xffffu);
+                hd.dmin = f16_bits_to_f32(r[0].x >> 16);
+                hd.s0 = r[0].y;
+                hd.s1 = r[0].z;
+                hd.s2 = r[0].w;
+                _Float16* dst = &lds.b[stage][pt][0];
+                dequant_piece_to_lds<false>(hd, r[1 + 2 * c], r[1 + 2 * c], c, 0, dst);
+                dequant_piece_to_lds<false>(hd, r[2 + 2 * c], r[2 + 2 * c], c, 1, dst);
+            };
+            const int last = a.nk - 1;
+            load_sb(0, sbr[0]);
+            load_sb(1, sbr[1]);
+            load_a(0);
+            store_a(0);
+            if (a.nk > 1) load_a(1);
+            deq_step(sbr[0], 0, 0);
+            __syncthreads();   // stage 0 ready
+            // steps 4*p0 .. 4*p0+7 use superblocks p0 (slot 0) and p0+1 (slot 1)
+            for (int p0 = 0; p0 < nsb; p0 += 2) {
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int kk = 4 * p0 + u;
+                    if (kk > last) break;
+                    const int nxt = kk + 1;
+                    if (nxt <= last) {
+                        store_a(nxt & 1);
+                        if (nxt + 1 <= last) load_a(nxt + 1);
+                        const int un = u + 1;   // step nxt: slot (un >> 2) & 1, sub-block pair un & 3
+                        deq_step(sbr[(un >> 2) & 1], un & 3, nxt & 1);
+                        if ((un & 3) == 3) load_sb(p0 + (un >> 2) + 2, sbr[(un >> 2) & 1]);
+                    }
+                    __syncthreads();
+                }
+            }
+            return;
+        }
         const uint8_t* wsrc[kBTasks];   // MODE 0: the row's superblocks; MODE 1: matrix base
         size_t eoff[kBTasks];           // MODE 1: element offset of the row's range
         int bhh[kBTasks], brr[kBTasks];
-        bool bok[kBTasks];
+        // weight rows past the matrix end (a ragged last column tile) read the
+        // tile's first row instead: their LDS columns only feed outputs that
+        // the epilogue discards
 #pragma unroll
         for (int q = 0; q < kBTasks; ++q) {
             const int task = pt + 64 * kProducers * q;
@@ -162,15 +291,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileInfo& ti,
             brr[q] = r;
             eoff[q] = 0;
             if (MODE == 0) {
-                const int col = r & (kTN / 2 - 1);
-                bok[q] = n0 + col < Iloc;
+                const int col = n0 + (r & (kTN / 2 - 1)) < Iloc ? (r & (kTN / 2 - 1)) : 0;
                 const size_t mat = (size_t)a.I * a.H / kSbWeights * kQ4Bytes;
                 const uint8_t* m = is_sh ? (r < kTN / 2 ? a.w_shared : a.w_shared2)
                                          : (r < kTN / 2 ? a.w_routed : a.w_routed2) + (size_t)g * mat;
                 wsrc[q] = m + (size_t)(i0 + n0 + col) * (a.H / kSbWeights) * kQ4Bytes;
             } else {
-                const int o = n0 + r;
-                bok[q] = o < a.H;
+                const int o = n0 + r < a.H ? n0 + r : n0;
                 wsrc[q] = is_sh ? a.w_shared
                                 : a.w_routed + (size_t)g * ((size_t)a.H * a.I / kSbWeights * kQ5Bytes);
                 eoff[q] = (size_t)o * Iexp + i0;
@@ -179,10 +306,6 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileInfo& ti,
         auto load_b = [&](int kk, BRegs* rg) {
 #pragma unroll
             for (int q = 0; q < kBTasks; ++q) {
-                rg[q].head = make_uint4(0, 0, 0, 0);
-                rg[q].qs = make_uint4(0, 0, 0, 0);
-                rg[q].qh = make_uint4(0, 0, 0, 0);
-                if (!bok[q]) continue;
                 if (MODE == 0) {
                     const uint8_t* sb = wsrc[q] + (kk >> 2) * kQ4Bytes;
                     rg[q].head = *reinterpret_cast<const uint4*>(sb);
@@ -212,33 +335,6 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileInfo& ti,
                                                 &lds.b[stage][brr[q]][0]);
             }
         };
-        // A: MB*32 rows x 8 chunks of 16 bytes; chunk task = pt + 256 i
-        size_t asrc[MB];
-        bool aok[MB];
-#pragma unroll
-        for (int i = 0; i < MB; ++i) {
-            const int task = pt + 256 * i;
-            const int r = task >> 3, c8 = task & 7;
-            const int src = row_src[r];
-            aok[i] = src >= 0;
-            asrc[i] = (MODE == 0 ? (size_t)max(src, 0) : (size_t)(grow0 + r)) * a.a_stride + c8 * 8;
-        }
-        uint4 areg[MB];
-        auto load_a = [&](int kk) {
-#pragma unroll
-            for (int i = 0; i < MB; ++i) {
-                areg[i] = make_uint4(0, 0, 0, 0);
-                if (aok[i]) areg[i] = *reinterpret_cast<const uint4*>(a.a_src + asrc[i] + kk * kBK);
-            }
-        };
-        auto store_a = [&](int stage) {
-#pragma unroll
-            for (int i = 0; i < MB; ++i) {
-                const int task = pt + 256 * i;
-                *reinterpret_cast<uint4*>(&lds.a[stage][task >> 3][(task & 7) * 8]) = areg[i];
-            }
-        };
-
         BRegs ring[kPD][kBTasks];
 #pragma unroll
         for (int s = 0; s < kPD; ++s)

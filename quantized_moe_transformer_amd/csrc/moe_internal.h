@@ -116,8 +116,9 @@ __device__ __forceinline__ float wave_sum_group(float v, int group) {
 }
 
 __device__ __forceinline__ float silu_f(float z) {
-    // z * sigmoid(z); expf(-z) overflows to +inf for very negative z, giving -0
-    return z / (1.0f + __expf(-z));
+    // z * sigmoid(z) with the hardware reciprocal (about 1 ulp); expf(-z)
+    // overflows to +inf for very negative z, and rcp(inf) = 0 gives -0
+    return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
 }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
