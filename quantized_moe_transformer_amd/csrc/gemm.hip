@@ -154,6 +154,7 @@ struct GemmArgs {
     float sw;
     int n_ntiles;                   // weight-row tiles per group
     int nk;                         // K steps
+    int sb_rows;                    // MODE 1: every row's K range is whole superblocks
     _Float16* h_out;                // MODE 0
     int h_stride;
     float* y;                       // MODE 1: [T*k][H]
@@ -269,6 +270,60 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileInfo& ti,
                         store_a(nxt & 1);
                         if (nxt + 1 <= last) load_a(nxt + 1);
                         const int un = u + 1;   // step nxt: slot (un >> 2) & 1, sub-block pair un & 3
+                        deq_step(sbr[(un >> 2) & 1], un & 3, nxt & 1);
+                        if ((un & 3) == 3) load_sb(p0 + (un >> 2) + 2, sbr[(un >> 2) & 1]);
+                    }
+                    __syncthreads();
+                }
+            }
+            return;
+        }
+        if (MODE == 1 && a.sb_rows) {
+            // The down rows' K ranges are whole 5-bit superblocks: producer
+            // thread pt owns output row n0 + pt and loads each 176-byte
+            // superblock of it -- eleven 16-byte loads, contiguous -- once per
+            // four steps, one superblock ahead, as the gate/up path does.
+            const int o = n0 + pt < a.H ? n0 + pt : n0;   // ragged tile: discarded rows
+            const uint8_t* m = is_sh ? a.w_shared
+                                     : a.w_routed + (size_t)g * ((size_t)a.H * a.I / kSbWeights * kQ5Bytes);
+            const int nsb = Iloc / kSbWeights;
+            const uint8_t* rowp = m + (((size_t)o * Iexp + i0) >> 8) * kQ5Bytes;
+            uint4 sbr[2][kQ5Bytes / 16];
+            auto load_sb = [&](int p, uint4* r) {
+                const uint4* src =
+                    reinterpret_cast<const uint4*>(rowp + (size_t)min(p, nsb - 1) * kQ5Bytes);
+#pragma unroll
+                for (int i = 0; i < kQ5Bytes / 16; ++i) r[i] = src[i];
+            };
+            auto deq_step = [&](const uint4* r, int c, int stage) {
+                SbHead hd;
+                hd.d = f16_bits_to_f32(r[0].x & 0xffffu);
+                hd.dmin = f16_bits_to_f32(r[0].x >> 16);
+                hd.s0 = r[0].y;
+                hd.s1 = r[0].z;
+                hd.s2 = r[0].w;
+                _Float16* dst = &lds.b[stage][pt][0];
+                dequant_piece_to_lds<true>(hd, r[3 + 2 * c], r[1], c, 0, dst);
+                dequant_piece_to_lds<true>(hd, r[4 + 2 * c], r[2], c, 1, dst);
+            };
+            const int last = a.nk - 1;
+            load_sb(0, sbr[0]);
+            load_sb(1, sbr[1]);
+            load_a(0);
+            store_a(0);
+            if (a.nk > 1) load_a(1);
+            deq_step(sbr[0], 0, 0);
+            __syncthreads();   // stage 0 ready
+            for (int p0 = 0; p0 < nsb; p0 += 2) {
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int kk = 4 * p0 + u;
+                    if (kk > last) break;
+                    const int nxt = kk + 1;
+                    if (nxt <= last) {
+                        store_a(nxt & 1);
+                        if (nxt + 1 <= last) load_a(nxt + 1);
+                        const int un = u + 1;
                         deq_step(sbr[(un >> 2) & 1], un & 3, nxt & 1);
                         if ((un & 3) == 3) load_sb(p0 + (un >> 2) + 2, sbr[(un >> 2) & 1]);
                     }
@@ -572,6 +627,7 @@ hipError_t launch_mfma(const moe_layer_desc& d, const float* x, int T, const int
     g2.w_shared = d.sh_down_q;
     g2.n_ntiles = (H + kTN - 1) / kTN;
     g2.nk = Iloc / kBK;
+    g2.sb_rows = (d.inter % kSbWeights == 0 && Iloc % kSbWeights == 0) ? 1 : 0;
     g2.y = y;
     g2.ysh = ysh;
     launch_k(c, MOE_K_GEMM_DOWN, gemm_grouped_kernel<1>, dim3(max_tiles8 * g2.n_ntiles),
