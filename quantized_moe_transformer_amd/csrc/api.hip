@@ -123,6 +123,7 @@ WsLayout ws_layout(const moe_layer_desc& d, int T, int num_shards) {
     L.counts = off;       off = align256(off + (E + 1) * 4);
     L.offsets = off;      off = align256(off + (E + 2) * 4);
     L.tile_off = off;     off = align256(off + (E + 3) * 4);
+    L.tile_rec = off;     off = align256(off + (size_t)max_row_tiles(T, (int)k, (int)E, d.shared_inter > 0) * 16);
     L.perm = off;         off = align256(off + Tz * k * 4);
     L.h16 = off;          off = align256(off + (Tz * k + Tz) * Iloc * 2);
     L.y = off;            off = align256(off + Tz * k * H * 4);
@@ -327,9 +328,10 @@ int moe_route_bucket(const moe_layer_desc* desc, const int32_t* topk_idx, int32_
     int32_t* wc = reinterpret_cast<int32_t*>(wsp + L.counts);
     int32_t* wo = reinterpret_cast<int32_t*>(wsp + L.offsets);
     int32_t* wt = reinterpret_cast<int32_t*>(wsp + L.tile_off);
+    int4* wr = reinterpret_cast<int4*>(wsp + L.tile_rec);
     int32_t* bh = reinterpret_cast<int32_t*>(wsp + L.bhist);
     if (launch_bucket(topk_idx, T, desc->top_k, desc->n_experts, desc->shared_inter > 0, wc, wo,
-                      wt, perm, bh, c) != hipSuccess)
+                      wt, wr, perm, bh, c) != hipSuccess)
         return MOE_ELAUNCH;
     const size_t E = desc->n_experts;
     if (hipMemcpyAsync(counts, wc, E * 4, hipMemcpyDeviceToDevice, s) != hipSuccess ||

@@ -40,13 +40,21 @@ bucket_hist_kernel(const int32_t* __restrict__ idx, int n, int E, int32_t* __res
 __global__ void __launch_bounds__(1024)
 bucket_scan_kernel(int nblk, int E, int T, int shared, int32_t* __restrict__ bhist,
                    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-                   int32_t* __restrict__ tile_off) {
+                   int32_t* __restrict__ tile_off, int4* __restrict__ tile_rec) {
     __shared__ int32_t sc[1024];
     __shared__ int32_t st[1024];
     const int e = threadIdx.x;
+    constexpr int kBatch = 16;   // block counts in flight per thread
     int c = 0;
     if (e < E)
-        for (int b = 0; b < nblk; ++b) c += bhist[(size_t)b * E + e];
+        for (int b0 = 0; b0 < nblk; b0 += kBatch) {
+            int v[kBatch];
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j)
+                v[j] = b0 + j < nblk ? bhist[(size_t)(b0 + j) * E + e] : 0;
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) c += v[j];
+        }
     const int tiles = (c + kTileM - 1) / kTileM;
     sc[e] = e < E ? c : 0;
     st[e] = e < E ? tiles : 0;
@@ -65,13 +73,30 @@ bucket_scan_kernel(int nblk, int E, int T, int shared, int32_t* __restrict__ bhi
         counts[e] = c;
         offsets[e] = excl;
         tile_off[e] = st[e] - tiles;
+        // the expert's row tiles: (group, first sorted row, rows, row offset)
+        for (int j = 0; j < tiles; ++j)
+            tile_rec[st[e] - tiles + j] = make_int4(e, excl + j * kTileM, min(kTileM, c - j * kTileM),
+                                                    j * kTileM);
         // per-block bases for the scatter, in place
         int base = excl;
-        for (int b = 0; b < nblk; ++b) {
-            const int h = bhist[(size_t)b * E + e];
-            bhist[(size_t)b * E + e] = base;
-            base += h;
+        for (int b0 = 0; b0 < nblk; b0 += kBatch) {
+            int v[kBatch];
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j)
+                v[j] = b0 + j < nblk ? bhist[(size_t)(b0 + j) * E + e] : 0;
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                if (b0 + j < nblk) bhist[(size_t)(b0 + j) * E + e] = base;
+                base += v[j];
+            }
         }
+    }
+    if (shared) {
+        // the shared expert (group E, all T rows in order) after the routed tiles
+        const int nsh = (T + kTileM - 1) / kTileM;
+        for (int j = threadIdx.x; j < nsh; j += blockDim.x)
+            tile_rec[st[1023] + j] = make_int4(E, sc[1023] + j * kTileM, min(kTileM, T - j * kTileM),
+                                               j * kTileM);
     }
     if (e == E - 1) {
         offsets[E] = sc[e];
@@ -117,14 +142,14 @@ bucket_scatter_kernel(const int32_t* __restrict__ idx, int n, int E,
 }
 
 hipError_t launch_bucket(const int32_t* idx, int T, int k, int E, bool shared, int32_t* counts,
-                         int32_t* offsets, int32_t* tile_off, int32_t* perm, int32_t* bhist,
-                         const Ctx& c) {
+                         int32_t* offsets, int32_t* tile_off, int4* tile_rec, int32_t* perm,
+                         int32_t* bhist, const Ctx& c) {
     const int n = T * k;
     const int nblk = bucket_blocks(T, k);
     launch_k(c, MOE_K_BUCKET_HIST, bucket_hist_kernel, dim3(nblk), dim3(kBucketBlock),
              (uint32_t)(E * sizeof(int32_t)), idx, n, E, bhist);
     launch_k(c, MOE_K_BUCKET_SCAN, bucket_scan_kernel, dim3(1), dim3(1024), 0, nblk, E, T,
-             shared ? 1 : 0, bhist, counts, offsets, tile_off);
+             shared ? 1 : 0, bhist, counts, offsets, tile_off, tile_rec);
     launch_k(c, MOE_K_BUCKET_SCATTER, bucket_scatter_kernel, dim3(nblk), dim3(kBucketBlock),
              (uint32_t)(kBucketWaves * E * sizeof(int32_t)), idx, n, E, bhist, perm);
     return hipGetLastError();

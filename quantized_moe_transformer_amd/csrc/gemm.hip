@@ -19,9 +19,11 @@
 //   4 consumer waves: MFMA only, from one LDS stage; wave w owns two 32-wide
 //     column blocks times every 32-row block the tile has (up to 5), so each
 //     fragment read from LDS feeds several MFMAs;
-//   4 producer waves: gather the next step's rows (fp16) into the other LDS
-//     stage and dequantise the next step's packed weights there, with the
-//     weight loads issued 2-3 steps ahead into a register ring;
+//   4 producer waves: dequantise the next step's packed weights into the
+//     other LDS stage, with the weight loads issued ahead into a register
+//     ring (whole superblocks per row where the layout allows);
+//   the consumer waves also gather the next step's token rows (fp16) into the
+//     other stage, so each group of waves waits only for its own loads;
 // so dequantisation (VALU) and matrix work (MFMA) run side by side.
 //
 //   gateup (MODE 0): A = token rows of x16 gathered through the expert-sorted
@@ -52,17 +54,6 @@ constexpr int kConsumers = 4;           // consumer waves (two 32-column blocks 
 constexpr int kProducers = 4;           // producer waves
 constexpr int kGemmThreads = 64 * (kConsumers + kProducers);
 constexpr int kBTasks = kTN * 2 / (64 * kProducers);   // 16-byte code pieces per producer thread
-
-__device__ __forceinline__ int find_group(const int32_t* __restrict__ tile_off, int ngroups,
-                                          int tile) {
-    // largest g with tile_off[g] <= tile (groups with no tiles are skipped)
-    int lo = 0, hi = ngroups;
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (tile_off[mid] <= tile) lo = mid; else hi = mid;
-    }
-    return lo;
-}
 
 // Dequantise one 16-byte code piece (32 weights: sub-block 2c low nibbles and
 // sub-block 2c+1 high nibbles) to fp16 and store it into an LDS row at k
@@ -148,6 +139,7 @@ struct GemmArgs {
     const int32_t* perm;            // expert-sorted slot ids
     const int32_t* offsets;         // [E+2]: group row starts (group E = shared expert)
     const int32_t* tile_off;        // [E+2]: group tile starts
+    const int4* tile_rec;           // per row tile: group, first sorted row, rows, row offset
     int T, H, E, k, I, Is, shard, nshards;
     const uint8_t *w_routed, *w_routed2, *w_shared, *w_shared2;   // MODE 0: gate, up
     const float* route_w;           // [T*k] routing weights
@@ -166,10 +158,35 @@ struct BRegs {
     uint4 head, qs, qh;
 };
 
+// A stages hold kTM rows of kBK halves with no padding; the 16-byte chunk c
+// of row r sits at chunk position c ^ (r & 7), so the 32 rows that one MFMA
+// fragment read touches spread over all banks.
+constexpr int kAStages = 3;
+__device__ __forceinline__ int a_chunk(int r, int c) { return r * (kBK / 8) + (c ^ (r & 7)); }
+
 struct __align__(16) GemmLds {
-    _Float16 a[2][kTM][kLdsRow];
+    _Float16 a[kAStages][kTM * kBK];
     _Float16 b[2][kTN][kLdsRow];
 };
+
+// One 16-byte global-to-LDS load per lane: lane l's bytes land at LDS offset
+// lds_off + 16 l.  Written as asm so that the compiler does not order it
+// against LDS reads of other stages with waits of its own; the caller waits
+// for these loads (wait_vmcnt) before any wave reads what they wrote.  Extra
+// loads in the counter only make the compiler's own vmcnt waits stricter.
+__device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_off) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(gptr), "s"(lds_off)
+                 : "m0");
+}
+
+// s_waitcnt with only the vector-memory count bounded (<= 63)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 
 // Everything a workgroup knows about its tile.
 struct TileInfo {
@@ -193,33 +210,6 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileInfo& ti,
     if (wave >= kConsumers) {
         // ------------------------------- producers -------------------------------
         const int pt = tid - 64 * kConsumers;
-        // A: MB*32 rows x 8 chunks of 16 bytes; chunk task = pt + 256 i
-        size_t asrc[MB];
-        bool aok[MB];
-#pragma unroll
-        for (int i = 0; i < MB; ++i) {
-            const int task = pt + 256 * i;
-            const int r = task >> 3, c8 = task & 7;
-            const int src = row_src[r];
-            aok[i] = src >= 0;
-            asrc[i] = (MODE == 0 ? (size_t)max(src, 0) : (size_t)(grow0 + r)) * a.a_stride + c8 * 8;
-        }
-        uint4 areg[MB];
-        auto load_a = [&](int kk) {
-#pragma unroll
-            for (int i = 0; i < MB; ++i) {
-                areg[i] = make_uint4(0, 0, 0, 0);
-                if (aok[i]) areg[i] = *reinterpret_cast<const uint4*>(a.a_src + asrc[i] + kk * kBK);
-            }
-        };
-        auto store_a = [&](int stage) {
-#pragma unroll
-            for (int i = 0; i < MB; ++i) {
-                const int task = pt + 256 * i;
-                *reinterpret_cast<uint4*>(&lds.a[stage][task >> 3][(task & 7) * 8]) = areg[i];
-            }
-        };
-
         if constexpr (MODE == 0) {
             // Producer thread pt owns weight row pt of the tile (gate rows
             // 0-127, the matching up rows 128-255) and loads the row's whole
@@ -254,9 +244,6 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileInfo& ti,
             const int last = a.nk - 1;
             load_sb(0, sbr[0]);
             load_sb(1, sbr[1]);
-            load_a(0);
-            store_a(0);
-            if (a.nk > 1) load_a(1);
             deq_step(sbr[0], 0, 0);
             __syncthreads();   // stage 0 ready
             // steps 4*p0 .. 4*p0+7 use superblocks p0 (slot 0) and p0+1 (slot 1)
@@ -267,8 +254,6 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileInfo& ti,
                     if (kk > last) break;
                     const int nxt = kk + 1;
                     if (nxt <= last) {
-                        store_a(nxt & 1);
-                        if (nxt + 1 <= last) load_a(nxt + 1);
                         const int un = u + 1;   // step nxt: slot (un >> 2) & 1, sub-block pair un & 3
                         deq_step(sbr[(un >> 2) & 1], un & 3, nxt & 1);
                         if ((un & 3) == 3) load_sb(p0 + (un >> 2) + 2, sbr[(un >> 2) & 1]);
@@ -309,9 +294,6 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileInfo& ti,
             const int last = a.nk - 1;
             load_sb(0, sbr[0]);
             load_sb(1, sbr[1]);
-            load_a(0);
-            store_a(0);
-            if (a.nk > 1) load_a(1);
             deq_step(sbr[0], 0, 0);
             __syncthreads();   // stage 0 ready
             for (int p0 = 0; p0 < nsb; p0 += 2) {
@@ -321,8 +303,6 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileInfo& ti,
                     if (kk > last) break;
                     const int nxt = kk + 1;
                     if (nxt <= last) {
-                        store_a(nxt & 1);
-                        if (nxt + 1 <= last) load_a(nxt + 1);
                         const int un = u + 1;
                         deq_step(sbr[(un >> 2) & 1], un & 3, nxt & 1);
                         if ((un & 3) == 3) load_sb(p0 + (un >> 2) + 2, sbr[(un >> 2) & 1]);
@@ -394,9 +374,6 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileInfo& ti,
 #pragma unroll
         for (int s = 0; s < kPD; ++s)
             if (s < a.nk) load_b(s, ring[s]);
-        load_a(0);
-        store_a(0);
-        if (a.nk > 1) load_a(1);
         store_b(0, ring[0], 0);
         if (kPD < a.nk) load_b(kPD, ring[0]);
         __syncthreads();   // stage 0 ready
@@ -408,8 +385,6 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileInfo& ti,
                 // while the consumers work on step kk: step kk+1 into the other stage
                 const int nxt = kk + 1;
                 if (nxt < a.nk) {
-                    store_a(nxt & 1);
-                    if (nxt + 1 < a.nk) load_a(nxt + 1);
                     store_b(nxt, ring[(u + 1) % kPD], nxt & 1);
                     if (nxt + kPD < a.nk) load_b(nxt + kPD, ring[(u + 1) % kPD]);
                 }
@@ -420,6 +395,31 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileInfo& ti,
     }
 
     // ------------------------------- consumers -------------------------------
+    // The consumer waves move the token rows (A) into LDS themselves with direct
+    // global-to-LDS loads (no registers), two steps ahead into a three-stage ring,
+    // so their waits cover only these loads and the producers' waits only the
+    // weight loads.  Thread tid's load i fills chunk slot q = tid + 256 i: row
+    // q >> 3, chunk position q & 7, i.e. logical chunk (q & 7) ^ (row & 7).  Rows
+    // past the tile's end re-read one of its rows (row r mod mcount): their
+    // results are discarded, and every load is unconditional so each step
+    // issues exactly MB of them per wave.
+    size_t asrc[MB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+        const int q = tid + 256 * i;
+        const int r = q >> 3, c = (q & 7) ^ (r & 7);
+        const int rv = r < mcount ? r : r % mcount;
+        const size_t row = MODE == 0 ? (size_t)row_src[rv] : (size_t)(grow0 + rv);
+        asrc[i] = row * a.a_stride + c * 8;
+    }
+    auto issue_a = [&](int kk) {
+        const uint32_t stage = (uint32_t)(uintptr_t)&lds.a[kk % kAStages][0];
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+            lds_dma16(a.a_src + asrc[i] + (size_t)kk * kBK,
+                      __builtin_amdgcn_readfirstlane(stage + (64 * wave + 256 * i) * 16));
+    };
+
     float16v acc[MB][2];
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
@@ -430,9 +430,17 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileInfo& ti,
     // or output blocks 2w and 2w+1 (MODE 1)
     const int bc0 = MODE == 0 ? 32 * wave : 64 * wave;
     const int bc1 = MODE == 0 ? kTN / 2 + 32 * wave : 64 * wave + 32;
+    issue_a(0);
+    if (a.nk > 1) {
+        issue_a(1);
+        wait_vmcnt<MB>();         // step 0's rows landed
+    } else {
+        wait_vmcnt<0>();
+    }
     __syncthreads();              // stage 0 ready
     for (int kk = 0; kk < a.nk; ++kk) {
         const int st = kk & 1;
+        const _Float16* sa = &lds.a[kk % kAStages][0];
 #pragma unroll
         for (int ks = 0; ks < kBK / 16; ++ks) {
             const int kof = ks * 16 + 8 * (lane >> 5);
@@ -441,12 +449,22 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileInfo& ti,
             half8 av[MB];
 #pragma unroll
             for (int i = 0; i < MB; ++i)
-                av[i] = *reinterpret_cast<const half8*>(&lds.a[st][32 * i + (lane & 31)][kof]);
+                av[i] = *reinterpret_cast<const half8*>(
+                    sa + 8 * a_chunk(32 * i + (lane & 31), 2 * ks + (lane >> 5)));
 #pragma unroll
             for (int i = 0; i < MB; ++i) {
                 acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], b0, acc[i][0], 0, 0, 0);
                 acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], b1, acc[i][1], 0, 0, 0);
             }
+        }
+        // the rows of step kk + 2 go to the stage that step kk - 1 read (all
+        // waves left it at the last barrier); step kk + 1's must have landed
+        // before the barrier
+        if (kk + 2 < a.nk) {
+            issue_a(kk + 2);
+            wait_vmcnt<MB>();
+        } else {
+            wait_vmcnt<0>();
         }
         __syncthreads();
     }
@@ -499,13 +517,13 @@ gemm_grouped_kernel(GemmArgs a) {
     const int ntile = (b >> 3) % nt;
     if (tile_raw >= ntiles) return;
     const int tile = ntiles - 1 - tile_raw;
+    const int4 rec = a.tile_rec[tile];   // written by the bucketing scan
     TileInfo ti;
-    ti.g = find_group(a.tile_off, ngroups, tile);
+    ti.g = rec.x;
     ti.is_sh = ti.g == a.E;
-    ti.m0 = (tile - a.tile_off[ti.g]) * kTM;
-    const int rows = ti.is_sh ? a.T : a.offsets[ti.g + 1] - a.offsets[ti.g];
-    ti.mcount = min(kTM, rows - ti.m0);
-    ti.grow0 = a.offsets[ti.g] + ti.m0;   // first row of the tile in sorted order
+    ti.grow0 = rec.y;                      // first row of the tile in sorted order
+    ti.mcount = rec.z;
+    ti.m0 = rec.w;
     ti.Iexp = ti.is_sh ? a.Is : a.I;
     ti.Iloc = ti.Iexp / a.nshards;
     ti.i0 = a.shard * ti.Iloc;
@@ -585,16 +603,19 @@ hipError_t launch_mfma(const moe_layer_desc& d, const float* x, int T, const int
         hipError_t e = launch_x16(x, T, H, ws, L, c);
         if (e != hipSuccess) return e;
     }
-    hipError_t err = launch_bucket(idx, T, k, E, shared, counts, offsets, tile_off, perm, bhist, c);
+    int4* tile_rec = reinterpret_cast<int4*>(ws + L.tile_rec);
+    hipError_t err =
+        launch_bucket(idx, T, k, E, shared, counts, offsets, tile_off, tile_rec, perm, bhist, c);
     if (err != hipSuccess) return err;
     // an upper bound on the number of row tiles; blocks past the real count exit
-    const int max_tiles = (T * k + kTM - 1) / kTM + E + (shared ? (T + kTM - 1) / kTM : 0);
+    const int max_tiles = max_row_tiles(T, k, E, shared);
     const int max_tiles8 = (max_tiles + 7) / 8 * 8;
 
     GemmArgs a = {};
     a.perm = perm;
     a.offsets = offsets;
     a.tile_off = tile_off;
+    a.tile_rec = tile_rec;
     a.T = T;
     a.H = H;
     a.E = E;

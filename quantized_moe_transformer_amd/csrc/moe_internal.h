@@ -146,6 +146,7 @@ struct WsLayout {
     size_t counts;        // int32 [E+1]
     size_t offsets;       // int32 [E+2]
     size_t tile_off;      // int32 [E+3]
+    size_t tile_rec;      // int4 per row tile: group, first sorted row, rows, row offset in group
     size_t perm;          // int32 [T*k]
     size_t h16;           // fp16 [T*k + T][I_loc]
     size_t y;             // float [T*k][H]
@@ -157,6 +158,11 @@ struct WsLayout {
 int router_splits(int T, int H);
 WsLayout ws_layout(const moe_layer_desc& d, int T, int num_shards);
 inline int bucket_blocks(int T, int k) { return (T * k + 1023) / 1024; }
+// upper bound on the grouped GEMM's row tiles: sum over experts of
+// ceil(count / kTileM) <= T*k / kTileM + E, plus the shared expert's
+inline int max_row_tiles(int T, int k, int E, bool shared) {
+    return (T * k + kTileM - 1) / kTileM + E + (shared ? (T + kTileM - 1) / kTileM : 0);
+}
 
 // ---------------------------------------------------------------------------
 // Launchers (enqueue only; arguments already validated)
@@ -190,7 +196,8 @@ hipError_t launch_gemv(const moe_layer_desc& d, const float* x, int T, const int
                        const float* w, int shard, int nshards, float* out, char* ws,
                        const WsLayout& L, const Ctx& c, bool route);
 hipError_t launch_bucket(const int32_t* idx, int T, int k, int E, bool shared, int32_t* counts,
-                         int32_t* offsets, int32_t* tile_off, int32_t* perm, int32_t* bhist,
+                         int32_t* offsets, int32_t* tile_off, int4* tile_rec, int32_t* perm,
+                         int32_t* bhist,
                          const Ctx& c);
 // x16_ready: the router already wrote the fp16 tokens (L.x16)
 hipError_t launch_mfma(const moe_layer_desc& d, const float* x, int T, const int32_t* idx,
