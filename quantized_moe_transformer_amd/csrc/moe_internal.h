@@ -128,6 +128,25 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     return (uint16_t)(u >> 16);
 }
 
+// One 16-byte global-to-LDS load per lane: lane l's bytes land at LDS offset
+// lds_off + 16 l.  Written as asm so that the compiler does not order it
+// against LDS reads of other stages with waits of its own; the caller waits
+// for these loads (wait_vmcnt) before any wave reads what they wrote.  Extra
+// loads in the counter only make the compiler's own vmcnt waits stricter.
+__device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_off) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(gptr), "s"(lds_off)
+                 : "m0");
+}
+
+// s_waitcnt with only the vector-memory count bounded (<= 63)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // ---------------------------------------------------------------------------
 // Workspace layout
 // ---------------------------------------------------------------------------

@@ -32,7 +32,7 @@ int router_splits(int T, int H) { return T <= kGemvMaxT ? kRouterSplits : 1; }
 // |x| < 65504 and |w| < 64.
 // ---------------------------------------------------------------------------
 constexpr float kWrScale = 1024.0f, kLoScale = 2048.0f;
-constexpr int kRgT = 32, kRgE = 128, kRgK = 64, kRgRow = kRgK + 8;
+constexpr int kRgT = 32, kRgE = 128, kRgK = 64;
 
 // x fp32 [T][H] -> hi (x16, also the grouped GEMM's operand) and lo parts
 __global__ void __launch_bounds__(256)
@@ -77,66 +77,83 @@ w_split_kernel(const float* __restrict__ wr, int H, int E, _Float16* __restrict_
 }
 
 // grid (ceil(T/32), ceil(E/128)); 4 waves, wave w owns experts [32w, 32w+32)
-// of the block's 128.  K advances 64 at a time; the next step's operands are
-// fetched into registers while the current one runs on the matrix cores.
+// of the block's 128.  K advances 64 at a time.  A step's operands -- hi and
+// lo parts of 32 token rows and of 128 router rows, 40 KB -- arrive by direct
+// global-to-LDS loads two steps ahead into a three-stage ring (ten 16-byte
+// loads per thread per step).  Each row's eight 16-byte chunks sit XOR-
+// swizzled by the row index (chunk c at position c ^ (row & 7)).  Rows past T
+// or E re-read the last valid row; their results are not written.
+constexpr int kRgStages = 3;
+constexpr int kRgStageHalves = 2 * (kRgT + kRgE) * kRgK;   // 40 KB
+constexpr int kRgDma = kRgStageHalves * 2 / 16 / 256;       // 10 loads per thread per step
+
+__device__ __forceinline__ int rg_chunk(int row, int c) { return row * 8 + (c ^ (row & 7)); }
+
 __global__ void __launch_bounds__(256)
 router_gemm_kernel(const _Float16* __restrict__ xh, const _Float16* __restrict__ xl,
                    const _Float16* __restrict__ wh, const _Float16* __restrict__ wl, int T, int H,
                    int E, float* __restrict__ logits) {
-    __shared__ _Float16 as[2][kRgT][kRgRow];    // [hi/lo][token][k]
-    __shared__ _Float16 bs[2][kRgE][kRgRow];    // [hi/lo][expert][k]
+    // per stage: A hi [32][64], A lo, B hi [128][64], B lo
+    __shared__ __align__(16) _Float16 st[kRgStages][kRgStageHalves];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int t0 = blockIdx.x * kRgT, e0 = blockIdx.y * kRgE;
-    // loaders: A: 2 parts x 32 rows x 8 chunks = 512 chunks (2 per thread);
-    //          B: 2 parts x 128 rows x 8 chunks = 2048 chunks (8 per thread)
-    uint4 ra[2], rb[8];
-    auto fetch = [&](int k0) {
+    const int nk = H / kRgK;
+    // chunk q = (10 wave + j) * 64 + lane of a stage: A parts first (512 chunks)
+    const _Float16* src[kRgDma];
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int f = tid + 256 * q;
-            const int part = f >> 8, r = (f >> 3) & 31, c8 = f & 7;
-            const int t = t0 + r;
-            const _Float16* src = part ? xl : xh;
-            ra[q] = t < T ? *reinterpret_cast<const uint4*>(src + (size_t)t * H + k0 + c8 * 8)
-                          : make_uint4(0, 0, 0, 0);
+    for (int j = 0; j < kRgDma; ++j) {
+        const int q = (kRgDma * wave + j) * 64 + lane;
+        if (q < 2 * kRgT * 8) {
+            const int part = q >> 8, row = (q >> 3) & (kRgT - 1), c = (q & 7) ^ (row & 7);
+            const int t = min(t0 + row, T - 1);
+            src[j] = (part ? xl : xh) + (size_t)t * H + c * 8;
+        } else {
+            const int qb = q - 2 * kRgT * 8;
+            const int part = qb >> 10, row = (qb >> 3) & (kRgE - 1), c = (qb & 7) ^ (row & 7);
+            const int e = min(e0 + row, E - 1);
+            src[j] = (part ? wl : wh) + (size_t)e * H + c * 8;
         }
+    }
+    auto issue = [&](int kk) {
+        const uint32_t base = (uint32_t)(uintptr_t)&st[kk % kRgStages][0];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const int f = tid + 256 * q;
-            const int part = f >> 10, r = (f >> 3) & 127, c8 = f & 7;
-            const int e = e0 + r;
-            const _Float16* src = part ? wl : wh;
-            rb[q] = e < E ? *reinterpret_cast<const uint4*>(src + (size_t)e * H + k0 + c8 * 8)
-                          : make_uint4(0, 0, 0, 0);
-        }
+        for (int j = 0; j < kRgDma; ++j)
+            lds_dma16(src[j] + (size_t)kk * kRgK,
+                      __builtin_amdgcn_readfirstlane(base + (kRgDma * wave + j) * 1024));
     };
-    fetch(0);
+    issue(0);
+    if (nk > 1) {
+        issue(1);
+        wait_vmcnt<kRgDma>();
+    } else {
+        wait_vmcnt<0>();
+    }
+    __syncthreads();
     float16v acc = {}, acc_lo = {};
-    for (int k0 = 0; k0 < H; k0 += kRgK) {
-        __syncthreads();
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int f = tid + 256 * q;
-            *reinterpret_cast<uint4*>(&as[f >> 8][(f >> 3) & 31][(f & 7) * 8]) = ra[q];
-        }
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const int f = tid + 256 * q;
-            *reinterpret_cast<uint4*>(&bs[f >> 10][(f >> 3) & 127][(f & 7) * 8]) = rb[q];
-        }
-        __syncthreads();
-        if (k0 + kRgK < H) fetch(k0 + kRgK);
+    for (int kk = 0; kk < nk; ++kk) {
+        // step kk + 2 into the stage step kk - 1 read (every wave passed the barrier)
+        const bool more = kk + 2 < nk;
+        if (more) issue(kk + 2);
+        const _Float16* sa_h = &st[kk % kRgStages][0];
+        const _Float16* sa_l = sa_h + kRgT * kRgK;
+        const _Float16* sb_h = sa_h + 2 * kRgT * kRgK;
+        const _Float16* sb_l = sb_h + kRgE * kRgK;
+        const int ra = lane & 31, rb = 32 * wave + (lane & 31);
 #pragma unroll
         for (int s = 0; s < kRgK / 16; ++s) {
-            const int kof = s * 16 + 8 * (lane >> 5);
-            const half8 ah = *reinterpret_cast<const half8*>(&as[0][lane & 31][kof]);
-            const half8 al = *reinterpret_cast<const half8*>(&as[1][lane & 31][kof]);
-            const half8 bh = *reinterpret_cast<const half8*>(&bs[0][32 * wave + (lane & 31)][kof]);
-            const half8 bl = *reinterpret_cast<const half8*>(&bs[1][32 * wave + (lane & 31)][kof]);
+            const int c = 2 * s + (lane >> 5);
+            const half8 ah = *reinterpret_cast<const half8*>(sa_h + 8 * rg_chunk(ra, c));
+            const half8 al = *reinterpret_cast<const half8*>(sa_l + 8 * rg_chunk(ra, c));
+            const half8 bh = *reinterpret_cast<const half8*>(sb_h + 8 * rg_chunk(rb, c));
+            const half8 bl = *reinterpret_cast<const half8*>(sb_l + 8 * rg_chunk(rb, c));
             acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bh, acc, 0, 0, 0);
             acc_lo = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bl, acc_lo, 0, 0, 0);
             acc_lo = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, bh, acc_lo, 0, 0, 0);
         }
+        // step kk + 1's operands must have landed; step kk + 2's may be in flight
+        if (more) wait_vmcnt<kRgDma>();
+        else wait_vmcnt<0>();
+        __syncthreads();
     }
     const int e = e0 + 32 * wave + (lane & 31);
 #pragma unroll
