@@ -350,6 +350,35 @@ def test_empty_batch_leaves_output_untouched():
     assert torch.all(out == 7.0)
 
 
+@pytest.mark.parametrize("H,I,T", [(512, 256, 45), (1024, 512, 70), (4096, 256, 33), (4096, 512, 200),
+                                   (4096, 512, 8), (1024, 256, 1)])
+@pytest.mark.parametrize("path,tol", [(qm.MOE_PATH_GEMV, GEMV_TOL), (qm.MOE_PATH_MFMA, MFMA_TOL)])
+def test_other_widths(H, I, T, path, tol):
+    """Hidden widths of 2, 4 and 16 superblocks per row and expert widths of one
+    and two superblocks, through both paths (the weight rings and the router
+    splits depend on them), with a two-shard run of the grouped GEMM."""
+    shp = mi.LayerShape(H=H, E=16, k=4, I=I, Is=I)
+    layer = mi.make_layer(shp, seed=31)
+    x = mi.make_tokens(shp, 31, T)
+    dl = DeviceLayer.from_shape(layer, shp)
+    ol = oracle.Layer.from_shape(layer, shp)
+    say(f"width H={H} I={I} T={T} path={path}")
+    got, used = run_forward(dl, x, path)
+    assert used == path
+    oi, ow, _, logits = oracle.router(x, layer["router_w"], shp.k)
+    gi, gw = run_router(dl, x)
+    exact, exempt, wrong = topk_check(gi, oi, logits)
+    assert len(wrong) == 0
+    ref = oracle.forward(ol, x)
+    assert rel_err(got[exact], ref[exact]) <= tol
+    if path == qm.MOE_PATH_MFMA:
+        parts = [run_shard(dl, x, oi, ow, s, 2, path)[0] for s in range(2)]
+        red = torch.empty((T, H), device=DEV)
+        qm.moe_reduce_partials(parts, T * H, red)
+        torch.cuda.synchronize()
+        assert rel_err(red.cpu().numpy(), ref) <= tol
+
+
 @pytest.mark.parametrize("E,k,Is", [(8, 8, 128), (1, 1, 0), (4, 3, 0)])
 @pytest.mark.parametrize("path,tol", [(qm.MOE_PATH_GEMV, GEMV_TOL), (qm.MOE_PATH_MFMA, MFMA_TOL)])
 def test_degenerate_layers(E, k, Is, path, tol):
