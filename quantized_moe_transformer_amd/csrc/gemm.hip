@@ -176,10 +176,12 @@ struct TileInfo {
     bool is_sh;
 };
 
-// The tile's K loop and epilogue for exactly MB 32-row blocks (straight-line
+// The tile's K loop and epilogue for exactly MB 32-row blocks, in three parts:
+// producer waves, consumer waves, and an epilogue that all 8 waves run.
+// Producers: (straight-line
 // code: the fragment reads of a 16-wide K slice are issued before its MFMAs).
 template <int MODE, int MB>
-__device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileInfo& ti, GemmLds& lds,
+__device__ __forceinline__ void gemm_produce(const GemmArgs& a, const TileInfo& ti, GemmLds& lds,
                                           const int32_t* row_src, const float* row_w) {
     constexpr int kPD = PrefetchDistance<MODE>::v;
     const int tid = threadIdx.x;
@@ -189,192 +191,204 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileInfo& ti,
     const bool is_sh = ti.is_sh;
     (void)m0;
 
-    if (wave >= kConsumers) {
-        // ------------------------------- producers -------------------------------
-        const int pt = tid - 64 * kConsumers;
-        if constexpr (MODE == 0) {
-            // Producer thread pt owns weight row pt of the tile (gate rows
-            // 0-127, the matching up rows 128-255) and loads the row's whole
-            // 144-byte superblock -- nine 16-byte loads, contiguous -- once per
-            // four steps into a two-slot register ring, one superblock ahead;
-            // each step dequantises its 64 weights of the current one.
-            const int col = pt & (kTN / 2 - 1);
-            const int colc = n0 + col < Iloc ? col : 0;   // ragged tile: discarded columns
-            const size_t mat = (size_t)a.I * a.H / kSbWeights * kQ4Bytes;
-            const uint8_t* m = is_sh ? (pt < kTN / 2 ? a.w_shared : a.w_shared2)
-                                     : (pt < kTN / 2 ? a.w_routed : a.w_routed2) + (size_t)g * mat;
-            const int nsb = a.H / kSbWeights;
-            const uint8_t* rowp = m + (size_t)(i0 + n0 + colc) * nsb * kQ4Bytes;
-            uint4 sbr[2][kQ4Bytes / 16];
-            auto load_sb = [&](int p, uint4* r) {
-                const uint4* src =
-                    reinterpret_cast<const uint4*>(rowp + (size_t)min(p, nsb - 1) * kQ4Bytes);
+    // ------------------------------- producers -------------------------------
+    const int pt = tid - 64 * kConsumers;
+    if constexpr (MODE == 0) {
+        // Producer thread pt owns weight row pt of the tile (gate rows
+        // 0-127, the matching up rows 128-255) and loads the row's whole
+        // 144-byte superblock -- nine 16-byte loads, contiguous -- once per
+        // four steps into a two-slot register ring, one superblock ahead;
+        // each step dequantises its 64 weights of the current one.
+        const int col = pt & (kTN / 2 - 1);
+        const int colc = n0 + col < Iloc ? col : 0;   // ragged tile: discarded columns
+        const size_t mat = (size_t)a.I * a.H / kSbWeights * kQ4Bytes;
+        const uint8_t* m = is_sh ? (pt < kTN / 2 ? a.w_shared : a.w_shared2)
+                                 : (pt < kTN / 2 ? a.w_routed : a.w_routed2) + (size_t)g * mat;
+        const int nsb = a.H / kSbWeights;
+        const uint8_t* rowp = m + (size_t)(i0 + n0 + colc) * nsb * kQ4Bytes;
+        uint4 sbr[2][kQ4Bytes / 16];
+        auto load_sb = [&](int p, uint4* r) {
+            const uint4* src =
+                reinterpret_cast<const uint4*>(rowp + (size_t)min(p, nsb - 1) * kQ4Bytes);
 #pragma unroll
-                for (int i = 0; i < kQ4Bytes / 16; ++i) r[i] = src[i];
-            };
-            auto deq_step = [&](const uint4* r, int c, int stage) {
-                SbHead hd;
-                hd.d = f16_bits_to_f32(r[0].x & 0xffffu);
-                hd.dmin = f16_bits_to_f32(r[0].x >> 16);
-                hd.s0 = r[0].y;
-                hd.s1 = r[0].z;
-                hd.s2 = r[0].w;
-                _Float16* dst = &lds.b[stage][pt][0];
-                dequant_piece_to_lds<false>(hd, r[1 + 2 * c], r[1 + 2 * c], c, 0, dst);
-                dequant_piece_to_lds<false>(hd, r[2 + 2 * c], r[2 + 2 * c], c, 1, dst);
-            };
-            const int last = a.nk - 1;
-            load_sb(0, sbr[0]);
-            load_sb(1, sbr[1]);
-            deq_step(sbr[0], 0, 0);
-            __syncthreads();   // stage 0 ready
-            // steps 4*p0 .. 4*p0+7 use superblocks p0 (slot 0) and p0+1 (slot 1)
-            for (int p0 = 0; p0 < nsb; p0 += 2) {
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const int kk = 4 * p0 + u;
-                    if (kk > last) break;
-                    const int nxt = kk + 1;
-                    if (nxt <= last) {
-                        const int un = u + 1;   // step nxt: slot (un >> 2) & 1, sub-block pair un & 3
-                        deq_step(sbr[(un >> 2) & 1], un & 3, nxt & 1);
-                        if ((un & 3) == 3) load_sb(p0 + (un >> 2) + 2, sbr[(un >> 2) & 1]);
-                    }
-                    __syncthreads();
-                }
-            }
-            return;
-        }
-        if (MODE == 1 && a.sb_rows) {
-            // The down rows' K ranges are whole 5-bit superblocks: producer
-            // thread pt owns output row n0 + pt and loads each 176-byte
-            // superblock of it -- eleven 16-byte loads, contiguous -- once per
-            // four steps, one superblock ahead, as the gate/up path does.
-            const int o = n0 + pt < a.H ? n0 + pt : n0;   // ragged tile: discarded rows
-            const uint8_t* m = is_sh ? a.w_shared
-                                     : a.w_routed + (size_t)g * ((size_t)a.H * a.I / kSbWeights * kQ5Bytes);
-            const int nsb = Iloc / kSbWeights;
-            const uint8_t* rowp = m + (((size_t)o * Iexp + i0) >> 8) * kQ5Bytes;
-            uint4 sbr[2][kQ5Bytes / 16];
-            auto load_sb = [&](int p, uint4* r) {
-                const uint4* src =
-                    reinterpret_cast<const uint4*>(rowp + (size_t)min(p, nsb - 1) * kQ5Bytes);
-#pragma unroll
-                for (int i = 0; i < kQ5Bytes / 16; ++i) r[i] = src[i];
-            };
-            auto deq_step = [&](const uint4* r, int c, int stage) {
-                SbHead hd;
-                hd.d = f16_bits_to_f32(r[0].x & 0xffffu);
-                hd.dmin = f16_bits_to_f32(r[0].x >> 16);
-                hd.s0 = r[0].y;
-                hd.s1 = r[0].z;
-                hd.s2 = r[0].w;
-                _Float16* dst = &lds.b[stage][pt][0];
-                dequant_piece_to_lds<true>(hd, r[3 + 2 * c], r[1], c, 0, dst);
-                dequant_piece_to_lds<true>(hd, r[4 + 2 * c], r[2], c, 1, dst);
-            };
-            const int last = a.nk - 1;
-            load_sb(0, sbr[0]);
-            load_sb(1, sbr[1]);
-            deq_step(sbr[0], 0, 0);
-            __syncthreads();   // stage 0 ready
-            for (int p0 = 0; p0 < nsb; p0 += 2) {
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const int kk = 4 * p0 + u;
-                    if (kk > last) break;
-                    const int nxt = kk + 1;
-                    if (nxt <= last) {
-                        const int un = u + 1;
-                        deq_step(sbr[(un >> 2) & 1], un & 3, nxt & 1);
-                        if ((un & 3) == 3) load_sb(p0 + (un >> 2) + 2, sbr[(un >> 2) & 1]);
-                    }
-                    __syncthreads();
-                }
-            }
-            return;
-        }
-        const uint8_t* wsrc[kBTasks];   // MODE 0: the row's superblocks; MODE 1: matrix base
-        size_t eoff[kBTasks];           // MODE 1: element offset of the row's range
-        int bhh[kBTasks], brr[kBTasks];
-        // weight rows past the matrix end (a ragged last column tile) read the
-        // tile's first row instead: their LDS columns only feed outputs that
-        // the epilogue discards
-#pragma unroll
-        for (int q = 0; q < kBTasks; ++q) {
-            const int task = pt + 64 * kProducers * q;
-            const int r = task >> 1;
-            bhh[q] = task & 1;
-            brr[q] = r;
-            eoff[q] = 0;
-            if (MODE == 0) {
-                const int col = n0 + (r & (kTN / 2 - 1)) < Iloc ? (r & (kTN / 2 - 1)) : 0;
-                const size_t mat = (size_t)a.I * a.H / kSbWeights * kQ4Bytes;
-                const uint8_t* m = is_sh ? (r < kTN / 2 ? a.w_shared : a.w_shared2)
-                                         : (r < kTN / 2 ? a.w_routed : a.w_routed2) + (size_t)g * mat;
-                wsrc[q] = m + (size_t)(i0 + n0 + col) * (a.H / kSbWeights) * kQ4Bytes;
-            } else {
-                const int o = n0 + r < a.H ? n0 + r : n0;
-                wsrc[q] = is_sh ? a.w_shared
-                                : a.w_routed + (size_t)g * ((size_t)a.H * a.I / kSbWeights * kQ5Bytes);
-                eoff[q] = (size_t)o * Iexp + i0;
-            }
-        }
-        auto load_b = [&](int kk, BRegs* rg) {
-#pragma unroll
-            for (int q = 0; q < kBTasks; ++q) {
-                if (MODE == 0) {
-                    const uint8_t* sb = wsrc[q] + (kk >> 2) * kQ4Bytes;
-                    rg[q].head = *reinterpret_cast<const uint4*>(sb);
-                    rg[q].qs = *reinterpret_cast<const uint4*>(sb + 16 + 32 * (kk & 3) + 16 * bhh[q]);
-                } else {
-                    const size_t base = eoff[q] + (size_t)kk * kBK;
-                    const int c = (int)((base & 255) >> 6);
-                    const uint8_t* sb = wsrc[q] + (base >> 8) * kQ5Bytes;
-                    rg[q].head = *reinterpret_cast<const uint4*>(sb);
-                    rg[q].qh = *reinterpret_cast<const uint4*>(sb + 16 + 16 * bhh[q]);
-                    rg[q].qs = *reinterpret_cast<const uint4*>(sb + 48 + 32 * c + 16 * bhh[q]);
-                }
-            }
+            for (int i = 0; i < kQ4Bytes / 16; ++i) r[i] = src[i];
         };
-        auto store_b = [&](int kk, const BRegs* rg, int stage) {
-#pragma unroll
-            for (int q = 0; q < kBTasks; ++q) {
-                SbHead hd;
-                hd.d = f16_bits_to_f32(rg[q].head.x & 0xffffu);
-                hd.dmin = f16_bits_to_f32(rg[q].head.x >> 16);
-                hd.s0 = rg[q].head.y;
-                hd.s1 = rg[q].head.z;
-                hd.s2 = rg[q].head.w;
-                const int c = MODE == 0 ? (kk & 3)
-                                        : (int)(((eoff[q] + (size_t)kk * kBK) & 255) >> 6);
-                dequant_piece_to_lds<MODE == 1>(hd, rg[q].qs, rg[q].qh, c, bhh[q],
-                                                &lds.b[stage][brr[q]][0]);
-            }
+        auto deq_step = [&](const uint4* r, int c, int stage) {
+            SbHead hd;
+            hd.d = f16_bits_to_f32(r[0].x & 0xffffu);
+            hd.dmin = f16_bits_to_f32(r[0].x >> 16);
+            hd.s0 = r[0].y;
+            hd.s1 = r[0].z;
+            hd.s2 = r[0].w;
+            _Float16* dst = &lds.b[stage][pt][0];
+            dequant_piece_to_lds<false>(hd, r[1 + 2 * c], r[1 + 2 * c], c, 0, dst);
+            dequant_piece_to_lds<false>(hd, r[2 + 2 * c], r[2 + 2 * c], c, 1, dst);
         };
-        BRegs ring[kPD][kBTasks];
-#pragma unroll
-        for (int s = 0; s < kPD; ++s)
-            if (s < a.nk) load_b(s, ring[s]);
-        store_b(0, ring[0], 0);
-        if (kPD < a.nk) load_b(kPD, ring[0]);
+        const int last = a.nk - 1;
+        load_sb(0, sbr[0]);
+        load_sb(1, sbr[1]);
+        deq_step(sbr[0], 0, 0);
         __syncthreads();   // stage 0 ready
-        for (int kk0 = 0; kk0 < a.nk; kk0 += kPD) {
+        // steps 4*p0 .. 4*p0+7 use superblocks p0 (slot 0) and p0+1 (slot 1)
+        for (int p0 = 0; p0 < nsb; p0 += 2) {
 #pragma unroll
-            for (int u = 0; u < kPD; ++u) {
-                const int kk = kk0 + u;
-                if (kk >= a.nk) break;
-                // while the consumers work on step kk: step kk+1 into the other stage
+            for (int u = 0; u < 8; ++u) {
+                const int kk = 4 * p0 + u;
+                if (kk > last) break;
                 const int nxt = kk + 1;
-                if (nxt < a.nk) {
-                    store_b(nxt, ring[(u + 1) % kPD], nxt & 1);
-                    if (nxt + kPD < a.nk) load_b(nxt + kPD, ring[(u + 1) % kPD]);
+                if (nxt <= last) {
+                    const int un = u + 1;   // step nxt: slot (un >> 2) & 1, sub-block pair un & 3
+                    deq_step(sbr[(un >> 2) & 1], un & 3, nxt & 1);
+                    if ((un & 3) == 3) load_sb(p0 + (un >> 2) + 2, sbr[(un >> 2) & 1]);
                 }
                 __syncthreads();
             }
         }
         return;
     }
+    if (MODE == 1 && a.sb_rows) {
+        // The down rows' K ranges are whole 5-bit superblocks: producer
+        // thread pt owns output row n0 + pt and loads each 176-byte
+        // superblock of it -- eleven 16-byte loads, contiguous -- once per
+        // four steps, one superblock ahead, as the gate/up path does.
+        const int o = n0 + pt < a.H ? n0 + pt : n0;   // ragged tile: discarded rows
+        const uint8_t* m = is_sh ? a.w_shared
+                                 : a.w_routed + (size_t)g * ((size_t)a.H * a.I / kSbWeights * kQ5Bytes);
+        const int nsb = Iloc / kSbWeights;
+        const uint8_t* rowp = m + (((size_t)o * Iexp + i0) >> 8) * kQ5Bytes;
+        uint4 sbr[2][kQ5Bytes / 16];
+        auto load_sb = [&](int p, uint4* r) {
+            const uint4* src =
+                reinterpret_cast<const uint4*>(rowp + (size_t)min(p, nsb - 1) * kQ5Bytes);
+#pragma unroll
+            for (int i = 0; i < kQ5Bytes / 16; ++i) r[i] = src[i];
+        };
+        auto deq_step = [&](const uint4* r, int c, int stage) {
+            SbHead hd;
+            hd.d = f16_bits_to_f32(r[0].x & 0xffffu);
+            hd.dmin = f16_bits_to_f32(r[0].x >> 16);
+            hd.s0 = r[0].y;
+            hd.s1 = r[0].z;
+            hd.s2 = r[0].w;
+            _Float16* dst = &lds.b[stage][pt][0];
+            dequant_piece_to_lds<true>(hd, r[3 + 2 * c], r[1], c, 0, dst);
+            dequant_piece_to_lds<true>(hd, r[4 + 2 * c], r[2], c, 1, dst);
+        };
+        const int last = a.nk - 1;
+        load_sb(0, sbr[0]);
+        load_sb(1, sbr[1]);
+        deq_step(sbr[0], 0, 0);
+        __syncthreads();   // stage 0 ready
+        for (int p0 = 0; p0 < nsb; p0 += 2) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int kk = 4 * p0 + u;
+                if (kk > last) break;
+                const int nxt = kk + 1;
+                if (nxt <= last) {
+                    const int un = u + 1;
+                    deq_step(sbr[(un >> 2) & 1], un & 3, nxt & 1);
+                    if ((un & 3) == 3) load_sb(p0 + (un >> 2) + 2, sbr[(un >> 2) & 1]);
+                }
+                __syncthreads();
+            }
+        }
+        return;
+    }
+    const uint8_t* wsrc[kBTasks];   // MODE 0: the row's superblocks; MODE 1: matrix base
+    size_t eoff[kBTasks];           // MODE 1: element offset of the row's range
+    int bhh[kBTasks], brr[kBTasks];
+    // weight rows past the matrix end (a ragged last column tile) read the
+    // tile's first row instead: their LDS columns only feed outputs that
+    // the epilogue discards
+#pragma unroll
+    for (int q = 0; q < kBTasks; ++q) {
+        const int task = pt + 64 * kProducers * q;
+        const int r = task >> 1;
+        bhh[q] = task & 1;
+        brr[q] = r;
+        eoff[q] = 0;
+        if (MODE == 0) {
+            const int col = n0 + (r & (kTN / 2 - 1)) < Iloc ? (r & (kTN / 2 - 1)) : 0;
+            const size_t mat = (size_t)a.I * a.H / kSbWeights * kQ4Bytes;
+            const uint8_t* m = is_sh ? (r < kTN / 2 ? a.w_shared : a.w_shared2)
+                                     : (r < kTN / 2 ? a.w_routed : a.w_routed2) + (size_t)g * mat;
+            wsrc[q] = m + (size_t)(i0 + n0 + col) * (a.H / kSbWeights) * kQ4Bytes;
+        } else {
+            const int o = n0 + r < a.H ? n0 + r : n0;
+            wsrc[q] = is_sh ? a.w_shared
+                            : a.w_routed + (size_t)g * ((size_t)a.H * a.I / kSbWeights * kQ5Bytes);
+            eoff[q] = (size_t)o * Iexp + i0;
+        }
+    }
+    auto load_b = [&](int kk, BRegs* rg) {
+#pragma unroll
+        for (int q = 0; q < kBTasks; ++q) {
+            if (MODE == 0) {
+                const uint8_t* sb = wsrc[q] + (kk >> 2) * kQ4Bytes;
+                rg[q].head = *reinterpret_cast<const uint4*>(sb);
+                rg[q].qs = *reinterpret_cast<const uint4*>(sb + 16 + 32 * (kk & 3) + 16 * bhh[q]);
+            } else {
+                const size_t base = eoff[q] + (size_t)kk * kBK;
+                const int c = (int)((base & 255) >> 6);
+                const uint8_t* sb = wsrc[q] + (base >> 8) * kQ5Bytes;
+                rg[q].head = *reinterpret_cast<const uint4*>(sb);
+                rg[q].qh = *reinterpret_cast<const uint4*>(sb + 16 + 16 * bhh[q]);
+                rg[q].qs = *reinterpret_cast<const uint4*>(sb + 48 + 32 * c + 16 * bhh[q]);
+            }
+        }
+    };
+    auto store_b = [&](int kk, const BRegs* rg, int stage) {
+#pragma unroll
+        for (int q = 0; q < kBTasks; ++q) {
+            SbHead hd;
+            hd.d = f16_bits_to_f32(rg[q].head.x & 0xffffu);
+            hd.dmin = f16_bits_to_f32(rg[q].head.x >> 16);
+            hd.s0 = rg[q].head.y;
+            hd.s1 = rg[q].head.z;
+            hd.s2 = rg[q].head.w;
+            const int c = MODE == 0 ? (kk & 3)
+                                    : (int)(((eoff[q] + (size_t)kk * kBK) & 255) >> 6);
+            dequant_piece_to_lds<MODE == 1>(hd, rg[q].qs, rg[q].qh, c, bhh[q],
+                                            &lds.b[stage][brr[q]][0]);
+        }
+    };
+    BRegs ring[kPD][kBTasks];
+#pragma unroll
+    for (int s = 0; s < kPD; ++s)
+        if (s < a.nk) load_b(s, ring[s]);
+    store_b(0, ring[0], 0);
+    if (kPD < a.nk) load_b(kPD, ring[0]);
+    __syncthreads();   // stage 0 ready
+    for (int kk0 = 0; kk0 < a.nk; kk0 += kPD) {
+#pragma unroll
+        for (int u = 0; u < kPD; ++u) {
+            const int kk = kk0 + u;
+            if (kk >= a.nk) break;
+            // while the consumers work on step kk: step kk+1 into the other stage
+            const int nxt = kk + 1;
+            if (nxt < a.nk) {
+                store_b(nxt, ring[(u + 1) % kPD], nxt & 1);
+                if (nxt + kPD < a.nk) load_b(nxt + kPD, ring[(u + 1) % kPD]);
+            }
+            __syncthreads();
+        }
+    }
+    return;
+}
+
+// Consumers: token rows into LDS, MFMAs into acc.
+template <int MODE, int MB>
+__device__ __forceinline__ void gemm_consume(const GemmArgs& a, const TileInfo& ti, GemmLds& lds,
+                                          const int32_t* row_src, const float* row_w,
+                                             float16v (&acc)[MB][2]) {
+    constexpr int kPD = PrefetchDistance<MODE>::v;
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int g = ti.g, m0 = ti.m0, mcount = ti.mcount, grow0 = ti.grow0;
+    const int Iexp = ti.Iexp, Iloc = ti.Iloc, i0 = ti.i0, n0 = ti.n0;
+    const bool is_sh = ti.is_sh;
+    (void)m0;
 
     // ------------------------------- consumers -------------------------------
     // The consumer waves move the token rows (A) into LDS themselves with direct
@@ -402,12 +416,6 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileInfo& ti,
                       __builtin_amdgcn_readfirstlane(stage + (64 * wave + 256 * i) * 16));
     };
 
-    float16v acc[MB][2];
-#pragma unroll
-    for (int i = 0; i < MB; ++i) {
-        acc[i][0] = float16v{};
-        acc[i][1] = float16v{};
-    }
     // this wave's two 32-row blocks of B: gate block w and up block w (MODE 0),
     // or output blocks 2w and 2w+1 (MODE 1)
     const int bc0 = MODE == 0 ? 32 * wave : 64 * wave;
@@ -451,34 +459,84 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileInfo& ti,
         __syncthreads();
     }
 
-    if (MODE == 0) {
-        const int n = n0 + 32 * wave + (lane & 31);
+}
+
+// Epilogue, all 8 waves: each 32-row block of the tile is staged through LDS
+// (the operand stages are no longer read) and written with 16-byte stores of
+// whole row segments.
+//   MODE 0: h = silu(gate) * up * 2^-4 as fp16, rows in sorted order.
+//   MODE 1: the slot's row (the shared expert: its own buffer) times the
+//   row's weight * 2^4, fp32.
+template <int MODE, int MB>
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const TileInfo& ti, GemmLds& lds,
+                                          const int32_t* row_src, const float* row_w,
+                                              const float16v (&acc)[MB][2]) {
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const bool consumer = wave < kConsumers;
+    constexpr int kPitch = MODE == 0 ? kTN / 2 + 8 : kTN + 4;   // LDS row pitch (elements)
+    __syncthreads();   // every wave is past its last operand read
 #pragma unroll
-        for (int i = 0; i < MB; ++i)
+    for (int i = 0; i < MB; ++i) {
+        if (MODE == 0) {
+            _Float16* t = reinterpret_cast<_Float16*>(&lds);   // [32][kPitch]
+            if (consumer) {
+                const int n = 32 * wave + (lane & 31);
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int m = 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-                if (m < mcount && n < Iloc) {
-                    const float h = silu_f(acc[i][0][v]) * acc[i][1][v] * kHScale;
-                    a.h_out[(size_t)(grow0 + m) * a.h_stride + n] = (_Float16)h;
+                for (int v = 0; v < 16; ++v) {
+                    const int r = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                    t[r * kPitch + n] = (_Float16)(silu_f(acc[i][0][v]) * acc[i][1][v] * kHScale);
                 }
             }
-    } else {
-        const int oa = n0 + 64 * wave + (lane & 31);
-        float* dst = is_sh ? a.ysh : a.y;
+            __syncthreads();
+            // 32 rows x 128 halves = 512 chunks of 8 halves, one per thread
+            const int r = tid >> 4, c8 = tid & 15;
+            const int m = 32 * i + r, n = ti.n0 + 8 * c8;
+            if (m < ti.mcount && n < ti.Iloc)
+                *reinterpret_cast<uint4*>(a.h_out + (size_t)(ti.grow0 + m) * a.h_stride + n) =
+                    *reinterpret_cast<const uint4*>(t + r * kPitch + 8 * c8);
+        } else {
+            float* t = reinterpret_cast<float*>(&lds);   // [32][kPitch]
+            if (consumer) {
 #pragma unroll
-        for (int i = 0; i < MB; ++i)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int m = 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-                if (m < mcount) {
-                    const float sc = row_w[m];
-                    float* drow = dst + (size_t)row_src[m] * a.H;
-                    if (oa < a.H) drow[oa] = acc[i][0][v] * sc;
-                    if (oa + 32 < a.H) drow[oa + 32] = acc[i][1][v] * sc;
+                for (int v = 0; v < 16; ++v) {
+                    const int r = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                    const float sc = row_w[32 * i + r];
+                    t[r * kPitch + 64 * wave + (lane & 31)] = acc[i][0][v] * sc;
+                    t[r * kPitch + 64 * wave + 32 + (lane & 31)] = acc[i][1][v] * sc;
                 }
             }
+            __syncthreads();
+            // 32 rows x 256 floats = 2048 chunks of 4 floats, four per thread
+            float* dst = ti.is_sh ? a.ysh : a.y;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int q = tid + 512 * j;
+                const int r = q >> 6, c4 = q & 63;
+                const int m = 32 * i + r, o = ti.n0 + 4 * c4;
+                if (m < ti.mcount && o < a.H)
+                    *reinterpret_cast<float4*>(dst + (size_t)row_src[m] * a.H + o) =
+                        *reinterpret_cast<const float4*>(t + r * kPitch + 4 * c4);
+            }
+        }
+        __syncthreads();   // the staging buffer is rewritten by the next block
     }
+}
+
+template <int MODE, int MB>
+__device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileInfo& ti, GemmLds& lds,
+                                          const int32_t* row_src, const float* row_w) {
+    float16v acc[MB][2];
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+        acc[i][0] = float16v{};
+        acc[i][1] = float16v{};
+    }
+    if (threadIdx.x >> 6 >= kConsumers)
+        gemm_produce<MODE, MB>(a, ti, lds, row_src, row_w);
+    else
+        gemm_consume<MODE, MB>(a, ti, lds, row_src, row_w, acc);
+    gemm_epilogue<MODE, MB>(a, ti, lds, row_src, row_w, acc);
 }
 
 template <int MODE>
