@@ -405,7 +405,10 @@ __device__ __forceinline__ void gemm_consume(const GemmArgs& a, const TileInfo& 
         const int q = tid + 256 * i;
         const int r = q >> 3, c = (q & 7) ^ (r & 7);
         const int rv = r < mcount ? r : r % mcount;
-        const size_t row = MODE == 0 ? (size_t)row_src[rv] : (size_t)(grow0 + rv);
+        // MODE 0: the row's token, read here rather than from row_src so that
+        // no barrier stands between the tile record and the first loads
+        const size_t row = MODE == 0 ? (size_t)(is_sh ? ti.m0 + rv : a.perm[grow0 + rv] / a.k)
+                                     : (size_t)(grow0 + rv);
         asrc[i] = row * a.a_stride + c * 8;
     }
     auto issue_a = [&](int kk) {
@@ -583,7 +586,8 @@ gemm_grouped_kernel(GemmArgs a) {
         row_src[tid] = src;
         row_w[tid] = rw;
     }
-    __syncthreads();
+    // row_src and row_w are read only in the epilogue, after the K loop's
+    // barriers; the weight and token-row loads start without waiting for them
     switch ((ti.mcount + 31) >> 5) {
         case 1: gemm_tile<MODE, 1>(a, ti, lds, row_src, row_w); break;
         case 2: gemm_tile<MODE, 2>(a, ti, lds, row_src, row_w); break;
