@@ -600,6 +600,15 @@ gemm_grouped_kernel(GemmArgs a) {
 // out[t] = ((y[t,0] + y[t,1]) + ... + y[t,k-1]) + ysh[t]; y rows already carry
 // their routing weight, ysh the shared weight.  Slots whose expert index is
 // out of range contribute nothing.
+// Every slot row of the token is requested before the first add (KMAX >= k
+// rows, streamed once: non-temporal), then added in slot order.
+__device__ __forceinline__ float4 ld_stream4(const float* p) {
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    return make_float4(v[0], v[1], v[2], v[3]);
+}
+
+template <int KMAX>
 __global__ void __launch_bounds__(256)
 combine_kernel(const float* __restrict__ y, const float* __restrict__ ysh,
                const int32_t* __restrict__ idx, int T, int H, int E, int k, int has_shared,
@@ -608,21 +617,33 @@ combine_kernel(const float* __restrict__ y, const float* __restrict__ ysh,
     const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= (size_t)T * h4) return;
     const int t = (int)(i / h4), o4 = (int)(i % h4);
+    float4 v[KMAX];
+    bool ok[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+        ok[j] = false;
+        if (j < k) {
+            ok[j] = (unsigned)idx[(size_t)t * k + j] < (unsigned)E;
+            v[j] = ld_stream4(y + ((size_t)t * k + j) * H + 4 * o4);
+        }
+    }
+    const float4 sh = has_shared ? ld_stream4(ysh + (size_t)t * H + 4 * o4)
+                                 : make_float4(0.f, 0.f, 0.f, 0.f);
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < k; ++j) {
-        if ((unsigned)idx[(size_t)t * k + j] >= (unsigned)E) continue;
-        const float4 v = reinterpret_cast<const float4*>(y + ((size_t)t * k + j) * H)[o4];
-        acc.x += v.x;
-        acc.y += v.y;
-        acc.z += v.z;
-        acc.w += v.w;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+        if (ok[j]) {   // a slot whose expert index is out of range adds nothing
+            acc.x += v[j].x;
+            acc.y += v[j].y;
+            acc.z += v[j].z;
+            acc.w += v[j].w;
+        }
     }
     if (has_shared) {
-        const float4 v = reinterpret_cast<const float4*>(ysh + (size_t)t * H)[o4];
-        acc.x += v.x;
-        acc.y += v.y;
-        acc.z += v.z;
-        acc.w += v.w;
+        acc.x += sh.x;
+        acc.y += sh.y;
+        acc.z += sh.z;
+        acc.w += sh.w;
     }
     reinterpret_cast<float4*>(out + (size_t)t * H)[o4] = acc;
 }
@@ -699,8 +720,12 @@ hipError_t launch_mfma(const moe_layer_desc& d, const float* x, int T, const int
              dim3(kGemmThreads), 0, g2);
 
     const size_t nc = (size_t)T * H / 4;
-    launch_k(c, MOE_K_COMBINE, combine_kernel, dim3((unsigned)((nc + 255) / 256)), dim3(256), 0, y,
-             ysh, idx, T, H, E, k, shared ? 1 : 0, out);
+    if (k <= 8)
+        launch_k(c, MOE_K_COMBINE, combine_kernel<8>, dim3((unsigned)((nc + 255) / 256)), dim3(256),
+                 0, y, ysh, idx, T, H, E, k, shared ? 1 : 0, out);
+    else
+        launch_k(c, MOE_K_COMBINE, combine_kernel<16>, dim3((unsigned)((nc + 255) / 256)), dim3(256),
+                 0, y, ysh, idx, T, H, E, k, shared ? 1 : 0, out);
     return hipGetLastError();
 }
 
