@@ -11,7 +11,8 @@ of weights is not served from the 256 MB last-level cache left warm by the step
 before.  Steps are replayed from a HIP graph (one graph of 16 steps).
 
 Secondary (``prefill``): T = 4096 token rows per step, same layer shape (seed
-4, uniform router), grouped-GEMM path.
+4, uniform router), grouped-GEMM path, replayed from a HIP graph of two steps
+(one per weight copy); the eager rate is reported beside it.
 
 Per-kernel durations come from start/stop HIP events that the library attaches
 to each kernel launch (moe_opts.kernel_events, hipExtLaunchKernel) in an eager
@@ -266,7 +267,20 @@ def bench_prefill(args, torch, qm, mi, DeviceLayer):
         step(i)
     torch.cuda.synchronize()
     assert set(used) == {qm.MOE_PATH_MFMA}, used
-    secs = time_steps(torch, step, K)
+    eager_secs = time_steps(torch, step, K)
+    # graph replay: one graph of two steps (one per weight copy)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(0)
+        step(1)
+    g.replay()
+    torch.cuda.synchronize()
+    n_rep = max(1, K // 2)
+    t0 = time.perf_counter()
+    for _ in range(n_rep):
+        g.replay()
+    torch.cuda.synchronize()
+    secs = (time.perf_counter() - t0) * K / (2 * n_rep)
     names = ["x_f16", "router_split", "router_mfma", "router_topk", "bucket_hist", "bucket_scan",
              "bucket_scatter", "gemm_gateup", "gemm_down", "combine"]
     kms = kernel_profile(torch, qm, lambda i, e: step(i, e), K, names)
@@ -277,10 +291,12 @@ def bench_prefill(args, torch, qm, mi, DeviceLayer):
     d_ms = kms["gemm_down"]
     res = {
         "workload": ("prefill T=4096: same layer shape, seed 4, uniform router, "
-                     "grouped fp16-MFMA path, 2 rotating weight copies"),
+                     "grouped fp16-MFMA path, 2 rotating weight copies, HIP-graph replay"),
         "value": T * K / secs,
         "unit": "tokens/s",
         "ms_per_step": secs / K * 1e3,
+        "eager_tokens_per_s": T * K / eager_secs,
+        "eager_ms_per_step": eager_secs / K * 1e3,
         "steps": K,
         "warmup": W,
         "dtype": "fp16 operands, fp32 accumulate (router fp32)",
