@@ -281,7 +281,7 @@ def bench_prefill(args, torch, qm, mi, DeviceLayer):
         g.replay()
     torch.cuda.synchronize()
     secs = (time.perf_counter() - t0) * K / (2 * n_rep)
-    names = ["x_f16", "router_split", "router_mfma", "router_topk", "bucket_hist", "bucket_scan",
+    names = ["x_f16", "router_mfma", "router_topk", "bucket_hist", "bucket_scan",
              "bucket_scatter", "gemm_gateup", "gemm_down", "combine"]
     kms = kernel_profile(torch, qm, lambda i, e: step(i, e), K, names)
     slots = T * shp.k + T

@@ -118,15 +118,15 @@ typedef struct moe_opts {
 #define MOE_K_ROUTER_TOPK 2      /* top-k + weights */
 #define MOE_K_GATEUP_GEMV 3      /* decode: top-k (when routing) + routed gate/up + SwiGLU */
 #define MOE_K_DOWN_GEMV 4        /* decode: down + slot-order combine */
-#define MOE_K_X_F16 5            /* T > 32: tokens to fp16 (hi and, for the router, lo parts) */
+#define MOE_K_X_F16 5            /* T > 32: tokens to fp16 hi/lo parts (and, when the router runs,
+                                    the router matrix to fp16 hi/lo parts in the same launch) */
 #define MOE_K_BUCKET_HIST 6
 #define MOE_K_BUCKET_SCAN 7
 #define MOE_K_BUCKET_SCATTER 8
 #define MOE_K_GEMM_GATEUP 9      /* prefill: grouped GEMM gate/up + SwiGLU */
 #define MOE_K_GEMM_DOWN 10       /* prefill: grouped GEMM down */
 #define MOE_K_COMBINE 11         /* prefill: slot-order combine */
-#define MOE_K_ROUTER_SPLIT 12    /* T > 32: router matrix split into fp16 hi/lo parts */
-#define MOE_K_COUNT 13
+#define MOE_K_COUNT 12
 
 /* Bytes of device workspace that router_topk, moe_layer_forward and
  * moe_layer_forward_shard need for T token rows split into num_shards shards

@@ -9,8 +9,8 @@
 // Logits stay fp32 throughout (the top-k must be exact up to near-ties).
 // Few token rows (<= 32): split-K partial logits from the decode front
 // kernel (gemv.hip), then router_topk.  Many rows use:
-//   x_split, w_split, router_gemm  a dense [T x H] x [H x E] product on the
-//                   fp16 matrix cores with split operands (fp32 accuracy);
+//   split, router_gemm  a dense [T x H] x [H x E] product on the fp16 matrix
+//                   cores with split operands (fp32 accuracy);
 //   router_topk     one wave per token (topk.h).
 #include "moe_internal.h"
 #include "topk.h"
@@ -34,31 +34,35 @@ int router_splits(int T, int H) { return T <= kGemvMaxT ? kRouterSplits : 1; }
 constexpr float kWrScale = 1024.0f, kLoScale = 2048.0f;
 constexpr int kRgT = 32, kRgE = 128, kRgK = 64;
 
-// x fp32 [T][H] -> hi (x16, also the grouped GEMM's operand) and lo parts
+// One launch, two jobs.  Workgroups [0, nxb): x fp32 [T][H] -> hi (x16, also
+// the grouped GEMM's operand) and lo parts, four values per thread.
+// Workgroups [nxb, nxb + nwb): the router matrix fp32 [H][E] -> 2^10 * (hi, lo)
+// parts transposed to [E][H], one 32 x 32 tile each (LDS transpose).  xl and
+// wr may be null (tokens only).
 __global__ void __launch_bounds__(256)
-x_split_kernel(const float* __restrict__ x, _Float16* __restrict__ xh, _Float16* __restrict__ xl,
-               size_t n4) {
-    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= n4) return;
-    const float4 v = reinterpret_cast<const float4*>(x)[i];
-    typedef _Float16 half4 __attribute__((ext_vector_type(4)));
-    half4 h, l;
-    const float f[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        h[j] = (_Float16)f[j];
-        l[j] = (_Float16)((f[j] - (float)h[j]) * kLoScale);
-    }
-    reinterpret_cast<half4*>(xh)[i] = h;
-    if (xl) reinterpret_cast<half4*>(xl)[i] = l;
-}
-
-// router matrix fp32 [H][E] -> 2^10 * (hi, lo) parts, transposed to [E][H]
-__global__ void __launch_bounds__(256)
-w_split_kernel(const float* __restrict__ wr, int H, int E, _Float16* __restrict__ wh,
-               _Float16* __restrict__ wl) {
+split_kernel(const float* __restrict__ x, _Float16* __restrict__ xh, _Float16* __restrict__ xl,
+             size_t n4, int nxb, const float* __restrict__ wr, int H, int E,
+             _Float16* __restrict__ wh, _Float16* __restrict__ wl) {
     __shared__ float tile[32][33];
-    const int h0 = blockIdx.x * 32, e0 = blockIdx.y * 32;
+    const int b = blockIdx.x;
+    if (b < nxb) {
+        const size_t i = (size_t)b * blockDim.x + threadIdx.x;
+        if (i >= n4) return;
+        const float4 v = reinterpret_cast<const float4*>(x)[i];
+        typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+        half4 h, l;
+        const float f[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            h[j] = (_Float16)f[j];
+            l[j] = (_Float16)((f[j] - (float)h[j]) * kLoScale);
+        }
+        reinterpret_cast<half4*>(xh)[i] = h;
+        if (xl) reinterpret_cast<half4*>(xl)[i] = l;
+        return;
+    }
+    const int wb = b - nxb, nhb = (H + 31) / 32;
+    const int h0 = (wb % nhb) * 32, e0 = (wb / nhb) * 32;
     const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;   // 32 x 8
     for (int r = ty; r < 32; r += 8) {
         const int h = h0 + r, e = e0 + tx;
@@ -201,10 +205,9 @@ hipError_t launch_router(const moe_layer_desc& d, const float* x, int T, int32_t
     _Float16* wh = reinterpret_cast<_Float16*>(ws + L.w_hi);
     _Float16* wl = reinterpret_cast<_Float16*>(ws + L.w_lo);
     const size_t n4 = (size_t)T * H / 4;
-    launch_k(c, MOE_K_X_F16, x_split_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, x,
-             xh, xl, n4);
-    launch_k(c, MOE_K_ROUTER_SPLIT, w_split_kernel, dim3((H + 31) / 32, (E + 31) / 32), dim3(256),
-             0, d.router_w, H, E, wh, wl);
+    const int nxb = (int)((n4 + 255) / 256), nwb = ((H + 31) / 32) * ((E + 31) / 32);
+    launch_k(c, MOE_K_X_F16, split_kernel, dim3(nxb + nwb), dim3(256), 0, x, xh, xl, n4, nxb,
+             d.router_w, H, E, wh, wl);
     launch_k(c, MOE_K_ROUTER_MFMA, router_gemm_kernel, dim3((T + kRgT - 1) / kRgT, (E + kRgE - 1) / kRgE),
              dim3(256), 0, xh, xl, wh, wl, T, H, E, part);
     launch_k(c, MOE_K_ROUTER_TOPK, router_topk_kernel, dim3((T + 3) / 4), dim3(256), 0, part, 1,
@@ -215,8 +218,10 @@ hipError_t launch_router(const moe_layer_desc& d, const float* x, int T, int32_t
 // fp16 tokens for the grouped GEMM when the router did not already make them
 hipError_t launch_x16(const float* x, int T, int H, char* ws, const WsLayout& L, const Ctx& c) {
     const size_t n4 = (size_t)T * H / 4;
-    launch_k(c, MOE_K_X_F16, x_split_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, x,
-             reinterpret_cast<_Float16*>(ws + L.x16), (_Float16*)nullptr, n4);
+    const int nxb = (int)((n4 + 255) / 256);
+    launch_k(c, MOE_K_X_F16, split_kernel, dim3(nxb), dim3(256), 0, x,
+             reinterpret_cast<_Float16*>(ws + L.x16), (_Float16*)nullptr, n4, nxb,
+             (const float*)nullptr, H, 0, (_Float16*)nullptr, (_Float16*)nullptr);
     return hipGetLastError();
 }
 
