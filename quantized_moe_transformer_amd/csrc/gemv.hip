@@ -357,20 +357,25 @@ gemv_front_kernel(GemvArgs a) {
 template <int LPR, int NSBL>
 __global__ void __launch_bounds__(64 * kGuWaves)
 gemv_gateup_kernel(GemvArgs a) {
-    __shared__ int32_t s_idx[16];
-    __shared__ float s_w[16];
     const int q = blockIdx.y;
     const int t = q / a.k, j = q % a.k;
     XRegs<LPR, NSBL> X;
     X.load(a.x + (size_t)t * a.H);   // independent of the routing: in flight during the top-k
     int e;
     if (a.route) {
-        if (threadIdx.x < 64) wave_topk<4, kRouterSplits>(a.part, a.E, a.k, t, s_idx, s_w);   // E <= 256
-        __syncthreads();
-        e = s_idx[j];
-        if (blockIdx.x == 0 && j == 0 && threadIdx.x < a.k) {
-            a.idx_out[(size_t)t * a.k + threadIdx.x] = s_idx[threadIdx.x];
-            a.w_out[(size_t)t * a.k + threadIdx.x] = s_w[threadIdx.x];
+        // every wave selects for itself (the waves sit on different SIMDs:
+        // no barrier, no LDS round trip); slot j's expert from lane j.  The
+        // first wave of workgroup (0, t*k) also writes the token's routing.
+        if (blockIdx.x == 0 && j == 0 && threadIdx.x < 64) {
+            const int my_e = wave_topk<4, kRouterSplits>(a.part, a.E, a.k, t,
+                                                         a.idx_out + (size_t)t * a.k,
+                                                         a.w_out + (size_t)t * a.k);   // E <= 256
+            e = __shfl(my_e, j, 64);
+        } else {
+            float my_l, top;
+            int my_e;
+            wave_topk_select<4, kRouterSplits>(a.part, a.E, a.k, t, my_l, my_e, top);
+            e = __shfl(my_e, j, 64);
         }
     } else {
         e = a.idx[(size_t)t * a.k + j];

@@ -65,10 +65,11 @@ __device__ __forceinline__ float row_sum(float v) {
 // of key == m, scanned from the lowest expert block), so ties go to the
 // lower index; a tie group larger than the slots left is cut at the lowest
 // indices.  Selected experts' keys become INT32_MIN.  A NaN logit counts as
-// -inf: never preferred over a number.  Lane j keeps slot j.
+// -inf: never preferred over a number.  Lane j keeps slot j (its logit in
+// my_l, its expert in my_e); top is the largest logit.
 template <int NE, int KS>
-__device__ __forceinline__ void wave_topk(const float* __restrict__ part, int E, int k, int t,
-                                          int32_t* idx_row, float* w_row) {
+__device__ __forceinline__ void wave_topk_select(const float* __restrict__ part, int E, int k,
+                                                 int t, float& my_l, int& my_e, float& top) {
     static_assert(KS == 1 || KS % 4 == 0, "partials per expert: 1 or a multiple of 4");
     static_assert(NE <= 16, "at most 1024 experts");
     const int lane = threadIdx.x & 63;
@@ -98,8 +99,9 @@ __device__ __forceinline__ void wave_topk(const float* __restrict__ part, int E,
         for (int q = 1; q < KS; ++q) s += pv[i][q];
         key[i] = lane + 64 * i < E ? logit_key(s) : kKeyNone;
     }
-    float my_l = -INFINITY, top = 0.f;
-    int my_e = 0;
+    my_l = -INFINITY;
+    top = 0.f;
+    my_e = 0;
     int j = 0;   // slots filled (wave-uniform)
     while (j < k) {
         int m = key[0];
@@ -125,14 +127,26 @@ __device__ __forceinline__ void wave_topk(const float* __restrict__ part, int E,
             }
         }
     }
-    // softmax of the selected logits (= the full softmax renormalised over
-    // them); k <= 16, so the slots sit in row 0
+}
+
+// The selection plus the routing weights: the softmax of the selected logits
+// (= the full softmax renormalised over them); k <= 16, so the slots sit in
+// row 0.
+// Returns, in lane j, slot j's expert.
+template <int NE, int KS>
+__device__ __forceinline__ int wave_topk(const float* __restrict__ part, int E, int k, int t,
+                                         int32_t* idx_row, float* w_row) {
+    const int lane = threadIdx.x & 63;
+    float my_l, top;
+    int my_e;
+    wave_topk_select<NE, KS>(part, E, k, t, my_l, my_e, top);
     const float ex = lane < k ? expf(my_l - top) : 0.f;
     const float z = row_sum(ex);
     if (lane < k) {
         idx_row[lane] = my_e;
         w_row[lane] = ex / z;
     }
+    return my_e;
 }
 
 }  // namespace moe
