@@ -131,7 +131,9 @@ typedef struct moe_opts {
 /* Bytes of device workspace that router_topk, moe_layer_forward and
  * moe_layer_forward_shard need for T token rows split into num_shards shards
  * (any path).  Host-only; needs no device.  Returns 0 for an invalid
- * description.  Calls that share one workspace must not overlap in time. */
+ * description.  Its contents on entry do not matter (nothing is read before
+ * the call writes it).  Calls that share one workspace must not overlap in
+ * time. */
 size_t moe_workspace_bytes(const moe_layer_desc *desc, int32_t T, int32_t num_shards);
 
 /*

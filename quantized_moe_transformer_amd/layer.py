@@ -41,9 +41,11 @@ class DeviceLayer:
         return other
 
     def workspace(self, T: int, num_shards: int = 1):
-        """A zero-filled workspace (its leading counters must start at zero)."""
+        """A workspace for T rows.  The library needs no particular contents; it
+        is filled with 0xFF bytes (NaN as fp16 and fp32) so that a kernel that
+        read workspace it had not written would show in its results."""
         import torch
         nbytes = _lib.moe_workspace_bytes(self.desc, T, num_shards)
         if nbytes == 0 and T > 0:
             raise ValueError("invalid layer description")
-        return torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+        return torch.full((max(nbytes, 256),), 255, dtype=torch.uint8, device=self.device)
