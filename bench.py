@@ -46,12 +46,12 @@ FP16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak
 # --copy-probe).  Keyed by the SHA-256 of the kernel's sources: when they change,
 # the counters no longer describe the kernel and traffic is reported as null.
 TRAFFIC = {
-    # decode T=1, 180 dispatches: FETCH 4727.3 KiB x 1.99980, WRITE 16.1 KiB x 1.0
-    "gemv_gateup": {"sources_sha256": "df6806d31b9d9ca59fc4fc8bccd5ddccdf94678c4a93205a229dc76eff888cc1",
-                    "fetch_bytes": 9680585, "write_bytes": 16448},
-    # prefill T=4096, 9 dispatches: FETCH 224706.8 KiB x 1.99980, WRITE 36864.0 KiB x 1.0
-    "gemm_gateup": {"sources_sha256": "7085de05e2a6533a3719d341636d71bbd5a91cb6efe21e5d0491660a27305464",
-                    "fetch_bytes": 460152745, "write_bytes": 37748736},
+    # decode T=1, 180 dispatches: FETCH 4730.8 KiB x 1.99980, WRITE 16.1 KiB x 1.0
+    "gemv_gateup": {"sources_sha256": "81e2e507efe20c6a4fad911cf7895af1b7673eff93cfff77239774b60ca7533d",
+                    "fetch_bytes": 9687754, "write_bytes": 16448},
+    # prefill T=4096, 9 dispatches: FETCH 224456.6 KiB x 1.99980, WRITE 36864.0 KiB x 1.0
+    "gemm_gateup": {"sources_sha256": "bb5635a35c0e21515ee569554e35a3d5560ad54e034f51ae307501195e6b8758",
+                    "fetch_bytes": 459640338, "write_bytes": 37748736},
 }
 FETCH_SIZE_FACTOR = 1.99980   # plain 256 MiB copy: true bytes read / FETCH_SIZE bytes
 WRITE_SIZE_FACTOR = 1.0
@@ -318,6 +318,79 @@ def bench_prefill(args, torch, qm, mi, DeviceLayer):
     return res, layer, x_host
 
 
+CONTINUUM_T = (1, 2, 4, 8, 16, 32, 64, 128, 256, 512)
+
+
+def bench_continuum(args, torch, qm, mi, DeviceLayer):
+    """Both paths at T = 1 .. 512 rows on the decode-shaped layer (seed 2,
+    uniform router), each forced through moe_opts.path, replayed from HIP
+    graphs over 4 weight copies and 4 token batches.  One JSON line per (T,
+    path) on stdout: step time, tokens/s, algorithmic bytes (every distinct
+    touched expert once, the shared expert, the router matrix, x and out) and
+    FLOPs, GB/s and GFLOP/s, and the path the automatic rule takes at that T."""
+    shp = mi.QWEN35_MOE
+    seed = 2
+    layer = mi.make_layer(shp, seed)
+    base = DeviceLayer.from_shape(layer, shp)
+    copies = [base] + [base.clone_weights() for _ in range(3)]
+    E_bytes = (2 * (shp.I * shp.H // 256) * mi.Q4K_SB_BYTES
+               + (shp.H * shp.I // 256) * mi.Q5K_SB_BYTES)
+    G = 8   # steps per graph: two rounds over the weight copies
+    rows = []
+    for T in args.continuum_t:
+        xs = torch.from_numpy(mi.make_tokens(shp, seed, 4 * T, stream=7)).cuda().view(4, T, shp.H)
+        out = torch.empty((T, shp.H), device="cuda")
+        ws = base.workspace(T)
+        # distinct experts the routing touches, per batch (the library's own top-k)
+        idx = torch.empty((T, shp.k), dtype=torch.int32, device="cuda")
+        wts = torch.empty((T, shp.k), dtype=torch.float32, device="cuda")
+        distinct = []
+        for b in range(4):
+            qm.router_topk(base.desc, xs[b], T, idx, wts, ws)
+            distinct.append(int(torch.unique(idx).numel()))
+        torch.cuda.synchronize()
+        d_avg = float(np.mean(distinct))
+        alg_bytes = (d_avg + 1) * E_bytes + shp.H * shp.E * 4 + 2 * T * shp.H * 4
+        flops = T * (shp.k + 1) * 6.0 * shp.H * shp.I + 2.0 * T * shp.H * shp.E
+        auto_used = []
+        qm.moe_layer_forward(base.desc, xs[0], T, out, ws, path=qm.MOE_PATH_AUTO)
+        auto_used.append(qm.moe_layer_forward(base.desc, xs[0], T, out, ws))
+        for path, pname in ((qm.MOE_PATH_GEMV, "gemv"), (qm.MOE_PATH_MFMA, "mfma")):
+            def step(i, path=path):
+                return qm.moe_layer_forward(copies[i % 4].desc, xs[(i // 4 + i) % 4], T, out,
+                                            ws, path=path)
+            for i in range(2 * G):
+                assert step(i) == path
+            eager_n = max(G, min(256, int(4096 // T)))
+            eager_s = time_steps(torch, step, eager_n)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(G):
+                    step(i)
+            g.replay()
+            torch.cuda.synchronize()
+            n_rep = max(2, min(64, int(2048 // (G * T)) + 2))
+            t0 = time.perf_counter()
+            for _ in range(n_rep):
+                g.replay()
+            torch.cuda.synchronize()
+            secs = (time.perf_counter() - t0) / (n_rep * G)
+            del g
+            rows.append({
+                "T": T, "path": pname, "ms_per_step": secs * 1e3,
+                "tokens_per_s": T / secs,
+                "eager_ms_per_step": eager_s / eager_n * 1e3,
+                "distinct_experts": d_avg,
+                "algorithmic_bytes": alg_bytes, "gflop": flops / 1e9,
+                "gb_per_s": alg_bytes / secs / 1e9, "gflop_per_s": flops / secs / 1e9,
+                "hbm_frac": alg_bytes / secs / 1e9 / HBM_PEAK_GBS,
+                "auto_path": "gemv" if auto_used[0] == qm.MOE_PATH_GEMV else "mfma",
+                "steps_timed": n_rep * G,
+            })
+            print(json.dumps(rows[-1]), flush=True)
+    return rows
+
+
 def cpu_baseline_decode(layer, pool, budget_s):
     import moe_inputs as mi
     import oracle
@@ -361,6 +434,9 @@ def main():
     ap.add_argument("--cpu-prefill-rows", type=int, default=2048)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain MIB-MiB device copy five times (counter calibration)")
+    ap.add_argument("--continuum", action="store_true",
+                    help="only time both paths at T = 1 .. 512 (one JSON line per point)")
+    ap.add_argument("--continuum-t", type=int, nargs="+", default=list(CONTINUUM_T))
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -379,6 +455,9 @@ def main():
         sys.exit(1)
     if args.copy_probe:
         copy_probe(torch, args.copy_probe)
+        return
+    if args.continuum:
+        bench_continuum(args, torch, qm, mi, DeviceLayer)
         return
 
     print("[bench] decode T=1 ...", file=sys.stderr, flush=True)

@@ -69,7 +69,7 @@ extern "C" {
 #define MOE_ENODEVICE (-5)     /* no gfx950 device is current */
 
 /* Compute paths (moe_opts.path). */
-#define MOE_PATH_AUTO 0        /* GEMV for T <= 32, grouped MFMA GEMM above */
+#define MOE_PATH_AUTO 0        /* GEMV for T <= 14, grouped MFMA GEMM above (measured crossover) */
 #define MOE_PATH_GEMV 1        /* fp32 dequant-GEMV, fp32 accumulation */
 #define MOE_PATH_MFMA 2        /* fp16-operand MFMA grouped GEMM, fp32 accumulation */
 

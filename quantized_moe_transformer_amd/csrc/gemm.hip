@@ -16,21 +16,28 @@
 // up to 160 rows of one expert's group (a whole routed expert at T = 4096, so
 // its weights are dequantised once per column tile) times 256 weight rows, and
 // walks K in steps of 64 (one pair of K-quant sub-blocks).  Its 8 waves are
-//   4 consumer waves: MFMA only, from one LDS stage; wave w owns two 32-wide
-//     column blocks times every 32-row block the tile has (up to 5), so each
-//     fragment read from LDS feeds several MFMAs;
+//   4 consumer waves: MFMA only; wave w owns two 32-wide column blocks times
+//     every 32-row block the tile has (up to 5), so each fragment read from
+//     LDS feeds several MFMAs; the fragment reads of a 16-deep K slice are
+//     issued two slices ahead of its MFMAs;
 //   4 producer waves: dequantise the next step's packed weights into the
-//     other LDS stage, with the weight loads issued ahead into a register
-//     ring (whole superblocks per row where the layout allows);
-//   the consumer waves also gather the next step's token rows (fp16) into the
-//     other stage, so each group of waves waits only for its own loads;
-// so dequantisation (VALU) and matrix work (MFMA) run side by side.
+//     other fp16 weight stage.  Where every row's K range is whole
+//     superblocks they fetch superblock p of all 256 rows together with
+//     coalesced direct loads into LDS, one superblock ahead, and each copies
+//     its own row into registers once per four steps;
+//   the consumer waves also fetch the token rows (fp16) by direct loads, a
+//     step ahead, so each group of waves waits only for its own loads.
+// One producer and one consumer wave share each SIMD: the dequantisation
+// (VALU) of one wave runs beside the MFMAs of the other, which measured far
+// better than dequantising into MFMA operand registers in the MFMA wave
+// itself, where the two serialise.  The cost is LDS traffic: about 1.1 KB per
+// 32x32x16 MFMA, close to what the LDS delivers at the MFMA rate.
 //
 //   gateup (MODE 0): A = token rows of x16 gathered through the expert-sorted
 //     slot list, B = 128 gate rows + the matching 128 up rows (4-bit); each
 //     consumer wave holds a gate block and the matching up block, so the
-//     epilogue writes h = silu(g) * u (fp16, scaled by 2^-4) straight from
-//     registers, in sorted row order.
+//     epilogue forms h = silu(g) * u (fp16, scaled by 2^-4) in registers and
+//     writes it, staged through LDS, in sorted row order.
 //   down (MODE 1): A = h rows (contiguous per expert), B = 256 down rows
 //     (5-bit); the epilogue scales by the routing weight (and 2^4) and writes
 //     the slot's row of the per-slot buffer (the shared expert: its own
@@ -47,8 +54,8 @@ constexpr int kBK = 64;                 // K per step (one pair of sub-blocks)
 constexpr int kLdsRow = kBK + 8;        // halves per LDS row (8 halves of padding)
 constexpr int kTM = kTileM;             // rows per tile (up to 5 blocks of 32)
 constexpr int kTN = 256;                // weight rows per tile
-// weight-load prefetch distance (steps): 3 for the 4-bit gate/up stream, 2
-// for the 5-bit down stream (its pieces carry high bits too: more registers)
+// weight-load prefetch distance (steps) of the per-piece path (down rows whose
+// K range is not whole superblocks): 2 steps for the 5-bit stream
 template <int MODE> struct PrefetchDistance { static constexpr int v = MODE == 0 ? 3 : 2; };
 constexpr int kConsumers = 4;           // consumer waves (two 32-column blocks each)
 constexpr int kProducers = 4;           // producer waves
@@ -59,13 +66,15 @@ constexpr int kBTasks = kTN * 2 / (64 * kProducers);   // 16-byte code pieces pe
 // sub-block 2c+1 high nibbles) to fp16 and store it into an LDS row at k
 // offsets 16*hh + [0,16) and 32 + 16*hh + [0,16).
 //
-// The fp16 bit pattern 0x6400 | q is the number 1024 + q (q < 1024), so one
-// and-or turns two code bytes of a word into two fp16 numbers, and
-//   w = d*sc*q - dmin*m = (1024 + q) * (d*sc) - (1024*d*sc + dmin*m)
-// is one mixed-precision fma per weight (fp16 operand, fp32 arithmetic,
-// fp16 result).  The constant 1024*d*sc + dmin*m is rounded to fp32 once
-// (relative 2^-24 of a value <= 1024 |d*sc| + |dmin*m|): far below the fp16
-// rounding of w itself.
+// Two weights per instruction on the packed fp16 pipe.  A byte permute puts
+// the code bytes of two neighbouring k into the two halves of a word, and one
+// and-or with the fp16 pattern 0x6400 turns each code q into the number
+// 1024 + q; subtracting 1024 is exact, leaving q as fp16.  Then one packed
+// fused multiply-add gives w = q*(d*sc) - dmin*m, rounded once, with d*sc
+// and dmin*m (exact in fp32) each rounded to fp16 first: w is off by at most
+// 2^-11 (q*|d*sc| + |dmin*m|) plus its own rounding, where rounding the exact
+// value alone would give 2^-11 |w|.  The mixed-precision fma that keeps the
+// constants in fp32 runs at a quarter of this rate on gfx950.
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 
 // (x & m) | o in one v_and_or_b32 (the compiler splits it into an and and an
@@ -76,15 +85,6 @@ __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t o) {
     return r;
 }
 
-// bytes 0 and 2 of `bytes` (codes, masked by m) as the fp16 numbers 1024 + code
-__device__ __forceinline__ half2v code_pair(uint32_t bytes, uint32_t m) {
-    return __builtin_bit_cast(half2v, and_or(bytes, m, 0x64006400u));
-}
-
-__device__ __forceinline__ _Float16 mix_fma(_Float16 q1024, float ds, float c) {
-    return (_Float16)__builtin_fmaf((float)q1024, ds, c);
-}
-
 template <bool HIGH>
 __device__ __forceinline__ void dequant_piece_to_lds(const SbHead& hd, const uint4& qs,
                                                      const uint4& qh, int c, int hh,
@@ -92,45 +92,68 @@ __device__ __forceinline__ void dequant_piece_to_lds(const SbHead& hd, const uin
     float sca, ma, scb, mb;
     sub_scale_min(hd, 2 * c, sca, ma);
     sub_scale_min(hd, 2 * c + 1, scb, mb);
-    const float dsa = hd.d * sca, dsb = hd.d * scb;
-    const float ca = -__builtin_fmaf(1024.0f, dsa, hd.dmin * ma);
-    const float cb = -__builtin_fmaf(1024.0f, dsb, hd.dmin * mb);
+    const _Float16 dsa = (_Float16)(hd.d * sca), dsb = (_Float16)(hd.d * scb);
+    const _Float16 dma = (_Float16)(hd.dmin * ma), dmb = (_Float16)(hd.dmin * mb);
+    const half2v DSA = {dsa, dsa}, DSB = {dsb, dsb}, NMA = {-dma, -dma}, NMB = {-dmb, -dmb};
+    const half2v K1024 = {(_Float16)-1024.0f, (_Float16)-1024.0f};
     const uint32_t qw[4] = {qs.x, qs.y, qs.z, qs.w};
     const uint32_t hw[4] = {qh.x, qh.y, qh.z, qh.w};
-    half8 lo[2], hi[2];
+    uint32_t lo[8], hi[8];
 #pragma unroll
     for (int wi = 0; wi < 4; ++wi) {
-        half2v la, lb, ha, hb;   // codes (0, 2) and (1, 3) of the low and high nibbles
+        uint32_t l5 = qw[wi], h5 = qw[wi] >> 4;
         if (HIGH) {
-            const uint32_t l5 = (qw[wi] & 0x0f0f0f0fu) | (((hw[wi] >> (2 * c)) & 0x01010101u) << 4);
-            const uint32_t h5 =
-                ((qw[wi] >> 4) & 0x0f0f0f0fu) | (((hw[wi] >> (2 * c + 1)) & 0x01010101u) << 4);
-            la = code_pair(l5, 0x00ff00ffu);
-            lb = code_pair(l5 >> 8, 0x00ff00ffu);
-            ha = code_pair(h5, 0x00ff00ffu);
-            hb = code_pair(h5 >> 8, 0x00ff00ffu);
-        } else {
-            la = code_pair(qw[wi], 0x000f000fu);
-            lb = code_pair(qw[wi] >> 8, 0x000f000fu);
-            ha = code_pair(qw[wi] >> 4, 0x000f000fu);
-            hb = code_pair(qw[wi] >> 12, 0x000f000fu);
+            l5 = (qw[wi] & 0x0f0f0f0fu) | (((hw[wi] >> (2 * c)) & 0x01010101u) << 4);
+            h5 = ((qw[wi] >> 4) & 0x0f0f0f0fu) | (((hw[wi] >> (2 * c + 1)) & 0x01010101u) << 4);
         }
-        half8& L = lo[wi >> 1];
-        half8& Hh = hi[wi >> 1];
-        const int o = 4 * (wi & 1);
-        L[o + 0] = mix_fma(la[0], dsa, ca);
-        L[o + 1] = mix_fma(lb[0], dsa, ca);
-        L[o + 2] = mix_fma(la[1], dsa, ca);
-        L[o + 3] = mix_fma(lb[1], dsa, ca);
-        Hh[o + 0] = mix_fma(ha[0], dsb, cb);
-        Hh[o + 1] = mix_fma(hb[0], dsb, cb);
-        Hh[o + 2] = mix_fma(ha[1], dsb, cb);
-        Hh[o + 3] = mix_fma(hb[1], dsb, cb);
+        const uint32_t m = HIGH ? 0x00ff00ffu : 0x000f000fu;
+#pragma unroll
+        for (int pr = 0; pr < 2; ++pr) {
+            // bytes 2pr and 2pr+1 of the word into the two halves
+            const uint32_t sel = pr ? 0x0c030c02u : 0x0c010c00u;
+            const uint32_t pl = __builtin_amdgcn_perm(0u, l5, sel);
+            const uint32_t ph = HIGH ? __builtin_amdgcn_perm(0u, h5, sel) : pl >> 4;
+            const half2v ql = __builtin_bit_cast(half2v, and_or(pl, m, 0x64006400u)) + K1024;
+            const half2v qh2 = __builtin_bit_cast(half2v, and_or(ph, m, 0x64006400u)) + K1024;
+            lo[2 * wi + pr] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(ql, DSA, NMA));
+            hi[2 * wi + pr] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(qh2, DSB, NMB));
+        }
     }
-    *reinterpret_cast<half8*>(row + 16 * hh) = lo[0];
-    *reinterpret_cast<half8*>(row + 16 * hh + 8) = lo[1];
-    *reinterpret_cast<half8*>(row + 32 + 16 * hh) = hi[0];
-    *reinterpret_cast<half8*>(row + 32 + 16 * hh + 8) = hi[1];
+    *reinterpret_cast<uint4*>(row + 16 * hh) = uint4{lo[0], lo[1], lo[2], lo[3]};
+    *reinterpret_cast<uint4*>(row + 16 * hh + 8) = uint4{lo[4], lo[5], lo[6], lo[7]};
+    *reinterpret_cast<uint4*>(row + 32 + 16 * hh) = uint4{hi[0], hi[1], hi[2], hi[3]};
+    *reinterpret_cast<uint4*>(row + 32 + 16 * hh + 8) = uint4{hi[4], hi[5], hi[6], hi[7]};
+}
+
+// LDS operand fragments read as asm, so that the compiler keeps the reads
+// where they stand (it otherwise sinks each read to its first MFMA and waits
+// for it there); lds_wait_frags then waits for them.  LDS operations complete
+// in order, so waiting until at most N are outstanding, N being the reads
+// issued after the ones needed, is exact for this wave's own reads and only
+// stricter when the compiler's own LDS or scalar loads are in flight too.
+template <int OFF>
+__device__ __forceinline__ void lds_read_frag(half8& dst, uint32_t addr) {
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(dst) : "v"(addr), "i"(OFF));
+}
+
+// MB fragments at LDS byte addresses base + 4096 i (one per 32-row block)
+template <int MB>
+__device__ __forceinline__ void lds_read_rows(half8* dst, uint32_t base) {
+    if constexpr (MB > 0) lds_read_frag<0>(dst[0], base);
+    if constexpr (MB > 1) lds_read_frag<4096>(dst[1], base);
+    if constexpr (MB > 2) lds_read_frag<8192>(dst[2], base);
+    if constexpr (MB > 3) lds_read_frag<12288>(dst[3], base);
+    if constexpr (MB > 4) lds_read_frag<16384>(dst[4], base);
+}
+
+// wait until at most N LDS operations are outstanding; each fragment is tied
+// to the wait so that no use of it is scheduled above it
+template <int N, int CNT>
+__device__ __forceinline__ void lds_wait_frags(half8 (&f)[CNT]) {
+    static_assert(N >= 0 && N < 16, "lgkmcnt range");
+    asm volatile("s_waitcnt lgkmcnt(%0)" : : "i"(N));
+#pragma unroll
+    for (int i = 0; i < CNT; ++i) asm volatile("" : "+v"(f[i]));
 }
 
 struct GemmArgs {
@@ -161,12 +184,28 @@ struct BRegs {
 // A stages hold kTM rows of kBK halves with no padding; the 16-byte chunk c
 // of row r sits at chunk position c ^ (r & 7), so the 32 rows that one MFMA
 // fragment read touches spread over all banks.
-constexpr int kAStages = 3;
+// Token-row stages: the rows of step kk + kAStages - 1 are requested at the
+// start of step kk, into the stage that step kk - 1 read.
+constexpr int kAStages = 2;
 __device__ __forceinline__ int a_chunk(int r, int c) { return r * (kBK / 8) + (c ^ (r & 7)); }
+
+// wait until at most n later steps' token-row loads (MB per step) are in flight
+template <int MB>
+__device__ __forceinline__ void wait_a_steps(int n) {
+    static_assert(kAStages - 2 <= 2, "wait_a_steps covers up to two later steps");
+    if (n >= 2) wait_vmcnt<2 * MB>();
+    else if (n == 1) wait_vmcnt<MB>();
+    else wait_vmcnt<0>();
+}
+
+// Packed superblocks of the tile's 256 weight rows, one superblock per row,
+// row after row (the largest: 5-bit, 11 chunks of 16 bytes per row).
+constexpr int kRawChunks = kTN * (kQ5Bytes / 16);
 
 struct __align__(16) GemmLds {
     _Float16 a[kAStages][kTM * kBK];
     _Float16 b[2][kTN][kLdsRow];
+    uint4 raw[kRawChunks];
 };
 
 
@@ -185,116 +224,104 @@ __device__ __forceinline__ void gemm_produce(const GemmArgs& a, const TileInfo& 
                                           const int32_t* row_src, const float* row_w) {
     constexpr int kPD = PrefetchDistance<MODE>::v;
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
-    const int g = ti.g, m0 = ti.m0, mcount = ti.mcount, grow0 = ti.grow0;
+    const int wave = tid >> 6;
+    const int g = ti.g;
     const int Iexp = ti.Iexp, Iloc = ti.Iloc, i0 = ti.i0, n0 = ti.n0;
     const bool is_sh = ti.is_sh;
-    (void)m0;
 
     // ------------------------------- producers -------------------------------
     const int pt = tid - 64 * kConsumers;
-    if constexpr (MODE == 0) {
-        // Producer thread pt owns weight row pt of the tile (gate rows
-        // 0-127, the matching up rows 128-255) and loads the row's whole
-        // 144-byte superblock -- nine 16-byte loads, contiguous -- once per
-        // four steps into a two-slot register ring, one superblock ahead;
-        // each step dequantises its 64 weights of the current one.
-        const int col = pt & (kTN / 2 - 1);
-        const int colc = n0 + col < Iloc ? col : 0;   // ragged tile: discarded columns
-        const size_t mat = (size_t)a.I * a.H / kSbWeights * kQ4Bytes;
-        const uint8_t* m = is_sh ? (pt < kTN / 2 ? a.w_shared : a.w_shared2)
-                                 : (pt < kTN / 2 ? a.w_routed : a.w_routed2) + (size_t)g * mat;
-        const int nsb = a.H / kSbWeights;
-        const uint8_t* rowp = m + (size_t)(i0 + n0 + colc) * nsb * kQ4Bytes;
-        uint4 sbr[2][kQ4Bytes / 16];
-        auto load_sb = [&](int p, uint4* r) {
-            const uint4* src =
-                reinterpret_cast<const uint4*>(rowp + (size_t)min(p, nsb - 1) * kQ4Bytes);
-#pragma unroll
-            for (int i = 0; i < kQ4Bytes / 16; ++i) r[i] = src[i];
+    if (MODE == 0 || a.sb_rows) {
+        // Every weight row's K range is whole superblocks (gate/up always; the
+        // down rows when the shard boundary falls on superblocks).  The
+        // producer waves fetch superblock p of all 256 rows together -- chunk
+        // q = 16-byte piece q % NCH of row q / NCH, consecutive lanes on
+        // consecutive bytes of a row -- by direct loads into lds.raw, one
+        // superblock ahead; producer thread pt owns row pt, copies its
+        // superblock into registers once per four steps and dequantises one
+        // sub-block pair of it per step.
+        constexpr int SBB = MODE == 0 ? kQ4Bytes : kQ5Bytes;
+        constexpr int NCH = SBB / 16;
+        const int nsb = a.nk / 4;
+        auto row_base = [&](int r) -> const uint8_t* {
+            if (MODE == 0) {
+                const int col = r & (kTN / 2 - 1);
+                const int colc = n0 + col < Iloc ? col : 0;   // ragged tile: discarded columns
+                const size_t mat = (size_t)a.I * a.H / kSbWeights * kQ4Bytes;
+                const uint8_t* m = is_sh ? (r < kTN / 2 ? a.w_shared : a.w_shared2)
+                                         : (r < kTN / 2 ? a.w_routed : a.w_routed2) + (size_t)g * mat;
+                return m + (size_t)(i0 + n0 + colc) * (a.H / kSbWeights) * kQ4Bytes;
+            } else {
+                const int o = n0 + r < a.H ? n0 + r : n0;     // ragged tile: discarded rows
+                const uint8_t* m = is_sh ? a.w_shared
+                                         : a.w_routed + (size_t)g * ((size_t)a.H * a.I / kSbWeights * kQ5Bytes);
+                return m + (((size_t)o * Iexp + i0) >> 8) * kQ5Bytes;
+            }
         };
-        auto deq_step = [&](const uint4* r, int c, int stage) {
+        const uint8_t* gsrc[NCH];
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+            const int q = pt + 64 * kProducers * i;
+            gsrc[i] = row_base(q / NCH) + 16 * (q % NCH);
+        }
+        const uint32_t raw_lds = (uint32_t)(uintptr_t)&lds.raw[0];
+        const int pw = wave - kConsumers;
+        auto issue_raw = [&](int p) {
+#pragma unroll
+            for (int i = 0; i < NCH; ++i)
+                lds_dma16(gsrc[i] + (size_t)p * SBB,
+                          __builtin_amdgcn_readfirstlane(raw_lds + (64 * pw + 64 * kProducers * i) * 16));
+        };
+        uint4 R[NCH];
+        auto read_raw = [&]() {
+#pragma unroll
+            for (int i = 0; i < NCH; ++i) R[i] = lds.raw[pt * NCH + i];
+        };
+        auto deq_step = [&](int c, int stage) {
             SbHead hd;
-            hd.d = f16_bits_to_f32(r[0].x & 0xffffu);
-            hd.dmin = f16_bits_to_f32(r[0].x >> 16);
-            hd.s0 = r[0].y;
-            hd.s1 = r[0].z;
-            hd.s2 = r[0].w;
+            hd.d = f16_bits_to_f32(R[0].x & 0xffffu);
+            hd.dmin = f16_bits_to_f32(R[0].x >> 16);
+            hd.s0 = R[0].y;
+            hd.s1 = R[0].z;
+            hd.s2 = R[0].w;
             _Float16* dst = &lds.b[stage][pt][0];
-            dequant_piece_to_lds<false>(hd, r[1 + 2 * c], r[1 + 2 * c], c, 0, dst);
-            dequant_piece_to_lds<false>(hd, r[2 + 2 * c], r[2 + 2 * c], c, 1, dst);
+            if (MODE == 0) {
+                dequant_piece_to_lds<false>(hd, R[1 + 2 * c], R[1 + 2 * c], c, 0, dst);
+                dequant_piece_to_lds<false>(hd, R[2 + 2 * c], R[2 + 2 * c], c, 1, dst);
+            } else {
+                dequant_piece_to_lds<true>(hd, R[3 + 2 * c], R[1], c, 0, dst);
+                dequant_piece_to_lds<true>(hd, R[4 + 2 * c], R[2], c, 1, dst);
+            }
         };
-        const int last = a.nk - 1;
-        load_sb(0, sbr[0]);
-        load_sb(1, sbr[1]);
-        deq_step(sbr[0], 0, 0);
-        __syncthreads();   // stage 0 ready
-        // steps 4*p0 .. 4*p0+7 use superblocks p0 (slot 0) and p0+1 (slot 1)
-        for (int p0 = 0; p0 < nsb; p0 += 2) {
+        issue_raw(0);
+        wait_vmcnt<0>();
+        __syncthreads();   // superblock 0 of every row in lds.raw
+        read_raw();
+        deq_step(0, 0);
+        __syncthreads();   // stage 0 ready; lds.raw free
+        if (nsb > 1) issue_raw(1);
+        // step kk = 4p + u: the consumers read stage kk & 1 while this
+        // dequantises step kk + 1 into the other; superblock p + 1 is copied
+        // from lds.raw in step 4p + 3, requested at the start of step 4p
+        // and waited for at the end of step 4p + 2
+        for (int p = 0; p < nsb; ++p) {
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int kk = 4 * p0 + u;
-                if (kk > last) break;
-                const int nxt = kk + 1;
-                if (nxt <= last) {
-                    const int un = u + 1;   // step nxt: slot (un >> 2) & 1, sub-block pair un & 3
-                    deq_step(sbr[(un >> 2) & 1], un & 3, nxt & 1);
-                    if ((un & 3) == 3) load_sb(p0 + (un >> 2) + 2, sbr[(un >> 2) & 1]);
+            for (int u = 0; u < 4; ++u) {
+                const int nxt = 4 * p + u + 1;
+                if (u < 3) {
+                    deq_step(u + 1, nxt & 1);
+                } else if (p + 1 < nsb) {
+                    read_raw();
+                    deq_step(0, nxt & 1);
                 }
+                if (u == 2 && p + 1 < nsb) wait_vmcnt<0>();
                 __syncthreads();
+                if (u == 3 && p + 2 < nsb) issue_raw(p + 2);
             }
         }
         return;
     }
-    if (MODE == 1 && a.sb_rows) {
-        // The down rows' K ranges are whole 5-bit superblocks: producer
-        // thread pt owns output row n0 + pt and loads each 176-byte
-        // superblock of it -- eleven 16-byte loads, contiguous -- once per
-        // four steps, one superblock ahead, as the gate/up path does.
-        const int o = n0 + pt < a.H ? n0 + pt : n0;   // ragged tile: discarded rows
-        const uint8_t* m = is_sh ? a.w_shared
-                                 : a.w_routed + (size_t)g * ((size_t)a.H * a.I / kSbWeights * kQ5Bytes);
-        const int nsb = Iloc / kSbWeights;
-        const uint8_t* rowp = m + (((size_t)o * Iexp + i0) >> 8) * kQ5Bytes;
-        uint4 sbr[2][kQ5Bytes / 16];
-        auto load_sb = [&](int p, uint4* r) {
-            const uint4* src =
-                reinterpret_cast<const uint4*>(rowp + (size_t)min(p, nsb - 1) * kQ5Bytes);
-#pragma unroll
-            for (int i = 0; i < kQ5Bytes / 16; ++i) r[i] = src[i];
-        };
-        auto deq_step = [&](const uint4* r, int c, int stage) {
-            SbHead hd;
-            hd.d = f16_bits_to_f32(r[0].x & 0xffffu);
-            hd.dmin = f16_bits_to_f32(r[0].x >> 16);
-            hd.s0 = r[0].y;
-            hd.s1 = r[0].z;
-            hd.s2 = r[0].w;
-            _Float16* dst = &lds.b[stage][pt][0];
-            dequant_piece_to_lds<true>(hd, r[3 + 2 * c], r[1], c, 0, dst);
-            dequant_piece_to_lds<true>(hd, r[4 + 2 * c], r[2], c, 1, dst);
-        };
-        const int last = a.nk - 1;
-        load_sb(0, sbr[0]);
-        load_sb(1, sbr[1]);
-        deq_step(sbr[0], 0, 0);
-        __syncthreads();   // stage 0 ready
-        for (int p0 = 0; p0 < nsb; p0 += 2) {
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int kk = 4 * p0 + u;
-                if (kk > last) break;
-                const int nxt = kk + 1;
-                if (nxt <= last) {
-                    const int un = u + 1;
-                    deq_step(sbr[(un >> 2) & 1], un & 3, nxt & 1);
-                    if ((un & 3) == 3) load_sb(p0 + (un >> 2) + 2, sbr[(un >> 2) & 1]);
-                }
-                __syncthreads();
-            }
-        }
-        return;
-    }
+    __syncthreads();   // matches the superblock paths' first barrier
     const uint8_t* wsrc[kBTasks];   // MODE 0: the row's superblocks; MODE 1: matrix base
     size_t eoff[kBTasks];           // MODE 1: element offset of the row's range
     int bhh[kBTasks], brr[kBTasks];
@@ -382,17 +409,14 @@ template <int MODE, int MB>
 __device__ __forceinline__ void gemm_consume(const GemmArgs& a, const TileInfo& ti, GemmLds& lds,
                                           const int32_t* row_src, const float* row_w,
                                              float16v (&acc)[MB][2]) {
-    constexpr int kPD = PrefetchDistance<MODE>::v;
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
-    const int g = ti.g, m0 = ti.m0, mcount = ti.mcount, grow0 = ti.grow0;
-    const int Iexp = ti.Iexp, Iloc = ti.Iloc, i0 = ti.i0, n0 = ti.n0;
+    const int mcount = ti.mcount, grow0 = ti.grow0;
     const bool is_sh = ti.is_sh;
-    (void)m0;
 
     // ------------------------------- consumers -------------------------------
     // The consumer waves move the token rows (A) into LDS themselves with direct
-    // global-to-LDS loads (no registers), two steps ahead into a three-stage ring,
+    // global-to-LDS loads (no registers), into a ring of kAStages stages,
     // so their waits cover only these loads and the producers' waits only the
     // weight loads.  Thread tid's load i fills chunk slot q = tid + 256 i: row
     // q >> 3, chunk position q & 7, i.e. logical chunk (q & 7) ^ (row & 7).  Rows
@@ -419,46 +443,48 @@ __device__ __forceinline__ void gemm_consume(const GemmArgs& a, const TileInfo& 
                       __builtin_amdgcn_readfirstlane(stage + (64 * wave + 256 * i) * 16));
     };
 
-    // this wave's two 32-row blocks of B: gate block w and up block w (MODE 0),
-    // or output blocks 2w and 2w+1 (MODE 1)
+    // this wave's two 32-row blocks of B: gate block w and up block w (MODE 0,
+    // rows 32w and 128 + 32w), or output blocks 2w and 2w+1 (MODE 1)
     const int bc0 = MODE == 0 ? 32 * wave : 64 * wave;
-    const int bc1 = MODE == 0 ? kTN / 2 + 32 * wave : 64 * wave + 32;
-    issue_a(0);
-    if (a.nk > 1) {
-        issue_a(1);
-        wait_vmcnt<MB>();         // step 0's rows landed
-    } else {
-        wait_vmcnt<0>();
-    }
+    for (int s = 0; s < kAStages - 1; ++s)
+        if (s < a.nk) issue_a(s);
+    __syncthreads();              // the producers' first superblock fetch
+    wait_a_steps<MB>(min(kAStages - 1, a.nk) - 1);   // step 0's rows landed
     __syncthreads();              // stage 0 ready
     for (int kk = 0; kk < a.nk; ++kk) {
         const int st = kk & 1;
-        const _Float16* sa = &lds.a[kk % kAStages][0];
+        // the rows of step kk + kAStages - 1 go to the stage that step kk - 1
+        // read (every wave left it at the last barrier)
+        if (kk + kAStages - 1 < a.nk) issue_a(kk + kAStages - 1);
+        // fragments of K slice ks: f[ks][0..MB) token rows, f[ks][MB], f[ks][MB+1]
+        // the two weight blocks; slice ks + 2's reads are issued before the
+        // MFMAs of slice ks
+        const int nl = lane & 31, kh = lane >> 5;
+        const uint32_t sa = (uint32_t)(uintptr_t)&lds.a[kk % kAStages][0] + 128 * nl;
+        const uint32_t sb = (uint32_t)(uintptr_t)&lds.b[st][bc0 + nl][8 * kh];
+        constexpr int kB1 = (MODE == 0 ? kTN / 2 : 32) * kLdsRow * 2;   // bytes from block bc0 to bc1
+        half8 f[4][MB + 2];
+        auto read_slice = [&](int ks) {
+            lds_read_rows<MB>(f[ks], sa + 16 * ((2 * ks + kh) ^ (nl & 7)));
+            lds_read_frag<0>(f[ks][MB], sb + 32 * ks);
+            lds_read_frag<kB1>(f[ks][MB + 1], sb + 32 * ks);
+        };
+        read_slice(0);
+        read_slice(1);
 #pragma unroll
         for (int ks = 0; ks < kBK / 16; ++ks) {
-            const int kof = ks * 16 + 8 * (lane >> 5);
-            const half8 b0 = *reinterpret_cast<const half8*>(&lds.b[st][bc0 + (lane & 31)][kof]);
-            const half8 b1 = *reinterpret_cast<const half8*>(&lds.b[st][bc1 + (lane & 31)][kof]);
-            half8 av[MB];
-#pragma unroll
-            for (int i = 0; i < MB; ++i)
-                av[i] = *reinterpret_cast<const half8*>(
-                    sa + 8 * a_chunk(32 * i + (lane & 31), 2 * ks + (lane >> 5)));
+            if (ks > 0) __builtin_amdgcn_sched_barrier(0x6);
+            if (ks < 3) lds_wait_frags<MB + 2>(f[ks]);   // slice ks + 1 may still be in flight
+            else lds_wait_frags<0>(f[ks]);
+            if (ks < 2) read_slice(ks + 2);
 #pragma unroll
             for (int i = 0; i < MB; ++i) {
-                acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], b0, acc[i][0], 0, 0, 0);
-                acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], b1, acc[i][1], 0, 0, 0);
+                acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f[ks][i], f[ks][MB], acc[i][0], 0, 0, 0);
+                acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f[ks][i], f[ks][MB + 1], acc[i][1], 0, 0, 0);
             }
         }
-        // the rows of step kk + 2 go to the stage that step kk - 1 read (all
-        // waves left it at the last barrier); step kk + 1's must have landed
-        // before the barrier
-        if (kk + 2 < a.nk) {
-            issue_a(kk + 2);
-            wait_vmcnt<MB>();
-        } else {
-            wait_vmcnt<0>();
-        }
+        // step kk + 1's rows must have landed before the barrier
+        wait_a_steps<MB>(min(kAStages - 2, a.nk - kk - 2));
         __syncthreads();
     }
 

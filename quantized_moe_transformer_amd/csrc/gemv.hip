@@ -528,7 +528,7 @@ static void launch_gateup_t(const GemvArgs& a, const Ctx& c) {
 
 static int lanes_per_row(int nsb) { return nsb >= 8 ? 64 : 8 * nsb; }
 
-// Front kernel: router partials (T <= kGemvMaxT) and/or the shared expert's gate/up.
+// Front kernel: router partials (T <= kRouterSmallMaxT) and/or the shared expert's gate/up.
 static hipError_t launch_front(GemvArgs& a, bool route, bool shared, const WsLayout& L, char* ws,
                                const Ctx& c) {
     const int nsb = a.H / kSbWeights;
@@ -548,7 +548,7 @@ static hipError_t launch_front(GemvArgs& a, bool route, bool shared, const WsLay
     return hipGetLastError();
 }
 
-// Router partial logits only (router_topk at T <= kGemvMaxT).
+// Router partial logits only (router_topk at T <= kRouterSmallMaxT).
 hipError_t launch_router_small(const moe_layer_desc& d, const float* x, int T, char* ws,
                                const WsLayout& L, const Ctx& c) {
     GemvArgs a = base_args(d, x, T, 0, 1);
@@ -568,7 +568,7 @@ hipError_t launch_gemv(const moe_layer_desc& d, const float* x, int T, const int
     a.out = out;
     // small T: partials in the front kernel, top-k inside the gate/up kernel;
     // otherwise the matrix-core router runs first
-    const bool fused_route = route && T <= kGemvMaxT && d.n_experts <= 256;
+    const bool fused_route = route && T <= kRouterSmallMaxT && d.n_experts <= 256;
     if (route) {
         a.idx_out = reinterpret_cast<int32_t*>(ws + L.idx);
         a.w_out = reinterpret_cast<float*>(ws + L.w);

@@ -18,7 +18,9 @@ constexpr int kWave = 64;
 constexpr int kQ4Bytes = 144;   // 4-bit K-quant superblock
 constexpr int kQ5Bytes = 176;   // 5-bit K-quant superblock
 constexpr int kSbWeights = 256;
-constexpr int kGemvMaxT = 32;   // automatic path: GEMV up to this many rows
+// router: split-K fp32 partials on the vector units up to this many rows (the
+// GEMV path folds them into its first kernel), the matrix-core router beyond
+constexpr int kRouterSmallMaxT = 32;
 constexpr int kTileM = 160;     // grouped-GEMM rows (slots) per tile (5 blocks of 32)
 constexpr int kRouterSplits = 8;   // split-K partial logits per expert at small T
 // h is carried into the down projection as fp16 scaled by 2^-4: the SwiGLU

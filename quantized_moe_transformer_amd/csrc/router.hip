@@ -17,7 +17,7 @@
 
 namespace moe {
 
-int router_splits(int T, int H) { return T <= kGemvMaxT ? kRouterSplits : 1; }
+int router_splits(int T, int H) { return T <= kRouterSmallMaxT ? kRouterSplits : 1; }
 
 // ---------------------------------------------------------------------------
 // Many rows: logits on the fp16 matrix cores with fp32 accuracy.  Each fp32
@@ -193,7 +193,7 @@ hipError_t launch_router(const moe_layer_desc& d, const float* x, int T, int32_t
                          char* ws, const WsLayout& L, const Ctx& c) {
     const int H = d.hidden, E = d.n_experts;
     float* part = reinterpret_cast<float*>(ws + L.router_part);
-    if (T <= kGemvMaxT) {
+    if (T <= kRouterSmallMaxT) {
         hipError_t e = launch_router_small(d, x, T, ws, L, c);
         if (e != hipSuccess) return e;
         launch_k(c, MOE_K_ROUTER_TOPK, router_topk_kernel, dim3((T + 3) / 4), dim3(256), 0, part,

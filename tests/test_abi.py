@@ -114,7 +114,7 @@ def test_empty_batch_is_a_no_op(L):
 
 def test_path_choice_reported(L):
     d = desc()
-    for T, path, expect in [(1, 0, 1), (32, 0, 1), (33, 0, 2), (1, 2, 2), (4096, 1, 1)]:
+    for T, path, expect in [(1, 0, 1), (14, 0, 1), (15, 0, 2), (32, 0, 2), (1, 2, 2), (4096, 1, 1)]:
         used = ctypes.c_int32(-1)
         o = L.moe_opts(path, ctypes.pointer(used), None, 0)
         # a too-small workspace stops the call after the path is chosen

@@ -260,8 +260,16 @@ def test_gemv_decode_tokens():
 
 
 def test_gemv_batched_decode():
-    check_layer("decode_batched", 32, qm.MOE_PATH_AUTO, GEMV_TOL)
+    check_layer("decode_batched", 32, qm.MOE_PATH_GEMV, GEMV_TOL)
     check_layer("decode_batched", 7, qm.MOE_PATH_GEMV, GEMV_TOL, stream=5)
+
+
+def test_auto_path_switch():
+    # the automatic rule: GEMV up to 14 rows, the grouped GEMM from 15 rows on
+    _, used = check_layer("decode_batched", 14, qm.MOE_PATH_AUTO, GEMV_TOL, stream=6)
+    assert used == qm.MOE_PATH_GEMV
+    _, used = check_layer("decode_batched", 15, qm.MOE_PATH_AUTO, MFMA_TOL, stream=6)
+    assert used == qm.MOE_PATH_MFMA
 
 
 def test_mfma_tiny_and_ragged():
@@ -289,7 +297,8 @@ def test_mfma_prefill_4096_sampled():
     ("tiny", 4, qm.MOE_PATH_GEMV, GEMV_TOL),
     ("tiny", 4, qm.MOE_PATH_MFMA, MFMA_TOL),
     ("decode_sharded", 1, qm.MOE_PATH_AUTO, GEMV_TOL),
-    ("decode_batched", 32, qm.MOE_PATH_AUTO, GEMV_TOL),
+    ("decode_batched", 32, qm.MOE_PATH_GEMV, GEMV_TOL),
+    ("decode_batched", 32, qm.MOE_PATH_AUTO, MFMA_TOL),
     ("prefill4096", 512, qm.MOE_PATH_MFMA, MFMA_TOL),
 ])
 def test_shard_partials_and_reduce(name, T, path, tol):
