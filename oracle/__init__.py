@@ -64,6 +64,9 @@ def lib():
         L.oracle_forward.argtypes = [ctypes.POINTER(_Layer), P, ctypes.c_int, P, P,
                                      ctypes.c_int, ctypes.c_int, P, P, ctypes.c_int]
         L.oracle_reduce.argtypes = [ctypes.POINTER(P), ctypes.c_int, ctypes.c_int64, P]
+        L.oracle_sumsq.argtypes = [P, ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_int, P]
+        L.oracle_rmsnorm.argtypes = [P, ctypes.c_int, ctypes.c_int, P, ctypes.c_float, P]
+        L.oracle_reduce_residual.argtypes = [ctypes.POINTER(P), ctypes.c_int, ctypes.c_int64, P, P]
         L.oracle_max_threads.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -168,4 +171,34 @@ def reduce_partials(partials: Sequence[np.ndarray]) -> np.ndarray:
     arr = (ctypes.c_void_p * len(ps))(*[p.ctypes.data for p in ps])
     out = np.empty_like(ps[0])
     _check(lib().oracle_reduce(arr, len(ps), n, _p(out)), "reduce")
+    return out
+
+
+def sumsq(x: np.ndarray, c0: int = 0, c1: Optional[int] = None) -> np.ndarray:
+    """Per-row sum of squares of columns [c0, c1) (double)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    T, H = x.shape
+    c1 = H if c1 is None else c1
+    out = np.empty(T, np.float64)
+    _check(lib().oracle_sumsq(_p(x), T, H, c0, c1, _p(out)), "sumsq")
+    return out
+
+
+def rmsnorm(x: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
+    """RMSNorm of each row: g * x / sqrt(mean(x^2) + eps), fp32 result."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    g = np.ascontiguousarray(g, dtype=np.float32)
+    T, H = x.shape
+    out = np.empty_like(x)
+    _check(lib().oracle_rmsnorm(_p(x), T, H, _p(g), ctypes.c_float(eps), _p(out)), "rmsnorm")
+    return out
+
+
+def reduce_residual(partials: Sequence[np.ndarray], residual: np.ndarray) -> np.ndarray:
+    """(p_0 + ... + p_{n-1}) + residual, in double, rounded once."""
+    ps = [np.ascontiguousarray(p, dtype=np.float32) for p in partials]
+    r = np.ascontiguousarray(residual, dtype=np.float32)
+    arr = (ctypes.c_void_p * len(ps))(*[p.ctypes.data for p in ps])
+    out = np.empty_like(ps[0])
+    _check(lib().oracle_reduce_residual(arr, len(ps), ps[0].size, _p(r), _p(out)), "reduce_residual")
     return out

@@ -45,6 +45,11 @@
  *     added after the routed slots.
  *   - Shards: shard s of n owns intermediate rows [s*I/n, (s+1)*I/n) of every
  *     routed expert and [s*Is/n, (s+1)*Is/n) of the shared one.
+ *   - RMSNorm (section 5): y = g * x / sqrt(mean(x^2) + eps) with eps and g
+ *     from the caller; in shard mode the row's sum of squares is the sum of
+ *     the shards' partial sums in ascending shard order.
+ *   - Residual (section 5): out = (sum of the partials in ascending order)
+ *     + residual.
  */
 #include <math.h>
 #include <stdint.h>
@@ -419,6 +424,69 @@ int oracle_reduce(const float *const *partials, int num_shards, int64_t n, float
         double acc = 0.0;
         for (int s = 0; s < num_shards; ++s) acc += (double)partials[s][i];
         out[i] = (float)acc;
+    }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* 5. The steps either side of the layer: RMSNorm before, residual after     */
+/* ------------------------------------------------------------------------ */
+
+/* Page "Distributed CPU: Zip Fusion Beyond Tensor Parallelism", section "What
+ * Must Cross the Fabric: The Reduction Algebra": RMSNorm needs the whole
+ * row, but only through one number, the row's sum of squares; split over
+ * column shards, each shard forms the sum over its own columns and only those
+ * scalars meet.  The pages print no formula; read as the usual RMSNorm,
+ *   y[c] = g[c] * x[c] / sqrt(S / H + eps),  S = sum over the H columns of x^2,
+ * with eps and the per-column weight g supplied by the caller. */
+
+/* Sum of squares of columns [c0, c1) of each of T rows (row stride ld),
+ * double, ascending column. */
+int oracle_sumsq(const float *x, int T, int64_t ld, int c0, int c1, double *ssq)
+{
+    if (!x || !ssq || T < 0 || c0 < 0 || c1 < c0) return ORC_EINVAL;
+    for (int t = 0; t < T; ++t) {
+        double s = 0.0;
+        for (int c = c0; c < c1; ++c) {
+            const double v = (double)x[(int64_t)t * ld + c];
+            s += v * v;
+        }
+        ssq[t] = s;
+    }
+    return ORC_OK;
+}
+
+/* RMSNorm of T rows of H columns (row stride H), rounded once to fp32. */
+int oracle_rmsnorm(const float *x, int T, int H, const float *g, float eps, float *y)
+{
+    if (!x || !g || !y || T < 0 || H < 1) return ORC_EINVAL;
+    double *ssq = (double *)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1));
+    if (!ssq) return ORC_ENOMEM;
+    oracle_sumsq(x, T, H, 0, H, ssq);
+    for (int t = 0; t < T; ++t) {
+        const double r = sqrt(ssq[t] / (double)H + (double)eps);
+        for (int c = 0; c < H; ++c) {
+            const int64_t i = (int64_t)t * H + c;
+            y[i] = (float)((double)g[c] * (double)x[i] / r);
+        }
+    }
+    free(ssq);
+    return ORC_OK;
+}
+
+/* The block's residual after the layer (page "CKE Zip: From Splitting Tokens
+ * To Splitting Qwen3.5 Weights", section "What PR #382 Now Splits": the MoE
+ * partials are reduced and the block completes its residual):
+ *   out = (p_0 + p_1 + ... + p_{n-1}) + residual,
+ * in double, rounded once. */
+int oracle_reduce_residual(const float *const *partials, int num_shards, int64_t n,
+                           const float *residual, float *out)
+{
+    if (num_shards < 1 || n < 0 || !partials || !residual || !out) return ORC_EINVAL;
+    for (int64_t i = 0; i < n; ++i) {
+        double acc = 0.0;
+        for (int s = 0; s < num_shards; ++s) acc += (double)partials[s][i];
+        out[i] = (float)(acc + (double)residual[i]);
     }
     return ORC_OK;
 }

@@ -367,3 +367,82 @@ def test_empty_batch():
     L = oracle.Layer.from_shape(layer, mi.TINY)
     out = oracle.forward(L, np.zeros((0, 256), np.float32))
     assert out.shape == (0, 256)
+
+
+# --------------------------------------------------------------------------
+# RMSNorm before the layer and the residual after it (page "Distributed CPU:
+# Zip Fusion Beyond Tensor Parallelism", "What Must Cross the Fabric: The
+# Reduction Algebra"; page "CKE Zip: From Splitting Tokens To Splitting
+# Qwen3.5 Weights", "What PR #382 Now Splits").  Pinned by closed forms.
+# --------------------------------------------------------------------------
+
+def test_rmsnorm_constant_row_is_sign_times_weight():
+    # every column equal to c, eps = 0: mean(x^2) = c^2, so y = g * c / |c|
+    # (a sum in place of the mean would give g / sqrt(H) instead)
+    H = 64
+    g = np.linspace(-2.0, 3.0, H).astype(np.float32)
+    x = np.stack([np.full(H, 3.0), np.full(H, -0.25)]).astype(np.float32)
+    y = oracle.rmsnorm(x, g, 0.0)
+    assert np.array_equal(y[0], g)
+    assert np.array_equal(y[1], -g)
+
+
+def test_rmsnorm_one_hot_row():
+    # x = a e_i, eps = 0: mean(x^2) = a^2 / H, so y_i = g_i sqrt(H) sign(a), all
+    # other columns 0
+    H = 256
+    g = np.full(H, 0.5, np.float32)
+    x = np.zeros((1, H), np.float32)
+    x[0, 37] = -7.0
+    y = oracle.rmsnorm(x, g, 0.0)
+    assert y[0, 37] == np.float32(-0.5 * 16.0)
+    assert np.count_nonzero(y) == 1
+
+
+def test_rmsnorm_three_four_five():
+    # H = 2, x = (3, 4): mean(x^2) = 25/2, y = x * sqrt(2) / 5 = (0.6, 0.8) * sqrt(2)
+    y = oracle.rmsnorm(np.array([[3.0, 4.0]], np.float32), np.ones(2, np.float32), 0.0)
+    assert np.array_equal(y[0], np.array([0.6 * math.sqrt(2.0), 0.8 * math.sqrt(2.0)], np.float32))
+
+
+def test_rmsnorm_eps_scale_and_sign():
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((4, 96)).astype(np.float32)
+    g = rng.standard_normal(96).astype(np.float32)
+    # eps = 0: invariant under positive scaling by a power of two, odd in x
+    y = oracle.rmsnorm(x, g, 0.0)
+    assert np.array_equal(oracle.rmsnorm(x * np.float32(8.0), g, 0.0), y)
+    assert np.array_equal(oracle.rmsnorm(-x, g, 0.0), -y)
+    # eps enters under the root: for a row scaled to mean(x^2) = 1, y = g x / sqrt(1 + eps)
+    z = x / np.sqrt(np.mean(x.astype(np.float64) ** 2, axis=1, keepdims=True))
+    z = z.astype(np.float32)
+    ms = np.mean(z.astype(np.float64) ** 2, axis=1, keepdims=True)
+    want = (g.astype(np.float64) * z / np.sqrt(ms + 0.25)).astype(np.float32)
+    assert np.abs(oracle.rmsnorm(z, g, 0.25) - want).max() <= 1e-6
+    assert np.abs(ms - 1.0).max() < 1e-6
+    # a zero row stays zero (no 0/0) once eps > 0
+    assert not np.any(oracle.rmsnorm(np.zeros((1, 96), np.float32), g, 1e-6))
+
+
+@pytest.mark.parametrize("cuts", [(0, 1024, 2048), (0, 512, 1024, 1536, 2048), (0, 640, 2048)])
+def test_rmsnorm_sum_of_squares_splits_into_shard_scalars(cuts):
+    # the reduction algebra: the row's sum of squares is the sum of the
+    # shards' partial sums (exactly up to double rounding)
+    rng = np.random.default_rng(len(cuts))
+    x = rng.standard_normal((9, 2048)).astype(np.float32) * 3.0
+    full = oracle.sumsq(x)
+    parts = [oracle.sumsq(x, a, b) for a, b in zip(cuts[:-1], cuts[1:])]
+    assert np.abs(sum(parts) - full).max() <= 1e-12 * full.max()
+    # and the per-column squares add up to the same (independent check)
+    assert np.abs((x.astype(np.float64) ** 2).sum(axis=1) - full).max() <= 1e-12 * full.max()
+
+
+def test_reduce_residual_order_and_cancellation():
+    p0 = np.array([1.0, 1e8, 3.0], np.float32)
+    p1 = np.array([2.0 ** -30, -1e8, -3.0], np.float32)
+    r = np.array([0.5, 2.0 ** -26, 7.0], np.float32)
+    out = oracle.reduce_residual([p0, p1], r)
+    # exact sums rounded once: 1.5 (+2^-30 lost), 2^-26, 7
+    assert np.array_equal(out, np.array([1.5, 2.0 ** -26, 7.0], np.float32))
+    # one partial: the layer output plus the residual
+    assert np.array_equal(oracle.reduce_residual([p0], -p0), np.zeros(3, np.float32))
