@@ -14,6 +14,10 @@ Secondary (``prefill``): T = 4096 token rows per step, same layer shape (seed
 4, uniform router), grouped-GEMM path, replayed from a HIP graph of two steps
 (one per weight copy); the eager rate is reported beside it.
 
+Beside the layer (``edges``): the steps either side of it at T = 4096, H =
+2048 -- RMSNorm of the input rows and the reduce of two shard partials plus
+the residual -- timed with stream events over 20 calls each.
+
 Per-kernel durations come from start/stop HIP events that the library attaches
 to each kernel launch (moe_opts.kernel_events, hipExtLaunchKernel) in an eager
 pass over the same workload.
@@ -46,12 +50,12 @@ FP16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak
 # --copy-probe).  Keyed by the SHA-256 of the kernel's sources: when they change,
 # the counters no longer describe the kernel and traffic is reported as null.
 TRAFFIC = {
-    # decode T=1, 180 dispatches: FETCH 4730.8 KiB x 1.99980, WRITE 16.1 KiB x 1.0
-    "gemv_gateup": {"sources_sha256": "81e2e507efe20c6a4fad911cf7895af1b7673eff93cfff77239774b60ca7533d",
-                    "fetch_bytes": 9687754, "write_bytes": 16448},
-    # prefill T=4096, 9 dispatches: FETCH 224456.6 KiB x 1.99980, WRITE 36864.0 KiB x 1.0
-    "gemm_gateup": {"sources_sha256": "bb5635a35c0e21515ee569554e35a3d5560ad54e034f51ae307501195e6b8758",
-                    "fetch_bytes": 459640338, "write_bytes": 37748736},
+    # decode T=1, 180 dispatches: FETCH 4730.7 KiB x 1.99980, WRITE 16.1 KiB x 1.0
+    "gemv_gateup": {"sources_sha256": "a915bf1ed8416af992e5a4f89a0f00f1ccc549dd348136e7ee46ac711bc4925f",
+                    "fetch_bytes": 9687539, "write_bytes": 16448},
+    # prefill T=4096, 9 dispatches: FETCH 224623.8 KiB x 1.99980, WRITE 36864.0 KiB x 1.0
+    "gemm_gateup": {"sources_sha256": "b159c0486656fd36787a88a17bf752d7dffc10d9daff4f148000dc67920b6203",
+                    "fetch_bytes": 459982778, "write_bytes": 37748736},
 }
 FETCH_SIZE_FACTOR = 1.99980   # plain 256 MiB copy: true bytes read / FETCH_SIZE bytes
 WRITE_SIZE_FACTOR = 1.0
@@ -391,6 +395,38 @@ def bench_continuum(args, torch, qm, mi, DeviceLayer):
     return rows
 
 
+def bench_edges(torch, qm, T=4096, H=2048, reps=20):
+    """The steps either side of the layer at the prefill size: RMSNorm of the
+    input rows, and the reduce of two shard partials plus the residual.  Both
+    are HBM-bound; algorithmic bytes are one read of every input and one write
+    of the output."""
+    g = torch.Generator(device="cuda").manual_seed(9)
+    x = torch.randn((T, H), device="cuda", generator=g)
+    w = torch.randn(H, device="cuda", generator=g)
+    y = torch.empty_like(x)
+    parts = [torch.randn((T, H), device="cuda", generator=g) for _ in range(2)]
+    r = torch.randn((T, H), device="cuda", generator=g)
+    out = torch.empty_like(r)
+    res = {}
+    for name, fn, nbytes in (
+            ("rmsnorm", lambda: qm.moe_rmsnorm(x, w, 1e-6, y), 2 * T * H * 4 + H * 4),
+            ("reduce_residual_2", lambda: qm.moe_reduce_residual(parts, T * H, r, out),
+             4 * T * H * 4)):
+        for _ in range(3):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) / reps * 1e3
+        res[name] = {"T": T, "H": H, "us": us, "algorithmic_bytes": nbytes,
+                     "gb_per_s": nbytes / (us * 1e-6) / 1e9,
+                     "hbm_frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
+    return res
+
+
 def cpu_baseline_decode(layer, pool, budget_s):
     import moe_inputs as mi
     import oracle
@@ -466,6 +502,10 @@ def main():
     if not args.no_prefill:
         print("[bench] prefill T=4096 ...", file=sys.stderr, flush=True)
         pre, pre_layer, x_pre = bench_prefill(args, torch, qm, mi, DeviceLayer)
+    edges = None
+    if not args.no_prefill:
+        print("[bench] RMSNorm / residual at T=4096 ...", file=sys.stderr, flush=True)
+        edges = bench_edges(torch, qm)
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] oracle on the host ...", file=sys.stderr, flush=True)
@@ -498,6 +538,7 @@ def main():
         "cpu_baseline": cpu,
         "decode": {k: v for k, v in dec.items() if k not in ("value", "ms_per_step", "roofline")},
         "prefill": pre,
+        "edges": edges,
     }
     print(json.dumps(line), flush=True)
 

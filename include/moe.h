@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 /* Status codes returned by every entry point. */
 #define MOE_OK 0
@@ -191,6 +191,56 @@ int moe_layer_forward_shard(const moe_layer_desc *desc, const float *x, int32_t 
  */
 int moe_reduce_partials(const float *const *partials, int32_t num_shards, int64_t n_elems,
                         float *out, void *stream);
+
+/*
+ * The block's residual after the layer: out[i] = (partials[0][i] + ... +
+ * partials[num_shards-1][i]) + residual[i], fp32, shards in ascending order,
+ * then the residual (page "CKE Zip: From Splitting Tokens To Splitting
+ * Qwen3.5 Weights", section "What PR #382 Now Splits": the MoE partials are
+ * reduced and the block completes its residual).  num_shards = 1 adds the
+ * residual to an unsplit layer output.  `partials` is a HOST array of
+ * num_shards (1..16) device pointers; residual and out are device fp32
+ * [n_elems].  out may alias residual or partials[0].  Errors: -1 for a null
+ * pointer or num_shards outside 1..16; n_elems = 0 enqueues nothing.
+ */
+int moe_reduce_residual(const float *const *partials, int32_t num_shards, int64_t n_elems,
+                        const float *residual, float *out, void *stream);
+
+/*
+ * RMSNorm of the layer's input rows (page "Distributed CPU: Zip Fusion Beyond
+ * Tensor Parallelism", section "What Must Cross the Fabric: The Reduction
+ * Algebra": the norm depends on the whole row only through its sum of
+ * squares):
+ *   y[t][c] = g[c] * x[t][c] / sqrt(S_t / H + eps),  S_t = sum_c x[t][c]^2.
+ * The pages print no formula; this is the usual RMSNorm, with eps (>= 0) and
+ * the per-column weight g [H] given by the caller.  x, y fp32 [T][H] (device,
+ * 16-byte aligned, H % 4 == 0); y may alias x.  S_t is summed in fp32 in a
+ * fixed order, so results are deterministic.  Errors: -1 for T < 0, a null
+ * pointer or eps < 0 / NaN; -2 for H % 4 != 0 or misaligned pointers.
+ */
+int moe_rmsnorm(const float *x, int32_t T, int32_t H, const float *g, float eps, float *y,
+                void *stream);
+
+/*
+ * RMSNorm over column shards (same section: each shard forms the sum of
+ * squares of its own columns, and only those scalars meet):
+ *   moe_rmsnorm_sumsq: ssq[t] = sum of x[t][c]^2 over the shard's `cols`
+ *     columns, x pointing at the shard's first column, rows ldx floats apart
+ *     (ldx = H for a view into the full rows, ldx = cols for a shard of its
+ *     own);
+ *   moe_rmsnorm_apply: S_t = ((ssq_parts[0][t] + ssq_parts[1][t]) + ...), the
+ *     shards in ascending order, then y[t][c] = g[c] * x[t][c] / sqrt(S_t / H
+ *     + eps) on the shard's columns, H being the full row width; g points at
+ *     the shard's part of the weight, y rows are ldy floats apart.
+ * `ssq_parts` is a HOST array of n_parts (1..16) device pointers to fp32 [T].
+ * cols, ldx, ldy must be multiples of 4 and x, y, g 16-byte aligned (else
+ * -2); y may alias x.
+ */
+int moe_rmsnorm_sumsq(const float *x, int32_t T, int32_t cols, int64_t ldx, float *ssq,
+                      void *stream);
+int moe_rmsnorm_apply(const float *x, int32_t T, int32_t cols, int64_t ldx,
+                      const float *const *ssq_parts, int32_t n_parts, int32_t H, const float *g,
+                      float eps, float *y, int64_t ldy, void *stream);
 
 /*
  * Test hook: decode n_sb superblocks (bits = 4: Q4_K, 5: Q5_K) into

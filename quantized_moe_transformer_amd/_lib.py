@@ -63,8 +63,14 @@ def _load():
     L.moe_reduce_partials.argtypes = [ctypes.POINTER(P), I32, I64, P, P]
     L.moe_dequant.argtypes = [P, I32, I64, I32, P, P]
     L.moe_route_bucket.argtypes = [D, P, I32, P, P, P, P, SZ, P]
+    L.moe_reduce_residual.argtypes = [ctypes.POINTER(P), I32, I64, P, P, P]
+    L.moe_rmsnorm.argtypes = [P, I32, I32, P, ctypes.c_float, P, P]
+    L.moe_rmsnorm_sumsq.argtypes = [P, I32, I32, I64, P, P]
+    L.moe_rmsnorm_apply.argtypes = [P, I32, I32, I64, ctypes.POINTER(P), I32, I32, P,
+                                    ctypes.c_float, P, I64, P]
     for f in ("router_topk", "moe_layer_forward", "moe_layer_forward_shard", "moe_reduce_partials",
-              "moe_dequant", "moe_route_bucket"):
+              "moe_dequant", "moe_route_bucket", "moe_reduce_residual", "moe_rmsnorm",
+              "moe_rmsnorm_sumsq", "moe_rmsnorm_apply"):
         getattr(L, f).restype = ctypes.c_int
     return L
 
@@ -151,6 +157,44 @@ def moe_reduce_partials(partials: Sequence, n_elems: int, out, stream=None):
     arr = (ctypes.c_void_p * len(partials))(*[_ptr(p) for p in partials])
     _check("moe_reduce_partials", lib.moe_reduce_partials(arr, len(partials), n_elems, _ptr(out),
                                                           _stream(stream)))
+
+
+def moe_reduce_residual(partials: Sequence, n_elems: int, residual, out, stream=None):
+    arr = (ctypes.c_void_p * len(partials))(*[_ptr(p) for p in partials])
+    _check("moe_reduce_residual", lib.moe_reduce_residual(arr, len(partials), n_elems,
+                                                          _ptr(residual), _ptr(out),
+                                                          _stream(stream)))
+
+
+def _rows(t):
+    """(rows, columns, row stride in elements) of a 2-D fp32 view with unit
+    column stride (a whole tensor, or a column slice of one)."""
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError("expected a 2-D view with contiguous columns")
+    return t.shape[0], t.shape[1], t.stride(0)
+
+
+def moe_rmsnorm(x, g, eps: float, y, stream=None):
+    T, H, ld = _rows(x)
+    if ld != H or y.shape != x.shape:
+        raise ValueError("moe_rmsnorm takes whole contiguous rows")
+    _check("moe_rmsnorm", lib.moe_rmsnorm(_ptr(x), T, H, _ptr(g), ctypes.c_float(eps), _ptr(y),
+                                          _stream(stream)))
+
+
+def moe_rmsnorm_sumsq(x, ssq, stream=None):
+    T, cols, ld = _rows(x)
+    _check("moe_rmsnorm_sumsq", lib.moe_rmsnorm_sumsq(_ptr(x), T, cols, ld, _ptr(ssq),
+                                                      _stream(stream)))
+
+
+def moe_rmsnorm_apply(x, ssq_parts: Sequence, H: int, g, eps: float, y, stream=None):
+    T, cols, ldx = _rows(x)
+    _, _, ldy = _rows(y)
+    arr = (ctypes.c_void_p * len(ssq_parts))(*[_ptr(p) for p in ssq_parts])
+    _check("moe_rmsnorm_apply", lib.moe_rmsnorm_apply(_ptr(x), T, cols, ldx, arr, len(ssq_parts),
+                                                      H, _ptr(g), ctypes.c_float(eps), _ptr(y),
+                                                      ldy, _stream(stream)))
 
 
 def moe_dequant(sbs, bits: int, n_sb: int, out_dtype: int, out, stream=None):

@@ -3,7 +3,7 @@
 // contracts) in include/moe.h.
 #include <string.h>
 
-#include "moe_internal.h"
+#include "launch.h"
 
 namespace moe {
 
@@ -44,9 +44,13 @@ struct PartialPtrs {
     const float* p[16];
 };
 
-// out = ((p0 + p1) + p2) + ...: ascending shard order, fp32.
+// out = ((p0 + p1) + p2) + ... [+ residual]: ascending shard order, then the
+// residual (page "CKE Zip: From Splitting Tokens To Splitting Qwen3.5
+// Weights", section "What PR #382 Now Splits": the partials are reduced and
+// the block completes its residual), fp32.
 __global__ void __launch_bounds__(256)
-reduce4_kernel(PartialPtrs ps, int n, size_t n4, float* __restrict__ out) {
+reduce4_kernel(PartialPtrs ps, int n, size_t n4, const float* __restrict__ res,
+               float* __restrict__ out) {
     const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n4) return;
     float4 acc = reinterpret_cast<const float4*>(ps.p[0])[i];
@@ -57,31 +61,41 @@ reduce4_kernel(PartialPtrs ps, int n, size_t n4, float* __restrict__ out) {
         acc.z += v.z;
         acc.w += v.w;
     }
+    if (res) {
+        const float4 v = reinterpret_cast<const float4*>(res)[i];
+        acc.x += v.x;
+        acc.y += v.y;
+        acc.z += v.z;
+        acc.w += v.w;
+    }
     reinterpret_cast<float4*>(out)[i] = acc;
 }
 
 __global__ void __launch_bounds__(256)
-reduce1_kernel(PartialPtrs ps, int n, size_t count, float* __restrict__ out) {
+reduce1_kernel(PartialPtrs ps, int n, size_t count, const float* __restrict__ res,
+               float* __restrict__ out) {
     const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= count) return;
     float acc = ps.p[0][i];
     for (int s = 1; s < n; ++s) acc += ps.p[s][i];
+    if (res) acc += res[i];
     out[i] = acc;
 }
 
-hipError_t launch_reduce(const float* const* partials, int n, int64_t count, float* out,
-                         hipStream_t s) {
+hipError_t launch_reduce(const float* const* partials, int n, int64_t count, const float* res,
+                         float* out, hipStream_t s) {
     PartialPtrs ps = {};
-    bool vec = (count % 4) == 0 && ((uintptr_t)out & 15) == 0;
+    bool vec = (count % 4) == 0 && ((uintptr_t)out & 15) == 0 && ((uintptr_t)res & 15) == 0;
     for (int i = 0; i < n; ++i) {
         ps.p[i] = partials[i];
         vec = vec && (((uintptr_t)partials[i] & 15) == 0);
     }
     if (vec) {
         const size_t n4 = (size_t)count / 4;
-        reduce4_kernel<<<(unsigned)((n4 + 255) / 256), 256, 0, s>>>(ps, n, n4, out);
+        reduce4_kernel<<<(unsigned)((n4 + 255) / 256), 256, 0, s>>>(ps, n, n4, res, out);
     } else {
-        reduce1_kernel<<<(unsigned)((count + 255) / 256), 256, 0, s>>>(ps, n, (size_t)count, out);
+        reduce1_kernel<<<(unsigned)((count + 255) / 256), 256, 0, s>>>(ps, n, (size_t)count, res,
+                                                                      out);
     }
     return hipGetLastError();
 }
@@ -302,7 +316,63 @@ int moe_reduce_partials(const float* const* partials, int32_t num_shards, int64_
         if (!partials[i]) return MOE_EINVAL;
     int rc = check_device();
     if (rc) return rc;
-    return launched(launch_reduce(partials, num_shards, n_elems, out, (hipStream_t)stream));
+    return launched(launch_reduce(partials, num_shards, n_elems, nullptr, out, (hipStream_t)stream));
+}
+
+int moe_reduce_residual(const float* const* partials, int32_t num_shards, int64_t n_elems,
+                        const float* residual, float* out, void* stream) {
+    if (!partials || num_shards < 1 || num_shards > 16 || n_elems < 0) return MOE_EINVAL;
+    if (n_elems == 0) return MOE_OK;
+    if (!out || !residual) return MOE_EINVAL;
+    for (int i = 0; i < num_shards; ++i)
+        if (!partials[i]) return MOE_EINVAL;
+    int rc = check_device();
+    if (rc) return rc;
+    return launched(launch_reduce(partials, num_shards, n_elems, residual, out, (hipStream_t)stream));
+}
+
+static bool norm_shape_ok(int cols, int64_t ld, const void* p) {
+    return cols % 4 == 0 && ld % 4 == 0 && ld >= cols && al16(p);
+}
+
+int moe_rmsnorm(const float* x, int32_t T, int32_t H, const float* g, float eps, float* y,
+                void* stream) {
+    if (T < 0 || H < 1 || !(eps >= 0.f) || eps > 3.0e38f) return MOE_EINVAL;
+    if (T == 0) return MOE_OK;
+    if (!x || !g || !y) return MOE_EINVAL;
+    if (!norm_shape_ok(H, H, x) || !al16(g) || !al16(y)) return MOE_EUNSUPPORTED;
+    int rc = check_device();
+    if (rc) return rc;
+    return launched(launch_rmsnorm(x, T, H, H, nullptr, 0, H, g, eps, y, H, (hipStream_t)stream));
+}
+
+int moe_rmsnorm_sumsq(const float* x, int32_t T, int32_t cols, int64_t ldx, float* ssq,
+                      void* stream) {
+    if (T < 0 || cols < 1) return MOE_EINVAL;
+    if (T == 0) return MOE_OK;
+    if (!x || !ssq) return MOE_EINVAL;
+    if (!norm_shape_ok(cols, ldx, x)) return MOE_EUNSUPPORTED;
+    int rc = check_device();
+    if (rc) return rc;
+    return launched(launch_rmsnorm_sumsq(x, T, cols, ldx, ssq, (hipStream_t)stream));
+}
+
+int moe_rmsnorm_apply(const float* x, int32_t T, int32_t cols, int64_t ldx,
+                      const float* const* ssq_parts, int32_t n_parts, int32_t H, const float* g,
+                      float eps, float* y, int64_t ldy, void* stream) {
+    if (T < 0 || cols < 1 || H < cols || n_parts < 1 || n_parts > 16 || !(eps >= 0.f) ||
+        eps > 3.0e38f)
+        return MOE_EINVAL;
+    if (T == 0) return MOE_OK;
+    if (!x || !g || !y || !ssq_parts) return MOE_EINVAL;
+    for (int i = 0; i < n_parts; ++i)
+        if (!ssq_parts[i]) return MOE_EINVAL;
+    if (!norm_shape_ok(cols, ldx, x) || !norm_shape_ok(cols, ldy, y) || !al16(g))
+        return MOE_EUNSUPPORTED;
+    int rc = check_device();
+    if (rc) return rc;
+    return launched(launch_rmsnorm(x, T, cols, ldx, ssq_parts, n_parts, H, g, eps, y, ldy,
+                                   (hipStream_t)stream));
 }
 
 int moe_dequant(const uint8_t* sbs, int32_t bits, int64_t n_sb, int32_t out_dtype, void* out,

@@ -15,7 +15,7 @@
 //                   64-step lane scan, perm[base + rank] = s.
 // Integer counts are order-independent and the ranks are positional, so the
 // result is deterministic.
-#include "moe_internal.h"
+#include "launch.h"
 
 namespace moe {
 

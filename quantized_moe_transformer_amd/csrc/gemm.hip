@@ -46,7 +46,7 @@
 //     expert (page "CKE Zip: From Splitting Tokens To Splitting Qwen3.5
 //     Weights", section "A Separate Decode Result Shows Why Axis Choice
 //     Matters").
-#include "moe_internal.h"
+#include "launch.h"
 
 namespace moe {
 

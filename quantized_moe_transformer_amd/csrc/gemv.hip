@@ -24,7 +24,7 @@
 // of a row.  The per-sub-block scale factors out of the dot product:
 //   sum_i w_i x_i = d*sc_a*sum(q x)_a + d*sc_b*sum(q x)_b - dmin*(m_a sum x_a + m_b sum x_b)
 // Every weight load of a wave is issued before the first one is consumed.
-#include "moe_internal.h"
+#include "launch.h"
 #include "topk.h"
 
 namespace moe {

@@ -1,0 +1,55 @@
+// launch.h -- host side of libmoe_hip.so: the launch context and the kernel
+// launchers (enqueue only; arguments already validated by api.hip).
+#pragma once
+
+#include "moe_internal.h"
+
+namespace moe {
+
+// Launch context: the stream, and (optionally) caller-owned start/stop events
+// per kernel id (moe_opts.kernel_events).  A timed kernel is launched with
+// hipExtLaunchKernel, whose events carry the dispatch's own timestamps.
+struct Ctx {
+    hipStream_t s = nullptr;
+    void** ev = nullptr;
+    int n_ev = 0;
+    hipEvent_t start(int id) const { return (ev && 2 * id + 1 < n_ev) ? (hipEvent_t)ev[2 * id] : nullptr; }
+    hipEvent_t stop(int id) const { return (ev && 2 * id + 1 < n_ev) ? (hipEvent_t)ev[2 * id + 1] : nullptr; }
+};
+
+template <typename... KArgs, typename... Args>
+inline void launch_k(const Ctx& c, int id, void (*kern)(KArgs...), dim3 grid, dim3 block,
+                     uint32_t shm, Args... args) {
+    const hipEvent_t a = c.start(id), z = c.stop(id);
+    if (a || z)
+        hipExtLaunchKernelGGL(kern, grid, block, shm, c.s, a, z, 0, static_cast<KArgs>(args)...);
+    else
+        kern<<<grid, block, shm, c.s>>>(static_cast<KArgs>(args)...);
+}
+
+hipError_t launch_router(const moe_layer_desc& d, const float* x, int T, int32_t* idx, float* w,
+                         char* ws, const WsLayout& L, const Ctx& c);
+// route: run the router (and top-k) in the front kernel, writing L.idx / L.w
+hipError_t launch_gemv(const moe_layer_desc& d, const float* x, int T, const int32_t* idx,
+                       const float* w, int shard, int nshards, float* out, char* ws,
+                       const WsLayout& L, const Ctx& c, bool route);
+hipError_t launch_bucket(const int32_t* idx, int T, int k, int E, bool shared, int32_t* counts,
+                         int32_t* offsets, int32_t* tile_off, int4* tile_rec, int32_t* perm,
+                         int32_t* bhist,
+                         const Ctx& c);
+// x16_ready: the router already wrote the fp16 tokens (L.x16)
+hipError_t launch_mfma(const moe_layer_desc& d, const float* x, int T, const int32_t* idx,
+                       const float* w, int shard, int nshards, float* out, char* ws,
+                       const WsLayout& L, const Ctx& c, bool x16_ready);
+hipError_t launch_x16(const float* x, int T, int H, char* ws, const WsLayout& L, const Ctx& c);
+hipError_t launch_reduce(const float* const* partials, int n, int64_t count, const float* res,
+                         float* out, hipStream_t s);
+hipError_t launch_rmsnorm_sumsq(const float* x, int T, int cols, int64_t ldx, float* ssq,
+                                hipStream_t s);
+hipError_t launch_rmsnorm(const float* x, int T, int cols, int64_t ldx,
+                          const float* const* parts, int n_parts, int H, const float* g,
+                          float eps, float* y, int64_t ldy, hipStream_t s);
+hipError_t launch_dequant(const uint8_t* sbs, int bits, int64_t n_sb, int out_dtype, void* out,
+                          hipStream_t s);
+
+}  // namespace moe

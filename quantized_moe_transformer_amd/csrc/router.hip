@@ -12,7 +12,7 @@
 //   split, router_gemm  a dense [T x H] x [H x E] product on the fp16 matrix
 //                   cores with split operands (fp32 accuracy);
 //   router_topk     one wave per token (topk.h).
-#include "moe_internal.h"
+#include "launch.h"
 #include "topk.h"
 
 namespace moe {

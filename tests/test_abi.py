@@ -27,14 +27,15 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for fn in ("router_topk", "moe_layer_forward", "moe_layer_forward_shard",
                "moe_reduce_partials", "moe_dequant", "moe_workspace_bytes", "moe_route_bucket",
-               "moe_status_str", "moe_abi_version"):
+               "moe_status_str", "moe_abi_version", "moe_reduce_residual", "moe_rmsnorm",
+               "moe_rmsnorm_sumsq", "moe_rmsnorm_apply"):
         assert fn in names
 
 
 def test_library_exports_every_declared_symbol(L):
     for fn in declared_functions():
         assert hasattr(L.lib, fn), fn
-    assert L.moe_abi_version() == 1
+    assert L.moe_abi_version() == 2
     assert L.moe_status_str(-3) == "workspace too small"
 
 
@@ -98,6 +99,34 @@ def test_argument_errors_before_any_launch(L):
     assert L.lib.moe_reduce_partials(arr, 17, 16, FAKE, None) == L.MOE_EINVAL
     assert L.lib.moe_dequant(FAKE, 6, 1, 0, FAKE, None) == L.MOE_EINVAL
     assert L.lib.moe_dequant(FAKE, 4, 1, 3, FAKE, None) == L.MOE_EINVAL
+
+
+def test_norm_and_residual_argument_errors(L):
+    f = ctypes.c_float
+    # moe_rmsnorm: bad T, null pointers, negative or NaN eps, width or alignment
+    assert L.lib.moe_rmsnorm(FAKE, -1, 2048, FAKE, f(1e-6), FAKE, None) == L.MOE_EINVAL
+    assert L.lib.moe_rmsnorm(None, 4, 2048, FAKE, f(1e-6), FAKE, None) == L.MOE_EINVAL
+    assert L.lib.moe_rmsnorm(FAKE, 4, 2048, FAKE, f(-1.0), FAKE, None) == L.MOE_EINVAL
+    assert L.lib.moe_rmsnorm(FAKE, 4, 2048, FAKE, f(float("nan")), FAKE, None) == L.MOE_EINVAL
+    assert L.lib.moe_rmsnorm(FAKE, 4, 2046, FAKE, f(1e-6), FAKE, None) == L.MOE_EUNSUPPORTED
+    assert L.lib.moe_rmsnorm(FAKE + 4, 4, 2048, FAKE, f(1e-6), FAKE, None) == L.MOE_EUNSUPPORTED
+    assert L.lib.moe_rmsnorm(None, 0, 2048, None, f(1e-6), None, None) == L.MOE_OK   # T = 0
+    # shard form: row stride below the width, too many or no partial sums, H < cols
+    assert L.lib.moe_rmsnorm_sumsq(FAKE, 4, 1024, 512, FAKE, None) == L.MOE_EUNSUPPORTED
+    arr = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    assert L.lib.moe_rmsnorm_apply(FAKE, 4, 1024, 2048, arr, 0, 2048, FAKE, f(1e-6), FAKE,
+                                   2048, None) == L.MOE_EINVAL
+    assert L.lib.moe_rmsnorm_apply(FAKE, 4, 1024, 2048, arr, 17, 2048, FAKE, f(1e-6), FAKE,
+                                   2048, None) == L.MOE_EINVAL
+    assert L.lib.moe_rmsnorm_apply(FAKE, 4, 1024, 2048, arr, 2, 512, FAKE, f(1e-6), FAKE,
+                                   2048, None) == L.MOE_EINVAL
+    lost = (ctypes.c_void_p * 2)(FAKE, None)
+    assert L.lib.moe_rmsnorm_apply(FAKE, 4, 1024, 2048, lost, 2, 2048, FAKE, f(1e-6), FAKE,
+                                   2048, None) == L.MOE_EINVAL
+    # moe_reduce_residual: the residual is required
+    assert L.lib.moe_reduce_residual(arr, 2, 16, None, FAKE, None) == L.MOE_EINVAL
+    assert L.lib.moe_reduce_residual(lost, 2, 16, FAKE, FAKE, None) == L.MOE_EINVAL
+    assert L.lib.moe_reduce_residual(arr, 2, 0, None, None, None) == L.MOE_OK
 
 
 def test_empty_batch_is_a_no_op(L):
