@@ -64,6 +64,8 @@ def lib():
         L.oracle_forward.argtypes = [ctypes.POINTER(_Layer), P, ctypes.c_int, P, P,
                                      ctypes.c_int, ctypes.c_int, P, P, ctypes.c_int]
         L.oracle_reduce.argtypes = [ctypes.POINTER(P), ctypes.c_int, ctypes.c_int64, P]
+        L.oracle_forward_range.argtypes = [ctypes.POINTER(_Layer), P, ctypes.c_int, P, P,
+                                           ctypes.c_int, ctypes.c_int, P, P, ctypes.c_int]
         L.oracle_sumsq.argtypes = [P, ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_int, P]
         L.oracle_rmsnorm.argtypes = [P, ctypes.c_int, ctypes.c_int, P, ctypes.c_float, P]
         L.oracle_reduce_residual.argtypes = [ctypes.POINTER(P), ctypes.c_int, ctypes.c_int64, P, P]
@@ -202,3 +204,18 @@ def reduce_residual(partials: Sequence[np.ndarray], residual: np.ndarray) -> np.
     out = np.empty_like(ps[0])
     _check(lib().oracle_reduce_residual(arr, len(ps), ps[0].size, _p(r), _p(out)), "reduce_residual")
     return out
+
+
+def forward_range(layer: Layer, x: np.ndarray, idx: np.ndarray, w: np.ndarray, i_begin: int,
+                  i_end: int, nthreads: int = 0, want_double: bool = False):
+    """A shard of any width: intermediate rows [i_begin, i_end) of every routed
+    expert and of the shared one, under the given routing."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    T = x.shape[0]
+    out = np.empty((T, layer.H), np.float32)
+    out_d = np.empty((T, layer.H), np.float64) if want_double else None
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    _check(lib().oracle_forward_range(ctypes.byref(layer.c), _p(x), T, _p(idx), _p(w), i_begin,
+                                      i_end, _p(out), _p(out_d), nthreads), "forward_range")
+    return (out, out_d) if want_double else out

@@ -326,13 +326,49 @@ static void free_expert(decoded_expert *e)
  * Decoded weights of the experts that are touched are held for the call; the
  * decode is exact, so holding it changes no arithmetic.
  */
+static int forward_rows(const oracle_layer *L, const float *x, int T,
+                        const int32_t *idx_in, const float *w_in, int i0, int i1, int s0,
+                        int s1, float *out, double *out_d, int nthreads);
+
 int oracle_forward(const oracle_layer *L, const float *x, int T,
                    const int32_t *idx_in, const float *w_in,
                    int shard, int num_shards, float *out, double *out_d, int nthreads)
 {
     if (!L || T < 0 || num_shards < 1 || shard < 0 || shard >= num_shards)
         return ORC_EINVAL;
-    if (L->I % num_shards || L->Is % num_shards || L->k < 1 || L->k > L->E)
+    if (L->I % num_shards || L->Is % num_shards)
+        return ORC_EINVAL;
+    const int I = L->I, Is = L->Is;
+    return forward_rows(L, x, T, idx_in, w_in, shard * (I / num_shards),
+                        (shard + 1) * (I / num_shards), shard * (Is / num_shards),
+                        (shard + 1) * (Is / num_shards), out, out_d, nthreads);
+}
+
+/*
+ * A shard of any size (page "Distributed CPU: Zip Fusion Beyond Tensor
+ * Parallelism", section "Heterogeneous Topology": shards proportional to each
+ * lane's measured throughput, e.g. 30 % and 70 %): intermediate rows
+ * [i_begin, i_end) of every routed expert and of the shared expert (which then
+ * has the routed width, or none).  Partials over any partition of [0, I) add
+ * up to the layer.
+ */
+int oracle_forward_range(const oracle_layer *L, const float *x, int T,
+                         const int32_t *idx_in, const float *w_in, int i_begin, int i_end,
+                         float *out, double *out_d, int nthreads)
+{
+    if (!L || i_begin < 0 || i_end < i_begin || i_end > L->I) return ORC_EINVAL;
+    if (L->Is != 0 && L->Is != L->I) return ORC_EINVAL;
+    return forward_rows(L, x, T, idx_in, w_in, i_begin, i_end, i_begin, i_end, out, out_d,
+                        nthreads);
+}
+
+/* The layer restricted to routed intermediate rows [i0, i1) and shared rows
+ * [s0, s1). */
+static int forward_rows(const oracle_layer *L, const float *x, int T,
+                        const int32_t *idx_in, const float *w_in, int i0, int i1, int s0,
+                        int s1, float *out, double *out_d, int nthreads)
+{
+    if (!L || T < 0 || L->k < 1 || L->k > L->E)
         return ORC_EINVAL;
     if ((L->H * L->I) % 256 || (L->H * L->Is) % 256)
         return ORC_EINVAL;
@@ -375,8 +411,6 @@ int oracle_forward(const oracle_layer *L, const float *x, int T,
         fail |= decode_expert(L->sh_gate, L->sh_up, L->sh_down, H, Is, &sh) != ORC_OK;
     if (fail) { rc = ORC_ENOMEM; goto done; }
 
-    int i0 = shard * (I / num_shards), i1 = (shard + 1) * (I / num_shards);
-    int s0 = shard * (Is / num_shards), s1 = (shard + 1) * (Is / num_shards);
     int amax = I > Is ? I : Is;
 #pragma omp parallel num_threads(nthr)
     {

@@ -446,3 +446,24 @@ def test_reduce_residual_order_and_cancellation():
     assert np.array_equal(out, np.array([1.5, 2.0 ** -26, 7.0], np.float32))
     # one partial: the layer output plus the residual
     assert np.array_equal(oracle.reduce_residual([p0], -p0), np.zeros(3, np.float32))
+
+
+@pytest.mark.parametrize("cuts", [(0, 48, 128), (0, 32, 64, 96, 128), (0, 96, 128), (0, 64, 128), (0, 128)])
+def test_uneven_shard_ranges_sum_to_whole(cuts):
+    # page "Distributed CPU: Zip Fusion Beyond Tensor Parallelism", "Heterogeneous
+    # Topology": shards sized to each lane's throughput, not equal; any
+    # partition of the intermediate rows adds up to the layer
+    import moe_inputs as mi
+    layer, x = mi.workload_inputs("tiny")
+    L = oracle.Layer.from_shape(layer, mi.TINY)
+    idx, w, _, _ = oracle.router(x, layer["router_w"], mi.TINY.k)
+    _, full = oracle.forward(L, x, idx, w, want_double=True)
+    parts = [oracle.forward_range(L, x, idx, w, a, b, want_double=True)[1]
+             for a, b in zip(cuts[:-1], cuts[1:])]
+    rms = np.sqrt(np.mean(full ** 2))
+    assert np.abs(sum(parts) - full).max() <= 1e-12 * rms
+    # an equal split through the range form is the equal-shard form, bit for bit
+    if len(cuts) == 3 and cuts[1] == 64:
+        assert np.array_equal(parts[0], oracle.forward(L, x, idx, w, 0, 2, want_double=True)[1])
+    # an empty range contributes nothing
+    assert not np.any(oracle.forward_range(L, x, idx, w, 64, 64))
