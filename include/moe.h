@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 /* Status codes returned by every entry point. */
 #define MOE_OK 0
@@ -180,6 +180,22 @@ int moe_layer_forward(const moe_layer_desc *desc, const float *x, int32_t T, flo
 int moe_layer_forward_shard(const moe_layer_desc *desc, const float *x, int32_t T,
                             const int32_t *topk_idx, const float *topk_w,
                             int32_t shard, int32_t num_shards, float *partial,
+                            const moe_opts *opts, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * A shard of any width (page "Distributed CPU: Zip Fusion Beyond Tensor
+ * Parallelism", section "Heterogeneous Topology": shards sized in proportion
+ * to each lane's measured throughput, e.g. 30 % and 70 %, rather than equal):
+ * the same sum as moe_layer_forward_shard restricted to intermediate rows
+ * [i_begin, i_end) of every routed expert and of the shared expert (whose
+ * width equals I).  Partials over any partition of [0, I) add up to the
+ * unsplit output.  Requires i_begin and i_end to be multiples of 64 with
+ * 0 <= i_begin < i_end <= I (else -1, or -2 for misaligned bounds).  The
+ * workspace of moe_workspace_bytes(desc, T, 1) is enough for any range.
+ */
+int moe_layer_forward_range(const moe_layer_desc *desc, const float *x, int32_t T,
+                            const int32_t *topk_idx, const float *topk_w,
+                            int32_t i_begin, int32_t i_end, float *partial,
                             const moe_opts *opts, void *ws, size_t ws_bytes, void *stream);
 
 /*

@@ -60,6 +60,7 @@ def _load():
     L.router_topk.argtypes = [D, P, I32, P, P, P, SZ, P]
     L.moe_layer_forward.argtypes = [D, P, I32, P, O, P, SZ, P]
     L.moe_layer_forward_shard.argtypes = [D, P, I32, P, P, I32, I32, P, O, P, SZ, P]
+    L.moe_layer_forward_range.argtypes = [D, P, I32, P, P, I32, I32, P, O, P, SZ, P]
     L.moe_reduce_partials.argtypes = [ctypes.POINTER(P), I32, I64, P, P]
     L.moe_dequant.argtypes = [P, I32, I64, I32, P, P]
     L.moe_route_bucket.argtypes = [D, P, I32, P, P, P, P, SZ, P]
@@ -70,6 +71,7 @@ def _load():
                                     ctypes.c_float, P, I64, P]
     for f in ("router_topk", "moe_layer_forward", "moe_layer_forward_shard", "moe_reduce_partials",
               "moe_dequant", "moe_route_bucket", "moe_reduce_residual", "moe_rmsnorm",
+              "moe_layer_forward_range",
               "moe_rmsnorm_sumsq", "moe_rmsnorm_apply"):
         getattr(L, f).restype = ctypes.c_int
     return L
@@ -149,6 +151,16 @@ def moe_layer_forward_shard(desc, x, T, topk_idx, topk_w, shard, num_shards, par
     _check("moe_layer_forward_shard",
            lib.moe_layer_forward_shard(ctypes.byref(desc), _ptr(x), T, _ptr(topk_idx),
                                        _ptr(topk_w), shard, num_shards, _ptr(partial),
+                                       ctypes.byref(o), _ptr(ws), _nbytes(ws), _stream(stream)))
+    return used.value
+
+
+def moe_layer_forward_range(desc, x, T, topk_idx, topk_w, i_begin, i_end, partial, ws,
+                            path: int = MOE_PATH_AUTO, stream=None, events=None) -> int:
+    o, used = _opts(path, events)
+    _check("moe_layer_forward_range",
+           lib.moe_layer_forward_range(ctypes.byref(desc), _ptr(x), T, _ptr(topk_idx),
+                                       _ptr(topk_w), i_begin, i_end, _ptr(partial),
                                        ctypes.byref(o), _ptr(ws), _nbytes(ws), _stream(stream)))
     return used.value
 

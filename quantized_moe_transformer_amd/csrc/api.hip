@@ -113,11 +113,11 @@ hipError_t launch_dequant(const uint8_t* sbs, int bits, int64_t n_sb, int out_dt
 
 static inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-WsLayout ws_layout(const moe_layer_desc& d, int T, int num_shards) {
+WsLayout ws_layout(const moe_layer_desc& d, int T, int iloc) {
     WsLayout L = {};
     const size_t H = d.hidden, E = d.n_experts, k = d.top_k;
     const size_t Tz = T;
-    const size_t Iloc = (size_t)(d.inter / num_shards);
+    const size_t Iloc = (size_t)iloc;
     const size_t nslot = k + (d.shared_inter > 0 ? 1 : 0);
     size_t off = 0;
     L.router_ks = router_splits(T, d.hidden);
@@ -179,20 +179,17 @@ static int check_desc(const moe_layer_desc* d) {
 // streams its own experts) while the GEMM reads each touched expert once.
 constexpr int kGemvMaxT = 14;
 
-static bool gemv_supports(const moe_layer_desc* d, int nshards) {
-    const int iloc = d->inter / nshards;
-    return iloc >= 64 && iloc <= 2048 && (iloc & (iloc - 1)) == 0;
-}
+static bool gemv_supports(int iloc) { return iloc >= 64 && iloc <= 2048 && iloc % 64 == 0; }
 
-static int choose_path(const moe_layer_desc* d, int T, int nshards, const moe_opts* o, int* path) {
+static int choose_path(int T, int iloc, const moe_opts* o, int* path) {
     const int req = o ? o->path : MOE_PATH_AUTO;
     if (req == MOE_PATH_GEMV) {
-        if (!gemv_supports(d, nshards)) return MOE_EUNSUPPORTED;
+        if (!gemv_supports(iloc)) return MOE_EUNSUPPORTED;
         *path = MOE_PATH_GEMV;
     } else if (req == MOE_PATH_MFMA) {
         *path = MOE_PATH_MFMA;
     } else if (req == MOE_PATH_AUTO) {
-        *path = (T <= kGemvMaxT && gemv_supports(d, nshards)) ? MOE_PATH_GEMV : MOE_PATH_MFMA;
+        *path = (T <= kGemvMaxT && gemv_supports(iloc)) ? MOE_PATH_GEMV : MOE_PATH_MFMA;
     } else {
         return MOE_EINVAL;
     }
@@ -237,7 +234,7 @@ const char* moe_status_str(int status) {
 size_t moe_workspace_bytes(const moe_layer_desc* desc, int32_t T, int32_t num_shards) {
     if (check_desc(desc) != MOE_OK || T < 0 || num_shards < 1 || num_shards > 16) return 0;
     if (desc->inter % num_shards) return 0;
-    return ws_layout(*desc, T, num_shards).total;
+    return ws_layout(*desc, T, desc->inter / num_shards).total;
 }
 
 int router_topk(const moe_layer_desc* desc, const float* x, int32_t T, int32_t* topk_idx,
@@ -247,7 +244,7 @@ int router_topk(const moe_layer_desc* desc, const float* x, int32_t T, int32_t* 
     if (T < 0) return MOE_EINVAL;
     if (T == 0) return MOE_OK;
     if (!x || !topk_idx || !topk_w || !ws) return MOE_EINVAL;
-    const WsLayout L = ws_layout(*desc, T, 1);
+    const WsLayout L = ws_layout(*desc, T, desc->inter);
     if (ws_bytes < L.total) return MOE_EWORKSPACE;
     if ((uintptr_t)ws & 255) return MOE_EUNSUPPORTED;
     if ((rc = check_device())) return rc;
@@ -256,21 +253,21 @@ int router_topk(const moe_layer_desc* desc, const float* x, int32_t T, int32_t* 
     return launched(launch_router(*desc, x, T, topk_idx, topk_w, (char*)ws, L, c));
 }
 
+// i0, iloc: intermediate rows [i0, i0 + iloc) of every expert, already
+// checked against the descriptor (multiples of 64 inside [0, I))
 static int forward_common(const moe_layer_desc* desc, const float* x, int32_t T,
-                          const int32_t* idx, const float* w, int32_t shard, int32_t nshards,
-                          float* out, const moe_opts* opts, void* ws, size_t ws_bytes,
-                          void* stream, bool route) {
-    int rc = check_desc(desc);
-    if (rc) return rc;
-    if (T < 0 || nshards < 1 || nshards > 16 || shard < 0 || shard >= nshards) return MOE_EINVAL;
-    if (desc->inter % nshards || (desc->inter / nshards) % 64) return MOE_EUNSUPPORTED;
+                          const int32_t* idx, const float* w, int i0, int iloc, float* out,
+                          const moe_opts* opts, void* ws, size_t ws_bytes, void* stream,
+                          bool route) {
+    int rc;
+    if (T < 0) return MOE_EINVAL;
     int path = 0;
-    if ((rc = choose_path(desc, T, nshards, opts, &path))) return rc;
+    if ((rc = choose_path(T, iloc, opts, &path))) return rc;
     if (opts && opts->path_used) *opts->path_used = path;
     if (T == 0) return MOE_OK;
     if (!x || !out || !ws || (!route && (!idx || !w))) return MOE_EINVAL;
     if (!al16(x) || !al16(out) || ((uintptr_t)ws & 255)) return MOE_EUNSUPPORTED;
-    const WsLayout L = ws_layout(*desc, T, nshards);
+    const WsLayout L = ws_layout(*desc, T, iloc);
     if (ws_bytes < L.total) return MOE_EWORKSPACE;
     if ((rc = check_device())) return rc;
     char* wsp = (char*)ws;
@@ -281,7 +278,7 @@ static int forward_common(const moe_layer_desc* desc, const float* x, int32_t T,
         c.n_ev = opts->n_kernel_events;
     }
     if (path == MOE_PATH_GEMV)
-        return launched(launch_gemv(*desc, x, T, idx, w, shard, nshards, out, wsp, L, c, route));
+        return launched(launch_gemv(*desc, x, T, idx, w, i0, iloc, out, wsp, L, c, route));
     if (route) {
         int32_t* ridx = reinterpret_cast<int32_t*>(wsp + L.idx);
         float* rw = reinterpret_cast<float*>(wsp + L.w);
@@ -289,22 +286,41 @@ static int forward_common(const moe_layer_desc* desc, const float* x, int32_t T,
         idx = ridx;
         w = rw;
     }
-    return launched(launch_mfma(*desc, x, T, idx, w, shard, nshards, out, wsp, L, c,
+    return launched(launch_mfma(*desc, x, T, idx, w, i0, iloc, out, wsp, L, c,
                                 route && T > kRouterSmallMaxT));
 }
 
 int moe_layer_forward(const moe_layer_desc* desc, const float* x, int32_t T, float* out,
                       const moe_opts* opts, void* ws, size_t ws_bytes, void* stream) {
-    return forward_common(desc, x, T, nullptr, nullptr, 0, 1, out, opts, ws, ws_bytes, stream,
-                          true);
+    const int rc = check_desc(desc);
+    if (rc) return rc;
+    return forward_common(desc, x, T, nullptr, nullptr, 0, desc->inter, out, opts, ws, ws_bytes,
+                          stream, true);
 }
 
 int moe_layer_forward_shard(const moe_layer_desc* desc, const float* x, int32_t T,
                             const int32_t* topk_idx, const float* topk_w, int32_t shard,
                             int32_t num_shards, float* partial, const moe_opts* opts, void* ws,
                             size_t ws_bytes, void* stream) {
-    return forward_common(desc, x, T, topk_idx, topk_w, shard, num_shards, partial, opts, ws,
+    const int rc = check_desc(desc);
+    if (rc) return rc;
+    if (num_shards < 1 || num_shards > 16 || shard < 0 || shard >= num_shards) return MOE_EINVAL;
+    if (desc->inter % num_shards || (desc->inter / num_shards) % 64) return MOE_EUNSUPPORTED;
+    const int iloc = desc->inter / num_shards;
+    return forward_common(desc, x, T, topk_idx, topk_w, shard * iloc, iloc, partial, opts, ws,
                           ws_bytes, stream, false);
+}
+
+int moe_layer_forward_range(const moe_layer_desc* desc, const float* x, int32_t T,
+                            const int32_t* topk_idx, const float* topk_w, int32_t i_begin,
+                            int32_t i_end, float* partial, const moe_opts* opts, void* ws,
+                            size_t ws_bytes, void* stream) {
+    const int rc = check_desc(desc);
+    if (rc) return rc;
+    if (i_begin < 0 || i_end <= i_begin || i_end > desc->inter) return MOE_EINVAL;
+    if (i_begin % 64 || i_end % 64) return MOE_EUNSUPPORTED;
+    return forward_common(desc, x, T, topk_idx, topk_w, i_begin, i_end - i_begin, partial, opts,
+                          ws, ws_bytes, stream, false);
 }
 
 int moe_reduce_partials(const float* const* partials, int32_t num_shards, int64_t n_elems,
@@ -395,7 +411,7 @@ int moe_route_bucket(const moe_layer_desc* desc, const int32_t* topk_idx, int32_
     if (T == 0) return MOE_OK;
     if (!topk_idx || !counts || !offsets || !perm || !ws) return MOE_EINVAL;
     if ((uintptr_t)ws & 255) return MOE_EUNSUPPORTED;
-    const WsLayout L = ws_layout(*desc, T, 1);
+    const WsLayout L = ws_layout(*desc, T, desc->inter);
     if (ws_bytes < L.total) return MOE_EWORKSPACE;
     if ((rc = check_device())) return rc;
     hipStream_t s = (hipStream_t)stream;

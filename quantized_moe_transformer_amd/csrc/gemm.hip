@@ -163,7 +163,8 @@ struct GemmArgs {
     const int32_t* offsets;         // [E+2]: group row starts (group E = shared expert)
     const int32_t* tile_off;        // [E+2]: group tile starts
     const int4* tile_rec;           // per row tile: group, first sorted row, rows, row offset
-    int T, H, E, k, I, Is, shard, nshards;
+    int T, H, E, k, I, Is;
+    int i0, iloc;                   // intermediate rows [i0, i0 + iloc) of every expert
     const uint8_t *w_routed, *w_routed2, *w_shared, *w_shared2;   // MODE 0: gate, up
     const float* route_w;           // [T*k] routing weights
     float sw;
@@ -594,8 +595,8 @@ gemm_grouped_kernel(GemmArgs a) {
     ti.mcount = rec.z;
     ti.m0 = rec.w;
     ti.Iexp = ti.is_sh ? a.Is : a.I;
-    ti.Iloc = ti.Iexp / a.nshards;
-    ti.i0 = a.shard * ti.Iloc;
+    ti.Iloc = a.iloc;   // the shared expert has the routed width
+    ti.i0 = a.i0;
     ti.n0 = ntile * (MODE == 0 ? kTN / 2 : kTN);
     const int tid = threadIdx.x;
     if (tid < kTM) {
@@ -675,11 +676,11 @@ combine_kernel(const float* __restrict__ y, const float* __restrict__ ysh,
 }
 
 hipError_t launch_mfma(const moe_layer_desc& d, const float* x, int T, const int32_t* idx,
-                       const float* w, int shard, int nshards, float* out, char* ws,
+                       const float* w, int i0, int iloc, float* out, char* ws,
                        const WsLayout& L, const Ctx& c, bool x16_ready) {
     const int H = d.hidden, E = d.n_experts, k = d.top_k;
     const bool shared = d.shared_inter > 0;
-    const int Iloc = d.inter / nshards;
+    const int Iloc = iloc;
     _Float16* x16 = reinterpret_cast<_Float16*>(ws + L.x16);
     int32_t* bhist = reinterpret_cast<int32_t*>(ws + L.bhist);
     int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
@@ -713,8 +714,8 @@ hipError_t launch_mfma(const moe_layer_desc& d, const float* x, int T, const int
     a.k = k;
     a.I = d.inter;
     a.Is = d.shared_inter;
-    a.shard = shard;
-    a.nshards = nshards;
+    a.i0 = i0;
+    a.iloc = iloc;
     a.route_w = w;
     a.sw = d.shared_weight;
 
@@ -739,7 +740,7 @@ hipError_t launch_mfma(const moe_layer_desc& d, const float* x, int T, const int
     g2.w_shared = d.sh_down_q;
     g2.n_ntiles = (H + kTN - 1) / kTN;
     g2.nk = Iloc / kBK;
-    g2.sb_rows = (d.inter % kSbWeights == 0 && Iloc % kSbWeights == 0) ? 1 : 0;
+    g2.sb_rows = (d.inter % kSbWeights == 0 && Iloc % kSbWeights == 0 && i0 % kSbWeights == 0) ? 1 : 0;
     g2.y = y;
     g2.ysh = ysh;
     launch_k(c, MOE_K_GEMM_DOWN, gemm_grouped_kernel<1>, dim3(max_tiles8 * g2.n_ntiles),

@@ -233,7 +233,8 @@ struct GemvArgs {
     const uint8_t *gate, *up, *down, *sh_gate, *sh_up, *sh_down;
     const float* router_w;
     const float* x;
-    int T, H, E, k, I, Is, shard, nshards, nslot;
+    int T, H, E, k, I, Is, nslot;
+    int i0, iloc;         // intermediate rows [i0, i0 + iloc) of every expert
     float sw;
     const int32_t* idx;   // routing read by gateup (when given) and by down
     const float* w;
@@ -340,7 +341,7 @@ gemv_front_kernel(GemvArgs a) {
     const int sb = b - a.n_router_blocks;
     const int t = sb / a.shared_rows_blocks;
     const int rblk = sb % a.shared_rows_blocks;
-    const int Iloc = a.Is / a.nshards, i0 = a.shard * Iloc;
+    const int Iloc = a.iloc, i0 = a.i0;   // the shared expert has the routed width
     const int wave = threadIdx.x >> 6;
     if (wave >= kShWaves) return;
     constexpr int rows_per_wave = kShSteps * (64 / LPR);
@@ -382,7 +383,7 @@ gemv_gateup_kernel(GemvArgs a) {
     }
     if ((unsigned)e >= (unsigned)a.E) return;
     const size_t mat = (size_t)a.I * a.H / kSbWeights * kQ4Bytes;
-    const int Iloc = a.I / a.nshards, i0 = a.shard * Iloc;
+    const int Iloc = a.iloc, i0 = a.i0;
     const int wave = threadIdx.x >> 6;
     constexpr int rows_per_wave = kGuSteps * (64 / LPR);
     const int rbase = (blockIdx.x * kGuWaves + wave) * rows_per_wave;
@@ -399,7 +400,9 @@ gemv_gateup_kernel(GemvArgs a) {
 constexpr int kDnPasses = 2;   // row passes per wave in the down kernel
 
 // Block: one wave per slot (nw = min(nslot, 16) waves, slot j on wave j % nw),
-// kDnPasses * (64 / lprd) output rows of one token; lprd = I_loc / 32.
+// kDnPasses * (64 / lprd) output rows of one token.  A row's I_loc inputs are
+// I_loc / 32 lane tasks of 32 (a 16-byte code piece each); lprd, the lanes per
+// row, is that count rounded up to a power of two, the extra lanes adding 0.
 __global__ void __launch_bounds__(1024)
 gemv_down_kernel(GemvArgs a, int lprd) {
     __shared__ float ys[17][kDnPasses * 64];
@@ -409,7 +412,8 @@ gemv_down_kernel(GemvArgs a, int lprd) {
     const int nw = blockDim.x >> 6;
     const int rs = 64 / lprd;                     // rows per pass
     const int rslot = lane / lprd, task = lane % lprd;
-    const int cg = task >> 1, hh = task & 1;
+    const bool active = task < (a.iloc >> 5);
+    const int cg = active ? task >> 1 : 0, hh = task & 1;
     const int obase = blockIdx.x * kDnPasses * rs;
     const int H = a.H;
     for (int j = wave; j < a.nslot; j += nw) {
@@ -429,7 +433,7 @@ gemv_down_kernel(GemvArgs a, int lprd) {
             Iexp = a.Is;
         }
         if (lane == 0) s_wt[j] = valid ? wj : 0.f;
-        const int Iloc = Iexp / a.nshards, i0 = a.shard * Iloc;
+        const int i0 = a.i0;
         SbHead hd[kDnPasses];
         uint4 qh[kDnPasses], qs[kDnPasses];
         int cc[kDnPasses];
@@ -455,7 +459,8 @@ gemv_down_kernel(GemvArgs a, int lprd) {
         }
 #pragma unroll
         for (int ps = 0; ps < kDnPasses; ++ps) {
-            const float part = piece_dot<true>(hd[ps], qs[ps], qh[ps], cc[ps], hl, hu, sa, sb2);
+            const float part =
+                active ? piece_dot<true>(hd[ps], qs[ps], qh[ps], cc[ps], hl, hu, sa, sb2) : 0.f;
             const float y = wave_sum_group(part, lprd);
             if (task == 0) ys[j][ps * rs + rslot] = valid ? y : 0.f;
         }
@@ -476,7 +481,7 @@ gemv_down_kernel(GemvArgs a, int lprd) {
 // launchers
 // ---------------------------------------------------------------------------
 
-static GemvArgs base_args(const moe_layer_desc& d, const float* x, int T, int shard, int nshards) {
+static GemvArgs base_args(const moe_layer_desc& d, const float* x, int T, int i0, int iloc) {
     GemvArgs a = {};
     a.gate = d.gate_q;
     a.up = d.up_q;
@@ -492,8 +497,8 @@ static GemvArgs base_args(const moe_layer_desc& d, const float* x, int T, int sh
     a.k = d.top_k;
     a.I = d.inter;
     a.Is = d.shared_inter;
-    a.shard = shard;
-    a.nshards = nshards;
+    a.i0 = i0;
+    a.iloc = iloc;
     a.nslot = d.top_k + (d.shared_inter > 0 ? 1 : 0);
     a.sw = d.shared_weight;
     return a;
@@ -511,7 +516,7 @@ static void launch_front_t(const GemvArgs& a, int n_shared_blocks, const Ctx& c)
 template <int LPR, int NSBL>
 static void launch_gateup_t(const GemvArgs& a, const Ctx& c) {
     constexpr int rows_per_block = kGuWaves * kGuSteps * (64 / LPR);
-    const int Iloc = a.I / a.nshards;
+    const int Iloc = a.iloc;
     const dim3 grid((Iloc + rows_per_block - 1) / rows_per_block, a.T * a.k);
     launch_k(c, MOE_K_GATEUP_GEMV, gemv_gateup_kernel<LPR, NSBL>, grid, dim3(64 * kGuWaves), 0, a);
 }
@@ -539,7 +544,7 @@ static hipError_t launch_front(GemvArgs& a, bool route, bool shared, const WsLay
     int n_shared = 0;
     if (shared) {
         const int rows_per_block = kShWaves * kShSteps * (64 / lanes_per_row(nsb));
-        const int Iloc = a.Is / a.nshards;
+        const int Iloc = a.iloc;
         a.shared_rows_blocks = (Iloc + rows_per_block - 1) / rows_per_block;
         n_shared = a.shared_rows_blocks * a.T;
     }
@@ -559,10 +564,10 @@ hipError_t launch_router(const moe_layer_desc& d, const float* x, int T, int32_t
                          char* ws, const WsLayout& L, const Ctx& c);   // router.hip
 
 hipError_t launch_gemv(const moe_layer_desc& d, const float* x, int T, const int32_t* idx,
-                       const float* w, int shard, int nshards, float* out, char* ws,
+                       const float* w, int i0, int iloc, float* out, char* ws,
                        const WsLayout& L, const Ctx& c, bool route) {
-    GemvArgs a = base_args(d, x, T, shard, nshards);
-    const int Iloc = d.inter / nshards;
+    GemvArgs a = base_args(d, x, T, i0, iloc);
+    const int Iloc = iloc;
     a.hbuf = reinterpret_cast<float*>(ws + L.hbuf);
     a.hstride = Iloc;
     a.out = out;
@@ -586,7 +591,8 @@ hipError_t launch_gemv(const moe_layer_desc& d, const float* x, int T, const int
     a.w = w;
     const int nsb = d.hidden / kSbWeights;
     MOE_DISPATCH_H(nsb, launch_gateup_t, a, c);
-    const int lprd = Iloc / 32;
+    int lprd = 2;   // lanes per down row: Iloc / 32 rounded up to a power of two
+    while (lprd < Iloc / 32) lprd *= 2;
     const int rows_per_block = kDnPasses * (64 / lprd);
     const int nw = a.nslot < 16 ? a.nslot : 16;
     const dim3 grid2((d.hidden + rows_per_block - 1) / rows_per_block, T);

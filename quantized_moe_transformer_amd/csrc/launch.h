@@ -1,10 +1,48 @@
-// launch.h -- host side of libmoe_hip.so: the launch context and the kernel
-// launchers (enqueue only; arguments already validated by api.hip).
+// launch.h -- host side of libmoe_hip.so: the workspace layout, the launch
+// context and the kernel launchers (enqueue only; arguments already validated
+// by api.hip).
 #pragma once
 
 #include "moe_internal.h"
 
 namespace moe {
+
+// ---------------------------------------------------------------------------
+// Workspace layout
+// ---------------------------------------------------------------------------
+
+struct WsLayout {
+    // shared by both paths
+    size_t router_part;   // float [T][E][ks]
+    size_t x_lo;          // fp16 [T][H] low parts of x (router at large T)
+    size_t w_hi, w_lo;    // fp16 [E][H] split router matrix (router at large T)
+    size_t idx, w;        // int32 / float [T][k] (routing computed inside the forward call)
+    // GEMV path
+    size_t hbuf;          // float [T*(k+1)][I_loc]
+    // grouped-GEMM path (overlays the GEMV region)
+    size_t x16;           // fp16 [T][H]
+    size_t bhist;         // int32 [nblk][E]
+    size_t counts;        // int32 [E+1]
+    size_t offsets;       // int32 [E+2]
+    size_t tile_off;      // int32 [E+3]
+    size_t tile_rec;      // int4 per row tile: group, first sorted row, rows, row offset in group
+    size_t perm;          // int32 [T*k]
+    size_t h16;           // fp16 [T*k + T][I_loc]
+    size_t y;             // float [T*k][H]
+    size_t ysh;           // float [T][H]
+    size_t total;
+    int router_ks;        // router K-splits
+};
+
+int router_splits(int T, int H);
+// iloc: the intermediate rows per expert that the call computes (I, or a shard's)
+WsLayout ws_layout(const moe_layer_desc& d, int T, int iloc);
+inline int bucket_blocks(int T, int k) { return (T * k + 1023) / 1024; }
+// upper bound on the grouped GEMM's row tiles: sum over experts of
+// ceil(count / kTileM) <= T*k / kTileM + E, plus the shared expert's
+inline int max_row_tiles(int T, int k, int E, bool shared) {
+    return (T * k + kTileM - 1) / kTileM + E + (shared ? (T + kTileM - 1) / kTileM : 0);
+}
 
 // Launch context: the stream, and (optionally) caller-owned start/stop events
 // per kernel id (moe_opts.kernel_events).  A timed kernel is launched with
@@ -30,8 +68,9 @@ inline void launch_k(const Ctx& c, int id, void (*kern)(KArgs...), dim3 grid, di
 hipError_t launch_router(const moe_layer_desc& d, const float* x, int T, int32_t* idx, float* w,
                          char* ws, const WsLayout& L, const Ctx& c);
 // route: run the router (and top-k) in the front kernel, writing L.idx / L.w
+// i0, iloc: intermediate rows [i0, i0 + iloc) of every expert (the shard)
 hipError_t launch_gemv(const moe_layer_desc& d, const float* x, int T, const int32_t* idx,
-                       const float* w, int shard, int nshards, float* out, char* ws,
+                       const float* w, int i0, int iloc, float* out, char* ws,
                        const WsLayout& L, const Ctx& c, bool route);
 hipError_t launch_bucket(const int32_t* idx, int T, int k, int E, bool shared, int32_t* counts,
                          int32_t* offsets, int32_t* tile_off, int4* tile_rec, int32_t* perm,
@@ -39,7 +78,7 @@ hipError_t launch_bucket(const int32_t* idx, int T, int k, int E, bool shared, i
                          const Ctx& c);
 // x16_ready: the router already wrote the fp16 tokens (L.x16)
 hipError_t launch_mfma(const moe_layer_desc& d, const float* x, int T, const int32_t* idx,
-                       const float* w, int shard, int nshards, float* out, char* ws,
+                       const float* w, int i0, int iloc, float* out, char* ws,
                        const WsLayout& L, const Ctx& c, bool x16_ready);
 hipError_t launch_x16(const float* x, int T, int H, char* ws, const WsLayout& L, const Ctx& c);
 hipError_t launch_reduce(const float* const* partials, int n, int64_t count, const float* res,

@@ -1,4 +1,4 @@
-// moe_internal.h -- device helpers, constants and the workspace layout of libmoe_hip.so
+// moe_internal.h -- device helpers and constants of libmoe_hip.so
 //
 // Everything here is gfx950 (CDNA4) code: 64-lane wavefronts, MFMA matrix
 // cores, 160 KB of LDS per CU.  Nothing in this directory is shared with the
@@ -147,42 +147,6 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// ---------------------------------------------------------------------------
-// Workspace layout
-// ---------------------------------------------------------------------------
-
-struct WsLayout {
-    // shared by both paths
-    size_t router_part;   // float [T][E][ks]
-    size_t x_lo;          // fp16 [T][H] low parts of x (router at large T)
-    size_t w_hi, w_lo;    // fp16 [E][H] split router matrix (router at large T)
-    size_t idx, w;        // int32 / float [T][k] (routing computed inside the forward call)
-    // GEMV path
-    size_t hbuf;          // float [T*(k+1)][I_loc]
-    // grouped-GEMM path (overlays the GEMV region)
-    size_t x16;           // fp16 [T][H]
-    size_t bhist;         // int32 [nblk][E]
-    size_t counts;        // int32 [E+1]
-    size_t offsets;       // int32 [E+2]
-    size_t tile_off;      // int32 [E+3]
-    size_t tile_rec;      // int4 per row tile: group, first sorted row, rows, row offset in group
-    size_t perm;          // int32 [T*k]
-    size_t h16;           // fp16 [T*k + T][I_loc]
-    size_t y;             // float [T*k][H]
-    size_t ysh;           // float [T][H]
-    size_t total;
-    int router_ks;        // router K-splits
-};
-
-int router_splits(int T, int H);
-WsLayout ws_layout(const moe_layer_desc& d, int T, int num_shards);
-inline int bucket_blocks(int T, int k) { return (T * k + 1023) / 1024; }
-// upper bound on the grouped GEMM's row tiles: sum over experts of
-// ceil(count / kTileM) <= T*k / kTileM + E, plus the shared expert's
-inline int max_row_tiles(int T, int k, int E, bool shared) {
-    return (T * k + kTileM - 1) / kTileM + E + (shared ? (T + kTileM - 1) / kTileM : 0);
 }
 
 }  // namespace moe

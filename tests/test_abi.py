@@ -28,6 +28,7 @@ def test_header_declares_the_boundary():
     for fn in ("router_topk", "moe_layer_forward", "moe_layer_forward_shard",
                "moe_reduce_partials", "moe_dequant", "moe_workspace_bytes", "moe_route_bucket",
                "moe_status_str", "moe_abi_version", "moe_reduce_residual", "moe_rmsnorm",
+               "moe_layer_forward_range",
                "moe_rmsnorm_sumsq", "moe_rmsnorm_apply"):
         assert fn in names
 
@@ -35,7 +36,7 @@ def test_header_declares_the_boundary():
 def test_library_exports_every_declared_symbol(L):
     for fn in declared_functions():
         assert hasattr(L.lib, fn), fn
-    assert L.moe_abi_version() == 2
+    assert L.moe_abi_version() == 3
     assert L.moe_status_str(-3) == "workspace too small"
 
 
@@ -74,6 +75,11 @@ def raw_shard(L, d, T, shard, n, ws_bytes=1 << 40, idx=FAKE, w=FAKE):
                                          FAKE, ws_bytes, None)
 
 
+def raw_range(L, d, T, i_begin, i_end, ws_bytes=1 << 40, idx=FAKE, w=FAKE):
+    return L.lib.moe_layer_forward_range(ctypes.byref(d), FAKE, T, idx, w, i_begin, i_end, FAKE,
+                                         None, FAKE, ws_bytes, None)
+
+
 def test_argument_errors_before_any_launch(L):
     assert raw_forward(L, desc(k=0), 1) == L.MOE_EINVAL
     assert raw_forward(L, desc(k=17, E=32), 1) == L.MOE_EINVAL
@@ -92,6 +98,13 @@ def test_argument_errors_before_any_launch(L):
     assert raw_shard(L, desc(), 1, -1, 2) == L.MOE_EINVAL
     assert raw_shard(L, desc(), 1, 0, 16) == L.MOE_EUNSUPPORTED     # 512/16 = 32 columns
     assert raw_shard(L, desc(), 1, 0, 2, idx=None) == L.MOE_EINVAL
+    # moe_layer_forward_range: empty, reversed, out-of-range or misaligned rows
+    assert raw_range(L, desc(), 1, 64, 64) == L.MOE_EINVAL
+    assert raw_range(L, desc(), 1, 128, 64) == L.MOE_EINVAL
+    assert raw_range(L, desc(), 1, 0, 576) == L.MOE_EINVAL
+    assert raw_range(L, desc(), 1, -64, 64) == L.MOE_EINVAL
+    assert raw_range(L, desc(), 1, 0, 160) == L.MOE_EUNSUPPORTED
+    assert raw_range(L, desc(), 1, 0, 192, ws_bytes=1024) == L.MOE_EWORKSPACE
     # moe_reduce_partials: wrong shard count or a lost shard
     arr = (ctypes.c_void_p * 2)(FAKE, None)
     assert L.lib.moe_reduce_partials(arr, 2, 16, FAKE, None) == L.MOE_EINVAL

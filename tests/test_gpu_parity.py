@@ -326,6 +326,43 @@ def test_shard_partials_and_reduce(name, T, path, tol):
     assert np.array_equal(o, p[0] + p[1])
 
 
+@pytest.mark.parametrize("name,T,path,cuts", [
+    ("decode", 1, qm.MOE_PATH_GEMV, (0, 128, 512)),                  # 25 / 75
+    ("decode", 1, qm.MOE_PATH_GEMV, (0, 192, 512)),                  # 37.5 / 62.5: widths 192, 320
+    ("decode_batched", 7, qm.MOE_PATH_GEMV, (0, 64, 192, 320, 512)),  # 4 lanes, uneven
+    ("decode_batched", 32, qm.MOE_PATH_MFMA, (0, 192, 512)),
+    ("prefill4096", 512, qm.MOE_PATH_MFMA, (0, 128, 512)),
+    ("prefill4096", 512, qm.MOE_PATH_MFMA, (0, 256, 320, 512)),       # superblock-aligned and not
+    ("tiny", 4, qm.MOE_PATH_GEMV, (0, 64, 128)),
+    ("tiny", 4, qm.MOE_PATH_MFMA, (0, 64, 128)),
+])
+def test_uneven_range_shards(name, T, path, cuts):
+    # shards proportional to lane throughput (page "Distributed CPU: Zip Fusion
+    # Beyond Tensor Parallelism", "Heterogeneous Topology"): any partition of
+    # the intermediate rows, each range against the oracle, their sum against
+    # the whole layer
+    w, layer, dl, ol = dev_layer(name)
+    tol = GEMV_TOL if path == qm.MOE_PATH_GEMV else MFMA_TOL
+    x = mi.make_tokens(w.shape, w.seed, T, stream=w.x_stream, zipf=w.zipf)
+    say(f"range shards {name} T={T} path={path} cuts={cuts}")
+    oi, ow, _, _ = oracle.router(x, layer["router_w"], w.shape.k)
+    full = oracle.forward(ol, x, oi, ow)
+    parts = []
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        part = torch.full((T, dl.H), float("nan"), device=DEV)
+        used = qm.moe_layer_forward_range(dl.desc, gpu(x), T, gpu(oi), gpu(ow), a, b, part,
+                                          dl.workspace(T), path=path)
+        torch.cuda.synchronize()
+        assert used == path
+        ref = oracle.forward_range(ol, x, oi, ow, a, b)
+        assert rel_err(part.cpu().numpy(), ref) <= tol * rel_scale(ref, full)
+        parts.append(part)
+    out = torch.empty((T, dl.H), device=DEV)
+    qm.moe_reduce_partials(parts, T * dl.H, out)
+    torch.cuda.synchronize()
+    assert rel_err(out.cpu().numpy(), full) <= tol
+
+
 def rel_scale(part, full):
     # a partial's own RMS is smaller than the layer's; measure both against the layer's RMS
     return float(np.sqrt(np.mean(np.asarray(full, np.float64) ** 2)) /
