@@ -427,6 +427,103 @@ def bench_edges(torch, qm, T=4096, H=2048, reps=20):
     return res
 
 
+def split_rows(fracs, I, q=64):
+    """Intermediate rows per lane for the given fractions, in multiples of q
+    (the kernels' column quantum), by largest remainder; every lane gets at
+    least q rows."""
+    units = I // q
+    raw = [f / sum(fracs) * units for f in fracs]
+    rows = [max(1, int(r)) for r in raw]
+    while sum(rows) > units:
+        rows[rows.index(max(rows))] -= 1
+    order = sorted(range(len(raw)), key=lambda i: raw[i] - int(raw[i]), reverse=True)
+    for i in order[:units - sum(rows)]:
+        rows[i] += 1
+    return [r * q for r in rows]
+
+
+def lane_times(torch, qm, dl, xd, idx, wts, T, rows, reps):
+    """Each lane's shard alone (moe_layer_forward_range, routing given), replayed
+    from a HIP graph of `reps` calls: microseconds per call."""
+    out, a = [], 0
+    for r in rows:
+        b = a + r
+        part = torch.empty((T, dl.H), device="cuda")
+        ws = dl.workspace(T)
+
+        def call(a=a, b=b, part=part, ws=ws):
+            qm.moe_layer_forward_range(dl.desc, xd, T, idx, wts, a, b, part, ws)
+
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for _ in range(3):
+                call()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                call()
+        g.replay()
+        torch.cuda.synchronize()
+        n_rep = 5
+        t0 = time.perf_counter()
+        for _ in range(n_rep):
+            g.replay()
+        torch.cuda.synchronize()
+        out.append((time.perf_counter() - t0) / (n_rep * reps) * 1e6)
+        del g
+        a = b
+    return out
+
+
+def lane_report(rows, us):
+    region = max(us)
+    return {"rows": rows, "fractions": [r / sum(rows) for r in rows],
+            "lane_us": [round(v, 2) for v in us], "region_us": round(region, 2),
+            "idle_us_at_barrier": round(sum(region - v for v in us), 2)}
+
+
+def bench_balance(args, torch, qm, mi, DeviceLayer):
+    """Lane-time balance of shards sized by fraction (page "Distributed CPU:
+    Zip Fusion Beyond Tensor Parallelism", "Heterogeneous Topology": shards in
+    proportion to each lane's measured throughput; the region ends with the
+    slowest lane).  Every lane here is the same GPU, timed alone: a lane's
+    throughput is its rows per microsecond, and the rebalanced split gives each
+    lane rows in proportion to it."""
+    shp = mi.QWEN35_MOE
+    report = {}
+    for label, wname, T, reps in (("decode_T1", "decode", 1, 32),
+                                  ("prefill_T4096", "prefill4096", 4096, 4)):
+        w = mi.WORKLOADS[wname]
+        layer = mi.make_layer(shp, w.seed)
+        dl = DeviceLayer.from_shape(layer, shp)
+        xd = torch.from_numpy(mi.make_tokens(shp, w.seed, T)).cuda()
+        idx = torch.empty((T, shp.k), dtype=torch.int32, device="cuda")
+        wts = torch.empty((T, shp.k), dtype=torch.float32, device="cuda")
+        qm.router_topk(dl.desc, xd, T, idx, wts, dl.workspace(T))   # the synchronised decision
+        torch.cuda.synchronize()
+        cases = {}
+        for name, fracs in (("equal_2", (1, 1)), ("equal_4", (1, 1, 1, 1)), ("30_70", (0.3, 0.7))):
+            rows = split_rows(fracs, shp.I)
+            us = lane_times(torch, qm, dl, xd, idx, wts, T, rows, reps)
+            cases[name] = lane_report(rows, us)
+            print(f"[balance] {label} {name} rows={rows} lane_us={[round(v, 1) for v in us]}",
+                  file=sys.stderr, flush=True)
+        # one rebalancing step of the 30/70 split: rows in proportion to each
+        # lane's measured rows per microsecond
+        c = cases["30_70"]
+        rates = [r / t for r, t in zip(c["rows"], c["lane_us"])]
+        rows = split_rows(rates, shp.I)
+        us = lane_times(torch, qm, dl, xd, idx, wts, T, rows, reps)
+        cases["30_70_rebalanced"] = lane_report(rows, us)
+        cases["30_70_rebalanced"]["from_rates_rows_per_us"] = [round(v, 3) for v in rates]
+        full = lane_times(torch, qm, dl, xd, idx, wts, T, [shp.I], reps)[0]
+        report[label] = {"T": T, "whole_layer_us": round(full, 2), "splits": cases}
+    return report
+
+
 def cpu_baseline_decode(layer, pool, budget_s):
     import moe_inputs as mi
     import oracle
@@ -473,6 +570,8 @@ def main():
     ap.add_argument("--continuum", action="store_true",
                     help="only time both paths at T = 1 .. 512 (one JSON line per point)")
     ap.add_argument("--continuum-t", type=int, nargs="+", default=list(CONTINUUM_T))
+    ap.add_argument("--balance", action="store_true",
+                    help="only report lane times of shards sized by fraction (one JSON object)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -494,6 +593,9 @@ def main():
         return
     if args.continuum:
         bench_continuum(args, torch, qm, mi, DeviceLayer)
+        return
+    if args.balance:
+        print(json.dumps(bench_balance(args, torch, qm, mi, DeviceLayer)), flush=True)
         return
 
     print("[bench] decode T=1 ...", file=sys.stderr, flush=True)
