@@ -50,12 +50,12 @@ FP16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak
 # --copy-probe).  Keyed by the SHA-256 of the kernel's sources: when they change,
 # the counters no longer describe the kernel and traffic is reported as null.
 TRAFFIC = {
-    # decode T=1, 180 dispatches: FETCH 4730.7 KiB x 1.99980, WRITE 16.1 KiB x 1.0
-    "gemv_gateup": {"sources_sha256": "a915bf1ed8416af992e5a4f89a0f00f1ccc549dd348136e7ee46ac711bc4925f",
-                    "fetch_bytes": 9687539, "write_bytes": 16448},
-    # prefill T=4096, 9 dispatches: FETCH 224623.8 KiB x 1.99980, WRITE 36864.0 KiB x 1.0
-    "gemm_gateup": {"sources_sha256": "b159c0486656fd36787a88a17bf752d7dffc10d9daff4f148000dc67920b6203",
-                    "fetch_bytes": 459982778, "write_bytes": 37748736},
+    # decode T=1, 180 dispatches: FETCH 4732.4 KiB x 1.99980, WRITE 16.1 KiB x 1.0
+    "gemv_gateup": {"sources_sha256": "ad3a4ed6dc5106808578e85b9800b0a2a44c872050a144d3012fd3454a681b54",
+                    "fetch_bytes": 9690891, "write_bytes": 16448},
+    # prefill T=4096, 9 dispatches: FETCH 224636.3 KiB x 1.99980, WRITE 36864.0 KiB x 1.0
+    "gemm_gateup": {"sources_sha256": "921152f0e92d94aa2170964d37323c1a2d4f0b45294c6e711e340e63bb18301b",
+                    "fetch_bytes": 460008154, "write_bytes": 37748736},
 }
 FETCH_SIZE_FACTOR = 1.99980   # plain 256 MiB copy: true bytes read / FETCH_SIZE bytes
 WRITE_SIZE_FACTOR = 1.0
