@@ -47,7 +47,7 @@ class moe_opts(ctypes.Structure):
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m quantized_moe_transformer_amd.build`")
+        raise ImportError(f"{LIB_PATH} is not built; run `python quantized_moe_transformer_amd/build.py`")
     L = ctypes.CDLL(LIB_PATH)
     P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     D = ctypes.POINTER(moe_layer_desc)

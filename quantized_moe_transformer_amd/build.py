@@ -1,6 +1,7 @@
 """Compile the HIP sources under csrc/ into libmoe_hip.so (gfx950 only).
 
-Run as ``python -m quantized_moe_transformer_amd.build``.  hipcc cross-compiles
+Run as ``python quantized_moe_transformer_amd/build.py`` (the package itself
+needs the library to import).  hipcc cross-compiles
 for gfx950 without a GPU present.
 """
 import glob
