@@ -22,6 +22,15 @@ workload's distributions: scales and mins uniform on 0..63, codes uniform on
 0..15 (4-bit) or 0..31 (5-bit).  ``d`` and ``dmin`` are fp16 roundings (round to
 nearest even) of fp32 draws uniform on [1e-3, 4e-3].
 
+MXFP4 blobs
+-----------
+The second weight format (``LayerShape.fmt == 1``; gate, up and down all use
+it): a 144-byte superblock of 256 weights, bytes 0..7 the E8M0 scale bytes of
+its eight 32-weight blocks, bytes 8..15 zero (reserved), bytes 16..143 the
+4-bit E2M1 codes in the nibble order of the 4-bit K-quant superblock.  Scale
+bytes are uniform on 121..125 (block scales 2^-6 .. 2^-2) and codes uniform on
+0..15.
+
 Weight matrices are stored one row per output feature with the reduction
 dimension contiguous, quantised in flat row-major order in 256-element
 superblocks (so a superblock may span several rows when the row is shorter
@@ -36,6 +45,8 @@ import numpy as np
 
 Q4K_SB_BYTES = 144   # fp16 d, fp16 dmin, 12 scale bytes, 128 code bytes
 Q5K_SB_BYTES = 176   # as Q4K plus 32 bytes of high code bits
+MXFP4_SB_BYTES = 144  # 8 E8M0 scale bytes, 8 reserved bytes, 128 code bytes
+MXFP4_SCALE_RANGE = (121, 125)   # E8M0 scale bytes drawn uniformly (inclusive)
 SB_WEIGHTS = 256
 
 # Stream ids: every tensor (and every expert of it) draws from its own stream
@@ -53,6 +64,7 @@ class LayerShape:
     I: int          # routed-expert intermediate width
     Is: int         # shared-expert intermediate width (0 = no shared expert)
     shared_weight: float = 1.0
+    fmt: int = 0    # 0: Q4_K gate/up and Q5_K down; 1: MXFP4 gate, up and down
 
     def sb_counts(self):
         """Superblocks per matrix: gate/up (I x H), down (H x I), shared ones."""
@@ -62,6 +74,8 @@ class LayerShape:
 
 QWEN35_MOE = LayerShape(H=2048, E=256, k=8, I=512, Is=512)
 TINY = LayerShape(H=256, E=8, k=2, I=128, Is=128)
+QWEN35_MOE_MX = LayerShape(H=2048, E=256, k=8, I=512, Is=512, fmt=1)
+TINY_MX = LayerShape(H=256, E=8, k=2, I=128, Is=128, fmt=1)
 
 
 @dataclass(frozen=True)
@@ -94,6 +108,13 @@ WORKLOADS: Dict[str, Workload] = {
                                 note="same layer, prefill T=512, Zipf-like expert load"),
     "prefill4096": Workload("prefill4096", QWEN35_MOE, seed=4, T=4096, shards=2,
                             note="same layer, prefill T=4096, uniform router (unsharded and 2-shard)"),
+    # the same shapes with MXFP4 expert weights
+    "tiny_mx": Workload("tiny_mx", TINY_MX, seed=5, T=4,
+                        note="tiny layer, MXFP4 weights, seed 5, T=4"),
+    "decode_mx": Workload("decode_mx", QWEN35_MOE_MX, seed=6, T=1,
+                          note="Qwen3.5-35B-A3B-shaped layer, MXFP4 weights, decode T=1"),
+    "prefill4096_mx": Workload("prefill4096_mx", QWEN35_MOE_MX, seed=7, T=4096, shards=2,
+                               note="same layer, MXFP4 weights, prefill T=4096, uniform router"),
 }
 
 
@@ -114,6 +135,20 @@ def kquant_blob(rng: np.random.Generator, n_sb: int, bits: int) -> np.ndarray:
     return blob.reshape(-1)
 
 
+def mxfp4_blob(rng: np.random.Generator, n_sb: int) -> np.ndarray:
+    """``n_sb`` random MXFP4 superblocks as a flat uint8 array."""
+    lo, hi = MXFP4_SCALE_RANGE
+    blob = np.zeros((n_sb, MXFP4_SB_BYTES), dtype=np.uint8)
+    blob[:, 0:8] = rng.integers(lo, hi + 1, size=(n_sb, 8), dtype=np.uint8)
+    blob[:, 16:] = np.frombuffer(rng.bytes(n_sb * 128), dtype=np.uint8).reshape(n_sb, 128)
+    return blob.reshape(-1)
+
+
+def weight_blob(rng: np.random.Generator, n_sb: int, bits: int, fmt: int) -> np.ndarray:
+    """Superblocks of a layer's format: K-quant of ``bits`` bits, or MXFP4."""
+    return mxfp4_blob(rng, n_sb) if fmt == 1 else kquant_blob(rng, n_sb, bits)
+
+
 def _zipf_parts(shape: LayerShape, seed: int):
     """Unit vector v and per-expert offsets b (b_e = -beta * ln(rank_e))."""
     rv = _rng(seed, _S_ZIPF_V)
@@ -131,6 +166,7 @@ def make_layer(shape: LayerShape, seed: int, zipf: bool = False) -> Dict[str, np
     gate, up  uint8 [E][I*H/256*144]  4-bit superblocks, rows = I outputs, K = H
     down      uint8 [E][H*I/256*176]  5-bit superblocks, rows = H outputs, K = I
     sh_gate, sh_up, sh_down           the shared expert, same formats, width Is
+    (shape.fmt == 1: every matrix in 144-byte MXFP4 superblocks instead)
     """
     n_gu, n_d, n_sgu, n_sd = shape.sb_counts()
     wr = _rng(seed, _S_ROUTER).normal(0.0, 0.02, size=(shape.H, shape.E)).astype(np.float32)
@@ -138,8 +174,10 @@ def make_layer(shape: LayerShape, seed: int, zipf: bool = False) -> Dict[str, np
         v, b, _ = _zipf_parts(shape, seed)
         wr = (wr + np.outer(v, b)).astype(np.float32)
 
+    f = shape.fmt
+
     def stack(stream, n_sb, bits):
-        return np.stack([kquant_blob(_rng(seed, stream, e), n_sb, bits) for e in range(shape.E)])
+        return np.stack([weight_blob(_rng(seed, stream, e), n_sb, bits, f) for e in range(shape.E)])
 
     layer = {
         "router_w": np.ascontiguousarray(wr),
@@ -148,9 +186,9 @@ def make_layer(shape: LayerShape, seed: int, zipf: bool = False) -> Dict[str, np
         "down": stack(_S_DOWN, n_d, 5),
     }
     if shape.Is > 0:
-        layer["sh_gate"] = kquant_blob(_rng(seed, _S_SH_GATE), n_sgu, 4)
-        layer["sh_up"] = kquant_blob(_rng(seed, _S_SH_UP), n_sgu, 4)
-        layer["sh_down"] = kquant_blob(_rng(seed, _S_SH_DOWN), n_sd, 5)
+        layer["sh_gate"] = weight_blob(_rng(seed, _S_SH_GATE), n_sgu, 4, f)
+        layer["sh_up"] = weight_blob(_rng(seed, _S_SH_UP), n_sgu, 4, f)
+        layer["sh_down"] = weight_blob(_rng(seed, _S_SH_DOWN), n_sd, 5, f)
     return layer
 
 

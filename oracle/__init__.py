@@ -10,7 +10,9 @@ marshals numpy arrays into it.  See the header of ``moe_oracle.c`` for the
 passages of the pages each function follows and for the readings taken where
 they are silent.
 
-Pins (tests/test_oracle.py): a hand-worked superblock of each format, an
+Pins (tests/test_oracle.py): a hand-worked superblock of each format (the two
+K-quant ones and MXFP4, whose element values are also checked against the E2M1
+table of the OCP MX specification), an
 exhaustive closed-form sweep of every (scale, min, code) field, a brute-force
 sort for the router on tiny inputs with constructed ties, closed-form FFN cases
 (silu at +-ln 3, constant weights), a two-expert mixture with known softmax
@@ -46,7 +48,9 @@ class _Layer(ctypes.Structure):
                 ("I", ctypes.c_int32), ("Is", ctypes.c_int32), ("shared_weight", ctypes.c_float),
                 ("router_w", ctypes.c_void_p), ("gate", ctypes.c_void_p), ("up", ctypes.c_void_p),
                 ("down", ctypes.c_void_p), ("sh_gate", ctypes.c_void_p), ("sh_up", ctypes.c_void_p),
-                ("sh_down", ctypes.c_void_p)]
+                ("sh_down", ctypes.c_void_p), ("fmt", ctypes.c_int32)]
+
+SB_MXFP4 = 14   # oracle_dequant's code for the MXFP4 superblock
 
 
 def lib():
@@ -57,6 +61,10 @@ def lib():
         P = ctypes.c_void_p
         L.oracle_half_to_double.argtypes = [ctypes.c_uint16]
         L.oracle_half_to_double.restype = ctypes.c_double
+        L.oracle_e2m1.argtypes = [ctypes.c_int]
+        L.oracle_e2m1.restype = ctypes.c_double
+        L.oracle_e8m0.argtypes = [ctypes.c_int]
+        L.oracle_e8m0.restype = ctypes.c_double
         L.oracle_dequant.argtypes = [P, ctypes.c_int, ctypes.c_int64, P]
         L.oracle_router.argtypes = [P, ctypes.c_int, ctypes.c_int, P, ctypes.c_int, ctypes.c_int,
                                     P, P, P, P]
@@ -91,10 +99,19 @@ def max_threads() -> int:
     return lib().oracle_max_threads()
 
 
+def e2m1(code: int) -> float:
+    return lib().oracle_e2m1(code)
+
+
+def e8m0(s: int) -> float:
+    return lib().oracle_e8m0(s)
+
+
 def dequant(blob: np.ndarray, bits: int) -> np.ndarray:
-    """Decode a flat blob of superblocks into fp32 (flat order)."""
+    """Decode a flat blob of superblocks into fp32 (flat order); bits = 4 (Q4_K),
+    5 (Q5_K) or SB_MXFP4."""
     blob = np.ascontiguousarray(blob, dtype=np.uint8).reshape(-1)
-    sbb = 144 if bits == 4 else 176
+    sbb = 176 if bits == 5 else 144
     if blob.size % sbb:
         raise ValueError("blob size is not a whole number of superblocks")
     n_sb = blob.size // sbb
@@ -135,17 +152,18 @@ class Layer:
     """Host-side layer description for the oracle (keeps the arrays alive)."""
 
     def __init__(self, arrays: dict, H: int, E: int, k: int, I: int, Is: int,
-                 shared_weight: float = 1.0):
+                 shared_weight: float = 1.0, fmt: int = 0):
         self.arrays = {n: np.ascontiguousarray(a) for n, a in arrays.items()}
         a = self.arrays
         self.c = _Layer(H, E, k, I, Is, shared_weight, _p(a["router_w"]), _p(a["gate"]),
                         _p(a["up"]), _p(a["down"]), _p(a.get("sh_gate")), _p(a.get("sh_up")),
-                        _p(a.get("sh_down")))
-        self.H, self.E, self.k, self.I, self.Is = H, E, k, I, Is
+                        _p(a.get("sh_down")), fmt)
+        self.H, self.E, self.k, self.I, self.Is, self.fmt = H, E, k, I, Is, fmt
 
     @classmethod
     def from_shape(cls, arrays: dict, shape) -> "Layer":
-        return cls(arrays, shape.H, shape.E, shape.k, shape.I, shape.Is, shape.shared_weight)
+        return cls(arrays, shape.H, shape.E, shape.k, shape.I, shape.Is, shape.shared_weight,
+                   getattr(shape, "fmt", 0))
 
 
 def forward(layer: Layer, x: np.ndarray, idx: Optional[np.ndarray] = None,

@@ -29,6 +29,8 @@
  * fp32 at the end.  Weights are decoded exactly (see oracle_dequant).
  *
  * Readings where the pages are silent (each listed in the design notes):
+ *   - MXFP4 (section 1b): OCP MX element and scale encodings in a 144-byte
+ *     superblock of this project's layout.
  *   - K-quant byte layout: the GGUF-shaped 144-byte Q4_K / 176-byte Q5_K
  *     superblock (fp16 d, fp16 dmin, 12 bytes of packed 6-bit scales/mins,
  *     [Q5_K: 32 bytes of high code bits], 128 bytes of code nibbles);
@@ -130,16 +132,63 @@ static void dequant_sb(const uint8_t *sb, int bits, float *out)
     }
 }
 
-int oracle_sb_bytes(int bits) { return bits == 4 ? 144 : bits == 5 ? 176 : 0; }
+/* ------------------------------------------------------------------------ */
+/* 1b. MXFP4 superblocks                                                      */
+/* ------------------------------------------------------------------------ */
 
-/* Decode n_sb consecutive superblocks into out[n_sb*256] (flat order). */
+/* The page "Distributed CPU: Zip Fusion Beyond Tensor Parallelism" (section
+ * "Decode vs Prefill: Same Weights, Different Bottlenecks") says the model
+ * class targeted ships its packed weights in an MXFP4-class format, and names
+ * nothing more.  The element and scale encodings are read as those of the OCP
+ * Microscaling (MX) formats, v1.0: 32 elements share one E8M0 scale
+ * X = 2^(s - 127) (s = 255 encodes NaN), each element is FP4 E2M1 (sign bit,
+ * two exponent bits with bias 1, one mantissa bit; exponent 0 is subnormal),
+ * and an element's value is X times the element's.  The byte layout is this
+ * project's reading: a 144-byte superblock of 256 weights (8 MX blocks) --
+ * bytes 0..7 the scales of blocks 0..7, bytes 8..15 reserved (zero), bytes
+ * 16..143 the codes in the nibble order of the 4-bit K-quant superblock. */
+#define ORC_SB_MXFP4 14
+
+/* E2M1 code (0..15) -> its value. */
+double oracle_e2m1(int code)
+{
+    int sign = (code >> 3) & 1, e = (code >> 1) & 3, m = code & 1;
+    double v = e == 0 ? 0.5 * m                      /* subnormal: 2^(1-1) * m/2 */
+                      : ldexp(1.0 + 0.5 * m, e - 1); /* 2^(e-1) * (1 + m/2)      */
+    return sign ? -v : v;
+}
+
+/* E8M0 scale byte -> 2^(s-127); 255 is NaN. */
+double oracle_e8m0(int s) { return s == 255 ? NAN : ldexp(1.0, s - 127); }
+
+/* One MXFP4 superblock into 256 floats: element value times its block's
+ * scale, exact in double (a power of two times a 2-bit significand), rounded
+ * once to fp32 (exact unless outside fp32's range). */
+static void dequant_mx_sb(const uint8_t *sb, float *out)
+{
+    const uint8_t *qs = sb + 16;
+    for (int i = 0; i < 256; ++i)
+        out[i] = (float)(oracle_e2m1(code_of(qs, NULL, i)) * oracle_e8m0(sb[i / 32]));
+}
+
+int oracle_sb_bytes(int bits)
+{
+    return bits == 4 ? 144 : bits == 5 ? 176 : bits == ORC_SB_MXFP4 ? 144 : 0;
+}
+
+/* Decode n_sb consecutive superblocks into out[n_sb*256] (flat order);
+ * bits = 4 (Q4_K), 5 (Q5_K) or 14 (MXFP4). */
 int oracle_dequant(const uint8_t *blob, int bits, int64_t n_sb, float *out)
 {
     int sbb = oracle_sb_bytes(bits);
     if (!sbb || n_sb < 0 || (n_sb && (!blob || !out)))
         return ORC_EINVAL;
-    for (int64_t b = 0; b < n_sb; ++b)
-        dequant_sb(blob + b * sbb, bits, out + b * 256);
+    for (int64_t b = 0; b < n_sb; ++b) {
+        if (bits == ORC_SB_MXFP4)
+            dequant_mx_sb(blob + b * sbb, out + b * 256);
+        else
+            dequant_sb(blob + b * sbb, bits, out + b * 256);
+    }
     return ORC_OK;
 }
 
@@ -257,6 +306,7 @@ typedef struct {
     const float *router_w;                           /* [H][E] */
     const uint8_t *gate, *up, *down;                 /* [E] blobs */
     const uint8_t *sh_gate, *sh_up, *sh_down;        /* shared expert blobs */
+    int32_t fmt;       /* 0: Q4_K gate/up, Q5_K down; 1: MXFP4 all three */
 } oracle_layer;
 
 /* silu(z) = z * sigmoid(z), evaluated without overflow on either side. */
@@ -297,16 +347,16 @@ static void expert_ffn(const float *Wg, const float *Wu, const float *Wd,
 typedef struct { float *g, *u, *d; } decoded_expert;
 
 static int decode_expert(const uint8_t *g, const uint8_t *u, const uint8_t *d,
-                         int H, int I, decoded_expert *out)
+                         int H, int I, int fmt, decoded_expert *out)
 {
     int64_t n = (int64_t)H * I;
     out->g = malloc(sizeof(float) * n);
     out->u = malloc(sizeof(float) * n);
     out->d = malloc(sizeof(float) * n);
     if (!out->g || !out->u || !out->d) return ORC_ENOMEM;
-    oracle_dequant(g, 4, n / 256, out->g);
-    oracle_dequant(u, 4, n / 256, out->u);
-    oracle_dequant(d, 5, n / 256, out->d);
+    oracle_dequant(g, fmt ? ORC_SB_MXFP4 : 4, n / 256, out->g);
+    oracle_dequant(u, fmt ? ORC_SB_MXFP4 : 4, n / 256, out->u);
+    oracle_dequant(d, fmt ? ORC_SB_MXFP4 : 5, n / 256, out->d);
     return ORC_OK;
 }
 
@@ -370,7 +420,7 @@ static int forward_rows(const oracle_layer *L, const float *x, int T,
 {
     if (!L || T < 0 || L->k < 1 || L->k > L->E)
         return ORC_EINVAL;
-    if ((L->H * L->I) % 256 || (L->H * L->Is) % 256)
+    if ((L->H * L->I) % 256 || (L->H * L->Is) % 256 || L->fmt < 0 || L->fmt > 1)
         return ORC_EINVAL;
     if (T == 0)
         return ORC_OK;
@@ -405,10 +455,11 @@ static int forward_rows(const oracle_layer *L, const float *x, int T,
     for (int e = 0; e < E; ++e)
         if (used[e])
             fail |= decode_expert(L->gate + e * nsb * 144, L->up + e * nsb * 144,
-                                  L->down + e * nsb * 176, H, I, &dec[e]) != ORC_OK;
+                                  L->down + e * nsb * (L->fmt ? 144 : 176), H, I, L->fmt,
+                                  &dec[e]) != ORC_OK;
     free(used);
     if (!fail && Is > 0)
-        fail |= decode_expert(L->sh_gate, L->sh_up, L->sh_down, H, Is, &sh) != ORC_OK;
+        fail |= decode_expert(L->sh_gate, L->sh_up, L->sh_down, H, Is, L->fmt, &sh) != ORC_OK;
     if (fail) { rc = ORC_ENOMEM; goto done; }
 
     int amax = I > Is ? I : Is;

@@ -45,9 +45,23 @@ def read_fixture(path):
         key, rest = line.split(None, 1)
         if key.endswith("_w512"):
             out[key] = {int(a): int(b) for a, b in (t.split(":") for t in rest.split())}
+        elif key.endswith("_values"):
+            out[key] = {int(a): b for a, b in (t.split(":") for t in rest.split())}
         elif key.endswith("_bits"):
             out[key] = int(rest, 16)
         else:
             out.setdefault(key, b"")
             out[key] += bytes(int(t, 16) for t in rest.split())
     return out
+
+
+def pack_mx_sb(scales, q):
+    """One MXFP4 superblock from 8 E8M0 scale bytes and 256 codes (0..15), in the
+    layout of tests/golden/mxfp4_handworked.txt."""
+    q = [int(v) for v in q]
+    assert len(q) == 256 and all(0 <= v < 16 for v in q) and len(scales) == 8
+    qs = bytearray(128)
+    for c in range(4):
+        for l in range(32):
+            qs[32 * c + l] = q[64 * c + l] | (q[64 * c + 32 + l] << 4)
+    return np.frombuffer(bytes(scales) + bytes(8) + bytes(qs), dtype=np.uint8).copy()

@@ -72,3 +72,18 @@ def test_zipf_load_slope():
     xu = mi.make_tokens(u.shape, u.seed, 512)
     iu, _, _, _ = oracle.router(xu, lu["router_w"], u.shape.k)
     assert len(np.unique(iu)) >= 250
+
+
+def test_mxfp4_blob_fields():
+    blob = mi.mxfp4_blob(mi._rng(0, 98), 4096).reshape(4096, mi.MXFP4_SB_BYTES)
+    lo, hi = mi.MXFP4_SCALE_RANGE
+    sc = blob[:, 0:8]
+    assert sc.min() == lo and sc.max() == hi
+    assert np.all(blob[:, 8:16] == 0)
+    codes = np.concatenate([blob[:, 16:] & 15, blob[:, 16:] >> 4]).ravel()
+    counts = np.bincount(codes, minlength=16)
+    assert counts.min() > 0.9 * codes.size / 16 and counts.max() < 1.1 * codes.size / 16
+    layer = mi.make_layer(mi.TINY_MX, 5)
+    assert layer["gate"].shape == (8, 128 * 256 // 256 * 144)
+    assert layer["down"].shape == (8, 256 * 128 // 256 * 144)
+    assert layer["sh_down"].shape == (256 * 128 // 256 * 144,)

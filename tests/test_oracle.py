@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 import oracle
-from kquant_pack import pack_sb, read_fixture
+from kquant_pack import pack_mx_sb, pack_sb, read_fixture
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "kquant_handworked.txt")
 FX = read_fixture(GOLDEN)
@@ -467,3 +467,98 @@ def test_uneven_shard_ranges_sum_to_whole(cuts):
         assert np.array_equal(parts[0], oracle.forward(L, x, idx, w, 0, 2, want_double=True)[1])
     # an empty range contributes nothing
     assert not np.any(oracle.forward_range(L, x, idx, w, 64, 64))
+
+
+# --------------------------------------------------------------------------
+# MXFP4 superblocks
+# --------------------------------------------------------------------------
+
+MX_GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "mxfp4_handworked.txt")
+MX = read_fixture(MX_GOLDEN)
+MX_SCALES = [127, 126, 128, 121, 130, 113, 125, 140]
+# FP4 E2M1 values of codes 0..15 as the OCP MX specification tabulates them
+E2M1_TABLE = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0,
+              -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0]
+
+
+def _mx_blob():
+    return np.frombuffer(MX["scales"] + MX["reserved"] + MX["mx_qs"], np.uint8)
+
+
+def test_e2m1_matches_the_spec_table():
+    for code, v in enumerate(E2M1_TABLE):
+        got = oracle.e2m1(code)
+        assert got == v and math.copysign(1.0, got) == math.copysign(1.0, v), code
+
+
+def test_e8m0_scales():
+    assert oracle.e8m0(127) == 1.0
+    assert oracle.e8m0(120) == 1.0 / 128
+    assert oracle.e8m0(140) == 8192.0
+    assert oracle.e8m0(0) == 2.0 ** -127
+    assert oracle.e8m0(254) == 2.0 ** 127
+    assert math.isnan(oracle.e8m0(255))
+
+
+def test_mx_packer_matches_fixture():
+    q = _q4_codes()   # i mod 16 in even sub-blocks, 15 - (i mod 16) in odd ones
+    assert MX["scales"] == bytes(MX_SCALES) and MX["reserved"] == bytes(8)
+    assert pack_mx_sb(MX_SCALES, q).tobytes() == _mx_blob().tobytes()
+
+
+def test_handworked_mxfp4():
+    w = oracle.dequant(_mx_blob(), oracle.SB_MXFP4)
+    for i, v in MX["mx_values"].items():
+        ref = float(Fraction(v))
+        assert w[i] == np.float32(ref), (i, w[i], v)
+        if v.startswith("-"):
+            assert np.signbit(w[i]), i          # -0 keeps its sign
+    # every element: the spec's table value of its code times its block's
+    # power of two (exact fractions)
+    q = _q4_codes()
+    expect = np.array([float(Fraction(E2M1_TABLE[q[i]]) * Fraction(2) ** (MX_SCALES[i // 32] - 127))
+                       for i in range(256)], np.float32)
+    assert np.array_equal(w, expect)
+
+
+def test_mx_every_code_and_scale():
+    """Each (code, scale byte) pair in one block: table value times 2^(s-127),
+    for every scale byte whose products stay normal in fp32."""
+    for s in list(range(1, 120, 7)) + list(range(120, 141)) + list(range(141, 250, 9)):
+        q = list(range(16)) * 16
+        w = oracle.dequant(pack_mx_sb([s] * 8, q), oracle.SB_MXFP4)
+        expect = np.array([float(Fraction(E2M1_TABLE[c]) * Fraction(2) ** (s - 127)) for c in q],
+                          np.float32)
+        assert np.array_equal(w, expect), s
+
+
+def test_mx_dense_ffn_special_case():
+    """E=1, k=1, no shared expert, MXFP4 weights: a dense SwiGLU FFN on the
+    decoded weights (numpy float64)."""
+    import moe_inputs as mi
+    shp = mi.LayerShape(H=256, E=1, k=1, I=128, Is=0, fmt=1)
+    arrays = mi.make_layer(shp, seed=12)
+    assert arrays["down"].shape == (1, 256 * 128 // 256 * mi.MXFP4_SB_BYTES)
+    L = oracle.Layer.from_shape(arrays, shp)
+    x = mi.make_tokens(shp, 12, 3)
+    o = oracle.forward(L, x)
+    Wg = oracle.dequant(arrays["gate"][0], oracle.SB_MXFP4).reshape(128, 256).astype(np.float64)
+    Wu = oracle.dequant(arrays["up"][0], oracle.SB_MXFP4).reshape(128, 256).astype(np.float64)
+    Wd = oracle.dequant(arrays["down"][0], oracle.SB_MXFP4).reshape(256, 128).astype(np.float64)
+    g = x.astype(np.float64) @ Wg.T
+    u = x.astype(np.float64) @ Wu.T
+    ref = ((g / (1 + np.exp(-g))) * u) @ Wd.T
+    assert np.allclose(o, ref, rtol=1e-6, atol=1e-6 * np.abs(ref).max())
+
+
+def test_mx_shard_partials_sum_to_whole():
+    """An MXFP4 layer's shard partials add up to the whole layer."""
+    import moe_inputs as mi
+    layer, x = mi.workload_inputs("tiny_mx")
+    Lmx = oracle.Layer.from_shape(layer, mi.TINY_MX)
+    idx, w, _, _ = oracle.router(x, layer["router_w"], mi.TINY_MX.k)
+    _, full = oracle.forward(Lmx, x, idx, w, want_double=True)
+    parts = [oracle.forward(Lmx, x, idx, w, s, 2, want_double=True)[1] for s in range(2)]
+    rms = np.sqrt(np.mean(full ** 2))
+    assert rms > 0 and np.all(np.isfinite(full))
+    assert np.abs(sum(parts) - full).max() <= 1e-12 * rms
