@@ -47,6 +47,22 @@
  *   A matrix is stored one row per output feature with the reduction
  *   dimension K contiguous, its flat row-major array cut into superblocks
  *   (a superblock may hold several rows when K < 256).
+ *
+ * Second weight format, MXFP4 (moe_layer_desc.weight_format = MOE_WFMT_MXFP4;
+ * the page "Distributed CPU: Zip Fusion Beyond Tensor Parallelism", section
+ * "Decode vs Prefill: Same Weights, Different Bottlenecks", says the model
+ * class targeted ships an MXFP4-class format; the encodings are those of the
+ * OCP Microscaling formats v1.0, the byte layout is this library's):
+ *     MXFP4, 144 bytes: 8 bytes E8M0 scales | 8 bytes reserved | 128 bytes qs
+ *   Sub-block j (32 weights) has the scale X_j = 2^(scales[j] - 127); codes
+ *   are FP4 E2M1 (bit 3 sign, bits 2..1 exponent e with bias 1, bit 0
+ *   mantissa m: e = 0 gives m/2, else 2^(e-1) * (1 + m/2)) in the nibble
+ *   order above; w = X_j * value(code).  Gate, up and down (and the shared
+ *   expert) all use it; every matrix has I*H/256 superblocks of 144 bytes.
+ *   The fp32 paths decode exactly for scale bytes 2..254 (smaller ones give
+ *   fp32 subnormals, larger products overflow to inf); the MFMA path's fp16
+ *   operands are exact for scale bytes 114..128 (outside that range weights
+ *   round, underflow or overflow in fp16; not checked at run time).
  */
 #ifndef MOE_HIP_H
 #define MOE_HIP_H
@@ -58,7 +74,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 
 /* Status codes returned by every entry point. */
 #define MOE_OK 0
@@ -67,6 +83,10 @@ extern "C" {
 #define MOE_EWORKSPACE (-3)    /* workspace smaller than moe_workspace_bytes() */
 #define MOE_ELAUNCH (-4)       /* a kernel launch failed (hipGetLastError) */
 #define MOE_ENODEVICE (-5)     /* no gfx950 device is current */
+
+/* Weight formats (moe_layer_desc.weight_format). */
+#define MOE_WFMT_KQUANT 0      /* Q4_K gate/up, Q5_K down */
+#define MOE_WFMT_MXFP4 1       /* MXFP4 gate, up and down */
 
 /* Compute paths (moe_opts.path). */
 #define MOE_PATH_AUTO 0        /* GEMV for T <= 14, grouped MFMA GEMM above (measured crossover) */
@@ -87,6 +107,8 @@ extern "C" {
  *   down_q        Q5_K, E consecutive matrices of [H rows][I] (H*I/256 superblocks each)
  *   sh_gate_q, sh_up_q, sh_down_q  the shared expert, same formats, width Is
  *                 (may be NULL when Is = 0)
+ *   weight_format MOE_WFMT_KQUANT (the formats above) or MOE_WFMT_MXFP4 (every
+ *                 matrix in 144-byte MXFP4 superblocks); anything else: -1
  * Every weight pointer must be 16-byte aligned; router_w and token buffers
  * 16-byte aligned as well.
  */
@@ -96,6 +118,7 @@ typedef struct moe_layer_desc {
     const float *router_w;
     const uint8_t *gate_q, *up_q, *down_q;
     const uint8_t *sh_gate_q, *sh_up_q, *sh_down_q;
+    int32_t weight_format;
 } moe_layer_desc;
 
 /* Options.  `path` forces a compute path (MOE_PATH_*); `path_used`, a HOST
@@ -259,11 +282,13 @@ int moe_rmsnorm_apply(const float *x, int32_t T, int32_t cols, int64_t ldx,
                       float eps, float *y, int64_t ldy, void *stream);
 
 /*
- * Test hook: decode n_sb superblocks (bits = 4: Q4_K, 5: Q5_K) into
- * n_sb*256 values in flat order.  out_dtype 0: fp32 (exactly the
- * round-to-nearest-even fp32 value of d*sc*q - dmin*m); 1: bf16 and 2: fp16,
+ * Test hook: decode n_sb superblocks (bits = 4: Q4_K, 5: Q5_K,
+ * MOE_SB_MXFP4: MXFP4) into n_sb*256 values in flat order.  out_dtype 0: fp32
+ * (exactly the round-to-nearest-even fp32 value of d*sc*q - dmin*m, or of
+ * X_j * value(code); MXFP4 scale byte 255 gives NaN); 1: bf16 and 2: fp16,
  * each the round-to-nearest-even conversion of that fp32 value.
  */
+#define MOE_SB_MXFP4 14
 int moe_dequant(const uint8_t *sbs, int32_t bits, int64_t n_sb, int32_t out_dtype,
                 void *out, void *stream);
 

@@ -17,6 +17,8 @@ LIB_PATH = os.path.join(HERE, "libmoe_hip.so")
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_ELAUNCH, MOE_ENODEVICE = 0, -1, -2, -3, -4, -5
 MOE_PATH_AUTO, MOE_PATH_GEMV, MOE_PATH_MFMA = 0, 1, 2
+MOE_WFMT_KQUANT, MOE_WFMT_MXFP4 = 0, 1
+MOE_SB_MXFP4 = 14
 # kernel ids for moe_opts.kernel_events (include/moe.h MOE_K_*)
 KERNEL_IDS = {"gemv_front": 0, "router_mfma": 1, "router_topk": 2, "gateup_gemv": 3,
               "down_gemv": 4, "x_f16": 5, "bucket_hist": 6, "bucket_scan": 7, "bucket_scatter": 8,
@@ -37,7 +39,7 @@ class moe_layer_desc(ctypes.Structure):
                 ("router_w", ctypes.c_void_p), ("gate_q", ctypes.c_void_p),
                 ("up_q", ctypes.c_void_p), ("down_q", ctypes.c_void_p),
                 ("sh_gate_q", ctypes.c_void_p), ("sh_up_q", ctypes.c_void_p),
-                ("sh_down_q", ctypes.c_void_p)]
+                ("sh_down_q", ctypes.c_void_p), ("weight_format", ctypes.c_int32)]
 
 
 class moe_opts(ctypes.Structure):
@@ -111,11 +113,12 @@ def moe_status_str(status: int) -> str:
 
 
 def make_desc(hidden, n_experts, top_k, inter, shared_inter, shared_weight, router_w, gate_q,
-              up_q, down_q, sh_gate_q=None, sh_up_q=None, sh_down_q=None) -> moe_layer_desc:
+              up_q, down_q, sh_gate_q=None, sh_up_q=None, sh_down_q=None,
+              weight_format=MOE_WFMT_KQUANT) -> moe_layer_desc:
     """A descriptor over device tensors (the caller keeps the tensors alive)."""
     return moe_layer_desc(hidden, n_experts, top_k, inter, shared_inter, shared_weight,
                           _ptr(router_w), _ptr(gate_q), _ptr(up_q), _ptr(down_q),
-                          _ptr(sh_gate_q), _ptr(sh_up_q), _ptr(sh_down_q))
+                          _ptr(sh_gate_q), _ptr(sh_up_q), _ptr(sh_down_q), weight_format)
 
 
 def moe_workspace_bytes(desc: moe_layer_desc, T: int, num_shards: int = 1) -> int:

@@ -13,23 +13,30 @@ namespace moe {
 
 // One workgroup (256 threads) per superblock, thread i decodes element i:
 // element 64c+l is the low nibble of qs[32c+l], 64c+32+l its high nibble;
-// the 5-bit format adds 16 * bit (2c or 2c+1) of qh[l].
+// the 5-bit format adds 16 * bit (2c or 2c+1) of qh[l]; MXFP4 reads the code
+// as E2M1 and scales it by its sub-block's E8M0 byte.
 __global__ void __launch_bounds__(256)
 dequant_kernel(const uint8_t* __restrict__ sbs, int bits, int64_t n_sb, int out_dtype,
                void* __restrict__ out) {
     const int i = threadIdx.x;
     const int c = i >> 6, r = i & 63, l = r & 31, upper = r >> 5;
-    const int sbb = bits == 4 ? kQ4Bytes : kQ5Bytes;
+    const int sbb = bits == 5 ? kQ5Bytes : kQ4Bytes;   // Q4_K and MXFP4: 144 bytes
     for (int64_t b = blockIdx.x; b < n_sb; b += gridDim.x) {
         const uint8_t* sb = sbs + b * sbb;
-        const SbHead hd = load_head(sb);
-        float sc, m;
-        sub_scale_min(hd, i >> 5, sc, m);
-        const uint8_t* qs = sb + (bits == 4 ? 16 : 48);
+        const uint8_t* qs = sb + (bits == 5 ? 48 : 16);
         const uint32_t byte = qs[32 * c + l];
         uint32_t q = upper ? (byte >> 4) : (byte & 15u);
-        if (bits == 5) q |= ((uint32_t)(sb[16 + l] >> (2 * c + upper)) & 1u) << 4;
-        const float wv = kq_weight(hd.d * sc, hd.dmin * m, (float)q);
+        float wv;
+        if (bits == MOE_SB_MXFP4) {
+            // MXFP4: the code's value times its sub-block's power of two
+            wv = e2m1_f32(q) * e8m0_f32(sb[i >> 5]);
+        } else {
+            const SbHead hd = load_head(sb);
+            float sc, m;
+            sub_scale_min(hd, i >> 5, sc, m);
+            if (bits == 5) q |= ((uint32_t)(sb[16 + l] >> (2 * c + upper)) & 1u) << 4;
+            wv = kq_weight(hd.d * sc, hd.dmin * m, (float)q);
+        }
         const int64_t o = b * kSbWeights + i;
         if (out_dtype == 0)
             reinterpret_cast<float*>(out)[o] = wv;
@@ -160,6 +167,7 @@ static int check_desc(const moe_layer_desc* d) {
     if (d->top_k > 16 || d->top_k > d->n_experts) return MOE_EINVAL;
     if (!d->router_w || !d->gate_q || !d->up_q || !d->down_q) return MOE_EINVAL;
     if (d->shared_inter > 0 && (!d->sh_gate_q || !d->sh_up_q || !d->sh_down_q)) return MOE_EINVAL;
+    if (d->weight_format != MOE_WFMT_KQUANT && d->weight_format != MOE_WFMT_MXFP4) return MOE_EINVAL;
     const int nsb = d->hidden / kSbWeights;
     if (d->hidden % kSbWeights || !(nsb == 1 || nsb == 2 || nsb == 4 || nsb == 8 || nsb == 16))
         return MOE_EUNSUPPORTED;
@@ -393,7 +401,9 @@ int moe_rmsnorm_apply(const float* x, int32_t T, int32_t cols, int64_t ldx,
 
 int moe_dequant(const uint8_t* sbs, int32_t bits, int64_t n_sb, int32_t out_dtype, void* out,
                 void* stream) {
-    if ((bits != 4 && bits != 5) || n_sb < 0 || out_dtype < 0 || out_dtype > 2) return MOE_EINVAL;
+    if ((bits != 4 && bits != 5 && bits != MOE_SB_MXFP4) || n_sb < 0 || out_dtype < 0 ||
+        out_dtype > 2)
+        return MOE_EINVAL;
     if (n_sb == 0) return MOE_OK;
     if (!sbs || !out) return MOE_EINVAL;
     if (!al16(sbs)) return MOE_EUNSUPPORTED;

@@ -17,6 +17,9 @@
 //           From Splitting Tokens To Splitting Qwen3.5 Weights", section "A
 //           Separate Decode Result Shows Why Axis Choice Matters").
 //
+// Both weight formats (K-quant and MXFP4) run through the same kernels,
+// templated on the format; only the piece decode and the superblock size differ.
+//
 // Work unit of a lane: a 16-byte piece of a superblock's codes -- 32 weights,
 // 16 from sub-block 2c and 16 from sub-block 2c+1 -- plus the superblock's
 // 16-byte head (and, at 5 bits, the matching 16 bytes of high bits).  Eight
@@ -71,6 +74,56 @@ __device__ __forceinline__ float piece_dot(const SbHead& h, const uint4& qs, con
         }
     }
     return h.d * (sca * dl + scb * dh) - h.dmin * (ma * sl + mb * sh);
+}
+
+// The same for an MXFP4 piece: 16 codes of sub-block 2c (low nibbles, under
+// xl) and 16 of sub-block 2c+1 (high nibbles, under xh).  Each sub-block's
+// scale is a power of two and factors out of its sum:
+//   sum_i w_i x_i = X_2c * sum(value(q) x)_lo + X_2c+1 * sum(value(q) x)_hi
+// s0 / s1: scale bytes 0..3 / 4..7 of the superblock.
+__device__ __forceinline__ float piece_dot_mx(uint32_t s0, uint32_t s1, const uint4& qs, int c,
+                                              const float* xl, const float* xh) {
+    const uint32_t sw = c < 2 ? s0 : s1;
+    const int sh = 16 * (c & 1);
+    const float xa = e8m0_f32((sw >> sh) & 0xffu), xb = e8m0_f32((sw >> (sh + 8)) & 0xffu);
+    const uint32_t qw[4] = {qs.x, qs.y, qs.z, qs.w};
+    float dl = 0.f, dh = 0.f;
+#pragma unroll
+    for (int wi = 0; wi < 4; ++wi) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const uint32_t byte = qw[wi] >> (8 * b);
+            dl = __builtin_fmaf(e2m1_f32(byte), xl[4 * wi + b], dl);
+            dh = __builtin_fmaf(e2m1_f32(byte >> 4), xh[4 * wi + b], dh);
+        }
+    }
+    return xa * dl + xb * dh;
+}
+
+// A superblock's 16-byte head for either format: K-quant d, dmin and scale
+// words; MXFP4 its eight scale bytes as s0, s1.
+template <int FMT>
+__device__ __forceinline__ SbHead load_head_f(const uint8_t* sb) {
+    if constexpr (FMT == MOE_WFMT_MXFP4) {
+        const uint4 v = *reinterpret_cast<const uint4*>(sb);
+        SbHead h;
+        h.d = h.dmin = 0.f;
+        h.s0 = v.x;
+        h.s1 = v.y;
+        h.s2 = 0u;
+        return h;
+    } else {
+        return load_head(sb);
+    }
+}
+
+template <int FMT, bool HIGH>
+__device__ __forceinline__ float piece_dot_f(const SbHead& h, const uint4& qs, const uint4& qh, int c,
+                                             const float* xl, const float* xh, float sl, float sh) {
+    if constexpr (FMT == MOE_WFMT_MXFP4)
+        return piece_dot_mx(h.s0, h.s1, qs, c, xl, xh);
+    else
+        return piece_dot<HIGH>(h, qs, qh, c, xl, xh, sl, sh);
 }
 
 __device__ __forceinline__ void load16(const float* p, float* v) {
@@ -160,7 +213,7 @@ struct XRegs {
 // LPR: lanes per row (8 * superblocks per row, capped at 64); NSBL:
 // superblocks per lane per row (H / 2048 when LPR = 64, else 1).
 // Rows [rbase, rbase + STEPS * 64/LPR) of the instance, h written to hrow.
-template <int LPR, int NSBL, int STEPS>
+template <int FMT, int LPR, int NSBL, int STEPS>
 __device__ __forceinline__ void gateup_rows(const uint8_t* __restrict__ G,
                                             const uint8_t* __restrict__ U, int H, int Iloc,
                                             int i0, XRegs<LPR, NSBL>& X, int rbase,
@@ -184,8 +237,8 @@ __device__ __forceinline__ void gateup_rows(const uint8_t* __restrict__ G,
             const uint8_t* us = U + (row + sb) * kQ4Bytes;
             qg[st][it] = stream_load(gs + 16 + 32 * c + 16 * hh);
             qu[st][it] = stream_load(us + 16 + 32 * c + 16 * hh);
-            hg[st][it] = load_head(gs);
-            hu[st][it] = load_head(us);
+            hg[st][it] = load_head_f<FMT>(gs);
+            hu[st][it] = load_head_f<FMT>(us);
         }
     }
     X.sums();
@@ -199,8 +252,8 @@ __device__ __forceinline__ void gateup_rows(const uint8_t* __restrict__ G,
         float pg = 0.f, pu = 0.f;
 #pragma unroll
         for (int it = 0; it < NSBL; ++it) {
-            pg += piece_dot<false>(hg[st][it], qg[st][it], qg[st][it], c, xl[it], xh[it], sl[it], sh[it]);
-            pu += piece_dot<false>(hu[st][it], qu[st][it], qu[st][it], c, xl[it], xh[it], sl[it], sh[it]);
+            pg += piece_dot_f<FMT, false>(hg[st][it], qg[st][it], qg[st][it], c, xl[it], xh[it], sl[it], sh[it]);
+            pu += piece_dot_f<FMT, false>(hu[st][it], qu[st][it], qu[st][it], c, xl[it], xh[it], sl[it], sh[it]);
         }
         v[2 * st] = pg;
         v[2 * st + 1] = pu;
@@ -234,6 +287,7 @@ struct GemvArgs {
     const float* router_w;
     const float* x;
     int T, H, E, k, I, Is, nslot;
+    int fmt;              // MOE_WFMT_*
     int i0, iloc;         // intermediate rows [i0, i0 + iloc) of every expert
     float sw;
     const int32_t* idx;   // routing read by gateup (when given) and by down
@@ -329,7 +383,7 @@ __device__ __forceinline__ void router_role(const GemvArgs& a, int rb) {
     }
 }
 
-template <int LPR, int NSBL, int TT>
+template <int FMT, int LPR, int NSBL, int TT>
 __global__ void __launch_bounds__(256)
 gemv_front_kernel(GemvArgs a) {
     const int b = blockIdx.x;
@@ -350,12 +404,12 @@ gemv_front_kernel(GemvArgs a) {
     const int p = t * a.nslot + a.k;
     XRegs<LPR, NSBL> X;
     X.load(a.x + (size_t)t * a.H);
-    gateup_rows<LPR, NSBL, kShSteps>(a.sh_gate, a.sh_up, a.H, Iloc, i0, X, rbase,
+    gateup_rows<FMT, LPR, NSBL, kShSteps>(a.sh_gate, a.sh_up, a.H, Iloc, i0, X, rbase,
                                      a.hbuf + (size_t)p * a.hstride);
 }
 
 // routed experts: grid (row blocks, T*k)
-template <int LPR, int NSBL>
+template <int FMT, int LPR, int NSBL>
 __global__ void __launch_bounds__(64 * kGuWaves)
 gemv_gateup_kernel(GemvArgs a) {
     const int q = blockIdx.y;
@@ -382,14 +436,14 @@ gemv_gateup_kernel(GemvArgs a) {
         e = a.idx[(size_t)t * a.k + j];
     }
     if ((unsigned)e >= (unsigned)a.E) return;
-    const size_t mat = (size_t)a.I * a.H / kSbWeights * kQ4Bytes;
+    const size_t mat = (size_t)a.I * a.H / kSbWeights * kQ4Bytes;   // MXFP4: the same size
     const int Iloc = a.iloc, i0 = a.i0;
     const int wave = threadIdx.x >> 6;
     constexpr int rows_per_wave = kGuSteps * (64 / LPR);
     const int rbase = (blockIdx.x * kGuWaves + wave) * rows_per_wave;
     if (rbase >= Iloc) return;
     const int p = t * a.nslot + j;
-    gateup_rows<LPR, NSBL, kGuSteps>(a.gate + (size_t)e * mat, a.up + (size_t)e * mat, a.H, Iloc,
+    gateup_rows<FMT, LPR, NSBL, kGuSteps>(a.gate + (size_t)e * mat, a.up + (size_t)e * mat, a.H, Iloc,
                                      i0, X, rbase, a.hbuf + (size_t)p * a.hstride);
 }
 
@@ -403,8 +457,10 @@ constexpr int kDnPasses = 2;   // row passes per wave in the down kernel
 // kDnPasses * (64 / lprd) output rows of one token.  A row's I_loc inputs are
 // I_loc / 32 lane tasks of 32 (a 16-byte code piece each); lprd, the lanes per
 // row, is that count rounded up to a power of two, the extra lanes adding 0.
+template <int FMT>
 __global__ void __launch_bounds__(1024)
 gemv_down_kernel(GemvArgs a, int lprd) {
+    constexpr int SBB = FMT == MOE_WFMT_MXFP4 ? kMxBytes : kQ5Bytes;
     __shared__ float ys[17][kDnPasses * 64];
     __shared__ float s_wt[17];   // each slot's weight (0 for an invalid expert)
     const int t = blockIdx.y;
@@ -425,7 +481,7 @@ gemv_down_kernel(GemvArgs a, int lprd) {
             const int e = a.idx[(size_t)t * a.k + j];
             wj = a.w[(size_t)t * a.k + j];
             valid = (unsigned)e < (unsigned)a.E;
-            D = a.down + (size_t)(valid ? e : 0) * ((size_t)H * a.I / kSbWeights * kQ5Bytes);
+            D = a.down + (size_t)(valid ? e : 0) * ((size_t)H * a.I / kSbWeights * SBB);
             Iexp = a.I;
         } else {
             wj = a.sw;
@@ -442,10 +498,15 @@ gemv_down_kernel(GemvArgs a, int lprd) {
             const int o = min(obase + ps * rs + rslot, H - 1);
             const size_t base = (size_t)o * Iexp + i0 + 64 * cg;
             cc[ps] = (int)((base & 255) >> 6);
-            const uint8_t* sb = D + (base >> 8) * kQ5Bytes;
-            qs[ps] = stream_load(sb + 48 + 32 * cc[ps] + 16 * hh);
-            qh[ps] = stream_load(sb + 16 + 16 * hh);
-            hd[ps] = load_head(sb);
+            const uint8_t* sb = D + (base >> 8) * SBB;
+            if (FMT == MOE_WFMT_MXFP4) {
+                qs[ps] = stream_load(sb + 16 + 32 * cc[ps] + 16 * hh);
+                qh[ps] = qs[ps];
+            } else {
+                qs[ps] = stream_load(sb + 48 + 32 * cc[ps] + 16 * hh);
+                qh[ps] = stream_load(sb + 16 + 16 * hh);
+            }
+            hd[ps] = load_head_f<FMT>(sb);
         }
         const float* hp = a.hbuf + (size_t)(t * a.nslot + j) * a.hstride + 64 * cg + 16 * hh;
         float hl[16], hu[16];
@@ -460,7 +521,7 @@ gemv_down_kernel(GemvArgs a, int lprd) {
 #pragma unroll
         for (int ps = 0; ps < kDnPasses; ++ps) {
             const float part =
-                active ? piece_dot<true>(hd[ps], qs[ps], qh[ps], cc[ps], hl, hu, sa, sb2) : 0.f;
+                active ? piece_dot_f<FMT, true>(hd[ps], qs[ps], qh[ps], cc[ps], hl, hu, sa, sb2) : 0.f;
             const float y = wave_sum_group(part, lprd);
             if (task == 0) ys[j][ps * rs + rslot] = valid ? y : 0.f;
         }
@@ -501,16 +562,25 @@ static GemvArgs base_args(const moe_layer_desc& d, const float* x, int T, int i0
     a.iloc = iloc;
     a.nslot = d.top_k + (d.shared_inter > 0 ? 1 : 0);
     a.sw = d.shared_weight;
+    a.fmt = d.weight_format;
     return a;
+}
+
+template <int FMT, int LPR, int NSBL>
+static void launch_front_f(const GemvArgs& a, int n_shared_blocks, const Ctx& c) {
+    const dim3 grid(a.n_router_blocks + n_shared_blocks);
+    if (a.T == 1)
+        launch_k(c, MOE_K_GEMV_FRONT, gemv_front_kernel<FMT, LPR, NSBL, 1>, grid, dim3(256), 0, a);
+    else
+        launch_k(c, MOE_K_GEMV_FRONT, gemv_front_kernel<FMT, LPR, NSBL, 4>, grid, dim3(256), 0, a);
 }
 
 template <int LPR, int NSBL>
 static void launch_front_t(const GemvArgs& a, int n_shared_blocks, const Ctx& c) {
-    const dim3 grid(a.n_router_blocks + n_shared_blocks);
-    if (a.T == 1)
-        launch_k(c, MOE_K_GEMV_FRONT, gemv_front_kernel<LPR, NSBL, 1>, grid, dim3(256), 0, a);
+    if (a.fmt == MOE_WFMT_MXFP4)
+        launch_front_f<MOE_WFMT_MXFP4, LPR, NSBL>(a, n_shared_blocks, c);
     else
-        launch_k(c, MOE_K_GEMV_FRONT, gemv_front_kernel<LPR, NSBL, 4>, grid, dim3(256), 0, a);
+        launch_front_f<MOE_WFMT_KQUANT, LPR, NSBL>(a, n_shared_blocks, c);
 }
 
 template <int LPR, int NSBL>
@@ -518,7 +588,12 @@ static void launch_gateup_t(const GemvArgs& a, const Ctx& c) {
     constexpr int rows_per_block = kGuWaves * kGuSteps * (64 / LPR);
     const int Iloc = a.iloc;
     const dim3 grid((Iloc + rows_per_block - 1) / rows_per_block, a.T * a.k);
-    launch_k(c, MOE_K_GATEUP_GEMV, gemv_gateup_kernel<LPR, NSBL>, grid, dim3(64 * kGuWaves), 0, a);
+    if (a.fmt == MOE_WFMT_MXFP4)
+        launch_k(c, MOE_K_GATEUP_GEMV, gemv_gateup_kernel<MOE_WFMT_MXFP4, LPR, NSBL>, grid,
+                 dim3(64 * kGuWaves), 0, a);
+    else
+        launch_k(c, MOE_K_GATEUP_GEMV, gemv_gateup_kernel<MOE_WFMT_KQUANT, LPR, NSBL>, grid,
+                 dim3(64 * kGuWaves), 0, a);
 }
 
 #define MOE_DISPATCH_H(nsb, F, ...)                                  \
@@ -596,7 +671,10 @@ hipError_t launch_gemv(const moe_layer_desc& d, const float* x, int T, const int
     const int rows_per_block = kDnPasses * (64 / lprd);
     const int nw = a.nslot < 16 ? a.nslot : 16;
     const dim3 grid2((d.hidden + rows_per_block - 1) / rows_per_block, T);
-    launch_k(c, MOE_K_DOWN_GEMV, gemv_down_kernel, grid2, dim3(64 * nw), 0, a, lprd);
+    if (a.fmt == MOE_WFMT_MXFP4)
+        launch_k(c, MOE_K_DOWN_GEMV, gemv_down_kernel<MOE_WFMT_MXFP4>, grid2, dim3(64 * nw), 0, a, lprd);
+    else
+        launch_k(c, MOE_K_DOWN_GEMV, gemv_down_kernel<MOE_WFMT_KQUANT>, grid2, dim3(64 * nw), 0, a, lprd);
     return hipGetLastError();
 }
 

@@ -17,6 +17,7 @@ namespace moe {
 constexpr int kWave = 64;
 constexpr int kQ4Bytes = 144;   // 4-bit K-quant superblock
 constexpr int kQ5Bytes = 176;   // 5-bit K-quant superblock
+constexpr int kMxBytes = 144;   // MXFP4 superblock (8 scale bytes, 8 reserved, 128 code bytes)
 constexpr int kSbWeights = 256;
 // router: split-K fp32 partials on the vector units up to this many rows (the
 // GEMV path folds them into its first kernel), the matrix-core router beyond
@@ -84,6 +85,26 @@ __device__ __forceinline__ void sub_scale_min(const SbHead& h, int j, float& sc,
 // so the result is the round-to-nearest-even fp32 of the real weight.
 __device__ __forceinline__ float kq_weight(float dsc, float dmm, float q) {
     return __builtin_fmaf(q, dsc, -dmm);
+}
+
+// ---------------------------------------------------------------------------
+// MXFP4 field decoding (device): OCP MX E8M0 block scales and E2M1 codes
+// ---------------------------------------------------------------------------
+
+// E8M0 scale byte s -> 2^(s-127), exact in fp32 (255: NaN; 0: 2^-127, a
+// subnormal).
+__device__ __forceinline__ float e8m0_f32(uint32_t s) {
+    return s == 255u ? __builtin_nanf("")
+                     : __uint_as_float(s == 0u ? 0x00400000u : (s << 23));
+}
+
+// E2M1 code (bits 0..3 of n) -> its value: magnitude m/2 for exponent 0,
+// else 2^(e-1) * (1 + m/2), whose fp32 pattern is 0x3F000000 + (e,m) << 22;
+// bit 3 is the sign.
+__device__ __forceinline__ float e2m1_f32(uint32_t n) {
+    const uint32_t em = n & 7u;
+    const float mag = em >= 2u ? __uint_as_float(0x3F000000u + (em << 22)) : 0.5f * (float)em;
+    return __uint_as_float(__float_as_uint(mag) | ((n & 8u) << 28));
 }
 
 // Code of byte b (0..15) of a 16-byte piece held as 4 words: low nibble.

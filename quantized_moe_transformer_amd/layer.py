@@ -13,9 +13,10 @@ class DeviceLayer:
     and keeps the C descriptor that points at them."""
 
     def __init__(self, arrays: Dict[str, np.ndarray], H: int, E: int, k: int, I: int, Is: int,
-                 shared_weight: float = 1.0, device: str = "cuda"):
+                 shared_weight: float = 1.0, device: str = "cuda", weight_format: int = 0):
         import torch
         self.H, self.E, self.k, self.I, self.Is = H, E, k, I, Is
+        self.weight_format = weight_format
         self.shared_weight = shared_weight
         self.device = device
         self.t = {n: torch.from_numpy(np.ascontiguousarray(a)).to(device) for n, a in arrays.items()}
@@ -23,12 +24,13 @@ class DeviceLayer:
 
     @classmethod
     def from_shape(cls, arrays, shape, device="cuda"):
-        return cls(arrays, shape.H, shape.E, shape.k, shape.I, shape.Is, shape.shared_weight, device)
+        return cls(arrays, shape.H, shape.E, shape.k, shape.I, shape.Is, shape.shared_weight, device,
+                   getattr(shape, "fmt", 0))
 
     def _make_desc(self, t):
         return _lib.make_desc(self.H, self.E, self.k, self.I, self.Is, self.shared_weight,
                               t["router_w"], t["gate"], t["up"], t["down"], t.get("sh_gate"),
-                              t.get("sh_up"), t.get("sh_down"))
+                              t.get("sh_up"), t.get("sh_down"), self.weight_format)
 
     def clone_weights(self):
         """Another copy of the weights at different addresses (for cache-cold timing)."""

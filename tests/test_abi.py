@@ -36,7 +36,7 @@ def test_header_declares_the_boundary():
 def test_library_exports_every_declared_symbol(L):
     for fn in declared_functions():
         assert hasattr(L.lib, fn), fn
-    assert L.moe_abi_version() == 3
+    assert L.moe_abi_version() == 4
     assert L.moe_status_str(-3) == "workspace too small"
 
 
@@ -63,6 +63,16 @@ def test_workspace_bytes_host_only(L):
     assert L.moe_workspace_bytes(desc(H=300), 1, 1) == 0
     assert L.moe_workspace_bytes(d, -1, 1) == 0
     assert L.moe_workspace_bytes(d, 1, 3) == 0          # 512 % 3 != 0
+
+
+def test_weight_format_is_checked(L):
+    # MXFP4 layers take the same workspace; an unknown format is an argument error
+    assert L.moe_workspace_bytes(desc(weight_format=1), 4096, 1) == L.moe_workspace_bytes(desc(), 4096, 1)
+    assert L.moe_workspace_bytes(desc(weight_format=2), 1, 1) == 0
+    assert raw_forward(L, desc(weight_format=2), 1) == -1
+    assert raw_forward(L, desc(weight_format=-1), 1) == -1
+    assert L.lib.moe_dequant(FAKE, 6, 1, 0, FAKE, None) == -1
+    assert L.lib.moe_dequant(FAKE, L.MOE_SB_MXFP4, 0, 0, FAKE, None) == 0
 
 
 def raw_forward(L, d, T, x=FAKE, out=FAKE, ws=FAKE, ws_bytes=1 << 40, path=0):

@@ -80,7 +80,7 @@ def run_shard(dl, x, idx, w, shard, n, path=qm.MOE_PATH_AUTO):
 
 def gpu_dequant(blob, bits, dtype):
     b = gpu(np.ascontiguousarray(blob).reshape(-1))
-    n_sb = b.numel() // (144 if bits == 4 else 176)
+    n_sb = b.numel() // (176 if bits == 5 else 144)
     tdt = {0: torch.float32, 1: torch.bfloat16, 2: torch.float16}[dtype]
     out = torch.empty(n_sb * 256, dtype=tdt, device=DEV)
     qm.moe_dequant(b, bits, n_sb, dtype, out)
