@@ -154,9 +154,13 @@ def time_steps(torch, run_step, K):
     return time.perf_counter() - t0
 
 
-def bench_decode(args, torch, qm, mi, DeviceLayer):
-    shp = mi.QWEN35_MOE
-    w = mi.WORKLOADS["decode"]
+def down_sb_bytes(mi, shp):
+    return mi.MXFP4_SB_BYTES if shp.fmt == 1 else mi.Q5K_SB_BYTES
+
+
+def bench_decode(args, torch, qm, mi, DeviceLayer, name="decode"):
+    w = mi.WORKLOADS[name]
+    shp = w.shape
     layer = mi.make_layer(shp, w.seed)
     base = DeviceLayer.from_shape(layer, shp)
     copies = [base] + [base.clone_weights() for _ in range(args.copies - 1)]
@@ -218,12 +222,12 @@ def bench_decode(args, torch, qm, mi, DeviceLayer):
                          ["gemv_front", "gateup_gemv", "down_gemv"])
     gateup_ms = kms["gateup_gemv"]
 
-    E_bytes_gu = 2 * (shp.I * shp.H // 256) * mi.Q4K_SB_BYTES          # gate + up of one expert
-    E_bytes_d = (shp.H * shp.I // 256) * mi.Q5K_SB_BYTES
+    E_bytes_gu = 2 * (shp.I * shp.H // 256) * mi.Q4K_SB_BYTES          # gate + up (MXFP4: same size)
+    E_bytes_d = (shp.H * shp.I // 256) * down_sb_bytes(mi, shp)
     n_inst = shp.k + 1                                                   # 8 routed + shared
     # the routed gate/up kernel: 8 experts' gate+up bytes, x, and h written
     gateup_bytes = shp.k * E_bytes_gu + shp.H * 4 + shp.k * shp.I * 4
-    layer_bytes = n_inst * (E_bytes_gu + E_bytes_d) + shp.H * shp.E * 4  # 19,202,048 B
+    layer_bytes = n_inst * (E_bytes_gu + E_bytes_d) + shp.H * shp.E * 4  # K-quant: 19,202,048 B
     ms_graph = graph_s / args.steps * 1e3
     res = {
         "value": T * args.steps / graph_s,
@@ -235,13 +239,13 @@ def bench_decode(args, torch, qm, mi, DeviceLayer):
         "layer_hbm_frac_graph": layer_bytes / (ms_graph * 1e-3) / (HBM_PEAK_GBS * 1e9),
         "layer_hbm_frac_kernels": layer_bytes / (sum(kms.values()) * 1e-3) / (HBM_PEAK_GBS * 1e9),
         "roofline": {
-            "kernel": "gemv_gateup_kernel<64,1> (8 routed experts)",
+            "kernel": "gemv_gateup_kernel<%s,64,1> (8 routed experts)" % ("MXFP4" if shp.fmt else "K-quant"),
             "bound": "hbm",
             "achieved": gateup_bytes / (gateup_ms * 1e-3) / 1e9,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": gateup_bytes / (gateup_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "traffic": traffic_for("gemv_gateup"),
+            "traffic": traffic_for("gemv_gateup") if shp.fmt == 0 else None,
             "algorithmic_bytes_per_launch": gateup_bytes,
             "avg_launch_ms": gateup_ms,
         },
@@ -249,9 +253,9 @@ def bench_decode(args, torch, qm, mi, DeviceLayer):
     return res, layer, pool.cpu().numpy()
 
 
-def bench_prefill(args, torch, qm, mi, DeviceLayer):
-    shp = mi.QWEN35_MOE
-    w = mi.WORKLOADS["prefill4096"]
+def bench_prefill(args, torch, qm, mi, DeviceLayer, name="prefill4096"):
+    w = mi.WORKLOADS[name]
+    shp = w.shape
     layer = mi.make_layer(shp, w.seed)
     base = DeviceLayer.from_shape(layer, shp)
     copies = [base, base.clone_weights()]
@@ -294,8 +298,9 @@ def bench_prefill(args, torch, qm, mi, DeviceLayer):
     gu_ms = kms["gemm_gateup"]
     d_ms = kms["gemm_down"]
     res = {
-        "workload": ("prefill T=4096: same layer shape, seed 4, uniform router, "
-                     "grouped fp16-MFMA path, 2 rotating weight copies, HIP-graph replay"),
+        "workload": ("prefill T=4096: same layer shape, %s weights, seed %d, uniform router, "
+                     "grouped fp16-MFMA path, 2 rotating weight copies, HIP-graph replay"
+                     % ("MXFP4" if shp.fmt else "Q4_K/Q5_K", w.seed)),
         "value": T * K / secs,
         "unit": "tokens/s",
         "ms_per_step": secs / K * 1e3,
@@ -314,7 +319,7 @@ def bench_prefill(args, torch, qm, mi, DeviceLayer):
             "peak": FP16_MFMA_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": flops_gu / (gu_ms * 1e-3) / 1e12 / FP16_MFMA_PEAK_TFLOPS,
-            "traffic": traffic_for("gemm_gateup"),
+            "traffic": traffic_for("gemm_gateup") if shp.fmt == 0 else None,
             "algorithmic_flops_per_launch": flops_gu,
             "avg_launch_ms": gu_ms,
         },
@@ -563,6 +568,8 @@ def main():
     ap.add_argument("--prefill-warmup", type=int, default=3)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-mxfp4", action="store_true",
+                    help="skip the decode and prefill runs of the MXFP4-weight layer")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle decode work")
     ap.add_argument("--cpu-prefill-rows", type=int, default=2048)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -608,6 +615,19 @@ def main():
     if not args.no_prefill:
         print("[bench] RMSNorm / residual at T=4096 ...", file=sys.stderr, flush=True)
         edges = bench_edges(torch, qm)
+    mx = None
+    if not args.no_mxfp4:
+        print("[bench] MXFP4 weights: decode T=1 ...", file=sys.stderr, flush=True)
+        mdec, _, _ = bench_decode(args, torch, qm, mi, DeviceLayer, "decode_mx")
+        mx = {"decode": {
+            "workload": ("decode T=1: the same layer shape with MXFP4 gate/up/down weights "
+                         "(144-byte superblocks), seed 6, 64-token pool, 4 rotating weight "
+                         "copies, HIP-graph replay"),
+            "value": mdec["value"], "unit": "tokens/s", **{k: v for k, v in mdec.items()
+                                                          if k != "value"}}}
+        if not args.no_prefill:
+            print("[bench] MXFP4 weights: prefill T=4096 ...", file=sys.stderr, flush=True)
+            mx["prefill"], _, _ = bench_prefill(args, torch, qm, mi, DeviceLayer, "prefill4096_mx")
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] oracle on the host ...", file=sys.stderr, flush=True)
@@ -640,6 +660,7 @@ def main():
         "cpu_baseline": cpu,
         "decode": {k: v for k, v in dec.items() if k not in ("value", "ms_per_step", "roofline")},
         "prefill": pre,
+        "mxfp4": mx,
         "edges": edges,
     }
     print(json.dumps(line), flush=True)

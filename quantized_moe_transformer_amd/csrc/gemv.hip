@@ -76,28 +76,43 @@ __device__ __forceinline__ float piece_dot(const SbHead& h, const uint4& qs, con
     return h.d * (sca * dl + scb * dh) - h.dmin * (ma * sl + mb * sh);
 }
 
+// E2M1 codes of a word's four bytes (bits 0..3 of each) -> the bytes
+// u = 2 * value + 12 (0..24): a byte permute looks the positive and the
+// negative values up in two 8-entry tables, and the sign bit picks one.
+__device__ __forceinline__ uint32_t e2m1_offset_bytes(uint32_t w) {
+    // u of codes 0..7: 12 + 2 * {0, 0.5, 1, 1.5, 2, 3, 4, 6}; of codes 8..15: 12 - the same
+    const uint32_t n7 = w & 0x07070707u;
+    const uint32_t pos = __builtin_amdgcn_perm(0x18141210u, 0x0F0E0D0Cu, n7);
+    const uint32_t neg = __builtin_amdgcn_perm(0x00040608u, 0x090A0B0Cu, n7);
+    const uint32_t neg_mask = ((w >> 3) & 0x01010101u) * 0xffu;
+    return (neg & neg_mask) | (pos & ~neg_mask);
+}
+
 // The same for an MXFP4 piece: 16 codes of sub-block 2c (low nibbles, under
-// xl) and 16 of sub-block 2c+1 (high nibbles, under xh).  Each sub-block's
-// scale is a power of two and factors out of its sum:
-//   sum_i w_i x_i = X_2c * sum(value(q) x)_lo + X_2c+1 * sum(value(q) x)_hi
-// s0 / s1: scale bytes 0..3 / 4..7 of the superblock.
+// xl, summing to sl) and 16 of sub-block 2c+1 (high nibbles, under xh, sh).
+// Each sub-block's scale is a power of two and factors out of its sum, and
+// with u = 2 value + 12 per code:
+//   sum_i w_i x_i = X_2c (sum(u x)_lo / 2 - 6 sl) + X_2c+1 (sum(u x)_hi / 2 - 6 sh)
+// (one byte-convert and one fma per code).  s0 / s1: the superblock's scale
+// bytes 0..3 / 4..7.
 __device__ __forceinline__ float piece_dot_mx(uint32_t s0, uint32_t s1, const uint4& qs, int c,
-                                              const float* xl, const float* xh) {
+                                              const float* xl, const float* xh, float sl, float sh) {
     const uint32_t sw = c < 2 ? s0 : s1;
-    const int sh = 16 * (c & 1);
-    const float xa = e8m0_f32((sw >> sh) & 0xffu), xb = e8m0_f32((sw >> (sh + 8)) & 0xffu);
+    const int sft = 16 * (c & 1);
+    const float xa = e8m0_f32((sw >> sft) & 0xffu), xb = e8m0_f32((sw >> (sft + 8)) & 0xffu);
     const uint32_t qw[4] = {qs.x, qs.y, qs.z, qs.w};
     float dl = 0.f, dh = 0.f;
 #pragma unroll
     for (int wi = 0; wi < 4; ++wi) {
+        const uint32_t ul = e2m1_offset_bytes(qw[wi]);
+        const uint32_t uh = e2m1_offset_bytes(qw[wi] >> 4);
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-            const uint32_t byte = qw[wi] >> (8 * b);
-            dl = __builtin_fmaf(e2m1_f32(byte), xl[4 * wi + b], dl);
-            dh = __builtin_fmaf(e2m1_f32(byte >> 4), xh[4 * wi + b], dh);
+            dl = __builtin_fmaf((float)((ul >> (8 * b)) & 0xffu), xl[4 * wi + b], dl);
+            dh = __builtin_fmaf((float)((uh >> (8 * b)) & 0xffu), xh[4 * wi + b], dh);
         }
     }
-    return xa * dl + xb * dh;
+    return xa * __builtin_fmaf(0.5f, dl, -6.f * sl) + xb * __builtin_fmaf(0.5f, dh, -6.f * sh);
 }
 
 // A superblock's 16-byte head for either format: K-quant d, dmin and scale
@@ -121,7 +136,7 @@ template <int FMT, bool HIGH>
 __device__ __forceinline__ float piece_dot_f(const SbHead& h, const uint4& qs, const uint4& qh, int c,
                                              const float* xl, const float* xh, float sl, float sh) {
     if constexpr (FMT == MOE_WFMT_MXFP4)
-        return piece_dot_mx(h.s0, h.s1, qs, c, xl, xh);
+        return piece_dot_mx(h.s0, h.s1, qs, c, xl, xh, sl, sh);
     else
         return piece_dot<HIGH>(h, qs, qh, c, xl, xh, sl, sh);
 }
