@@ -50,12 +50,18 @@ FP16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak
 # --copy-probe).  Keyed by the SHA-256 of the kernel's sources: when they change,
 # the counters no longer describe the kernel and traffic is reported as null.
 TRAFFIC = {
-    # decode T=1, 180 dispatches: FETCH 4732.4 KiB x 1.99980, WRITE 16.1 KiB x 1.0
-    "gemv_gateup": {"sources_sha256": "ad3a4ed6dc5106808578e85b9800b0a2a44c872050a144d3012fd3454a681b54",
-                    "fetch_bytes": 9690891, "write_bytes": 16448},
-    # prefill T=4096, 9 dispatches: FETCH 224636.3 KiB x 1.99980, WRITE 36864.0 KiB x 1.0
-    "gemm_gateup": {"sources_sha256": "921152f0e92d94aa2170964d37323c1a2d4f0b45294c6e711e340e63bb18301b",
-                    "fetch_bytes": 460008154, "write_bytes": 37748736},
+    # decode T=1, 288 dispatches: FETCH 4731.6 KiB x 1.99980, WRITE 16.1 KiB x 1.0
+    "gemv_gateup": {"sources_sha256": "982d3312e7597647413ee00e9b657a3df1b10d5e90da3a165756a831654fc409",
+                    "fetch_bytes": 9689274, "write_bytes": 16448},
+    # prefill T=4096, 15 dispatches: FETCH 224651.4 KiB x 1.99980, WRITE 36864.0 KiB x 1.0
+    "gemm_gateup": {"sources_sha256": "fbf31bb999119bcf1a13a6ccf1acb7919a5233154dde93dbdc8bdbe6ede20d1a",
+                    "fetch_bytes": 460040152, "write_bytes": 37748736},
+    # MXFP4 decode T=1, 288 dispatches: FETCH 4737.2 KiB x 1.99980, WRITE 16.1 KiB x 1.0
+    "gemv_gateup_mx": {"sources_sha256": "982d3312e7597647413ee00e9b657a3df1b10d5e90da3a165756a831654fc409",
+                    "fetch_bytes": 9700789, "write_bytes": 16448},
+    # MXFP4 prefill T=4096, 15 dispatches: FETCH 224577.3 KiB x 1.99980, WRITE 36864.0 KiB x 1.0
+    "gemm_gateup_mx": {"sources_sha256": "fbf31bb999119bcf1a13a6ccf1acb7919a5233154dde93dbdc8bdbe6ede20d1a",
+                    "fetch_bytes": 459888283, "write_bytes": 37748736},
 }
 FETCH_SIZE_FACTOR = 1.99980   # plain 256 MiB copy: true bytes read / FETCH_SIZE bytes
 WRITE_SIZE_FACTOR = 1.0
@@ -63,6 +69,8 @@ TRAFFIC_SOURCES = {
     "gemv_gateup": ["gemv.hip", "topk.h", "moe_internal.h"],
     "gemm_gateup": ["gemm.hip", "moe_internal.h"],
 }
+TRAFFIC_SOURCES["gemv_gateup_mx"] = TRAFFIC_SOURCES["gemv_gateup"]
+TRAFFIC_SOURCES["gemm_gateup_mx"] = TRAFFIC_SOURCES["gemm_gateup"]
 
 
 def sources_sha(kernel):
@@ -245,7 +253,7 @@ def bench_decode(args, torch, qm, mi, DeviceLayer, name="decode"):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": gateup_bytes / (gateup_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "traffic": traffic_for("gemv_gateup") if shp.fmt == 0 else None,
+            "traffic": traffic_for("gemv_gateup_mx" if shp.fmt else "gemv_gateup"),
             "algorithmic_bytes_per_launch": gateup_bytes,
             "avg_launch_ms": gateup_ms,
         },
@@ -319,7 +327,7 @@ def bench_prefill(args, torch, qm, mi, DeviceLayer, name="prefill4096"):
             "peak": FP16_MFMA_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": flops_gu / (gu_ms * 1e-3) / 1e12 / FP16_MFMA_PEAK_TFLOPS,
-            "traffic": traffic_for("gemm_gateup") if shp.fmt == 0 else None,
+            "traffic": traffic_for("gemm_gateup_mx" if shp.fmt else "gemm_gateup"),
             "algorithmic_flops_per_launch": flops_gu,
             "avg_launch_ms": gu_ms,
         },
