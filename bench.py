@@ -134,10 +134,11 @@ class HipEvents:
             self.hip.hipEventDestroy(ctypes.c_void_p(e))
 
 
-def kernel_profile(torch, qm, call, n_steps, names):
+def kernel_profile(torch, qm, call, n_steps, names, stats=None):
     """Average duration (ms) of each named kernel over n_steps eager calls, from
     start/stop events the library attaches to those launches (hipExtLaunchKernel
-    records the dispatch's own begin/end)."""
+    records the dispatch's own begin/end).  `stats` (a dict, optional) receives
+    each kernel's median and minimum as well."""
     from quantized_moe_transformer_amd._lib import KERNEL_IDS, N_KERNEL_IDS
     per_step = 2 * N_KERNEL_IDS
     ev = HipEvents(n_steps * per_step)
@@ -147,8 +148,10 @@ def kernel_profile(torch, qm, call, n_steps, names):
     out = {}
     for n in names:
         kid = KERNEL_IDS[n]
-        out[n] = float(np.mean([ev.ms(i * per_step + 2 * kid, i * per_step + 2 * kid + 1)
-                                for i in range(n_steps)]))
+        d = [ev.ms(i * per_step + 2 * kid, i * per_step + 2 * kid + 1) for i in range(n_steps)]
+        out[n] = float(np.mean(d))
+        if stats is not None:
+            stats[n] = {"median_ms": float(np.median(d)), "min_ms": float(np.min(d))}
     ev.close()
     return out
 
@@ -226,8 +229,9 @@ def bench_decode(args, torch, qm, mi, DeviceLayer, name="decode"):
 
     # per-kernel durations of the same calls
     nprof = min(args.steps, 256)
+    kst = {}
     kms = kernel_profile(torch, qm, lambda i, e: step(i, e), nprof,
-                         ["gemv_front", "gateup_gemv", "down_gemv"])
+                         ["gemv_front", "gateup_gemv", "down_gemv"], kst)
     gateup_ms = kms["gateup_gemv"]
 
     E_bytes_gu = 2 * (shp.I * shp.H // 256) * mi.Q4K_SB_BYTES          # gate + up (MXFP4: same size)
@@ -256,6 +260,9 @@ def bench_decode(args, torch, qm, mi, DeviceLayer, name="decode"):
             "traffic": traffic_for("gemv_gateup_mx" if shp.fmt else "gemv_gateup"),
             "algorithmic_bytes_per_launch": gateup_bytes,
             "avg_launch_ms": gateup_ms,
+            "median_launch_ms": kst["gateup_gemv"]["median_ms"],
+            "min_launch_ms": kst["gateup_gemv"]["min_ms"],
+            "launches": nprof,
         },
     }
     return res, layer, pool.cpu().numpy()
@@ -299,7 +306,8 @@ def bench_prefill(args, torch, qm, mi, DeviceLayer, name="prefill4096"):
     secs = (time.perf_counter() - t0) * K / (2 * n_rep)
     names = ["x_f16", "router_mfma", "router_topk", "bucket_hist", "bucket_scan",
              "bucket_scatter", "gemm_gateup", "gemm_down", "combine"]
-    kms = kernel_profile(torch, qm, lambda i, e: step(i, e), K, names)
+    kst = {}
+    kms = kernel_profile(torch, qm, lambda i, e: step(i, e), K, names, kst)
     slots = T * shp.k + T
     flops_gu = 2.0 * 2 * shp.H * shp.I * slots
     flops_d = 2.0 * shp.I * shp.H * slots
@@ -330,6 +338,9 @@ def bench_prefill(args, torch, qm, mi, DeviceLayer, name="prefill4096"):
             "traffic": traffic_for("gemm_gateup_mx" if shp.fmt else "gemm_gateup"),
             "algorithmic_flops_per_launch": flops_gu,
             "avg_launch_ms": gu_ms,
+            "median_launch_ms": kst["gemm_gateup"]["median_ms"],
+            "min_launch_ms": kst["gemm_gateup"]["min_ms"],
+            "launches": K,
         },
     }
     return res, layer, x_host
@@ -548,9 +559,19 @@ def cpu_baseline_decode(layer, pool, budget_s):
         oracle.forward(ol, pool[i:i + 1])
         n += 1
     dt = time.perf_counter() - t0
+    # the same calls on one thread (a token's arithmetic is the same either way)
+    n1 = 0
+    t1 = time.perf_counter()
+    while (time.perf_counter() - t1) < budget_s / 3:
+        i = n1 % pool.shape[0]
+        oracle.forward(ol, pool[i:i + 1], nthreads=1)
+        n1 += 1
+    dt1 = time.perf_counter() - t1
     return {"value": n / dt, "unit": "tokens/s", "cores": oracle.max_threads(), "kind": "oracle",
             "sample": f"{n} decode tokens (cycling a 64-token pool), one T=1 oracle call each (routing, decode of the 9 "
-                      f"touched experts, fp64 FFN), {dt:.1f} s"}
+                      f"touched experts, fp64 FFN), {dt:.1f} s",
+            "single_thread": {"value": n1 / dt1, "unit": "tokens/s", "cores": 1,
+                              "sample": f"{n1} decode tokens, {dt1:.1f} s"}}
 
 
 def cpu_baseline_prefill(layer, x, rows):
