@@ -399,16 +399,18 @@ def test_empty_batch_leaves_output_untouched():
 @pytest.mark.parametrize("H,I,T", [(512, 256, 45), (1024, 512, 70), (4096, 256, 33), (4096, 512, 200),
                                    (4096, 512, 8), (1024, 256, 1)])
 @pytest.mark.parametrize("path,tol", [(qm.MOE_PATH_GEMV, GEMV_TOL), (qm.MOE_PATH_MFMA, MFMA_TOL)])
-def test_other_widths(H, I, T, path, tol):
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_other_widths(H, I, T, path, tol, fmt):
     """Hidden widths of 2, 4 and 16 superblocks per row and expert widths of one
     and two superblocks, through both paths (the weight rings and the router
-    splits depend on them), with a two-shard run of the grouped GEMM."""
-    shp = mi.LayerShape(H=H, E=16, k=4, I=I, Is=I)
+    splits depend on them) and both weight formats (K-quant, MXFP4), with a
+    two-shard run of the grouped GEMM."""
+    shp = mi.LayerShape(H=H, E=16, k=4, I=I, Is=I, fmt=fmt)
     layer = mi.make_layer(shp, seed=31)
     x = mi.make_tokens(shp, 31, T)
     dl = DeviceLayer.from_shape(layer, shp)
     ol = oracle.Layer.from_shape(layer, shp)
-    say(f"width H={H} I={I} T={T} path={path}")
+    say(f"width H={H} I={I} T={T} path={path} fmt={fmt}")
     got, used = run_forward(dl, x, path)
     assert used == path
     oi, ow, _, logits = oracle.router(x, layer["router_w"], shp.k)
@@ -427,9 +429,11 @@ def test_other_widths(H, I, T, path, tol):
 
 @pytest.mark.parametrize("E,k,Is", [(8, 8, 128), (1, 1, 0), (4, 3, 0)])
 @pytest.mark.parametrize("path,tol", [(qm.MOE_PATH_GEMV, GEMV_TOL), (qm.MOE_PATH_MFMA, MFMA_TOL)])
-def test_degenerate_layers(E, k, Is, path, tol):
-    """k = E (full softmax mixture), a single dense expert, no shared expert."""
-    shp = mi.LayerShape(H=256, E=E, k=k, I=128, Is=Is)
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_degenerate_layers(E, k, Is, path, tol, fmt):
+    """k = E (full softmax mixture), a single dense expert, no shared expert;
+    both weight formats."""
+    shp = mi.LayerShape(H=256, E=E, k=k, I=128, Is=Is, fmt=fmt)
     layer = mi.make_layer(shp, seed=21)
     x = mi.make_tokens(shp, 21, 70)
     dl = DeviceLayer.from_shape(layer, shp)
