@@ -202,7 +202,7 @@ def test_router_exact_ties(dup, T):
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("name,T", [("tiny", 4), ("prefill512_zipf", 512), ("prefill4096", 4096),
-                                    ("prefill4096", 1500)])
+                                    ("prefill4096", 1500), ("prefill4096", 8192)])
 def test_bucket_bit_exact(name, T):
     w, layer, dl, ol = dev_layer(name)
     x = mi.make_tokens(w.shape, w.seed, T, zipf=w.zipf)
