@@ -17,7 +17,9 @@
 
 namespace moe {
 
-int router_splits(int T, int H) { return T <= kRouterSmallMaxT ? kRouterSplits : 1; }
+constexpr int kRgSplit = 2;   // K splits of the matrix-core router (partials added by the top-k)
+
+int router_splits(int T, int H) { return T <= kRouterSmallMaxT ? kRouterSplits : kRgSplit; }
 
 // ---------------------------------------------------------------------------
 // Many rows: logits on the fp16 matrix cores with fp32 accuracy.  Each fp32
@@ -32,7 +34,7 @@ int router_splits(int T, int H) { return T <= kRouterSmallMaxT ? kRouterSplits :
 // |x| < 65504 and |w| < 64.
 // ---------------------------------------------------------------------------
 constexpr float kWrScale = 1024.0f, kLoScale = 2048.0f;
-constexpr int kRgT = 32, kRgE = 128, kRgK = 64;
+constexpr int kRgT = 64, kRgE = 128, kRgK = 64;
 
 // One launch, two jobs.  Workgroups [0, nxb): x fp32 [T][H] -> hi (x16, also
 // the grouped GEMM's operand) and lo parts, four values per thread.
@@ -80,16 +82,21 @@ split_kernel(const float* __restrict__ x, _Float16* __restrict__ xh, _Float16* _
     }
 }
 
-// grid (ceil(T/32), ceil(E/128)); 4 waves, wave w owns experts [32w, 32w+32)
-// of the block's 128.  K advances 64 at a time.  A step's operands -- hi and
-// lo parts of 32 token rows and of 128 router rows, 40 KB -- arrive by direct
-// global-to-LDS loads two steps ahead into a three-stage ring (ten 16-byte
-// loads per thread per step).  Each row's eight 16-byte chunks sit XOR-
-// swizzled by the row index (chunk c at position c ^ (row & 7)).  Rows past T
-// or E re-read the last valid row; their results are not written.
+// grid (ceil(T/64), ceil(E/128), kRgSplit); 4 waves, wave w owns experts
+// [32w, 32w+32) of the block's 128 for all 64 token rows (two 32-row blocks,
+// so each router fragment read from LDS feeds two token blocks).  The K range
+// is split in kRgSplit parts (blockIdx.z), each written as a partial logit
+// [T][E][kRgSplit] that the top-k adds in ascending order; the split keeps
+// 256 workgroups at T = 4096.  K advances 64 at a time.  A step's operands --
+// hi and lo parts of 64 token rows and of 128 router rows, 48 KB -- arrive by
+// direct global-to-LDS loads two steps ahead into a three-stage ring (twelve
+// 16-byte loads per thread per step).  Each row's eight 16-byte chunks sit
+// XOR-swizzled by the row index (chunk c at position c ^ (row & 7)).  Rows
+// past T or E re-read the last valid row; their results are not written.
 constexpr int kRgStages = 3;
-constexpr int kRgStageHalves = 2 * (kRgT + kRgE) * kRgK;   // 40 KB
-constexpr int kRgDma = kRgStageHalves * 2 / 16 / 256;       // 10 loads per thread per step
+constexpr int kRgStageHalves = 2 * (kRgT + kRgE) * kRgK;   // 48 KB
+constexpr int kRgDma = kRgStageHalves * 2 / 16 / 256;       // 12 loads per thread per step
+constexpr int kRgAChunks = 2 * kRgT * 8;                    // A hi + lo chunks of a stage
 
 __device__ __forceinline__ int rg_chunk(int row, int c) { return row * 8 + (c ^ (row & 7)); }
 
@@ -97,25 +104,26 @@ __global__ void __launch_bounds__(256)
 router_gemm_kernel(const _Float16* __restrict__ xh, const _Float16* __restrict__ xl,
                    const _Float16* __restrict__ wh, const _Float16* __restrict__ wl, int T, int H,
                    int E, float* __restrict__ logits) {
-    // per stage: A hi [32][64], A lo, B hi [128][64], B lo
+    // per stage: A hi [64][64], A lo, B hi [128][64], B lo
     __shared__ __align__(16) _Float16 st[kRgStages][kRgStageHalves];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int t0 = blockIdx.x * kRgT, e0 = blockIdx.y * kRgE;
-    const int nk = H / kRgK;
-    // chunk q = (10 wave + j) * 64 + lane of a stage: A parts first (512 chunks)
+    const int t0 = blockIdx.x * kRgT, e0 = blockIdx.y * kRgE, z = blockIdx.z;
+    const int nk = H / kRgK / kRgSplit;
+    const size_t k0 = (size_t)z * nk * kRgK;   // first K of this split
+    // chunk q = (12 wave + j) * 64 + lane of a stage: A parts first
     const _Float16* src[kRgDma];
 #pragma unroll
     for (int j = 0; j < kRgDma; ++j) {
         const int q = (kRgDma * wave + j) * 64 + lane;
-        if (q < 2 * kRgT * 8) {
-            const int part = q >> 8, row = (q >> 3) & (kRgT - 1), c = (q & 7) ^ (row & 7);
+        if (q < kRgAChunks) {
+            const int part = q / (kRgT * 8), row = (q >> 3) & (kRgT - 1), c = (q & 7) ^ (row & 7);
             const int t = min(t0 + row, T - 1);
-            src[j] = (part ? xl : xh) + (size_t)t * H + c * 8;
+            src[j] = (part ? xl : xh) + (size_t)t * H + k0 + c * 8;
         } else {
-            const int qb = q - 2 * kRgT * 8;
-            const int part = qb >> 10, row = (qb >> 3) & (kRgE - 1), c = (qb & 7) ^ (row & 7);
+            const int qb = q - kRgAChunks;
+            const int part = qb / (kRgE * 8), row = (qb >> 3) & (kRgE - 1), c = (qb & 7) ^ (row & 7);
             const int e = min(e0 + row, E - 1);
-            src[j] = (part ? wl : wh) + (size_t)e * H + c * 8;
+            src[j] = (part ? wl : wh) + (size_t)e * H + k0 + c * 8;
         }
     }
     auto issue = [&](int kk) {
@@ -133,7 +141,7 @@ router_gemm_kernel(const _Float16* __restrict__ xh, const _Float16* __restrict__
         wait_vmcnt<0>();
     }
     __syncthreads();
-    float16v acc = {}, acc_lo = {};
+    float16v acc[2] = {}, acc_lo[2] = {};
     for (int kk = 0; kk < nk; ++kk) {
         // step kk + 2 into the stage step kk - 1 read (every wave passed the barrier)
         const bool more = kk + 2 < nk;
@@ -146,13 +154,16 @@ router_gemm_kernel(const _Float16* __restrict__ xh, const _Float16* __restrict__
 #pragma unroll
         for (int s = 0; s < kRgK / 16; ++s) {
             const int c = 2 * s + (lane >> 5);
-            const half8 ah = *reinterpret_cast<const half8*>(sa_h + 8 * rg_chunk(ra, c));
-            const half8 al = *reinterpret_cast<const half8*>(sa_l + 8 * rg_chunk(ra, c));
             const half8 bh = *reinterpret_cast<const half8*>(sb_h + 8 * rg_chunk(rb, c));
             const half8 bl = *reinterpret_cast<const half8*>(sb_l + 8 * rg_chunk(rb, c));
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bh, acc, 0, 0, 0);
-            acc_lo = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bl, acc_lo, 0, 0, 0);
-            acc_lo = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, bh, acc_lo, 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const half8 ah = *reinterpret_cast<const half8*>(sa_h + 8 * rg_chunk(32 * i + ra, c));
+                const half8 al = *reinterpret_cast<const half8*>(sa_l + 8 * rg_chunk(32 * i + ra, c));
+                acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bh, acc[i], 0, 0, 0);
+                acc_lo[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bl, acc_lo[i], 0, 0, 0);
+                acc_lo[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, bh, acc_lo[i], 0, 0, 0);
+            }
         }
         // step kk + 1's operands must have landed; step kk + 2's may be in flight
         if (more) wait_vmcnt<kRgDma>();
@@ -161,12 +172,14 @@ router_gemm_kernel(const _Float16* __restrict__ xh, const _Float16* __restrict__
     }
     const int e = e0 + 32 * wave + (lane & 31);
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-        const int t = t0 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if (t < T && e < E)
-            logits[(size_t)t * E + e] =
-                __builtin_fmaf(acc_lo[v], 1.0f / kLoScale, acc[v]) * (1.0f / kWrScale);
-    }
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int t = t0 + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+            if (t < T && e < E)
+                logits[((size_t)t * E + e) * kRgSplit + z] =
+                    __builtin_fmaf(acc_lo[i][v], 1.0f / kLoScale, acc[i][v]) * (1.0f / kWrScale);
+        }
 }
 
 // Four tokens per workgroup, one wave each.
@@ -180,6 +193,9 @@ router_topk_kernel(const float* __restrict__ part, int ks_n, int T, int E, int k
     if (ks_n == 1) {
         if (E <= 256) wave_topk<4, 1>(part, E, k, t, ir, wr);
         else wave_topk<16, 1>(part, E, k, t, ir, wr);
+    } else if (ks_n == kRgSplit) {
+        if (E <= 256) wave_topk<4, kRgSplit>(part, E, k, t, ir, wr);
+        else wave_topk<16, kRgSplit>(part, E, k, t, ir, wr);
     } else {
         if (E <= 256) wave_topk<4, kRouterSplits>(part, E, k, t, ir, wr);
         else wave_topk<16, kRouterSplits>(part, E, k, t, ir, wr);
@@ -208,10 +224,11 @@ hipError_t launch_router(const moe_layer_desc& d, const float* x, int T, int32_t
     const int nxb = (int)((n4 + 255) / 256), nwb = ((H + 31) / 32) * ((E + 31) / 32);
     launch_k(c, MOE_K_X_F16, split_kernel, dim3(nxb + nwb), dim3(256), 0, x, xh, xl, n4, nxb,
              d.router_w, H, E, wh, wl);
-    launch_k(c, MOE_K_ROUTER_MFMA, router_gemm_kernel, dim3((T + kRgT - 1) / kRgT, (E + kRgE - 1) / kRgE),
-             dim3(256), 0, xh, xl, wh, wl, T, H, E, part);
-    launch_k(c, MOE_K_ROUTER_TOPK, router_topk_kernel, dim3((T + 3) / 4), dim3(256), 0, part, 1,
-             T, E, d.top_k, idx, w);
+    launch_k(c, MOE_K_ROUTER_MFMA, router_gemm_kernel,
+             dim3((T + kRgT - 1) / kRgT, (E + kRgE - 1) / kRgE, kRgSplit), dim3(256), 0, xh, xl, wh,
+             wl, T, H, E, part);
+    launch_k(c, MOE_K_ROUTER_TOPK, router_topk_kernel, dim3((T + 3) / 4), dim3(256), 0, part,
+             kRgSplit, T, E, d.top_k, idx, w);
     return hipGetLastError();
 }
 

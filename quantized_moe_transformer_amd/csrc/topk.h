@@ -70,7 +70,7 @@ __device__ __forceinline__ float row_sum(float v) {
 template <int NE, int KS>
 __device__ __forceinline__ void wave_topk_select(const float* __restrict__ part, int E, int k,
                                                  int t, float& my_l, int& my_e, float& top) {
-    static_assert(KS == 1 || KS % 4 == 0, "partials per expert: 1 or a multiple of 4");
+    static_assert(KS == 1 || KS == 2 || KS % 4 == 0, "partials per expert: 1, 2 or a multiple of 4");
     static_assert(NE <= 16, "at most 1024 experts");
     const int lane = threadIdx.x & 63;
     float pv[NE][KS];
@@ -80,6 +80,10 @@ __device__ __forceinline__ void wave_topk_select(const float* __restrict__ part,
         const float* p = part + ((size_t)t * E + e) * KS;
         if (KS == 1) {
             pv[i][0] = p[0];
+        } else if (KS == 2) {
+            const float2 f = *reinterpret_cast<const float2*>(p);
+            pv[i][0] = f.x;
+            pv[i][KS - 1] = f.y;
         } else {
 #pragma unroll
             for (int q = 0; q < KS / 4; ++q) {
