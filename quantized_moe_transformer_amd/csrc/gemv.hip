@@ -315,42 +315,71 @@ struct GemvArgs {
     float* w_out;
     int n_router_blocks;  // front kernel: router workgroups (0: none)
     int shared_rows_blocks;
+    int n_shared_pad;     // front kernel: shared workgroups rounded up to kXcds
     float* out;
 };
 
-constexpr int kRtE = 32;       // experts per router workgroup
+constexpr int kRtE = 8;        // experts per router workgroup (two groups of four)
+constexpr int kRtLine = 32;    // experts in one 128-byte line of a router row
+constexpr int kXcds = 8;       // workgroups go to the XCDs round-robin by index
+
+// Router workgroups per token tile: the four 8-expert quarters of every
+// 32-expert line group, for each of the kRouterSplits K splits.
+__host__ __device__ inline int router_blocks_per_tile(int E) {
+    return (kRtLine / kRtE) * ((E + kRtLine - 1) / kRtLine) * kRouterSplits;
+}
 
 // ---------------------------------------------------------------------------
 // front: router partial logits and the shared expert's gate/up
 // ---------------------------------------------------------------------------
 
-// Partial logits of TT tokens x kRtE experts over the H / kRouterSplits rows
-// of one split (NSB = H / 256, so 32 * NSB rows).  Thread (q, g): four
-// consecutive experts 4q..4q+3 (one 16-byte load per row when E % 4 == 0)
-// of rows g, g + 32, ...; all of its router loads are issued before the
-// tokens arrive in LDS.  The 32 row groups are summed in a fixed order.
+// Partial logits of TT tokens x kRtE experts over the ROWS = H / kRouterSplits
+// rows of one split (NSB = H / 256, so ROWS = 32 * NSB).  Spread over many
+// small workgroups (8 KB of the router matrix each at H = 2048), the router
+// reads in about one memory round trip.  The four workgroups that read the
+// same 128-byte lines (one 32-expert group of a split) get indices congruent
+// modulo kXcds: they run on one XCD, whose L2 fetches each line once.
+//
+// Thread (q, g), q = tid % 2: experts 4q..4q+3 of the workgroup (one 16-byte
+// load per row when E % 4 == 0; a lane pair reads a row's 32 bytes);
+// g = tid / 2: rows g, g + G, ... of the split.  Each wave sums its 32 row
+// groups across its lanes, the four waves are added in LDS, in a fixed order.
 template <int TT, int NSB>
 __device__ __forceinline__ void router_role(const GemvArgs& a, int rb) {
     constexpr int KS = kRouterSplits;
+    static_assert(KS == kXcds, "one K split per XCD slot in the workgroup mapping");
     constexpr int ROWS = 32 * NSB;
+    constexpr int G = ROWS < 128 ? ROWS : 128;   // row groups per expert group
+    constexpr int RPT = ROWS / G;                // rows per thread
     __shared__ float xs[TT][ROWS];
-    __shared__ float red[32][TT][kRtE];
-    const int n_ec = (a.E + kRtE - 1) / kRtE;
-    const int tb = rb / (n_ec * KS);
-    const int rem = rb % (n_ec * KS);
-    const int ec = rem / KS, ks = rem % KS;
+    __shared__ float red[4][TT][kRtE];
+    const int nb = router_blocks_per_tile(a.E);
+    const int tb = rb / nb;
+    const int u = rb % nb;
+    const int w = u / kXcds;                     // index among the workgroups of its XCD
+    const int quarter = w % (kRtLine / kRtE);
+    const int pair = (w / (kRtLine / kRtE)) * kXcds + u % kXcds;   // (line group, split)
+    const int ks = pair % KS;
+    const int ec = (pair / KS) * (kRtLine / kRtE) + quarter;
+    if (ec * kRtE >= a.E) return;                // a quarter past the last expert
     const int t0 = tb * TT;
     const int nt = min(TT, a.T - t0);
     const int h0 = ks * ROWS;
     const int tid = threadIdx.x;
-    const int q = tid & 7, g = tid >> 3;
+    const int q = tid & 1, g = tid >> 1;
+    const bool rows_on = g < G;
     const int e0 = ec * kRtE + 4 * q;
-    float wv[NSB][4];
-    if ((a.E & 3) == 0 && e0 + 3 < a.E) {
+    float wv[RPT][4];
+    if (!rows_on) {
 #pragma unroll
-        for (int r = 0; r < NSB; ++r) {
+        for (int r = 0; r < RPT; ++r)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) wv[r][c] = 0.f;
+    } else if ((a.E & 3) == 0 && e0 + 3 < a.E) {
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) {
             const float4 f =
-                *reinterpret_cast<const float4*>(a.router_w + (size_t)(h0 + g + 32 * r) * a.E + e0);
+                *reinterpret_cast<const float4*>(a.router_w + (size_t)(h0 + g + G * r) * a.E + e0);
             wv[r][0] = f.x;
             wv[r][1] = f.y;
             wv[r][2] = f.z;
@@ -358,56 +387,61 @@ __device__ __forceinline__ void router_role(const GemvArgs& a, int rb) {
         }
     } else {
 #pragma unroll
-        for (int r = 0; r < NSB; ++r)
+        for (int r = 0; r < RPT; ++r)
 #pragma unroll
             for (int c = 0; c < 4; ++c)
-                wv[r][c] = a.router_w[(size_t)(h0 + g + 32 * r) * a.E + min(e0 + c, a.E - 1)];
+                wv[r][c] = a.router_w[(size_t)(h0 + g + G * r) * a.E + min(e0 + c, a.E - 1)];
     }
     for (int i = tid; i < TT * ROWS; i += blockDim.x) {
         const int tt = i / ROWS, hh = i % ROWS;
         xs[tt][hh] = tt < nt ? a.x[(size_t)(t0 + tt) * a.H + h0 + hh] : 0.f;
     }
     __syncthreads();
-    float acc[TT][4];
+    const int lane = tid & 63, wave = tid >> 6;
 #pragma unroll
-    for (int tt = 0; tt < TT; ++tt)
+    for (int tt = 0; tt < TT; ++tt) {
+        // values 0..3: this lane's experts if q = 0, 4..7 if q = 1; the
+        // other four are exact zeros
+        float acc[kRtE];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) acc[tt][c] = 0.f;
+        for (int c = 0; c < kRtE; ++c) acc[c] = 0.f;
 #pragma unroll
-    for (int r = 0; r < NSB; ++r)
+        for (int r = 0; r < RPT; ++r) {
+            const float xv = rows_on ? xs[tt][g + G * r] : 0.f;
 #pragma unroll
-        for (int tt = 0; tt < TT; ++tt) {
-            const float xv = xs[tt][g + 32 * r];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) acc[tt][c] = __builtin_fmaf(xv, wv[r][c], acc[tt][c]);
+            for (int c = 0; c < 4; ++c) {
+                const float p = __builtin_fmaf(xv, wv[r][c], q ? acc[4 + c] : acc[c]);
+                acc[c] = q ? acc[c] : p;
+                acc[4 + c] = q ? p : acc[4 + c];
+            }
         }
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) red[g][tt][4 * q + c] = acc[tt][c];
+        // expert ee's sum over the wave ends on lanes 8ee..8ee+7
+        const float sum = wave_sum_n<kRtE>(acc);
+        if ((lane & 7) == 0) red[wave][tt][lane >> 3] = sum;
+    }
     __syncthreads();
     if (tid < TT * kRtE) {
         const int tt = tid / kRtE, ee = tid % kRtE;
         const int eg = ec * kRtE + ee;
-        if (tt < nt && eg < a.E) {
-            float s = red[0][tt][ee];
-#pragma unroll
-            for (int gg = 1; gg < 32; ++gg) s += red[gg][tt][ee];
-            a.part[((size_t)(t0 + tt) * a.E + eg) * KS + ks] = s;
-        }
+        if (tt < nt && eg < a.E)
+            a.part[((size_t)(t0 + tt) * a.E + eg) * KS + ks] =
+                ((red[0][tt][ee] + red[1][tt][ee]) + red[2][tt][ee]) + red[3][tt][ee];
     }
 }
 
 template <int FMT, int LPR, int NSBL, int TT>
 __global__ void __launch_bounds__(256)
 gemv_front_kernel(GemvArgs a) {
+    // shared-expert workgroups first (each starts on a CU of its own), then
+    // the router's, from a multiple of kXcds on
     const int b = blockIdx.x;
-    if (b < a.n_router_blocks) {
-        router_role<TT, (LPR / 8) * NSBL>(a, b);
+    if (b >= a.n_shared_pad) {
+        router_role<TT, (LPR / 8) * NSBL>(a, b - a.n_shared_pad);
         return;
     }
     // shared expert: blocks per token = shared_rows_blocks, kShWaves waves each
-    const int sb = b - a.n_router_blocks;
+    const int sb = b;
+    if (sb >= a.shared_rows_blocks * a.T) return;   // padding
     const int t = sb / a.shared_rows_blocks;
     const int rblk = sb % a.shared_rows_blocks;
     const int Iloc = a.iloc, i0 = a.i0;   // the shared expert has the routed width
@@ -434,18 +468,19 @@ gemv_gateup_kernel(GemvArgs a) {
     int e;
     if (a.route) {
         // every wave selects for itself (the waves sit on different SIMDs:
-        // no barrier, no LDS round trip); slot j's expert from lane j.  The
-        // first wave of workgroup (0, t*k) also writes the token's routing.
+        // no barrier, no LDS round trip), stopping at slot j, whose expert
+        // lane j holds.  The first wave of workgroup (0, t*k) fills all k
+        // slots and writes the token's routing.
         if (blockIdx.x == 0 && j == 0 && threadIdx.x < 64) {
             const int my_e = wave_topk<4, kRouterSplits>(a.part, a.E, a.k, t,
                                                          a.idx_out + (size_t)t * a.k,
                                                          a.w_out + (size_t)t * a.k);   // E <= 256
-            e = __shfl(my_e, j, 64);
+            e = __builtin_amdgcn_readfirstlane(my_e);
         } else {
             float my_l, top;
             int my_e;
-            wave_topk_select<4, kRouterSplits>(a.part, a.E, a.k, t, my_l, my_e, top);
-            e = __shfl(my_e, j, 64);
+            wave_topk_select<4, kRouterSplits>(a.part, a.E, j + 1, t, my_l, my_e, top);
+            e = __builtin_amdgcn_readlane(my_e, j);
         }
     } else {
         e = a.idx[(size_t)t * a.k + j];
@@ -629,8 +664,7 @@ static hipError_t launch_front(GemvArgs& a, bool route, bool shared, const WsLay
     const int nsb = a.H / kSbWeights;
     a.part = reinterpret_cast<float*>(ws + L.router_part);
     const int TT = a.T == 1 ? 1 : 4;
-    const int n_ec = (a.E + kRtE - 1) / kRtE;
-    a.n_router_blocks = route ? ((a.T + TT - 1) / TT) * n_ec * kRouterSplits : 0;
+    a.n_router_blocks = route ? ((a.T + TT - 1) / TT) * router_blocks_per_tile(a.E) : 0;
     int n_shared = 0;
     if (shared) {
         const int rows_per_block = kShWaves * kShSteps * (64 / lanes_per_row(nsb));
@@ -638,8 +672,10 @@ static hipError_t launch_front(GemvArgs& a, bool route, bool shared, const WsLay
         a.shared_rows_blocks = (Iloc + rows_per_block - 1) / rows_per_block;
         n_shared = a.shared_rows_blocks * a.T;
     }
+    // router workgroups start at a multiple of kXcds (their XCD mapping)
+    a.n_shared_pad = a.n_router_blocks > 0 ? (n_shared + kXcds - 1) / kXcds * kXcds : n_shared;
     if (a.n_router_blocks + n_shared == 0) return hipSuccess;
-    MOE_DISPATCH_H(nsb, launch_front_t, a, n_shared, c);
+    MOE_DISPATCH_H(nsb, launch_front_t, a, a.n_shared_pad, c);
     return hipGetLastError();
 }
 

@@ -25,6 +25,7 @@ __device__ __forceinline__ float key_logit(int k) {
     return __builtin_bit_cast(float, k < 0 ? k ^ 0x7fffffff : k);
 }
 constexpr int kKeyNone = (int)0x80000000;
+constexpr int kFastK = 8;   // slots the branch-free selection pass covers
 
 // Wave-wide maximum of int keys, returned wave-uniform: within each 16-lane
 // row by DPP moves (xor 1, xor 2, half-row mirror, row mirror), then row 0
@@ -55,16 +56,18 @@ __device__ __forceinline__ float row_sum(float v) {
     return v;
 }
 
-// part: [T][E][KS] partial logits.  Writes the k slots of token t to
-// idx_row[0..k), w_row[0..k) (global or LDS).  Lane l holds experts l, l+64,
+// part: [T][E][KS] partial logits.  Fills the first k slots of token t (a
+// caller that needs only slot j passes k = j + 1: the rounds are greedy, so
+// the first slots do not depend on how many follow).  Lane l holds experts l, l+64,
 // ... (NE per lane: E <= 64*NE); every partial load is issued before any sum,
 // and each expert's partials are added in ascending split order.
 //
 // Each round takes the wave maximum m of the remaining keys and gives the
-// next slots to every expert holding m, in ascending expert index (ballots
-// of key == m, scanned from the lowest expert block), so ties go to the
-// lower index; a tie group larger than the slots left is cut at the lowest
-// indices.  Selected experts' keys become INT32_MIN.  A NaN logit counts as
+// next slot to the lowest-indexed expert holding m (ballots of key == m in
+// scalar registers), so tied experts fill consecutive slots in ascending
+// index and a tie group larger than the slots left is cut at the lowest
+// indices.  The selected expert's key becomes INT32_MIN.  For k <= kFastK a
+// branch-free pass runs first and the exact rounds run only after a tie.  A NaN logit counts as
 // -inf: never preferred over a number.  Lane j keeps slot j (its logit in
 // my_l, its expert in my_e); top is the largest logit.
 template <int NE, int KS>
@@ -106,8 +109,55 @@ __device__ __forceinline__ void wave_topk_select(const float* __restrict__ part,
     my_l = -INFINITY;
     top = 0.f;
     my_e = 0;
-    int j = 0;   // slots filled (wave-uniform)
-    while (j < k) {
+    if (k <= kFastK) {
+        // fast pass: unrolled rounds without data-dependent branches.  A
+        // round clears every holder of the maximum by value, so the next
+        // round's maximum waits only for the compare and the clear; the slot
+        // bookkeeping (the holder's index from the ballots, in scalar
+        // registers) runs beside it.  A round with more than one holder is a
+        // tie: the exact pass below then reruns the selection.
+        int kept[NE];
+#pragma unroll
+        for (int i = 0; i < NE; ++i) kept[i] = key[i];
+        bool tie = false;
+        int m = key[0];
+#pragma unroll
+        for (int i = 1; i < NE; ++i) m = max(m, key[i]);
+        m = wave_max_key(m);
+        top = key_logit(m);
+#pragma unroll
+        for (int j = 0; j < kFastK; ++j) {
+            int e = 0, hits = 0;
+#pragma unroll
+            for (int i = NE - 1; i >= 0; --i) {
+                const bool hit = key[i] == m;
+                const uint64_t bl = __builtin_amdgcn_ballot_w64(hit);
+                if (hit) key[i] = kKeyNone;
+                hits += __builtin_popcountll(bl);
+                if (bl != 0) e = (int)__builtin_ctzll(bl) + 64 * i;
+            }
+            // the next round's maximum comes before this round's exit test,
+            // so the scalar bookkeeping below shares its straight-line block
+            int mn = key[0];
+#pragma unroll
+            for (int i = 1; i < NE; ++i) mn = max(mn, key[i]);
+            mn = wave_max_key(mn);
+            asm volatile("" ::"s"(mn));   // keeps it above the exit test (no sinking)
+            tie |= hits != 1;
+            const bool mine = lane == j;   // selects, not a branch: nothing waits for e
+            my_l = mine ? key_logit(m) : my_l;
+            my_e = mine ? e : my_e;
+            if (j + 1 == k) break;
+            m = mn;
+        }
+        if (!tie) return;
+#pragma unroll
+        for (int i = 0; i < NE; ++i) key[i] = kept[i];
+        my_l = -INFINITY;
+        my_e = 0;
+    }
+    // exact pass: one expert per round, the lowest index holding the maximum
+    for (int j = 0; j < k; ++j) {   // j: slots filled (wave-uniform)
         int m = key[0];
 #pragma unroll
         for (int i = 1; i < NE; ++i) m = max(m, key[i]);
@@ -115,20 +165,18 @@ __device__ __forceinline__ void wave_topk_select(const float* __restrict__ part,
         if (m == kKeyNone) break;   // nothing left (cannot happen for k <= E)
         const float ml = key_logit(m);
         if (j == 0) top = ml;
+        int e = 0;
 #pragma unroll
-        for (int i = 0; i < NE; ++i) {
-            const bool hit = key[i] == m;
-            uint64_t b = __builtin_amdgcn_ballot_w64(hit);
-            if (hit) key[i] = kKeyNone;
-            while (b != 0 && j < k) {
-                const int wl = (int)__builtin_ctzll(b);
-                b &= b - 1;
-                if (lane == j) {
-                    my_l = ml;
-                    my_e = wl + 64 * i;
-                }
-                ++j;
-            }
+        for (int i = NE - 1; i >= 0; --i) {
+            const uint64_t bl = __builtin_amdgcn_ballot_w64(key[i] == m);
+            if (bl != 0) e = (int)__builtin_ctzll(bl) + 64 * i;
+        }
+#pragma unroll
+        for (int i = 0; i < NE; ++i)
+            if (lane + 64 * i == e) key[i] = kKeyNone;
+        if (lane == j) {
+            my_l = ml;
+            my_e = e;
         }
     }
 }
