@@ -467,21 +467,27 @@ gemv_gateup_kernel(GemvArgs a) {
     X.load(a.x + (size_t)t * a.H);   // independent of the routing: in flight during the top-k
     int e;
     if (a.route) {
-        // every wave selects for itself (the waves sit on different SIMDs:
-        // no barrier, no LDS round trip), stopping at slot j, whose expert
-        // lane j holds.  The first wave of workgroup (0, t*k) fills all k
-        // slots and writes the token's routing.
-        if (blockIdx.x == 0 && j == 0 && threadIdx.x < 64) {
-            const int my_e = wave_topk<4, kRouterSplits>(a.part, a.E, a.k, t,
-                                                         a.idx_out + (size_t)t * a.k,
-                                                         a.w_out + (size_t)t * a.k);   // E <= 256
-            e = __builtin_amdgcn_readfirstlane(my_e);
-        } else {
-            float my_l, top;
-            int my_e;
-            wave_topk_select<4, kRouterSplits>(a.part, a.E, j + 1, t, my_l, my_e, top);
-            e = __builtin_amdgcn_readlane(my_e, j);
+        // the first wave selects (stopping at slot j, whose expert lane j
+        // holds) and hands the expert to the others through LDS; the first
+        // wave of workgroup (0, t*k) fills all k slots and writes the
+        // token's routing
+        __shared__ int s_e;
+        if (threadIdx.x < 64) {
+            if (blockIdx.x == 0 && j == 0) {
+                const int my_e = wave_topk<4, kRouterSplits>(a.part, a.E, a.k, t,
+                                                             a.idx_out + (size_t)t * a.k,
+                                                             a.w_out + (size_t)t * a.k);   // E <= 256
+                e = __builtin_amdgcn_readfirstlane(my_e);
+            } else {
+                float my_l, top;
+                int my_e;
+                wave_topk_select<4, kRouterSplits>(a.part, a.E, j + 1, t, my_l, my_e, top);
+                e = __builtin_amdgcn_readlane(my_e, j);
+            }
+            if (threadIdx.x == 0) s_e = e;
         }
+        __syncthreads();
+        e = s_e;
     } else {
         e = a.idx[(size_t)t * a.k + j];
     }
