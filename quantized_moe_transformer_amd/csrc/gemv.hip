@@ -152,6 +152,14 @@ __device__ __forceinline__ void load16(const float* p, float* v) {
     }
 }
 
+// A wave-uniform read through the scalar cache (constant address space): its
+// wait is on the scalar counter, not behind the vector loads in flight.  Only
+// for data no kernel of the same grid writes.
+template <typename T>
+__device__ __forceinline__ T scalar_read(const T* p) {
+    return *(const __attribute__((address_space(4))) T*)p;
+}
+
 // 16-byte load of streamed-once weight bytes, marked non-temporal.
 __device__ __forceinline__ uint4 stream_load(const uint8_t* p) {
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -528,19 +536,30 @@ gemv_down_kernel(GemvArgs a, int lprd) {
     const int cg = active ? task >> 1 : 0, hh = task & 1;
     const int obase = blockIdx.x * kDnPasses * rs;
     const int H = a.H;
-    for (int j = wave; j < a.nslot; j += nw) {
+    for (int jv = wave; jv < a.nslot; jv += nw) {
+        const int j = __builtin_amdgcn_readfirstlane(jv);   // wave-uniform
+        // the routing reads first, then h (it does not depend on the
+        // routing): the wait for the expert index covers only the routing
+        // reads, and the h sums wait only for h (vector loads complete in
+        // issue order); the weight loads follow
+        int e = 0;
+        float wj = a.sw;
+        if (j < a.k) {
+            e = scalar_read(a.idx + (size_t)t * a.k + j);
+            wj = scalar_read(a.w + (size_t)t * a.k + j);
+        }
+        const float* hp = a.hbuf + (size_t)(t * a.nslot + j) * a.hstride + 64 * cg + 16 * hh;
+        float hl[16], hu[16];
+        load16(hp, hl);
+        load16(hp + 32, hu);
         const uint8_t* D;
         int Iexp;
         bool valid = true;
-        float wj;
         if (j < a.k) {
-            const int e = a.idx[(size_t)t * a.k + j];
-            wj = a.w[(size_t)t * a.k + j];
             valid = (unsigned)e < (unsigned)a.E;
             D = a.down + (size_t)(valid ? e : 0) * ((size_t)H * a.I / kSbWeights * SBB);
             Iexp = a.I;
         } else {
-            wj = a.sw;
             D = a.sh_down;
             Iexp = a.Is;
         }
@@ -564,10 +583,7 @@ gemv_down_kernel(GemvArgs a, int lprd) {
             }
             hd[ps] = load_head_f<FMT>(sb);
         }
-        const float* hp = a.hbuf + (size_t)(t * a.nslot + j) * a.hstride + 64 * cg + 16 * hh;
-        float hl[16], hu[16];
-        load16(hp, hl);
-        load16(hp + 32, hu);
+        asm volatile("" ::: "memory");   // every load above is issued before the sums
         float sa = 0.f, sb2 = 0.f;
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
