@@ -51,17 +51,17 @@ FP16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak
 # the counters no longer describe the kernel and traffic is reported as null.
 TRAFFIC = {
     # decode T=1, 288 dispatches: FETCH 4751.4 KiB x 1.99980, WRITE 16.1 KiB x 1.0
-    "gemv_gateup": {"sources_sha256": "f5ab53377e4557f39f1e63d786e62a7788f7bd797ed8d233b8b3539bd277a1de",
-                    "fetch_bytes": 9729933, "write_bytes": 16448},
-    # prefill T=4096, 15 dispatches: FETCH 224715.9 KiB x 1.99980, WRITE 36864.0 KiB x 1.0
+    "gemv_gateup": {"sources_sha256": "27f0eba9449c3df4f6b362c6d48e3b3048d8184a2ce10ca323dd4dda0e3e3c7b",
+                    "fetch_bytes": 9729881, "write_bytes": 16448},
+    # prefill T=4096, 15 dispatches: FETCH 224654.4 KiB x 1.99980, WRITE 36864.0 KiB x 1.0
     "gemm_gateup": {"sources_sha256": "fbf31bb999119bcf1a13a6ccf1acb7919a5233154dde93dbdc8bdbe6ede20d1a",
-                    "fetch_bytes": 460172193, "write_bytes": 37748736},
+                    "fetch_bytes": 460046219, "write_bytes": 37748736},
     # MXFP4 decode T=1, 288 dispatches: FETCH 4756.7 KiB x 1.99980, WRITE 16.1 KiB x 1.0
-    "gemv_gateup_mx": {"sources_sha256": "f5ab53377e4557f39f1e63d786e62a7788f7bd797ed8d233b8b3539bd277a1de",
-                    "fetch_bytes": 9740745, "write_bytes": 16448},
-    # MXFP4 prefill T=4096, 15 dispatches: FETCH 224547.9 KiB x 1.99980, WRITE 36864.0 KiB x 1.0
+    "gemv_gateup_mx": {"sources_sha256": "27f0eba9449c3df4f6b362c6d48e3b3048d8184a2ce10ca323dd4dda0e3e3c7b",
+                    "fetch_bytes": 9740744, "write_bytes": 16448},
+    # MXFP4 prefill T=4096, 15 dispatches: FETCH 224585.4 KiB x 1.99980, WRITE 36864.0 KiB x 1.0
     "gemm_gateup_mx": {"sources_sha256": "fbf31bb999119bcf1a13a6ccf1acb7919a5233154dde93dbdc8bdbe6ede20d1a",
-                    "fetch_bytes": 459828078, "write_bytes": 37748736},
+                    "fetch_bytes": 459904819, "write_bytes": 37748736},
 }
 FETCH_SIZE_FACTOR = 1.99980   # plain 256 MiB copy: true bytes read / FETCH_SIZE bytes
 WRITE_SIZE_FACTOR = 1.0

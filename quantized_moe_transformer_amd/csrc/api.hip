@@ -127,7 +127,7 @@ WsLayout ws_layout(const moe_layer_desc& d, int T, int iloc) {
     const size_t Iloc = (size_t)iloc;
     const size_t nslot = k + (d.shared_inter > 0 ? 1 : 0);
     size_t off = 0;
-    L.router_ks = router_splits(T, d.hidden);
+    L.router_ks = router_splits(T);
     L.router_part = off;  off = align256(off + (size_t)L.router_ks * Tz * E * 4);
     const bool big = T > kRouterSmallMaxT;
     L.x_lo = off;         off = align256(off + (big ? Tz * H * 2 : 0));

@@ -599,7 +599,7 @@ gemv_down_kernel(GemvArgs a, int lprd) {
         }
     }
     __syncthreads();
-    if (threadIdx.x < kDnPasses * rs) {
+    if ((int)threadIdx.x < kDnPasses * rs) {
         const int r = threadIdx.x;
         const int o = obase + r;
         if (o < H) {

@@ -34,7 +34,7 @@ struct WsLayout {
     int router_ks;        // router K-splits
 };
 
-int router_splits(int T, int H);
+int router_splits(int T);
 // iloc: the intermediate rows per expert that the call computes (I, or a shard's)
 WsLayout ws_layout(const moe_layer_desc& d, int T, int iloc);
 inline int bucket_blocks(int T, int k) { return (T * k + 1023) / 1024; }

@@ -19,7 +19,7 @@ namespace moe {
 
 constexpr int kRgSplit = 2;   // K splits of the matrix-core router (partials added by the top-k)
 
-int router_splits(int T, int H) { return T <= kRouterSmallMaxT ? kRouterSplits : kRgSplit; }
+int router_splits(int T) { return T <= kRouterSmallMaxT ? kRouterSplits : kRgSplit; }
 
 // ---------------------------------------------------------------------------
 // Many rows: logits on the fp16 matrix cores with fp32 accuracy.  Each fp32
