@@ -427,6 +427,31 @@ def test_other_widths(H, I, T, path, tol, fmt):
         assert rel_err(red.cpu().numpy(), ref) <= tol
 
 
+@pytest.mark.parametrize("E,k", [(37, 5), (100, 8), (300, 6)])
+@pytest.mark.parametrize("T", [1, 5, 32])
+def test_odd_expert_counts(E, k, T):
+    """Expert counts that leave the small-T router's 8-expert workgroups
+    partial (E % 8 != 0), its 32-expert line groups partial (E % 32 != 0) or
+    its per-lane expert count above four (E > 256: the router runs on its
+    own, with 16 keys per lane in the top-k); E = 37 also takes the scalar
+    router-matrix loads (E % 4 != 0).  Routing exact against the oracle up to
+    near-ties; the GEMV path's output to its tolerance."""
+    shp = mi.LayerShape(H=512, E=E, k=k, I=256, Is=256)
+    layer = mi.make_layer(shp, seed=41)
+    x = mi.make_tokens(shp, 41, T)
+    dl = DeviceLayer.from_shape(layer, shp)
+    say(f"odd experts E={E} k={k} T={T}")
+    oi, ow, owd, logits = oracle.router(x, layer["router_w"], k)
+    gi, gw = run_router(dl, x)
+    exact, exempt, wrong = topk_check(gi, oi, logits)
+    assert len(wrong) == 0
+    assert np.abs(gw[exact] - owd[exact]).max() <= 2e-5
+    got, used = run_forward(dl, x, qm.MOE_PATH_GEMV)
+    assert used == qm.MOE_PATH_GEMV
+    ol = oracle.Layer.from_shape(layer, shp)
+    assert rel_err(got[exact], oracle.forward(ol, x)[exact]) <= GEMV_TOL
+
+
 @pytest.mark.parametrize("E,k,Is", [(8, 8, 128), (1, 1, 0), (4, 3, 0)])
 @pytest.mark.parametrize("path,tol", [(qm.MOE_PATH_GEMV, GEMV_TOL), (qm.MOE_PATH_MFMA, MFMA_TOL)])
 @pytest.mark.parametrize("fmt", [0, 1])
