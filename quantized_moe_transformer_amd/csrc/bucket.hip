@@ -85,18 +85,30 @@ bucket_scan_kernel(int nblk, int E, int T, int shared, const int32_t* __restrict
             for (int j = 0; j < kBatch; ++j) c += v[j];
         }
     const int tiles = (c + kTileM - 1) / kTileM;
-    sc[e] = e < E ? c : 0;
-    st[e] = e < E ? tiles : 0;
-    __syncthreads();
-    // Hillis-Steele inclusive scans of counts and tiles
-    for (int off = 1; off < 1024; off <<= 1) {
-        const int a = e >= off ? sc[e - off] : 0;
-        const int b = e >= off ? st[e - off] : 0;
-        __syncthreads();
-        sc[e] += a;
-        st[e] += b;
-        __syncthreads();
+    // inclusive scans of counts and tiles: within each wave by lane shifts,
+    // then plus the totals of the waves before (integers: exact)
+    const int lane = e & 63, wv = e >> 6;
+    int ic = e < E ? c : 0, it = e < E ? tiles : 0;
+    for (int off = 1; off < 64; off <<= 1) {
+        const int a = __shfl_up(ic, off, 64), b = __shfl_up(it, off, 64);
+        if (lane >= off) {
+            ic += a;
+            it += b;
+        }
     }
+    __shared__ int32_t wc[16], wt[16];
+    if (lane == 63) {
+        wc[wv] = ic;
+        wt[wv] = it;
+    }
+    __syncthreads();
+    for (int w = 0; w < wv; ++w) {
+        ic += wc[w];
+        it += wt[w];
+    }
+    sc[e] = ic;
+    st[e] = it;
+    __syncthreads();
     if (e < E) {
         const int excl = sc[e] - c;
         counts[e] = c;
