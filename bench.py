@@ -51,17 +51,17 @@ FP16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak
 # the counters no longer describe the kernel and traffic is reported as null.
 TRAFFIC = {
     # decode T=1, 288 dispatches: FETCH 4751.4 KiB x 1.99980, WRITE 16.1 KiB x 1.0
-    "gemv_gateup": {"sources_sha256": "27f0eba9449c3df4f6b362c6d48e3b3048d8184a2ce10ca323dd4dda0e3e3c7b",
-                    "fetch_bytes": 9729910, "write_bytes": 16448},
-    # prefill T=4096, 15 dispatches: FETCH 224641.9 KiB x 1.99980, WRITE 36864.0 KiB x 1.0
+    "gemv_gateup": {"sources_sha256": "1a2aead47a400e21c45c8b1a87120e74c69d72231148bd03f0bcac7af52bcdb3",
+                    "fetch_bytes": 9729961, "write_bytes": 16448},
+    # prefill T=4096, 15 dispatches: FETCH 224666.3 KiB x 1.99980, WRITE 36864.0 KiB x 1.0
     "gemm_gateup": {"sources_sha256": "fbf31bb999119bcf1a13a6ccf1acb7919a5233154dde93dbdc8bdbe6ede20d1a",
-                    "fetch_bytes": 460020545, "write_bytes": 37748736},
+                    "fetch_bytes": 460070485, "write_bytes": 37748736},
     # MXFP4 decode T=1, 288 dispatches: FETCH 4756.7 KiB x 1.99980, WRITE 16.1 KiB x 1.0
-    "gemv_gateup_mx": {"sources_sha256": "27f0eba9449c3df4f6b362c6d48e3b3048d8184a2ce10ca323dd4dda0e3e3c7b",
-                    "fetch_bytes": 9740724, "write_bytes": 16448},
-    # MXFP4 prefill T=4096, 15 dispatches: FETCH 224572.7 KiB x 1.99980, WRITE 36864.0 KiB x 1.0
+    "gemv_gateup_mx": {"sources_sha256": "1a2aead47a400e21c45c8b1a87120e74c69d72231148bd03f0bcac7af52bcdb3",
+                    "fetch_bytes": 9740726, "write_bytes": 16448},
+    # MXFP4 prefill T=4096, 15 dispatches: FETCH 224579.4 KiB x 1.99980, WRITE 36864.0 KiB x 1.0
     "gemm_gateup_mx": {"sources_sha256": "fbf31bb999119bcf1a13a6ccf1acb7919a5233154dde93dbdc8bdbe6ede20d1a",
-                    "fetch_bytes": 459878872, "write_bytes": 37748736},
+                    "fetch_bytes": 459892643, "write_bytes": 37748736},
 }
 FETCH_SIZE_FACTOR = 1.99980   # plain 256 MiB copy: true bytes read / FETCH_SIZE bytes
 WRITE_SIZE_FACTOR = 1.0

@@ -4,14 +4,16 @@
 // each byte is read once and used once, so the work is bound by HBM
 // bandwidth (page "Distributed CPU: Zip Fusion Beyond Tensor Parallelism",
 // section "Decode vs Prefill: Same Weights, Different Bottlenecks").  On this
-// chip every dependent kernel adds a fixed ~2 us to a step, so the layer runs
-// as three kernels, each streaming its share of the bytes:
+// chip every dependent kernel adds a fixed cost of a few us to a step, so the
+// layer runs as three kernels, each streaming its share of the bytes:
 //
-//   front   the router's split-K partial logits and, side by side in the same
-//           grid, the shared expert's gate/up + SwiGLU, which needs no routing;
-//   gateup  every workgroup first sums its token's partial logits in a fixed
-//           order and runs the top-k (one wave, identical in every workgroup of
-//           the token), then gate/up + SwiGLU of its routed expert's rows;
+//   front   the router's split-K partial logits (many small XCD-grouped
+//           workgroups) and, side by side in the same grid, the shared
+//           expert's gate/up + SwiGLU, which needs no routing;
+//   gateup  the first wave of every workgroup sums its token's partial logits
+//           in a fixed order and runs the top-k up to the workgroup's slot
+//           (the same selection in every workgroup of the token), then all
+//           four waves compute gate/up + SwiGLU of the routed expert's rows;
 //   down    down projections, one wave per slot, slot results added in the
 //           selected-slot order with the shared expert last (page "CKE Zip:
 //           From Splitting Tokens To Splitting Qwen3.5 Weights", section "A
