@@ -37,9 +37,8 @@
  *     w = d*sc*q - dmin*m.
  *   - Orientation: one row per output feature, reduction dimension contiguous,
  *     superblocks laid over the flat row-major array.
- *   - Top-k: experts ordered by logit (descending), ties to the lower index;
- *     the comparison is made on the fp32 rounding of the exact logit, the
- *     precision the GPU kernel decides in.  Slot j holds the j-th expert.
+ *   - Top-k: experts ordered by their exact (double) logit, descending,
+ *     ties to the lower index.  Slot j holds the j-th expert.
  *   - Routing weights: softmax over all E logits, then renormalised over the
  *     k selected ones.
  *   - SwiGLU: h = silu(gate) * up, silu(z) = z / (1 + exp(-z)).
@@ -197,7 +196,8 @@ int oracle_dequant(const uint8_t *blob, int bits, int64_t n_sb, float *out)
 /* ------------------------------------------------------------------------ */
 
 /* Route one token: logits[e] = sum_h x[h]*Wr[h][e] (double, ascending h); the
- * k largest (compared as fp32, ties to the lower index) in descending order;
+ * k largest (compared exactly, in double; ties to the lower index) in
+ * descending order;
  * p = softmax over all E; w_j = p[idx_j] / sum of the selected p. */
 static void route_token(const float *x, int H, const float *Wr, int E, int k,
                         double *logits, int32_t *idx, double *w)
@@ -216,7 +216,7 @@ static void route_token(const float *x, int H, const float *Wr, int E, int k,
             for (int jj = 0; jj < j; ++jj)
                 if (idx[jj] == e) taken = 1;
             if (taken) continue;
-            if (best < 0 || (float)logits[e] > (float)logits[best])
+            if (best < 0 || logits[e] > logits[best])
                 best = e;          /* strict '>' keeps the lower index on ties */
         }
         idx[j] = best;

@@ -196,6 +196,19 @@ def test_router_weights_ignore_unselected_logits():
     assert np.allclose(wd, wd2, rtol=1e-14, atol=0)
 
 
+def test_router_orders_exact_logits():
+    # logits 1 and 1 + 2^-30 are equal once rounded to fp32; the exact order
+    # puts expert 1 first (an oracle that ranked fp32-rounded logits would keep
+    # the lower index, expert 0, first)
+    x = np.array([[1.0, 2.0 ** -30]], np.float32)
+    wr = np.array([[1.0, 1.0], [0.0, 1.0]], np.float32)
+    idx, _, wd, logits = oracle.router(x, wr, 2)
+    assert np.float32(logits[0, 0]) == np.float32(logits[0, 1])
+    assert logits[0, 1] - logits[0, 0] == 2.0 ** -30
+    assert list(idx[0]) == [1, 0]
+    assert math.isclose(wd[0, 0] / wd[0, 1], math.exp(2.0 ** -30), rel_tol=1e-15)
+
+
 def test_router_k_equals_e_is_full_softmax():
     x = np.array([[1.0]], np.float32)
     wr = np.array([[0.0, 1.0, 2.0]], np.float32)
