@@ -286,7 +286,10 @@ int moe_rmsnorm_apply(const float *x, int32_t T, int32_t cols, int64_t ldx,
  * MOE_SB_MXFP4: MXFP4) into n_sb*256 values in flat order.  out_dtype 0: fp32
  * (exactly the round-to-nearest-even fp32 value of d*sc*q - dmin*m, or of
  * X_j * value(code); MXFP4 scale byte 255 gives NaN); 1: bf16 and 2: fp16,
- * each the round-to-nearest-even conversion of that fp32 value.
+ * each the round-to-nearest-even conversion of that fp32 value.  For the
+ * K-quant formats the fp16 output is produced by the same device function
+ * that forms the grouped-GEMM path's fp16 matrix-core operands, so it shows
+ * bit for bit the weights that path multiplies.
  */
 #define MOE_SB_MXFP4 14
 int moe_dequant(const uint8_t *sbs, int32_t bits, int64_t n_sb, int32_t out_dtype,

@@ -3,6 +3,7 @@
 // contracts) in include/moe.h.
 #include <string.h>
 
+
 #include "launch.h"
 
 namespace moe {
@@ -44,6 +45,36 @@ dequant_kernel(const uint8_t* __restrict__ sbs, int bits, int64_t n_sb, int out_
             reinterpret_cast<uint16_t*>(out)[o] = f32_to_bf16_rne(wv);
         else
             reinterpret_cast<_Float16*>(out)[o] = (_Float16)wv;
+    }
+}
+
+// fp16 output of the K-quant formats: one thread per 16-byte code piece
+// (superblock b, sub-block pair c, half hh), through kq_piece_f16 -- the very
+// function whose results the grouped GEMM's producer waves store as matrix-core
+// operands -- written to elements 64c + 16hh + [0,16) and 64c + 32 + 16hh +
+// [0,16) of the superblock.
+template <bool HIGH>
+__global__ void __launch_bounds__(256)
+dequant_f16_kernel(const uint8_t* __restrict__ sbs, int64_t n_pieces,
+                   _Float16* __restrict__ out) {
+    constexpr int SBB = HIGH ? kQ5Bytes : kQ4Bytes;
+    for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < n_pieces;
+         p += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t b = p >> 3;
+        const int c = (int)(p >> 1) & 3, hh = (int)p & 1;
+        const uint8_t* sb = sbs + b * SBB;
+        const SbHead hd = load_head(sb);
+        const uint4 qs = *reinterpret_cast<const uint4*>(sb + (HIGH ? 48 : 16) + 32 * c + 16 * hh);
+        const uint4 qh = HIGH ? *reinterpret_cast<const uint4*>(sb + 16 + 16 * hh) : qs;
+        uint32_t lo[8], hi[8];
+        kq_piece_f16<HIGH>(hd, qs, qh, c, lo, hi);
+        _Float16* row = out + b * kSbWeights + 64 * c;
+        uint4* d0 = reinterpret_cast<uint4*>(row + 16 * hh);
+        uint4* d1 = reinterpret_cast<uint4*>(row + 32 + 16 * hh);
+        d0[0] = uint4{lo[0], lo[1], lo[2], lo[3]};
+        d0[1] = uint4{lo[4], lo[5], lo[6], lo[7]};
+        d1[0] = uint4{hi[0], hi[1], hi[2], hi[3]};
+        d1[1] = uint4{hi[4], hi[5], hi[6], hi[7]};
     }
 }
 
@@ -109,6 +140,16 @@ hipError_t launch_reduce(const float* const* partials, int n, int64_t count, con
 
 hipError_t launch_dequant(const uint8_t* sbs, int bits, int64_t n_sb, int out_dtype, void* out,
                           hipStream_t s) {
+    if (out_dtype == 2 && bits != MOE_SB_MXFP4) {
+        const int64_t n_pieces = n_sb * 8;
+        const int64_t nb = (n_pieces + 255) / 256;
+        const unsigned blocks = (unsigned)(nb < 65536 ? nb : 65536);
+        if (bits == 5)
+            dequant_f16_kernel<true><<<blocks, 256, 0, s>>>(sbs, n_pieces, (_Float16*)out);
+        else
+            dequant_f16_kernel<false><<<blocks, 256, 0, s>>>(sbs, n_pieces, (_Float16*)out);
+        return hipGetLastError();
+    }
     const int64_t blocks = n_sb < 65536 ? n_sb : 65536;
     dequant_kernel<<<(unsigned)blocks, 256, 0, s>>>(sbs, bits, n_sb, out_dtype, out);
     return hipGetLastError();

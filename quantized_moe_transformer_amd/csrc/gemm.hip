@@ -63,21 +63,11 @@ constexpr int kProducers = 4;           // producer waves
 constexpr int kGemmThreads = 64 * (kConsumers + kProducers);
 constexpr int kBTasks = kTN * 2 / (64 * kProducers);   // 16-byte code pieces per producer thread
 
-// Dequantise one 16-byte code piece (32 weights: sub-block 2c low nibbles and
-// sub-block 2c+1 high nibbles) to fp16 and store it into an LDS row at k
-// offsets 16*hh + [0,16) and 32 + 16*hh + [0,16).
-//
-// Two weights per instruction on the packed fp16 pipe.  A byte permute puts
-// the code bytes of two neighbouring k into the two halves of a word, and one
-// and-or with the fp16 pattern 0x6400 turns each code q into the number
-// 1024 + q; subtracting 1024 is exact, leaving q as fp16.  Then one packed
-// fused multiply-add gives w = q*(d*sc) - dmin*m, rounded once, with d*sc
-// and dmin*m (exact in fp32) each rounded to fp16 first: w is off by at most
-// 2^-11 (q*|d*sc| + |dmin*m|) plus its own rounding, where rounding the exact
-// value alone would give 2^-11 |w|.  The mixed-precision fma that keeps the
-// constants in fp32 runs at a quarter of this rate on gfx950.
-typedef _Float16 half2v __attribute__((ext_vector_type(2)));
-
+// Dequantise one 16-byte K-quant code piece (32 weights: sub-block 2c low
+// nibbles and sub-block 2c+1 high nibbles) to fp16 and store it into an LDS
+// row at k offsets 16*hh + [0,16) and 32 + 16*hh + [0,16).  The operands are
+// kq_piece_f16's: the round-to-nearest-even fp16 of the exact fp32 weight,
+// the same function the dequantisation test hook runs.
 // (x & m) | o in one v_and_or_b32 (the compiler splits it into an and and an
 // or when the constants are literals).
 __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t o) {
@@ -90,36 +80,8 @@ template <bool HIGH>
 __device__ __forceinline__ void dequant_piece_to_lds(const SbHead& hd, const uint4& qs,
                                                      const uint4& qh, int c, int hh,
                                                      _Float16* row) {
-    float sca, ma, scb, mb;
-    sub_scale_min(hd, 2 * c, sca, ma);
-    sub_scale_min(hd, 2 * c + 1, scb, mb);
-    const _Float16 dsa = (_Float16)(hd.d * sca), dsb = (_Float16)(hd.d * scb);
-    const _Float16 dma = (_Float16)(hd.dmin * ma), dmb = (_Float16)(hd.dmin * mb);
-    const half2v DSA = {dsa, dsa}, DSB = {dsb, dsb}, NMA = {-dma, -dma}, NMB = {-dmb, -dmb};
-    const half2v K1024 = {(_Float16)-1024.0f, (_Float16)-1024.0f};
-    const uint32_t qw[4] = {qs.x, qs.y, qs.z, qs.w};
-    const uint32_t hw[4] = {qh.x, qh.y, qh.z, qh.w};
     uint32_t lo[8], hi[8];
-#pragma unroll
-    for (int wi = 0; wi < 4; ++wi) {
-        uint32_t l5 = qw[wi], h5 = qw[wi] >> 4;
-        if (HIGH) {
-            l5 = (qw[wi] & 0x0f0f0f0fu) | (((hw[wi] >> (2 * c)) & 0x01010101u) << 4);
-            h5 = ((qw[wi] >> 4) & 0x0f0f0f0fu) | (((hw[wi] >> (2 * c + 1)) & 0x01010101u) << 4);
-        }
-        const uint32_t m = HIGH ? 0x00ff00ffu : 0x000f000fu;
-#pragma unroll
-        for (int pr = 0; pr < 2; ++pr) {
-            // bytes 2pr and 2pr+1 of the word into the two halves
-            const uint32_t sel = pr ? 0x0c030c02u : 0x0c010c00u;
-            const uint32_t pl = __builtin_amdgcn_perm(0u, l5, sel);
-            const uint32_t ph = HIGH ? __builtin_amdgcn_perm(0u, h5, sel) : pl >> 4;
-            const half2v ql = __builtin_bit_cast(half2v, and_or(pl, m, 0x64006400u)) + K1024;
-            const half2v qh2 = __builtin_bit_cast(half2v, and_or(ph, m, 0x64006400u)) + K1024;
-            lo[2 * wi + pr] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(ql, DSA, NMA));
-            hi[2 * wi + pr] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(qh2, DSB, NMB));
-        }
-    }
+    kq_piece_f16<HIGH>(hd, qs, qh, c, lo, hi);
     *reinterpret_cast<uint4*>(row + 16 * hh) = uint4{lo[0], lo[1], lo[2], lo[3]};
     *reinterpret_cast<uint4*>(row + 16 * hh + 8) = uint4{lo[4], lo[5], lo[6], lo[7]};
     *reinterpret_cast<uint4*>(row + 32 + 16 * hh) = uint4{hi[0], hi[1], hi[2], hi[3]};

@@ -38,16 +38,6 @@ namespace moe {
 // lane-level pieces
 // ---------------------------------------------------------------------------
 
-// x & m, computed where the compiler cannot see the mask: with the mask in
-// view it folds it into each later byte extraction (a bit-field extract per
-// code before the convert); opaque, each byte converts in one
-// v_cvt_f32_ubyteN.
-__device__ __forceinline__ uint32_t and_opaque(uint32_t x, uint32_t m) {
-    uint32_t r;
-    asm("v_and_b32 %0, %1, %2" : "=v"(r) : "v"(x), "v"(m));
-    return r;
-}
-
 // Partial dot product of one lane's piece.  xl/xh: the 16 activations under
 // the low / high nibbles; sl/sh their sums.  qh: the 16 high-bit bytes of the
 // piece (5-bit format only).  Codes are unpacked four at a time from masked

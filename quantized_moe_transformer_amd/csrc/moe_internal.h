@@ -87,6 +87,63 @@ __device__ __forceinline__ float kq_weight(float dsc, float dmm, float q) {
     return __builtin_fmaf(q, dsc, -dmm);
 }
 
+// x & m computed where the compiler cannot see the mask: with the mask in
+// view it folds it into each later byte extraction (a bit-field extract per
+// code before the convert); opaque, each byte converts in one
+// v_cvt_f32_ubyteN.
+__device__ __forceinline__ uint32_t and_opaque(uint32_t x, uint32_t m) {
+    uint32_t r;
+    asm("v_and_b32 %0, %1, %2" : "=v"(r) : "v"(x), "v"(m));
+    return r;
+}
+
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float float2v __attribute__((ext_vector_type(2)));
+
+// Two fp32 values to a packed pair of fp16, each rounded to nearest even
+// (v_cvt_pk_f16_f32; fp16 subnormals kept, overflow to inf).
+__device__ __forceinline__ uint32_t pack_f16_rne(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((float2v){a, b}, half2v));
+}
+
+// The 16-bit matrix-core operands of one 16-byte K-quant code piece: 16 codes
+// of sub-block 2c (low nibbles, elements 64c + 16hh + [0,16)) and 16 of
+// sub-block 2c+1 (high nibbles, elements 64c + 32 + 16hh + [0,16)), for the
+// 5-bit format with their high bits from qh (bits 2c and 2c+1 of each byte).
+// Each weight is formed exactly as kq_weight forms it (one fused multiply-add
+// of the exact d*sc and dmin*m: the round-to-nearest-even fp32 weight), then
+// rounded to the nearest-even fp16: lo[w] / hi[w] hold elements 2w, 2w+1 of
+// the two runs of 16.
+template <bool HIGH>
+__device__ __forceinline__ void kq_piece_f16(const SbHead& hd, const uint4& qs, const uint4& qh,
+                                             int c, uint32_t (&lo)[8], uint32_t (&hi)[8]) {
+    float sca, ma, scb, mb;
+    sub_scale_min(hd, 2 * c, sca, ma);
+    sub_scale_min(hd, 2 * c + 1, scb, mb);
+    const float dsa = hd.d * sca, dsb = hd.d * scb;      // exact in fp32
+    const float dma = hd.dmin * ma, dmb = hd.dmin * mb;  // exact in fp32
+    const uint32_t qw[4] = {qs.x, qs.y, qs.z, qs.w};
+    const uint32_t hw[4] = {qh.x, qh.y, qh.z, qh.w};
+#pragma unroll
+    for (int wi = 0; wi < 4; ++wi) {
+        uint32_t l5 = and_opaque(qw[wi], 0x0f0f0f0fu);
+        uint32_t h5 = and_opaque(qw[wi] >> 4, 0x0f0f0f0fu);
+        if (HIGH) {
+            l5 |= ((hw[wi] >> (2 * c)) & 0x01010101u) << 4;
+            h5 |= ((hw[wi] >> (2 * c + 1)) & 0x01010101u) << 4;
+        }
+#pragma unroll
+        for (int pr = 0; pr < 2; ++pr) {
+            const float a0 = (float)((l5 >> (16 * pr)) & 0xffu);
+            const float a1 = (float)((l5 >> (16 * pr + 8)) & 0xffu);
+            const float b0 = (float)((h5 >> (16 * pr)) & 0xffu);
+            const float b1 = (float)((h5 >> (16 * pr + 8)) & 0xffu);
+            lo[2 * wi + pr] = pack_f16_rne(kq_weight(dsa, dma, a0), kq_weight(dsa, dma, a1));
+            hi[2 * wi + pr] = pack_f16_rne(kq_weight(dsb, dmb, b0), kq_weight(dsb, dmb, b1));
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // MXFP4 field decoding (device): OCP MX E8M0 block scales and E2M1 codes
 // ---------------------------------------------------------------------------
