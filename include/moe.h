@@ -31,8 +31,9 @@
  *   - T = 0 is valid and enqueues nothing.  Outputs are overwritten, never
  *     accumulated into.  Inputs must not alias outputs.
  *   - Identical inputs give bit-identical outputs (fixed reduction orders, no
- *     floating-point atomics).  The library keeps no mutable global state;
- *     calls on different streams with different workspaces may overlap.
+ *     floating-point atomics).  Calls on different streams with different
+ *     workspaces may overlap.  The library's only global state is a per-device
+ *     record of its gfx950 check (set once, thread-safe).
  *
  * Weight format (a reading: the pages name Q4_K/Q5_K but print no layout)
  *   A superblock holds 256 weights, in 8 sub-blocks of 32:

@@ -3,6 +3,7 @@
 // contracts) in include/moe.h.
 #include <string.h>
 
+#include <atomic>
 
 #include "launch.h"
 
@@ -245,16 +246,23 @@ static int choose_path(int T, int iloc, const moe_opts* o, int* path) {
     return MOE_OK;
 }
 
-// gfx950 check of the current device, cached per device ordinal.
+constexpr int kMaxDevices = 64;
+
+// gfx950 check of the current device, remembered per device ordinal (0
+// unknown, 1 gfx950, 2 not).  Two threads that race on a first check store
+// the same value.
+static std::atomic<int> g_device_kind[kMaxDevices];
+
 static int check_device() {
-    static int cache[64];   // 0 unknown, 1 gfx950, 2 not (value races are benign: same result)
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return MOE_ENODEVICE;
-    if (dev >= 0 && dev < 64 && cache[dev]) return cache[dev] == 1 ? MOE_OK : MOE_ENODEVICE;
+    const bool slot = dev >= 0 && dev < kMaxDevices;
+    const int known = slot ? g_device_kind[dev].load(std::memory_order_relaxed) : 0;
+    if (known) return known == 1 ? MOE_OK : MOE_ENODEVICE;
     hipDeviceProp_t p;
     if (hipGetDeviceProperties(&p, dev) != hipSuccess) return MOE_ENODEVICE;
     const bool ok = strncmp(p.gcnArchName, "gfx950", 6) == 0;
-    if (dev >= 0 && dev < 64) cache[dev] = ok ? 1 : 2;
+    if (slot) g_device_kind[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
     return ok ? MOE_OK : MOE_ENODEVICE;
 }
 
