@@ -23,8 +23,10 @@
  *     is a hipStream_t (NULL = the default stream).  All work is enqueued on
  *     `stream`; nothing synchronises the host.  Results are valid once the
  *     caller has synchronised the stream.
- *   - The caller owns every buffer, including the workspace.  The library
- *     allocates and frees nothing and keeps no pointer after returning.
+ *   - The caller owns every buffer, including the workspace
+ *     (moe_layer_forward_noalloc uses the library's fixed scratch instead).
+ *     The library allocates and frees nothing and keeps no pointer after
+ *     returning.
  *   - Every argument is checked before anything is enqueued: on an error
  *     nothing runs and outputs are untouched.  Device faults surface at the
  *     caller's next synchronisation.  No exceptions cross the ABI.
@@ -33,7 +35,8 @@
  *   - Identical inputs give bit-identical outputs (fixed reduction orders, no
  *     floating-point atomics).  Calls on different streams with different
  *     workspaces may overlap.  The library's only global state is a per-device
- *     record of its gfx950 check (set once, thread-safe).
+ *     record of its gfx950 check (set once, thread-safe) and the fixed scratch
+ *     of moe_layer_forward_noalloc (one per device; see there).
  *
  * Weight format (a reading: the pages name Q4_K/Q5_K but print no layout)
  *   A superblock holds 256 weights, in 8 sub-blocks of 32:
@@ -75,7 +78,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 4
+#define MOE_ABI_VERSION 5
 
 /* Status codes returned by every entry point. */
 #define MOE_OK 0
@@ -84,6 +87,7 @@ extern "C" {
 #define MOE_EWORKSPACE (-3)    /* workspace smaller than moe_workspace_bytes() */
 #define MOE_ELAUNCH (-4)       /* a kernel launch failed (hipGetLastError) */
 #define MOE_ENODEVICE (-5)     /* no gfx950 device is current */
+#define MOE_ETOOBIG (-6)       /* moe_layer_forward_noalloc: T rows need more than its fixed scratch */
 
 /* Weight formats (moe_layer_desc.weight_format). */
 #define MOE_WFMT_KQUANT 0      /* Q4_K gate/up, Q5_K down */
@@ -190,6 +194,27 @@ int router_topk(const moe_layer_desc *desc, const float *x, int32_t T,
  */
 int moe_layer_forward(const moe_layer_desc *desc, const float *x, int32_t T, float *out,
                       const moe_opts *opts, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * computation, kernels and results as moe_layer_forward, with no workspace
+ * argument.  Its workspace is a fixed scratch array of
+ * MOE_NOALLOC_SCRATCH_BYTES bytes inside the library, one copy per device,
+ * which each device that runs this call holds until the process ends.  The
+ * call allocates and frees nothing; the caller still passes x and out.
+ *   Returns MOE_ETOOBIG, enqueuing nothing, when T rows need more workspace
+ *   than the scratch holds (moe_workspace_bytes(desc, T, 1) >
+ *   MOE_NOALLOC_SCRATCH_BYTES: above about 700 rows of the Qwen3.5-shaped
+ *   layer; any T of the decode path fits).  Other errors as moe_layer_forward.
+ *   Every call on one device shares that device's scratch and leaves its last
+ *   contents there (no call needs any particular contents on entry): calls
+ *   that overlap in time on one device -- on different streams, or from
+ *   different threads without ordering -- race and give undefined results.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int moe_layer_forward_noalloc(const moe_layer_desc *desc, const float *x, int32_t T, float *out,
+                              const moe_opts *opts, void *stream);
 
 /*
  * Shard `shard` of `num_shards` of the layer, with the routing given (the

@@ -16,6 +16,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe_hip.so")
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_ELAUNCH, MOE_ENODEVICE = 0, -1, -2, -3, -4, -5
+MOE_ETOOBIG = -6
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 MOE_PATH_AUTO, MOE_PATH_GEMV, MOE_PATH_MFMA = 0, 1, 2
 MOE_WFMT_KQUANT, MOE_WFMT_MXFP4 = 0, 1
 MOE_SB_MXFP4 = 14
@@ -61,6 +63,7 @@ def _load():
     L.moe_workspace_bytes.restype = SZ
     L.router_topk.argtypes = [D, P, I32, P, P, P, SZ, P]
     L.moe_layer_forward.argtypes = [D, P, I32, P, O, P, SZ, P]
+    L.moe_layer_forward_noalloc.argtypes = [D, P, I32, P, O, P]
     L.moe_layer_forward_shard.argtypes = [D, P, I32, P, P, I32, I32, P, O, P, SZ, P]
     L.moe_layer_forward_range.argtypes = [D, P, I32, P, P, I32, I32, P, O, P, SZ, P]
     L.moe_reduce_partials.argtypes = [ctypes.POINTER(P), I32, I64, P, P]
@@ -72,6 +75,7 @@ def _load():
     L.moe_rmsnorm_apply.argtypes = [P, I32, I32, I64, ctypes.POINTER(P), I32, I32, P,
                                     ctypes.c_float, P, I64, P]
     for f in ("router_topk", "moe_layer_forward", "moe_layer_forward_shard", "moe_reduce_partials",
+              "moe_layer_forward_noalloc",
               "moe_dequant", "moe_route_bucket", "moe_reduce_residual", "moe_rmsnorm",
               "moe_layer_forward_range",
               "moe_rmsnorm_sumsq", "moe_rmsnorm_apply"):
@@ -145,6 +149,17 @@ def moe_layer_forward(desc, x, T, out, ws, path: int = MOE_PATH_AUTO, stream=Non
     _check("moe_layer_forward", lib.moe_layer_forward(ctypes.byref(desc), _ptr(x), T, _ptr(out),
                                                       ctypes.byref(o), _ptr(ws), _nbytes(ws),
                                                       _stream(stream)))
+    return used.value
+
+
+def moe_layer_forward_noalloc(desc, x, T, out, path: int = MOE_PATH_AUTO, stream=None,
+                              events=None) -> int:
+    """moe_layer_forward on the library's fixed per-device scratch (no
+    workspace argument).  Returns the path that ran."""
+    o, used = _opts(path, events)
+    _check("moe_layer_forward_noalloc",
+           lib.moe_layer_forward_noalloc(ctypes.byref(desc), _ptr(x), T, _ptr(out),
+                                         ctypes.byref(o), _stream(stream)))
     return used.value
 
 

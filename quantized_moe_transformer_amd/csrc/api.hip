@@ -4,6 +4,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "launch.h"
 
@@ -266,6 +267,40 @@ static int check_device() {
     return ok ? MOE_OK : MOE_ENODEVICE;
 }
 
+// ---------------------------------------------------------------------------
+// The fixed scratch of moe_layer_forward_noalloc: a file-scope device array,
+// one copy per device at that device's own address.  In host code `scratch`
+// names only a host-side stand-in; the device address comes from
+// hipGetSymbolAddress, once per device with that device current, and only
+// that address is ever handed to kernels.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = MOE_NOALLOC_SCRATCH_BYTES;
+static_assert(kScratchBytes % 256 == 0, "scratch keeps the workspace alignment");
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+static std::atomic<void*> g_scratch[kMaxDevices];
+static std::mutex g_scratch_mu;
+
+// Device address of the current device's scratch (set up on its first use).
+static int scratch_address(void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ENODEVICE;
+    void* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+                (void)hipGetLastError();   // clear the error it left
+                return MOE_ELAUNCH;
+            }
+            g_scratch[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return MOE_OK;
+}
+
 static int launched(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ELAUNCH; }
 
 }  // namespace moe
@@ -284,6 +319,7 @@ const char* moe_status_str(int status) {
         case MOE_EWORKSPACE: return "workspace too small";
         case MOE_ELAUNCH: return "kernel launch failed";
         case MOE_ENODEVICE: return "no gfx950 device";
+        case MOE_ETOOBIG: return "input too large for the no-allocation scratch";
         default: return "unknown status";
     }
 }
@@ -353,6 +389,22 @@ int moe_layer_forward(const moe_layer_desc* desc, const float* x, int32_t T, flo
     if (rc) return rc;
     return forward_common(desc, x, T, nullptr, nullptr, 0, desc->inter, out, opts, ws, ws_bytes,
                           stream, true);
+}
+
+int moe_layer_forward_noalloc(const moe_layer_desc* desc, const float* x, int32_t T, float* out,
+                              const moe_opts* opts, void* stream) {
+    int rc = check_desc(desc);
+    if (rc) return rc;
+    if (T < 0) return MOE_EINVAL;
+    if (T == 0)   // nothing to enqueue: the scratch is not touched
+        return forward_common(desc, x, T, nullptr, nullptr, 0, desc->inter, out, opts, nullptr, 0,
+                              stream, true);
+    if (ws_layout(*desc, T, desc->inter).total > kScratchBytes) return MOE_ETOOBIG;
+    if ((rc = check_device())) return rc;
+    void* ws = nullptr;
+    if ((rc = scratch_address(&ws))) return rc;
+    return forward_common(desc, x, T, nullptr, nullptr, 0, desc->inter, out, opts, ws,
+                          kScratchBytes, stream, true);
 }
 
 int moe_layer_forward_shard(const moe_layer_desc* desc, const float* x, int32_t T,

@@ -28,7 +28,7 @@ def test_header_declares_the_boundary():
     for fn in ("router_topk", "moe_layer_forward", "moe_layer_forward_shard",
                "moe_reduce_partials", "moe_dequant", "moe_workspace_bytes", "moe_route_bucket",
                "moe_status_str", "moe_abi_version", "moe_reduce_residual", "moe_rmsnorm",
-               "moe_layer_forward_range",
+               "moe_layer_forward_range", "moe_layer_forward_noalloc",
                "moe_rmsnorm_sumsq", "moe_rmsnorm_apply"):
         assert fn in names
 
@@ -36,7 +36,7 @@ def test_header_declares_the_boundary():
 def test_library_exports_every_declared_symbol(L):
     for fn in declared_functions():
         assert hasattr(L.lib, fn), fn
-    assert L.moe_abi_version() == 4
+    assert L.moe_abi_version() == 5
     assert L.moe_status_str(-3) == "workspace too small"
 
 
@@ -174,3 +174,23 @@ def test_path_choice_reported(L):
                                      None)
         assert rc == L.MOE_EWORKSPACE
         assert used.value == expect
+
+
+def test_noalloc_host_checks(L):
+    # moe_layer_forward_noalloc: T = 0 is a no-op, bad arguments are rejected,
+    # and rows whose workspace would exceed the fixed scratch give MOE_ETOOBIG
+    # before any device is touched
+    f = L.lib.moe_layer_forward_noalloc
+    used = ctypes.c_int32(-1)
+    o = L.moe_opts(0, ctypes.pointer(used), None, 0)
+    d = desc()
+    assert f(ctypes.byref(d), None, 0, None, ctypes.byref(o), None) == L.MOE_OK
+    assert used.value == L.MOE_PATH_GEMV
+    assert f(ctypes.byref(desc(k=0)), FAKE, 1, FAKE, ctypes.byref(o), None) == L.MOE_EINVAL
+    assert f(ctypes.byref(d), FAKE, -1, FAKE, ctypes.byref(o), None) == L.MOE_EINVAL
+    fits = [T for T in range(1, 4097) if L.moe_workspace_bytes(d, T, 1) <= L.MOE_NOALLOC_SCRATCH_BYTES]
+    big = max(fits) + 1
+    assert fits == list(range(1, big)) and big > 256     # every decode and mid-size T fits
+    assert f(ctypes.byref(d), FAKE, big, FAKE, ctypes.byref(o), None) == L.MOE_ETOOBIG
+    assert f(ctypes.byref(d), FAKE, 4096, FAKE, ctypes.byref(o), None) == L.MOE_ETOOBIG
+    assert L.moe_status_str(L.MOE_ETOOBIG) == "input too large for the no-allocation scratch"
