@@ -6,21 +6,27 @@ Qwen3.5-35B-A3B-shaped layer (H=2048, 256 experts, top-8, I=512, a shared
 expert of I=512; Q4_K gate/up, Q5_K down; seeded synthetic weights and tokens).
 One step = one moe_layer_forward call (router + top-k + gate/up/SwiGLU + down +
 slot-order combine).  Steps cycle through a pool of 64 token rows and through
-several copies of the weights at different addresses, so that a step's 19.2 MB
-of weights is not served from the 256 MB last-level cache left warm by the step
-before.  Steps are replayed from a HIP graph (one graph of 16 steps).
+16 copies of the weights at different addresses, so that neither a step's
+routed experts nor a copy's router matrix and shared expert are served from
+the 256 MB last-level cache left warm by earlier steps.  Exactly `--steps`
+steps are captured in one HIP graph; after one untimed replay, one replay is
+timed with stream events.
 
-Secondary (``prefill``): T = 4096 token rows per step, same layer shape (seed
-4, uniform router), grouped-GEMM path, replayed from a HIP graph of two steps
-(one per weight copy); the eager rate is reported beside it.
-
-Beside the layer (``edges``): the steps either side of it at T = 4096, H =
-2048 -- RMSNorm of the input rows and the reduce of two shard partials plus
-the residual -- timed with stream events over 20 calls each.
-
+The other workloads of the layer, each its own JSON object, timed the same way
+(one graph of exactly the stated number of steps):
+  sharded_decode   T = 1, router_topk + the two 256/256 shards + the reduce;
+  batched_decode   T = 32 rows, automatic path;
+  zipf_prefill     T = 512 rows with Zipf-like expert load;
+  prefill          T = 4096 rows, uniform router;
+  sharded_prefill  T = 4096 rows in the two-shard mode;
+  mxfp4            decode and prefill with MXFP4 expert weights;
+  edges            RMSNorm before the layer and the partial reduce plus
+                   residual after it, at T = 4096.
 Per-kernel durations come from start/stop HIP events that the library attaches
 to each kernel launch (moe_opts.kernel_events, hipExtLaunchKernel) in an eager
-pass over the same workload.
+pass over the same workload.  The CPU-baseline leg times the oracle on the
+host and compares each workload's GPU output with it (max|err|/RMS over a
+stated sample of rows).
 
 Run: python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -165,16 +171,86 @@ def time_steps(torch, run_step, K):
     return time.perf_counter() - t0
 
 
+def graph_time(torch, step, K):
+    """Exactly K consecutive steps captured in ONE HIP graph; one untimed replay
+    (graph upload), then one timed replay bracketed by synchronisations, timed
+    by events on the replaying stream.  Returns (device s/step, host s/step)."""
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(K):
+            step(i)
+    g.replay()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    a.record()
+    g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    host = time.perf_counter() - t0
+    dev = a.elapsed_time(b) * 1e-3
+    del g
+    return dev / K, host / K
+
+
+def kernel_profile_calls(torch, call, n_steps, n_calls, names, stats=None):
+    """Like kernel_profile for a step made of n_calls library calls: call(i,
+    evs) passes evs[c] to call c.  Returns {(c, name): average ms}."""
+    from quantized_moe_transformer_amd._lib import KERNEL_IDS, N_KERNEL_IDS
+    per = 2 * N_KERNEL_IDS
+    ev = HipEvents(n_steps * n_calls * per)
+    for i in range(n_steps):
+        call(i, [ev.array((i * n_calls + c) * per, per) for c in range(n_calls)])
+    torch.cuda.synchronize()
+    out = {}
+    for c in range(n_calls):
+        for n in names:
+            kid = KERNEL_IDS[n]
+            d = [ev.ms((i * n_calls + c) * per + 2 * kid, (i * n_calls + c) * per + 2 * kid + 1)
+                 for i in range(n_steps)]
+            out[(c, n)] = float(np.mean(d))
+            if stats is not None:
+                stats[(c, n)] = {"median_ms": float(np.median(d)), "min_ms": float(np.min(d))}
+    ev.close()
+    return out
+
+
 def down_sb_bytes(mi, shp):
     return mi.MXFP4_SB_BYTES if shp.fmt == 1 else mi.Q5K_SB_BYTES
 
 
+def expert_bytes(mi, shp):
+    """(gate + up bytes, down bytes) of one expert."""
+    return (2 * (shp.I * shp.H // 256) * mi.Q4K_SB_BYTES,
+            (shp.H * shp.I // 256) * down_sb_bytes(mi, shp))
+
+
+def weight_copies(base, n):
+    return [base] + [base.clone_weights() for _ in range(n - 1)]
+
+
+def roofline(kernel, bound, work, ms, unit, peak, traffic=None, extra=None):
+    per_s = work / (ms * 1e-3)
+    achieved = per_s / (1e9 if unit == "GB/s" else 1e12)
+    r = {"kernel": kernel, "bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
+         "frac": achieved / peak, "traffic": traffic,
+         ("algorithmic_bytes_per_launch" if unit == "GB/s" else "algorithmic_flops_per_launch"): work,
+         "avg_launch_ms": ms}
+    if extra:
+        r.update(extra)
+    return r
+
+
 def bench_decode(args, torch, qm, mi, DeviceLayer, name="decode"):
+    """Decode, T = 1 row per step, one moe_layer_forward per step."""
     w = mi.WORKLOADS[name]
     shp = w.shape
     layer = mi.make_layer(shp, w.seed)
     base = DeviceLayer.from_shape(layer, shp)
-    copies = [base] + [base.clone_weights() for _ in range(args.copies - 1)]
+    copies = weight_copies(base, args.copies)
     pool = torch.from_numpy(mi.make_tokens(shp, w.seed, 64, stream=101)).cuda()
     T = 1
     ws = base.workspace(T)
@@ -190,85 +266,193 @@ def bench_decode(args, torch, qm, mi, DeviceLayer, name="decode"):
         step(i)
     torch.cuda.synchronize()
     assert set(used) == {qm.MOE_PATH_GEMV}, used
-
-    # eager throughput
     eager_s = time_steps(torch, step, args.steps)
+    dev_s, host_s = graph_time(torch, step, args.steps)
 
-    # graph replay: one graph of G consecutive steps (tokens and copies cycle)
-    G = 16
-    g = torch.cuda.CUDAGraph()
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        for i in range(G):
-            step(i)
-    torch.cuda.current_stream().wait_stream(s)
-    torch.cuda.synchronize()
-    graphs = []
-    for gi in range(64 // G):          # 4 graphs cover the 64-token pool
-        gg = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(gg):
-            for i in range(gi * G, gi * G + G):
-                step(i)
-        graphs.append(gg)
-    torch.cuda.synchronize()
-    for gg in graphs:
-        gg.replay()
-    torch.cuda.synchronize()
-    n_rep = args.steps // G
-    rest = args.steps - n_rep * G
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for r in range(n_rep):
-        graphs[r % len(graphs)].replay()
-    for i in range(rest):
-        step(i)
-    torch.cuda.synchronize()
-    graph_s = time.perf_counter() - t0
-    del g
-
-    # per-kernel durations of the same calls
     nprof = min(args.steps, 256)
     kst = {}
     kms = kernel_profile(torch, qm, lambda i, e: step(i, e), nprof,
                          ["gemv_front", "gateup_gemv", "down_gemv"], kst)
-    gateup_ms = kms["gateup_gemv"]
-
-    E_bytes_gu = 2 * (shp.I * shp.H // 256) * mi.Q4K_SB_BYTES          # gate + up (MXFP4: same size)
-    E_bytes_d = (shp.H * shp.I // 256) * down_sb_bytes(mi, shp)
-    n_inst = shp.k + 1                                                   # 8 routed + shared
-    # the routed gate/up kernel: 8 experts' gate+up bytes, x, and h written
-    gateup_bytes = shp.k * E_bytes_gu + shp.H * 4 + shp.k * shp.I * 4
-    layer_bytes = n_inst * (E_bytes_gu + E_bytes_d) + shp.H * shp.E * 4  # K-quant: 19,202,048 B
-    ms_graph = graph_s / args.steps * 1e3
+    gu, dn = expert_bytes(mi, shp)
+    gateup_bytes = shp.k * gu + shp.H * 4 + shp.k * shp.I * 4
+    layer_bytes = (shp.k + 1) * (gu + dn) + shp.H * shp.E * 4   # K-quant: 19,202,048 B
     res = {
-        "value": T * args.steps / graph_s,
-        "ms_per_step": ms_graph,
+        "value": T / dev_s,
+        "ms_per_step": dev_s * 1e3,
+        "host_ms_per_step": host_s * 1e3,
         "eager_tokens_per_s": T * args.steps / eager_s,
         "eager_ms_per_step": eager_s / args.steps * 1e3,
+        "weight_copies": len(copies),
         "kernel_ms": kms,
         "layer_algorithmic_bytes": layer_bytes,
-        "layer_hbm_frac_graph": layer_bytes / (ms_graph * 1e-3) / (HBM_PEAK_GBS * 1e9),
+        "layer_hbm_frac_graph": layer_bytes / dev_s / (HBM_PEAK_GBS * 1e9),
         "layer_hbm_frac_kernels": layer_bytes / (sum(kms.values()) * 1e-3) / (HBM_PEAK_GBS * 1e9),
-        "roofline": {
-            "kernel": "gemv_gateup_kernel<%s,64,1> (8 routed experts)" % ("MXFP4" if shp.fmt else "K-quant"),
-            "bound": "hbm",
-            "achieved": gateup_bytes / (gateup_ms * 1e-3) / 1e9,
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": gateup_bytes / (gateup_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "traffic": traffic_for("gemv_gateup_mx" if shp.fmt else "gemv_gateup"),
-            "algorithmic_bytes_per_launch": gateup_bytes,
-            "avg_launch_ms": gateup_ms,
-            "median_launch_ms": kst["gateup_gemv"]["median_ms"],
-            "min_launch_ms": kst["gateup_gemv"]["min_ms"],
-            "launches": nprof,
-        },
+        "roofline": roofline(
+            "gemv_gateup_kernel<%s,64,1> (8 routed experts)" % ("MXFP4" if shp.fmt else "K-quant"),
+            "hbm", gateup_bytes, kms["gateup_gemv"], "GB/s", HBM_PEAK_GBS,
+            traffic_for("gemv_gateup_mx" if shp.fmt else "gemv_gateup"),
+            {"median_launch_ms": kst["gateup_gemv"]["median_ms"],
+             "min_launch_ms": kst["gateup_gemv"]["min_ms"], "launches": nprof}),
     }
-    return res, layer, pool.cpu().numpy()
+    # outputs of 8 pool tokens (one T = 1 call each) for the oracle check
+    xs, outs = [], []
+    for i in range(8):
+        qm.moe_layer_forward(base.desc, pool[i:i + 1], T, out, ws)
+        torch.cuda.synchronize()
+        xs.append(pool[i:i + 1].cpu().numpy())
+        outs.append(out.cpu().numpy().copy())
+    check = {"name": name, "layer": layer, "shape": shp, "x": np.concatenate(xs),
+             "out": np.concatenate(outs), "tol": 1e-4}
+    return res, check
 
 
-def bench_prefill(args, torch, qm, mi, DeviceLayer, name="prefill4096"):
+def bench_layer_batches(args, torch, qm, mi, DeviceLayer, name, T, n_copies, K, W,
+                        label, x_stream=None):
+    """T rows per step through moe_layer_forward (automatic path), cycling
+    weight copies and 4 token batches; HIP graph of exactly K steps."""
+    w = mi.WORKLOADS[name]
+    shp = w.shape
+    layer = mi.make_layer(shp, w.seed, zipf=w.zipf)
+    base = DeviceLayer.from_shape(layer, shp)
+    copies = weight_copies(base, n_copies)
+    xs = mi.make_tokens(shp, w.seed, 4 * T, stream=w.x_stream if x_stream is None else x_stream,
+                        zipf=w.zipf)
+    xd = torch.from_numpy(xs).cuda().view(4, T, shp.H)
+    ws = base.workspace(T)
+    out = torch.empty((T, shp.H), device="cuda")
+    used = []
+
+    def step(i, events=None):
+        used.append(qm.moe_layer_forward(copies[i % len(copies)].desc, xd[(i // len(copies)) % 4],
+                                         T, out, ws, events=events))
+
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+    path = used[-1]
+    dev_s, host_s = graph_time(torch, step, K)
+    # distinct experts each batch touches (the library's own routing)
+    idx = torch.empty((T, shp.k), dtype=torch.int32, device="cuda")
+    wts = torch.empty((T, shp.k), dtype=torch.float32, device="cuda")
+    distinct = []
+    for bi in range(4):
+        qm.router_topk(base.desc, xd[bi], T, idx, wts, ws)
+        distinct.append(int(torch.unique(idx).numel()))
+    d_avg = float(np.mean(distinct))
+    gu, dn = expert_bytes(mi, shp)
+    alg_bytes = (d_avg + 1) * (gu + dn) + shp.H * shp.E * 4 + 2 * T * shp.H * 4
+    flops = T * (shp.k + 1) * 6.0 * shp.H * shp.I + 2.0 * T * shp.H * shp.E
+    if path == qm.MOE_PATH_MFMA:
+        names = ["gemm_gateup", "gemm_down", "combine"]
+        kms = kernel_profile(torch, qm, lambda i, e: step(i, e), min(K, 32), names)
+        gu_bytes = (d_avg + 1) * gu + T * shp.H * 2 + T * (shp.k + 1) * shp.I * 2
+        rl = roofline("gemm_grouped_kernel<0> (gate/up + SwiGLU)", "hbm", gu_bytes,
+                      kms["gemm_gateup"], "GB/s", HBM_PEAK_GBS)
+    else:
+        names = ["gemv_front", "gateup_gemv", "down_gemv"]
+        kms = kernel_profile(torch, qm, lambda i, e: step(i, e), min(K, 32), names)
+        gu_bytes = d_avg * gu + shp.H * 4 * T + T * shp.k * shp.I * 4
+        rl = roofline("gemv_gateup_kernel", "hbm", gu_bytes, kms["gateup_gemv"], "GB/s",
+                      HBM_PEAK_GBS)
+    qm.moe_layer_forward(base.desc, xd[0], T, out, ws)
+    qm.router_topk(base.desc, xd[0], T, idx, wts, ws)
+    torch.cuda.synchronize()
+    res = {
+        "workload": label,
+        "value": T / dev_s, "unit": "tokens/s", "T": T,
+        "ms_per_step": dev_s * 1e3, "host_ms_per_step": host_s * 1e3, "steps": K, "warmup": W,
+        "path": "gemv" if path == qm.MOE_PATH_GEMV else "mfma",
+        "weight_copies": len(copies), "distinct_experts": d_avg,
+        "layer_algorithmic_bytes": alg_bytes, "layer_gflop": flops / 1e9,
+        "layer_hbm_frac": alg_bytes / dev_s / (HBM_PEAK_GBS * 1e9),
+        "kernel_ms": kms, "roofline": rl,
+    }
+    check = {"name": name, "layer": layer, "shape": shp, "x": xs[:T], "out": out.cpu().numpy(),
+             "idx": idx.cpu().numpy(), "tol": 1e-4 if path == qm.MOE_PATH_GEMV else 1e-2}
+    return res, check
+
+
+def bench_sharded(args, torch, qm, mi, DeviceLayer, name, T, n_copies, n_batches, K, W, label,
+                  check_rows):
+    """The 256/256 shard mode as one step: router_topk once (the synchronised
+    decision), moe_layer_forward_shard(0, 2) and (1, 2), moe_reduce_partials."""
+    w = mi.WORKLOADS[name]
+    shp = w.shape
+    layer = mi.make_layer(shp, w.seed, zipf=w.zipf)
+    base = DeviceLayer.from_shape(layer, shp)
+    copies = weight_copies(base, n_copies)
+    xs = mi.make_tokens(shp, w.seed, n_batches * T, stream=101 if T == 1 else w.x_stream,
+                        zipf=w.zipf)
+    xd = torch.from_numpy(xs).cuda().view(n_batches, T, shp.H)
+    ws_r = base.workspace(T)
+    ws = [base.workspace(T, 2) for _ in range(2)]
+    idx = torch.empty((T, shp.k), dtype=torch.int32, device="cuda")
+    wts = torch.empty((T, shp.k), dtype=torch.float32, device="cuda")
+    parts = [torch.empty((T, shp.H), device="cuda") for _ in range(2)]
+    out = torch.empty((T, shp.H), device="cuda")
+    used = []
+
+    def step(i, evs=None):
+        c = copies[i % len(copies)]
+        x = xd[(i // len(copies)) % n_batches]
+        qm.router_topk(c.desc, x, T, idx, wts, ws_r)
+        for s in range(2):
+            used.append(qm.moe_layer_forward_shard(c.desc, x, T, idx, wts, s, 2, parts[s], ws[s],
+                                                   events=None if evs is None else evs[s]))
+        qm.moe_reduce_partials(parts, T * shp.H, out)
+
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+    path = used[-1]
+    dev_s, host_s = graph_time(torch, step, K)
+    gu, dn = expert_bytes(mi, shp)
+    if path == qm.MOE_PATH_MFMA:
+        names = ["gemm_gateup", "gemm_down", "combine"]
+    else:
+        names = ["gemv_front", "gateup_gemv", "down_gemv"]
+    kst = {}
+    kms = kernel_profile_calls(torch, lambda i, e: step(i, e), min(K, 64), 2, names, kst)
+    kms_flat = {f"shard{c}.{n}": v for (c, n), v in kms.items()}
+    if path == qm.MOE_PATH_MFMA:
+        slots = T * shp.k + T
+        flops_gu = 2.0 * 2 * shp.H * (shp.I // 2) * slots
+        flops = 3.0 * 2 * shp.H * shp.I * slots
+        rl = roofline("gemm_grouped_kernel<0> of shard 0 (gate/up + SwiGLU, I/2 = %d)" % (shp.I // 2),
+                      "mfma", flops_gu, kms[(0, "gemm_gateup")], "TFLOP/s", FP16_MFMA_PEAK_TFLOPS,
+                      extra={"median_launch_ms": kst[(0, "gemm_gateup")]["median_ms"],
+                             "min_launch_ms": kst[(0, "gemm_gateup")]["min_ms"]})
+        gemm_ms = sum(v for (c, n), v in kms.items() if n.startswith("gemm"))
+        whole = {"expert_gflop": flops / 1e9,
+                 "expert_mfma_frac": flops / (gemm_ms * 1e-3) / (FP16_MFMA_PEAK_TFLOPS * 1e12),
+                 "step_mfma_frac": flops / dev_s / (FP16_MFMA_PEAK_TFLOPS * 1e12)}
+    else:
+        gu_bytes = shp.k * gu // 2 + shp.H * 4 + shp.k * (shp.I // 2) * 4
+        rl = roofline("gemv_gateup_kernel of shard 0 (8 routed experts, I/2 = %d)" % (shp.I // 2),
+                      "hbm", gu_bytes, kms[(0, "gateup_gemv")], "GB/s", HBM_PEAK_GBS,
+                      extra={"median_launch_ms": kst[(0, "gateup_gemv")]["median_ms"],
+                             "min_launch_ms": kst[(0, "gateup_gemv")]["min_ms"]})
+        layer_bytes = (shp.k + 1) * (gu + dn) + shp.H * shp.E * 4 + 3 * T * shp.H * 4
+        whole = {"layer_algorithmic_bytes": layer_bytes,
+                 "layer_hbm_frac": layer_bytes / dev_s / (HBM_PEAK_GBS * 1e9)}
+    x0 = xd[0]
+    qm.router_topk(base.desc, x0, T, idx, wts, ws_r)
+    for s in range(2):
+        qm.moe_layer_forward_shard(base.desc, x0, T, idx, wts, s, 2, parts[s], ws[s])
+    qm.moe_reduce_partials(parts, T * shp.H, out)
+    torch.cuda.synchronize()
+    res = {"workload": label, "value": T / dev_s, "unit": "tokens/s", "T": T,
+           "ms_per_step": dev_s * 1e3, "host_ms_per_step": host_s * 1e3, "steps": K, "warmup": W,
+           "path": "gemv" if path == qm.MOE_PATH_GEMV else "mfma", "weight_copies": len(copies),
+           "kernel_ms": kms_flat, "roofline": rl, **whole}
+    r = min(T, check_rows)
+    check = {"name": name, "layer": layer, "shape": shp, "x": xs[:r], "out": out.cpu().numpy()[:r],
+             "idx": idx.cpu().numpy()[:r], "tol": 1e-4 if path == qm.MOE_PATH_GEMV else 1e-2,
+             "rows_note": f"first {r} of {T} rows"}
+    return res, check
+
+
+def bench_prefill(args, torch, qm, mi, DeviceLayer, name="prefill4096", check_rows=256):
     w = mi.WORKLOADS[name]
     shp = w.shape
     layer = mi.make_layer(shp, w.seed)
@@ -291,19 +475,7 @@ def bench_prefill(args, torch, qm, mi, DeviceLayer, name="prefill4096"):
     torch.cuda.synchronize()
     assert set(used) == {qm.MOE_PATH_MFMA}, used
     eager_secs = time_steps(torch, step, K)
-    # graph replay: one graph of two steps (one per weight copy)
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        step(0)
-        step(1)
-    g.replay()
-    torch.cuda.synchronize()
-    n_rep = max(1, K // 2)
-    t0 = time.perf_counter()
-    for _ in range(n_rep):
-        g.replay()
-    torch.cuda.synchronize()
-    secs = (time.perf_counter() - t0) * K / (2 * n_rep)
+    dev_s, host_s = graph_time(torch, step, K)
     names = ["x_f16", "router_mfma", "router_topk", "bucket_hist", "bucket_scan",
              "bucket_scatter", "gemm_gateup", "gemm_down", "combine"]
     kst = {}
@@ -315,11 +487,12 @@ def bench_prefill(args, torch, qm, mi, DeviceLayer, name="prefill4096"):
     d_ms = kms["gemm_down"]
     res = {
         "workload": ("prefill T=4096: same layer shape, %s weights, seed %d, uniform router, "
-                     "grouped fp16-MFMA path, 2 rotating weight copies, HIP-graph replay"
-                     % ("MXFP4" if shp.fmt else "Q4_K/Q5_K", w.seed)),
-        "value": T * K / secs,
+                     "grouped fp16-MFMA path, 2 rotating weight copies, HIP graph of exactly "
+                     "`steps` steps" % ("MXFP4" if shp.fmt else "Q4_K/Q5_K", w.seed)),
+        "value": T / dev_s,
         "unit": "tokens/s",
-        "ms_per_step": secs / K * 1e3,
+        "ms_per_step": dev_s * 1e3,
+        "host_ms_per_step": host_s * 1e3,
         "eager_tokens_per_s": T * K / eager_secs,
         "eager_ms_per_step": eager_secs / K * 1e3,
         "steps": K,
@@ -328,22 +501,22 @@ def bench_prefill(args, torch, qm, mi, DeviceLayer, name="prefill4096"):
         "kernel_ms": kms,
         "expert_gflop": (flops_gu + flops_d) / 1e9,
         "expert_mfma_frac": (flops_gu + flops_d) / ((gu_ms + d_ms) * 1e-3) / (FP16_MFMA_PEAK_TFLOPS * 1e12),
-        "roofline": {
-            "kernel": "gemm_gateup_kernel",
-            "bound": "mfma",
-            "achieved": flops_gu / (gu_ms * 1e-3) / 1e12,
-            "peak": FP16_MFMA_PEAK_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": flops_gu / (gu_ms * 1e-3) / 1e12 / FP16_MFMA_PEAK_TFLOPS,
-            "traffic": traffic_for("gemm_gateup_mx" if shp.fmt else "gemm_gateup"),
-            "algorithmic_flops_per_launch": flops_gu,
-            "avg_launch_ms": gu_ms,
-            "median_launch_ms": kst["gemm_gateup"]["median_ms"],
-            "min_launch_ms": kst["gemm_gateup"]["min_ms"],
-            "launches": K,
-        },
+        "step_mfma_frac": (flops_gu + flops_d) / dev_s / (FP16_MFMA_PEAK_TFLOPS * 1e12),
+        "roofline": roofline("gemm_gateup_kernel", "mfma", flops_gu, gu_ms, "TFLOP/s",
+                             FP16_MFMA_PEAK_TFLOPS,
+                             traffic_for("gemm_gateup_mx" if shp.fmt else "gemm_gateup"),
+                             {"median_launch_ms": kst["gemm_gateup"]["median_ms"],
+                              "min_launch_ms": kst["gemm_gateup"]["min_ms"], "launches": K}),
     }
-    return res, layer, x_host
+    qm.moe_layer_forward(base.desc, x, T, out, ws)
+    idx = torch.empty((T, shp.k), dtype=torch.int32, device="cuda")
+    wts = torch.empty((T, shp.k), dtype=torch.float32, device="cuda")
+    qm.router_topk(base.desc, x, T, idx, wts, ws)
+    torch.cuda.synchronize()
+    check = {"name": name, "layer": layer, "shape": shp, "x": x_host[:check_rows],
+             "out": out.cpu().numpy()[:check_rows], "idx": idx.cpu().numpy()[:check_rows],
+             "tol": 1e-2, "rows_note": f"first {check_rows} of {T} rows"}
+    return res, check, layer, x_host
 
 
 CONTINUUM_T = (1, 2, 4, 8, 16, 32, 64, 128, 256, 512)
@@ -548,10 +721,29 @@ def bench_balance(args, torch, qm, mi, DeviceLayer):
     return report
 
 
-def cpu_baseline_decode(layer, pool, budget_s):
-    import moe_inputs as mi
+def cpu_model():
+    """The host CPU's model name (lscpu, else /proc/cpuinfo)."""
+    import subprocess
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except Exception:
+        pass
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline_decode(layer, shape, pool, budget_s):
     import oracle
-    ol = oracle.Layer.from_shape(layer, mi.QWEN35_MOE)
+    ol = oracle.Layer.from_shape(layer, shape)
     n = 0
     t0 = time.perf_counter()
     while (time.perf_counter() - t0) < budget_s:
@@ -568,23 +760,42 @@ def cpu_baseline_decode(layer, pool, budget_s):
         n1 += 1
     dt1 = time.perf_counter() - t1
     return {"value": n / dt, "unit": "tokens/s", "cores": oracle.max_threads(), "kind": "oracle",
-            "sample": f"{n} decode tokens (cycling a 64-token pool), one T=1 oracle call each (routing, decode of the 9 "
-                      f"touched experts, fp64 FFN), {dt:.1f} s",
+            "cpu_model": cpu_model(),
+            "sample": f"{n} decode tokens (cycling {pool.shape[0]} pool tokens), one T=1 oracle call each "
+                      f"(routing, decode of the 9 touched experts, fp64 FFN), {dt:.1f} s",
             "single_thread": {"value": n1 / dt1, "unit": "tokens/s", "cores": 1,
                               "sample": f"{n1} decode tokens, {dt1:.1f} s"}}
 
 
-def cpu_baseline_prefill(layer, x, rows):
-    import moe_inputs as mi
+def cpu_baseline_prefill(layer, shape, x, rows):
     import oracle
-    ol = oracle.Layer.from_shape(layer, mi.QWEN35_MOE)
+    ol = oracle.Layer.from_shape(layer, shape)
     t0 = time.perf_counter()
     oracle.forward(ol, x[:rows])
     dt = time.perf_counter() - t0
     return {"value": rows / dt, "unit": "tokens/s", "cores": oracle.max_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"first {rows} of the 4096 prefill rows in one oracle call (routing, decode "
                       f"of every touched expert, fp64 FFN), {dt:.1f} s"}
+
+
+def oracle_check(chk):
+    """max|gpu - oracle| / RMS(oracle) over the rows of a config's sample whose
+    GPU routing equals the oracle's (rows that differ are near-ties, counted)."""
+    import oracle
+    shp = chk["shape"]
+    ol = oracle.Layer.from_shape(chk["layer"], shp)
+    x = np.ascontiguousarray(chk["x"])
+    oi, _, _, _ = oracle.router(x, chk["layer"]["router_w"], shp.k)
+    same = np.ones(x.shape[0], bool) if "idx" not in chk else np.all(chk["idx"] == oi, axis=1)
+    ref = oracle.forward(ol, x).astype(np.float64)[same]
+    got = np.asarray(chk["out"], np.float64)[same]
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    err = float(np.abs(got - ref).max() / rms) if ref.size else None
+    return {"max_err_over_rms": err, "tolerance": chk["tol"],
+            "within_tolerance": err is not None and err <= chk["tol"],
+            "rows_compared": int(same.sum()), "rows_near_tie_routing": int((~same).sum()),
+            "rows": chk.get("rows_note", f"{x.shape[0]} rows")}
 
 
 def main():
@@ -592,7 +803,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=800)
     ap.add_argument("--warmup", type=int, default=64)
-    ap.add_argument("--copies", type=int, default=4, help="weight copies cycled by decode steps")
+    ap.add_argument("--copies", type=int, default=16,
+                    help="weight copies cycled by decode steps (16 x 19 MB between reuses of a "
+                         "copy's router and shared expert exceeds the 256 MB last-level cache)")
+    ap.add_argument("--mid-steps", type=int, default=64,
+                    help="steps timed at T = 32 and T = 512")
     ap.add_argument("--prefill-steps", type=int, default=20)
     ap.add_argument("--prefill-warmup", type=int, default=3)
     ap.add_argument("--no-prefill", action="store_true")
@@ -634,35 +849,76 @@ def main():
         print(json.dumps(bench_balance(args, torch, qm, mi, DeviceLayer)), flush=True)
         return
 
-    print("[bench] decode T=1 ...", file=sys.stderr, flush=True)
-    dec, dec_layer, pool = bench_decode(args, torch, qm, mi, DeviceLayer)
-    pre = None
+    def say(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    checks = {}
+    say("C1 decode T=1 ...")
+    dec, checks["C1_decode_T1"] = bench_decode(args, torch, qm, mi, DeviceLayer)
+    say("C2 sharded decode T=1 ...")
+    c2s, checks["C2_sharded_T1"] = bench_sharded(
+        args, torch, qm, mi, DeviceLayer, "decode_sharded", 1, args.copies, 64, args.steps,
+        args.warmup, "sharded decode T=1: the same layer (seed 2), router_topk once, the 256/256 "
+        "shards as two moe_layer_forward_shard calls, moe_reduce_partials; 64-token pool, "
+        f"{args.copies} rotating weight copies, HIP graph of exactly `steps` steps", 64)
+    say("C2 batched decode T=32 ...")
+    c2b, checks["C2_batched_T32"] = bench_layer_batches(
+        args, torch, qm, mi, DeviceLayer, "decode_batched", 32, args.copies, args.mid_steps,
+        args.prefill_warmup, "batched decode T=32: the same layer (seed 2), rows N(0,1), "
+        f"automatic path, 4 token batches, {args.copies} rotating weight copies, HIP graph of "
+        "exactly `steps` steps")
+    pre = c3 = c4s = edges = mx = None
     if not args.no_prefill:
-        print("[bench] prefill T=4096 ...", file=sys.stderr, flush=True)
-        pre, pre_layer, x_pre = bench_prefill(args, torch, qm, mi, DeviceLayer)
-    edges = None
-    if not args.no_prefill:
-        print("[bench] RMSNorm / residual at T=4096 ...", file=sys.stderr, flush=True)
+        say("C3 prefill T=512 (Zipf-like expert load) ...")
+        c3, checks["C3_zipf_T512"] = bench_layer_batches(
+            args, torch, qm, mi, DeviceLayer, "prefill512_zipf", 512, 2, args.mid_steps,
+            args.prefill_warmup, "prefill T=512: the same layer (seed 3) with Zipf-like expert "
+            "load (slope -1), automatic path, 4 token batches, 2 rotating weight copies, HIP "
+            "graph of exactly `steps` steps")
+        say("C4 prefill T=4096 ...")
+        pre, checks["C4_prefill_T4096"], pre_layer, x_pre = bench_prefill(
+            args, torch, qm, mi, DeviceLayer)
+        say("C4 two-shard prefill T=4096 ...")
+        c4s, checks["C4_sharded_T4096"] = bench_sharded(
+            args, torch, qm, mi, DeviceLayer, "prefill4096", 4096, 2, 1, args.prefill_steps,
+            args.prefill_warmup, "two-shard prefill T=4096: the same layer (seed 4), router_topk "
+            "once, the 256/256 shards as two moe_layer_forward_shard calls, moe_reduce_partials; "
+            "2 rotating weight copies, HIP graph of exactly `steps` steps", 256)
+        say("RMSNorm / residual at T=4096 ...")
         edges = bench_edges(torch, qm)
-    mx = None
     if not args.no_mxfp4:
-        print("[bench] MXFP4 weights: decode T=1 ...", file=sys.stderr, flush=True)
-        mdec, _, _ = bench_decode(args, torch, qm, mi, DeviceLayer, "decode_mx")
+        say("MXFP4 weights: decode T=1 ...")
+        mdec, checks["mxfp4_decode_T1"] = bench_decode(args, torch, qm, mi, DeviceLayer,
+                                                       "decode_mx")
         mx = {"decode": {
             "workload": ("decode T=1: the same layer shape with MXFP4 gate/up/down weights "
-                         "(144-byte superblocks), seed 6, 64-token pool, 4 rotating weight "
-                         "copies, HIP-graph replay"),
+                         "(144-byte superblocks), seed 6, 64-token pool, "
+                         f"{args.copies} rotating weight copies, HIP graph of exactly `steps` "
+                         "steps"),
             "value": mdec["value"], "unit": "tokens/s", **{k: v for k, v in mdec.items()
                                                           if k != "value"}}}
         if not args.no_prefill:
-            print("[bench] MXFP4 weights: prefill T=4096 ...", file=sys.stderr, flush=True)
-            mx["prefill"], _, _ = bench_prefill(args, torch, qm, mi, DeviceLayer, "prefill4096_mx")
+            say("MXFP4 weights: prefill T=4096 ...")
+            mx["prefill"], checks["mxfp4_prefill_T4096"], _, _ = bench_prefill(
+                args, torch, qm, mi, DeviceLayer, "prefill4096_mx")
     cpu = None
     if not args.no_cpu_baseline:
-        print("[bench] oracle on the host ...", file=sys.stderr, flush=True)
-        cpu = cpu_baseline_decode(dec_layer, pool, args.cpu_budget)
+        say("oracle on the host: baseline and per-config max|err|/RMS ...")
+        cpu = cpu_baseline_decode(checks["C1_decode_T1"]["layer"], checks["C1_decode_T1"]["shape"],
+                                  checks["C1_decode_T1"]["x"], args.cpu_budget)
         if pre is not None:
-            pre["cpu_baseline"] = cpu_baseline_prefill(pre_layer, x_pre, args.cpu_prefill_rows)
+            pre["cpu_baseline"] = cpu_baseline_prefill(pre_layer, mi.QWEN35_MOE, x_pre,
+                                                       args.cpu_prefill_rows)
+        cpu["parity"] = {k: oracle_check(c) for k, c in checks.items()}
+        for key, obj in (("C1_decode_T1", dec), ("C2_sharded_T1", c2s), ("C2_batched_T32", c2b),
+                         ("C3_zipf_T512", c3), ("C4_prefill_T4096", pre),
+                         ("C4_sharded_T4096", c4s)):
+            if obj is not None:
+                obj["parity"] = cpu["parity"][key]
+        if mx is not None:
+            mx["decode"]["parity"] = cpu["parity"]["mxfp4_decode_T1"]
+            if mx.get("prefill"):
+                mx["prefill"]["parity"] = cpu["parity"]["mxfp4_prefill_T4096"]
 
     line = {
         "metric": METRIC,
@@ -680,7 +936,8 @@ def main():
         "config": {
             "workload": ("decode T=1: Qwen3.5-35B-A3B-shaped routed MoE layer, H=2048, 256 "
                          "experts, top-8, I=512, shared expert I=512, Q4_K gate/up, Q5_K down, "
-                         "seed 1, 64-token pool, 4 rotating weight copies, HIP-graph replay"),
+                         f"seed 1, 64-token pool, {args.copies} rotating weight copies, one HIP "
+                         "graph of exactly `steps` steps"),
             "T": 1,
             "path": "gemv",
             "parallelism": "single GPU",
@@ -688,7 +945,11 @@ def main():
         "roofline": dec["roofline"],
         "cpu_baseline": cpu,
         "decode": {k: v for k, v in dec.items() if k not in ("value", "ms_per_step", "roofline")},
+        "sharded_decode": c2s,
+        "batched_decode": c2b,
+        "zipf_prefill": c3,
         "prefill": pre,
+        "sharded_prefill": c4s,
         "mxfp4": mx,
         "edges": edges,
     }
