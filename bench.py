@@ -412,7 +412,7 @@ def bench_sharded(args, torch, qm, mi, DeviceLayer, name, T, n_copies, n_batches
     else:
         names = ["gemv_front", "gateup_gemv", "down_gemv"]
     kst = {}
-    kms = kernel_profile_calls(torch, lambda i, e: step(i, e), min(K, 64), 2, names, kst)
+    kms = kernel_profile_calls(torch, lambda i, e: step(i, e), min(K, 16), 2, names, kst)
     kms_flat = {f"shard{c}.{n}": v for (c, n), v in kms.items()}
     if path == qm.MOE_PATH_MFMA:
         slots = T * shp.k + T
@@ -821,6 +821,12 @@ def main():
     ap.add_argument("--continuum", action="store_true",
                     help="only time both paths at T = 1 .. 512 (one JSON line per point)")
     ap.add_argument("--continuum-t", type=int, nargs="+", default=list(CONTINUUM_T))
+    ap.add_argument("--only", nargs="+", default=None, metavar="WORKLOAD",
+                    choices=["decode", "sharded_decode", "batched_decode", "zipf_prefill",
+                             "prefill", "sharded_prefill", "edges", "mxfp4_decode",
+                             "mxfp4_prefill"],
+                    help="run only these workloads (profiler runs); the JSON line then holds "
+                         "only them")
     ap.add_argument("--balance", action="store_true",
                     help="only report lane times of shards sized by fraction (one JSON object)")
     args = ap.parse_args()
@@ -852,41 +858,50 @@ def main():
     def say(msg):
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
+    def want(name):
+        return args.only is None or name in args.only
+
     checks = {}
-    say("C1 decode T=1 ...")
-    dec, checks["C1_decode_T1"] = bench_decode(args, torch, qm, mi, DeviceLayer)
-    say("C2 sharded decode T=1 ...")
-    c2s, checks["C2_sharded_T1"] = bench_sharded(
+    dec = c2s = c2b = pre = c3 = c4s = edges = mx = None
+    if want("decode"):
+        say("C1 decode T=1 ...")
+        dec, checks["C1_decode_T1"] = bench_decode(args, torch, qm, mi, DeviceLayer)
+    if want("sharded_decode"):
+        say("C2 sharded decode T=1 ...")
+        c2s, checks["C2_sharded_T1"] = bench_sharded(
         args, torch, qm, mi, DeviceLayer, "decode_sharded", 1, args.copies, 64, args.steps,
         args.warmup, "sharded decode T=1: the same layer (seed 2), router_topk once, the 256/256 "
         "shards as two moe_layer_forward_shard calls, moe_reduce_partials; 64-token pool, "
         f"{args.copies} rotating weight copies, HIP graph of exactly `steps` steps", 64)
-    say("C2 batched decode T=32 ...")
-    c2b, checks["C2_batched_T32"] = bench_layer_batches(
-        args, torch, qm, mi, DeviceLayer, "decode_batched", 32, args.copies, args.mid_steps,
-        args.prefill_warmup, "batched decode T=32: the same layer (seed 2), rows N(0,1), "
-        f"automatic path, 4 token batches, {args.copies} rotating weight copies, HIP graph of "
-        "exactly `steps` steps")
-    pre = c3 = c4s = edges = mx = None
-    if not args.no_prefill:
+    if want("batched_decode"):
+        say("C2 batched decode T=32 ...")
+        c2b, checks["C2_batched_T32"] = bench_layer_batches(
+            args, torch, qm, mi, DeviceLayer, "decode_batched", 32, args.copies, args.mid_steps,
+            args.prefill_warmup, "batched decode T=32: the same layer (seed 2), rows N(0,1), "
+            f"automatic path, 4 token batches, {args.copies} rotating weight copies, HIP graph of "
+            "exactly `steps` steps")
+    if not args.no_prefill and want("zipf_prefill"):
         say("C3 prefill T=512 (Zipf-like expert load) ...")
         c3, checks["C3_zipf_T512"] = bench_layer_batches(
             args, torch, qm, mi, DeviceLayer, "prefill512_zipf", 512, 2, args.mid_steps,
             args.prefill_warmup, "prefill T=512: the same layer (seed 3) with Zipf-like expert "
             "load (slope -1), automatic path, 4 token batches, 2 rotating weight copies, HIP "
             "graph of exactly `steps` steps")
+    if not args.no_prefill and want("prefill"):
         say("C4 prefill T=4096 ...")
         pre, checks["C4_prefill_T4096"], pre_layer, x_pre = bench_prefill(
             args, torch, qm, mi, DeviceLayer)
+    if not args.no_prefill and want("sharded_prefill"):
         say("C4 two-shard prefill T=4096 ...")
         c4s, checks["C4_sharded_T4096"] = bench_sharded(
             args, torch, qm, mi, DeviceLayer, "prefill4096", 4096, 2, 1, args.prefill_steps,
             args.prefill_warmup, "two-shard prefill T=4096: the same layer (seed 4), router_topk "
             "once, the 256/256 shards as two moe_layer_forward_shard calls, moe_reduce_partials; "
             "2 rotating weight copies, HIP graph of exactly `steps` steps", 256)
+    if not args.no_prefill and want("edges"):
         say("RMSNorm / residual at T=4096 ...")
         edges = bench_edges(torch, qm)
-    if not args.no_mxfp4:
+    if not args.no_mxfp4 and want("mxfp4_decode"):
         say("MXFP4 weights: decode T=1 ...")
         mdec, checks["mxfp4_decode_T1"] = bench_decode(args, torch, qm, mi, DeviceLayer,
                                                        "decode_mx")
@@ -897,10 +912,16 @@ def main():
                          "steps"),
             "value": mdec["value"], "unit": "tokens/s", **{k: v for k, v in mdec.items()
                                                           if k != "value"}}}
-        if not args.no_prefill:
-            say("MXFP4 weights: prefill T=4096 ...")
-            mx["prefill"], checks["mxfp4_prefill_T4096"], _, _ = bench_prefill(
-                args, torch, qm, mi, DeviceLayer, "prefill4096_mx")
+    if not args.no_prefill and not args.no_mxfp4 and want("mxfp4_prefill"):
+        say("MXFP4 weights: prefill T=4096 ...")
+        mx = mx or {}
+        mx["prefill"], checks["mxfp4_prefill_T4096"], _, _ = bench_prefill(
+            args, torch, qm, mi, DeviceLayer, "prefill4096_mx")
+    if args.only is not None:
+        print(json.dumps({"only": args.only, "decode": dec, "sharded_decode": c2s,
+                          "batched_decode": c2b, "zipf_prefill": c3, "prefill": pre,
+                          "sharded_prefill": c4s, "mxfp4": mx, "edges": edges}), flush=True)
+        return
     cpu = None
     if not args.no_cpu_baseline:
         say("oracle on the host: baseline and per-config max|err|/RMS ...")
