@@ -47,6 +47,8 @@ sys.path.insert(0, ROOT)
 METRIC = ("MoE-layer tokens/s at T=1 and T=4096; % peak HBM BW (decode) / % MFMA (prefill)")
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 FP16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak
+FP8_MFMA_PEAK_TFLOPS = 5000.0   # MI355X dense fp8 matrix peak (fp8 x fp4 runs at the fp8 rate)
+MX_TERMS = 3                    # MX-FP8 terms per token / h value on the MXFP4 MFMA path
 
 
 # HBM bytes per launch of the roofline kernels, from two rocprofv3 --pmc passes
@@ -76,7 +78,7 @@ TRAFFIC_SOURCES = {
     "gemm_gateup": ["gemm.hip", "moe_internal.h"],
 }
 TRAFFIC_SOURCES["gemv_gateup_mx"] = TRAFFIC_SOURCES["gemv_gateup"]
-TRAFFIC_SOURCES["gemm_gateup_mx"] = TRAFFIC_SOURCES["gemm_gateup"]
+TRAFFIC_SOURCES["gemm_gateup_mx"] = ["gemm_mx.hip", "moe_internal.h"]
 
 
 def sources_sha(kernel):
@@ -132,6 +134,7 @@ class HipEvents:
         f = ctypes.c_float()
         if self.hip.hipEventElapsedTime(ctypes.byref(f), ctypes.c_void_p(self.ev[a]),
                                         ctypes.c_void_p(self.ev[b])) != 0:
+            self.hip.hipGetLastError()   # clear the error it left for later launch checks
             raise RuntimeError("hipEventElapsedTime failed")
         return f.value
 
@@ -154,7 +157,10 @@ def kernel_profile(torch, qm, call, n_steps, names, stats=None):
     out = {}
     for n in names:
         kid = KERNEL_IDS[n]
-        d = [ev.ms(i * per_step + 2 * kid, i * per_step + 2 * kid + 1) for i in range(n_steps)]
+        try:
+            d = [ev.ms(i * per_step + 2 * kid, i * per_step + 2 * kid + 1) for i in range(n_steps)]
+        except RuntimeError:
+            continue   # a kernel this path does not launch (its events were never recorded)
         out[n] = float(np.mean(d))
         if stats is not None:
             stats[n] = {"median_ms": float(np.median(d)), "min_ms": float(np.min(d))}
@@ -427,12 +433,13 @@ def bench_sharded(args, torch, qm, mi, DeviceLayer, name, T, n_copies, n_batches
                  "expert_mfma_frac": flops / (gemm_ms * 1e-3) / (FP16_MFMA_PEAK_TFLOPS * 1e12),
                  "step_mfma_frac": flops / dev_s / (FP16_MFMA_PEAK_TFLOPS * 1e12)}
     else:
-        gu_bytes = shp.k * gu // 2 + shp.H * 4 + shp.k * (shp.I // 2) * 4
-        rl = roofline("gemv_gateup_kernel of shard 0 (8 routed experts, I/2 = %d)" % (shp.I // 2),
-                      "hbm", gu_bytes, kms[(0, "gateup_gemv")], "GB/s", HBM_PEAK_GBS,
-                      extra={"median_launch_ms": kst[(0, "gateup_gemv")]["median_ms"],
-                             "min_launch_ms": kst[(0, "gateup_gemv")]["min_ms"]})
+        # the whole step (router_topk, two shards of three kernels, the reduce):
+        # eager per-kernel events of these many small calls run slow (the GPU
+        # idles between the host's calls), so the step's own graph time is
+        # the basis
         layer_bytes = (shp.k + 1) * (gu + dn) + shp.H * shp.E * 4 + 3 * T * shp.H * 4
+        rl = roofline("whole sharded step (router_topk + 2 x 3 shard kernels + reduce)", "hbm",
+                      layer_bytes, dev_s * 1e3, "GB/s", HBM_PEAK_GBS)
         whole = {"layer_algorithmic_bytes": layer_bytes,
                  "layer_hbm_frac": layer_bytes / dev_s / (HBM_PEAK_GBS * 1e9)}
     x0 = xd[0]
@@ -476,7 +483,7 @@ def bench_prefill(args, torch, qm, mi, DeviceLayer, name="prefill4096", check_ro
     assert set(used) == {qm.MOE_PATH_MFMA}, used
     eager_secs = time_steps(torch, step, K)
     dev_s, host_s = graph_time(torch, step, K)
-    names = ["x_f16", "router_mfma", "router_topk", "bucket_hist", "bucket_scan",
+    names = ["x_f16", "x_mx", "router_mfma", "router_topk", "bucket_hist", "bucket_scan",
              "bucket_scatter", "gemm_gateup", "gemm_down", "combine"]
     kst = {}
     kms = kernel_profile(torch, qm, lambda i, e: step(i, e), K, names, kst)
@@ -485,10 +492,14 @@ def bench_prefill(args, torch, qm, mi, DeviceLayer, name="prefill4096", check_ro
     flops_d = 2.0 * shp.I * shp.H * slots
     gu_ms = kms["gemm_gateup"]
     d_ms = kms["gemm_down"]
+    mx = shp.fmt == 1
+    # the contraction's own dtype: fp16 x fp16 (K-quant), fp8 x fp4 block-scaled (MXFP4)
+    peak = FP8_MFMA_PEAK_TFLOPS if mx else FP16_MFMA_PEAK_TFLOPS
     res = {
         "workload": ("prefill T=4096: same layer shape, %s weights, seed %d, uniform router, "
-                     "grouped fp16-MFMA path, 2 rotating weight copies, HIP graph of exactly "
-                     "`steps` steps" % ("MXFP4" if shp.fmt else "Q4_K/Q5_K", w.seed)),
+                     "grouped %s path, 2 rotating weight copies, HIP graph of exactly "
+                     "`steps` steps" % ("MXFP4" if mx else "Q4_K/Q5_K", w.seed,
+                                        "block-scaled fp8 x fp4 MFMA" if mx else "fp16-MFMA")),
         "value": T / dev_s,
         "unit": "tokens/s",
         "ms_per_step": dev_s * 1e3,
@@ -497,17 +508,23 @@ def bench_prefill(args, torch, qm, mi, DeviceLayer, name="prefill4096", check_ro
         "eager_ms_per_step": eager_secs / K * 1e3,
         "steps": K,
         "warmup": W,
-        "dtype": "fp16 operands, fp32 accumulate (router fp32)",
+        "dtype": ("fp4 E2M1 weights x fp8 e4m3 tokens and h (%d MX-FP8 terms per value), "
+                  "block-scaled MFMA, fp32 accumulate (router fp32)" % MX_TERMS if mx else
+                  "fp16 operands, fp32 accumulate (router fp32)"),
         "kernel_ms": kms,
         "expert_gflop": (flops_gu + flops_d) / 1e9,
-        "expert_mfma_frac": (flops_gu + flops_d) / ((gu_ms + d_ms) * 1e-3) / (FP16_MFMA_PEAK_TFLOPS * 1e12),
-        "step_mfma_frac": (flops_gu + flops_d) / dev_s / (FP16_MFMA_PEAK_TFLOPS * 1e12),
-        "roofline": roofline("gemm_gateup_kernel", "mfma", flops_gu, gu_ms, "TFLOP/s",
-                             FP16_MFMA_PEAK_TFLOPS,
-                             traffic_for("gemm_gateup_mx" if shp.fmt else "gemm_gateup"),
+        "expert_mfma_frac": (flops_gu + flops_d) / ((gu_ms + d_ms) * 1e-3) / (peak * 1e12),
+        "step_mfma_frac": (flops_gu + flops_d) / dev_s / (peak * 1e12),
+        "roofline": roofline("gemm_mx_kernel<0>" if mx else "gemm_grouped_kernel<0>", "mfma",
+                             flops_gu, gu_ms, "TFLOP/s", peak,
+                             traffic_for("gemm_gateup_mx" if mx else "gemm_gateup"),
                              {"median_launch_ms": kst["gemm_gateup"]["median_ms"],
                               "min_launch_ms": kst["gemm_gateup"]["min_ms"], "launches": K}),
     }
+    if mx:
+        # every product runs as MX_TERMS block-scaled MFMAs: executed matrix work
+        res["roofline"]["executed_flops_per_launch"] = MX_TERMS * flops_gu
+        res["roofline"]["executed_frac"] = MX_TERMS * res["roofline"]["frac"]
     qm.moe_layer_forward(base.desc, x, T, out, ws)
     idx = torch.empty((T, shp.k), dtype=torch.int32, device="cuda")
     wts = torch.empty((T, shp.k), dtype=torch.float32, device="cuda")

@@ -63,10 +63,13 @@
  *   mantissa m: e = 0 gives m/2, else 2^(e-1) * (1 + m/2)) in the nibble
  *   order above; w = X_j * value(code).  Gate, up and down (and the shared
  *   expert) all use it; every matrix has I*H/256 superblocks of 144 bytes.
- *   The fp32 paths decode exactly for scale bytes 2..254 (smaller ones give
- *   fp32 subnormals, larger products overflow to inf); the MFMA path's fp16
- *   operands are exact for scale bytes 114..128 (outside that range weights
- *   round, underflow or overflow in fp16; not checked at run time).
+ *   The fp32 GEMV path decodes exactly for scale bytes 2..254 (smaller ones
+ *   give fp32 subnormals, larger products overflow to inf).  The MFMA path
+ *   hands codes and scales to gfx950's block-scaled matrix cores unchanged, so
+ *   every scale byte 0..254 applies exactly (255, the format's NaN, gives
+ *   NaN); its tokens and SwiGLU outputs enter as the sum of three MX-FP8
+ *   (e4m3) terms with an E8M0 scale per 32 values, which represents each value
+ *   to within 2^-12 of its 32-value block's largest magnitude.
  */
 #ifndef MOE_HIP_H
 #define MOE_HIP_H
@@ -78,7 +81,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 5
+#define MOE_ABI_VERSION 6
 
 /* Status codes returned by every entry point. */
 #define MOE_OK 0
@@ -96,7 +99,8 @@ extern "C" {
 /* Compute paths (moe_opts.path). */
 #define MOE_PATH_AUTO 0        /* GEMV for T <= 14, grouped MFMA GEMM above (measured crossover) */
 #define MOE_PATH_GEMV 1        /* fp32 dequant-GEMV, fp32 accumulation */
-#define MOE_PATH_MFMA 2        /* fp16-operand MFMA grouped GEMM, fp32 accumulation */
+#define MOE_PATH_MFMA 2        /* grouped GEMM on the matrix cores, fp32 accumulation: fp16
+                                  operands (K-quant), block-scaled MX operands (MXFP4) */
 
 /*
  * Layer description: plain values and device pointers, read during the call
@@ -154,7 +158,8 @@ typedef struct moe_opts {
 #define MOE_K_GEMM_GATEUP 9      /* prefill: grouped GEMM gate/up + SwiGLU */
 #define MOE_K_GEMM_DOWN 10       /* prefill: grouped GEMM down */
 #define MOE_K_COMBINE 11         /* prefill: slot-order combine */
-#define MOE_K_COUNT 12
+#define MOE_K_X_MX 12            /* prefill, MXFP4 weights: tokens to MX-FP8 terms */
+#define MOE_K_COUNT 13
 
 /* Bytes of device workspace that router_topk, moe_layer_forward and
  * moe_layer_forward_shard need for T token rows split into num_shards shards

@@ -28,8 +28,8 @@ The second weight format (``LayerShape.fmt == 1``; gate, up and down all use
 it): a 144-byte superblock of 256 weights, bytes 0..7 the E8M0 scale bytes of
 its eight 32-weight blocks, bytes 8..15 zero (reserved), bytes 16..143 the
 4-bit E2M1 codes in the nibble order of the 4-bit K-quant superblock.  Scale
-bytes are uniform on 121..125 (block scales 2^-6 .. 2^-2) and codes uniform on
-0..15.
+bytes are uniform on ``LayerShape.mx_scales`` (by default 116..132, block
+scales 2^-11 .. 2^5) and codes uniform on 0..15.
 
 Weight matrices are stored one row per output feature with the reduction
 dimension contiguous, quantised in flat row-major order in 256-element
@@ -46,7 +46,7 @@ import numpy as np
 Q4K_SB_BYTES = 144   # fp16 d, fp16 dmin, 12 scale bytes, 128 code bytes
 Q5K_SB_BYTES = 176   # as Q4K plus 32 bytes of high code bits
 MXFP4_SB_BYTES = 144  # 8 E8M0 scale bytes, 8 reserved bytes, 128 code bytes
-MXFP4_SCALE_RANGE = (121, 125)   # E8M0 scale bytes drawn uniformly (inclusive)
+MXFP4_SCALE_RANGE = (116, 132)   # E8M0 scale bytes drawn uniformly (inclusive), by default
 SB_WEIGHTS = 256
 
 # Stream ids: every tensor (and every expert of it) draws from its own stream
@@ -65,6 +65,7 @@ class LayerShape:
     Is: int         # shared-expert intermediate width (0 = no shared expert)
     shared_weight: float = 1.0
     fmt: int = 0    # 0: Q4_K gate/up and Q5_K down; 1: MXFP4 gate, up and down
+    mx_scales: tuple = MXFP4_SCALE_RANGE   # MXFP4: E8M0 scale bytes drawn uniformly (inclusive)
 
     def sb_counts(self):
         """Superblocks per matrix: gate/up (I x H), down (H x I), shared ones."""
@@ -135,18 +136,20 @@ def kquant_blob(rng: np.random.Generator, n_sb: int, bits: int) -> np.ndarray:
     return blob.reshape(-1)
 
 
-def mxfp4_blob(rng: np.random.Generator, n_sb: int) -> np.ndarray:
-    """``n_sb`` random MXFP4 superblocks as a flat uint8 array."""
-    lo, hi = MXFP4_SCALE_RANGE
+def mxfp4_blob(rng: np.random.Generator, n_sb: int, scales=MXFP4_SCALE_RANGE) -> np.ndarray:
+    """``n_sb`` random MXFP4 superblocks as a flat uint8 array, scale bytes
+    uniform on ``scales`` (inclusive)."""
+    lo, hi = scales
     blob = np.zeros((n_sb, MXFP4_SB_BYTES), dtype=np.uint8)
     blob[:, 0:8] = rng.integers(lo, hi + 1, size=(n_sb, 8), dtype=np.uint8)
     blob[:, 16:] = np.frombuffer(rng.bytes(n_sb * 128), dtype=np.uint8).reshape(n_sb, 128)
     return blob.reshape(-1)
 
 
-def weight_blob(rng: np.random.Generator, n_sb: int, bits: int, fmt: int) -> np.ndarray:
+def weight_blob(rng: np.random.Generator, n_sb: int, bits: int, fmt: int,
+                mx_scales=MXFP4_SCALE_RANGE) -> np.ndarray:
     """Superblocks of a layer's format: K-quant of ``bits`` bits, or MXFP4."""
-    return mxfp4_blob(rng, n_sb) if fmt == 1 else kquant_blob(rng, n_sb, bits)
+    return mxfp4_blob(rng, n_sb, mx_scales) if fmt == 1 else kquant_blob(rng, n_sb, bits)
 
 
 def _zipf_parts(shape: LayerShape, seed: int):
@@ -176,8 +179,11 @@ def make_layer(shape: LayerShape, seed: int, zipf: bool = False) -> Dict[str, np
 
     f = shape.fmt
 
+    ms = shape.mx_scales
+
     def stack(stream, n_sb, bits):
-        return np.stack([weight_blob(_rng(seed, stream, e), n_sb, bits, f) for e in range(shape.E)])
+        return np.stack([weight_blob(_rng(seed, stream, e), n_sb, bits, f, ms)
+                         for e in range(shape.E)])
 
     layer = {
         "router_w": np.ascontiguousarray(wr),
@@ -186,9 +192,9 @@ def make_layer(shape: LayerShape, seed: int, zipf: bool = False) -> Dict[str, np
         "down": stack(_S_DOWN, n_d, 5),
     }
     if shape.Is > 0:
-        layer["sh_gate"] = weight_blob(_rng(seed, _S_SH_GATE), n_sgu, 4, f)
-        layer["sh_up"] = weight_blob(_rng(seed, _S_SH_UP), n_sgu, 4, f)
-        layer["sh_down"] = weight_blob(_rng(seed, _S_SH_DOWN), n_sd, 5, f)
+        layer["sh_gate"] = weight_blob(_rng(seed, _S_SH_GATE), n_sgu, 4, f, ms)
+        layer["sh_up"] = weight_blob(_rng(seed, _S_SH_UP), n_sgu, 4, f, ms)
+        layer["sh_down"] = weight_blob(_rng(seed, _S_SH_DOWN), n_sd, 5, f, ms)
     return layer
 
 

@@ -24,8 +24,8 @@ MOE_SB_MXFP4 = 14
 # kernel ids for moe_opts.kernel_events (include/moe.h MOE_K_*)
 KERNEL_IDS = {"gemv_front": 0, "router_mfma": 1, "router_topk": 2, "gateup_gemv": 3,
               "down_gemv": 4, "x_f16": 5, "bucket_hist": 6, "bucket_scan": 7, "bucket_scatter": 8,
-              "gemm_gateup": 9, "gemm_down": 10, "combine": 11}
-N_KERNEL_IDS = 12
+              "gemm_gateup": 9, "gemm_down": 10, "combine": 11, "x_mx": 12}
+N_KERNEL_IDS = 13
 
 
 class MoeError(RuntimeError):

@@ -189,7 +189,15 @@ WsLayout ws_layout(const moe_layer_desc& d, int T, int iloc) {
     L.tile_off = off;     off = align256(off + (E + 3) * 4);
     L.tile_rec = off;     off = align256(off + (size_t)max_row_tiles(T, (int)k, (int)E, d.shared_inter > 0) * 16);
     L.perm = off;         off = align256(off + Tz * k * 4);
-    L.h16 = off;          off = align256(off + (Tz * k + Tz) * Iloc * 2);
+    const size_t hrows = Tz * k + Tz;
+    if (d.weight_format == MOE_WFMT_MXFP4) {
+        L.mx_xq = off;    off = align256(off + (size_t)kMxTerms * Tz * H);
+        L.mx_xs = off;    off = align256(off + Tz * (H / 64) * 16);
+        L.mx_hq = off;    off = align256(off + (size_t)kMxTerms * hrows * Iloc);
+        L.mx_hs = off;    off = align256(off + hrows * (Iloc / 64) * 16);
+    } else {
+        L.h16 = off;      off = align256(off + hrows * Iloc * 2);
+    }
     L.y = off;            off = align256(off + Tz * k * H * 4);
     L.ysh = off;          off = align256(off + Tz * H * 4);
     L.total = gemv_end > off ? gemv_end : off;
@@ -379,6 +387,8 @@ static int forward_common(const moe_layer_desc* desc, const float* x, int32_t T,
         idx = ridx;
         w = rw;
     }
+    if (desc->weight_format == MOE_WFMT_MXFP4)
+        return launched(launch_mfma_mx(*desc, x, T, idx, w, i0, iloc, out, wsp, L, c));
     return launched(launch_mfma(*desc, x, T, idx, w, i0, iloc, out, wsp, L, c,
                                 route && T > kRouterSmallMaxT));
 }

@@ -12,8 +12,9 @@
 // exceeds a 1e-2 max-error/RMS bound while fp16 stays near 3e-3; gfx950 runs
 // both at the same rate.
 //
-// One kernel template serves both projections and both weight formats (the
-// MXFP4 producer differs only in its superblock size and piece decode).  A workgroup owns one tile:
+// This kernel serves the K-quant weight format (MXFP4 weights take the
+// block-scaled matrix cores, gemm_mx.hip).  One kernel template serves both
+// projections.  A workgroup owns one tile:
 // up to 160 rows of one expert's group (a whole routed expert at T = 4096, so
 // its weights are dequantised once per column tile) times 256 weight rows, and
 // walks K in steps of 64 (one pair of K-quant sub-blocks).  Its 8 waves are
@@ -82,43 +83,6 @@ __device__ __forceinline__ void dequant_piece_to_lds(const SbHead& hd, const uin
                                                      _Float16* row) {
     uint32_t lo[8], hi[8];
     kq_piece_f16<HIGH>(hd, qs, qh, c, lo, hi);
-    *reinterpret_cast<uint4*>(row + 16 * hh) = uint4{lo[0], lo[1], lo[2], lo[3]};
-    *reinterpret_cast<uint4*>(row + 16 * hh + 8) = uint4{lo[4], lo[5], lo[6], lo[7]};
-    *reinterpret_cast<uint4*>(row + 32 + 16 * hh) = uint4{hi[0], hi[1], hi[2], hi[3]};
-    *reinterpret_cast<uint4*>(row + 32 + 16 * hh + 8) = uint4{hi[4], hi[5], hi[6], hi[7]};
-}
-
-// The same for an MXFP4 code piece (no high bits; s0 / s1: the superblock's
-// scale bytes 0..3 / 4..7).  A code's sign, exponent and mantissa bits placed
-// in the top byte of an fp16 word make the number value * 2^-14 (exponent 0
-// lands on fp16's subnormals, which hold the E2M1 subnormals exactly); one
-// packed multiply by the fp16 number 2^14 * X then gives two weights, exact
-// whenever X * value is a normal fp16 number (scale bytes 114..128).
-__device__ __forceinline__ void dequant_mx_piece_to_lds(uint32_t s0, uint32_t s1, const uint4& qs,
-                                                        int c, int hh, _Float16* row) {
-    const uint32_t sw = c < 2 ? s0 : s1;
-    const int sh = 16 * (c & 1);
-    const _Float16 fa = (_Float16)(e8m0_f32((sw >> sh) & 0xffu) * 16384.0f);
-    const _Float16 fb = (_Float16)(e8m0_f32((sw >> (sh + 8)) & 0xffu) * 16384.0f);
-    const half2v FA = {fa, fa}, FB = {fb, fb};
-    const uint32_t qw[4] = {qs.x, qs.y, qs.z, qs.w};
-    uint32_t lo[8], hi[8];
-#pragma unroll
-    for (int wi = 0; wi < 4; ++wi) {
-        // top bytes of the fp16 patterns, four codes each: sign to bit 7,
-        // exponent and mantissa to bits 3..1 (low nibbles, then high nibbles)
-        const uint32_t bl = and_or(qw[wi] << 1, 0x0e0e0e0eu, (qw[wi] << 4) & 0x80808080u);
-        const uint32_t bh = and_or(qw[wi] >> 3, 0x0e0e0e0eu, qw[wi] & 0x80808080u);
-#pragma unroll
-        for (int pr = 0; pr < 2; ++pr) {
-            // bytes 2pr and 2pr+1 into the top bytes of the two halves
-            const uint32_t sel = pr ? 0x030c020cu : 0x010c000cu;
-            const half2v wl = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(0u, bl, sel)) * FA;
-            const half2v wh = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(0u, bh, sel)) * FB;
-            lo[2 * wi + pr] = __builtin_bit_cast(uint32_t, wl);
-            hi[2 * wi + pr] = __builtin_bit_cast(uint32_t, wh);
-        }
-    }
     *reinterpret_cast<uint4*>(row + 16 * hh) = uint4{lo[0], lo[1], lo[2], lo[3]};
     *reinterpret_cast<uint4*>(row + 16 * hh + 8) = uint4{lo[4], lo[5], lo[6], lo[7]};
     *reinterpret_cast<uint4*>(row + 32 + 16 * hh) = uint4{hi[0], hi[1], hi[2], hi[3]};
@@ -220,11 +184,10 @@ struct TileInfo {
 // producer waves, consumer waves, and an epilogue that all 8 waves run.
 // Producers: (straight-line
 // code: the fragment reads of a 16-wide K slice are issued before its MFMAs).
-template <int MODE, int MB, int FMT>
+template <int MODE, int MB>
 __device__ __forceinline__ void gemm_produce(const GemmArgs& a, const TileInfo& ti, GemmLds& lds,
                                           const int32_t* row_src, const float* row_w) {
-    constexpr bool MX = FMT == MOE_WFMT_MXFP4;
-    constexpr int DSB = MX ? kMxBytes : kQ5Bytes;   // bytes of a down superblock
+    constexpr int DSB = kQ5Bytes;   // bytes of a down superblock
     constexpr int kPD = PrefetchDistance<MODE>::v;
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -243,7 +206,7 @@ __device__ __forceinline__ void gemm_produce(const GemmArgs& a, const TileInfo& 
         // superblock ahead; producer thread pt owns row pt, copies its
         // superblock into registers once per four steps and dequantises one
         // sub-block pair of it per step.
-        constexpr int SBB = MODE == 0 ? kQ4Bytes : DSB;   // MXFP4 gate/up: kQ4Bytes too
+        constexpr int SBB = MODE == 0 ? kQ4Bytes : DSB;
         constexpr int NCH = SBB / 16;
         const int nsb = a.nk / 4;
         auto row_base = [&](int r) -> const uint8_t* {
@@ -281,12 +244,6 @@ __device__ __forceinline__ void gemm_produce(const GemmArgs& a, const TileInfo& 
             for (int i = 0; i < NCH; ++i) R[i] = lds.raw[pt * NCH + i];
         };
         auto deq_step = [&](int c, int stage) {
-            if constexpr (MX) {
-                _Float16* dst = &lds.b[stage][pt][0];
-                dequant_mx_piece_to_lds(R[0].x, R[0].y, R[1 + 2 * c], c, 0, dst);
-                dequant_mx_piece_to_lds(R[0].x, R[0].y, R[2 + 2 * c], c, 1, dst);
-                return;
-            }
             SbHead hd;
             hd.d = f16_bits_to_f32(R[0].x & 0xffffu);
             hd.dmin = f16_bits_to_f32(R[0].x >> 16);
@@ -369,12 +326,8 @@ __device__ __forceinline__ void gemm_produce(const GemmArgs& a, const TileInfo& 
                 const int c = (int)((base & 255) >> 6);
                 const uint8_t* sb = wsrc[q] + (base >> 8) * DSB;
                 rg[q].head = *reinterpret_cast<const uint4*>(sb);
-                if (MX) {
-                    rg[q].qs = *reinterpret_cast<const uint4*>(sb + 16 + 32 * c + 16 * bhh[q]);
-                } else {
-                    rg[q].qh = *reinterpret_cast<const uint4*>(sb + 16 + 16 * bhh[q]);
-                    rg[q].qs = *reinterpret_cast<const uint4*>(sb + 48 + 32 * c + 16 * bhh[q]);
-                }
+                rg[q].qh = *reinterpret_cast<const uint4*>(sb + 16 + 16 * bhh[q]);
+                rg[q].qs = *reinterpret_cast<const uint4*>(sb + 48 + 32 * c + 16 * bhh[q]);
             }
         }
     };
@@ -389,12 +342,8 @@ __device__ __forceinline__ void gemm_produce(const GemmArgs& a, const TileInfo& 
             hd.s2 = rg[q].head.w;
             const int c = MODE == 0 ? (kk & 3)
                                     : (int)(((eoff[q] + (size_t)kk * kBK) & 255) >> 6);
-            if (MX)
-                dequant_mx_piece_to_lds(rg[q].head.x, rg[q].head.y, rg[q].qs, c, bhh[q],
-                                        &lds.b[stage][brr[q]][0]);
-            else
-                dequant_piece_to_lds<MODE == 1>(hd, rg[q].qs, rg[q].qh, c, bhh[q],
-                                                &lds.b[stage][brr[q]][0]);
+            dequant_piece_to_lds<MODE == 1>(hd, rg[q].qs, rg[q].qh, c, bhh[q],
+                                            &lds.b[stage][brr[q]][0]);
         }
     };
     BRegs ring[kPD][kBTasks];
@@ -569,7 +518,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const TileInfo&
     }
 }
 
-template <int MODE, int MB, int FMT>
+template <int MODE, int MB>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileInfo& ti, GemmLds& lds,
                                           const int32_t* row_src, const float* row_w) {
     float16v acc[MB][2];
@@ -579,13 +528,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileInfo& ti,
         acc[i][1] = float16v{};
     }
     if (threadIdx.x >> 6 >= kConsumers)
-        gemm_produce<MODE, MB, FMT>(a, ti, lds, row_src, row_w);
+        gemm_produce<MODE, MB>(a, ti, lds, row_src, row_w);
     else
         gemm_consume<MODE, MB>(a, ti, lds, row_src, row_w, acc);
     gemm_epilogue<MODE, MB>(a, ti, lds, row_src, row_w, acc);
 }
 
-template <int MODE, int FMT>
+template <int MODE>
 __global__ void __launch_bounds__(kGemmThreads)
 gemm_grouped_kernel(GemmArgs a) {
     __shared__ GemmLds lds;
@@ -632,11 +581,11 @@ gemm_grouped_kernel(GemmArgs a) {
     // row_src and row_w are read only in the epilogue, after the K loop's
     // barriers; the weight and token-row loads start without waiting for them
     switch ((ti.mcount + 31) >> 5) {
-        case 1: gemm_tile<MODE, 1, FMT>(a, ti, lds, row_src, row_w); break;
-        case 2: gemm_tile<MODE, 2, FMT>(a, ti, lds, row_src, row_w); break;
-        case 3: gemm_tile<MODE, 3, FMT>(a, ti, lds, row_src, row_w); break;
-        case 4: gemm_tile<MODE, 4, FMT>(a, ti, lds, row_src, row_w); break;
-        default: gemm_tile<MODE, 5, FMT>(a, ti, lds, row_src, row_w); break;
+        case 1: gemm_tile<MODE, 1>(a, ti, lds, row_src, row_w); break;
+        case 2: gemm_tile<MODE, 2>(a, ti, lds, row_src, row_w); break;
+        case 3: gemm_tile<MODE, 3>(a, ti, lds, row_src, row_w); break;
+        case 4: gemm_tile<MODE, 4>(a, ti, lds, row_src, row_w); break;
+        default: gemm_tile<MODE, 5>(a, ti, lds, row_src, row_w); break;
     }
 }
 
@@ -746,10 +695,8 @@ hipError_t launch_mfma(const moe_layer_desc& d, const float* x, int T, const int
     g1.nk = H / kBK;
     g1.h_out = h16;
     g1.h_stride = Iloc;
-    const bool mx = d.weight_format == MOE_WFMT_MXFP4;
-    launch_k(c, MOE_K_GEMM_GATEUP,
-             mx ? gemm_grouped_kernel<0, MOE_WFMT_MXFP4> : gemm_grouped_kernel<0, MOE_WFMT_KQUANT>,
-             dim3(max_tiles8 * g1.n_ntiles), dim3(kGemmThreads), 0, g1);
+    launch_k(c, MOE_K_GEMM_GATEUP, gemm_grouped_kernel<0>, dim3(max_tiles8 * g1.n_ntiles),
+             dim3(kGemmThreads), 0, g1);
 
     GemmArgs g2 = a;
     g2.a_src = h16;
@@ -761,10 +708,14 @@ hipError_t launch_mfma(const moe_layer_desc& d, const float* x, int T, const int
     g2.sb_rows = (d.inter % kSbWeights == 0 && Iloc % kSbWeights == 0 && i0 % kSbWeights == 0) ? 1 : 0;
     g2.y = y;
     g2.ysh = ysh;
-    launch_k(c, MOE_K_GEMM_DOWN,
-             mx ? gemm_grouped_kernel<1, MOE_WFMT_MXFP4> : gemm_grouped_kernel<1, MOE_WFMT_KQUANT>,
-             dim3(max_tiles8 * g2.n_ntiles), dim3(kGemmThreads), 0, g2);
+    launch_k(c, MOE_K_GEMM_DOWN, gemm_grouped_kernel<1>, dim3(max_tiles8 * g2.n_ntiles),
+             dim3(kGemmThreads), 0, g2);
 
+    return launch_combine(y, ysh, idx, T, H, E, k, shared, out, c);
+}
+
+hipError_t launch_combine(const float* y, const float* ysh, const int32_t* idx, int T, int H,
+                          int E, int k, bool shared, float* out, const Ctx& c) {
     const size_t nc = (size_t)T * H / 4;
     if (k <= 8)
         launch_k(c, MOE_K_COMBINE, combine_kernel<8>, dim3((unsigned)((nc + 255) / 256)), dim3(256),

@@ -30,6 +30,12 @@ struct WsLayout {
     size_t h16;           // fp16 [T*k + T][I_loc]
     size_t y;             // float [T*k][H]
     size_t ysh;           // float [T][H]
+    // grouped GEMM on MXFP4 weights (block-scaled matrix cores): tokens and h
+    // as kMxTerms MX-FP8 terms (in place of x16 and h16)
+    size_t mx_xq;         // e4m3 [kMxTerms][T][H]
+    size_t mx_xs;         // E8M0 [T][H/64][16]
+    size_t mx_hq;         // e4m3 [kMxTerms][T*k + T][I_loc]
+    size_t mx_hs;         // E8M0 [T*k + T][I_loc/64][16]
     size_t total;
     int router_ks;        // router K-splits
 };
@@ -80,6 +86,13 @@ hipError_t launch_bucket(const int32_t* idx, int T, int k, int E, bool shared, i
 hipError_t launch_mfma(const moe_layer_desc& d, const float* x, int T, const int32_t* idx,
                        const float* w, int i0, int iloc, float* out, char* ws,
                        const WsLayout& L, const Ctx& c, bool x16_ready);
+// the same for MXFP4 weights, on the block-scaled matrix cores (gemm_mx.hip)
+hipError_t launch_mfma_mx(const moe_layer_desc& d, const float* x, int T, const int32_t* idx,
+                          const float* w, int i0, int iloc, float* out, char* ws,
+                          const WsLayout& L, const Ctx& c);
+// out[t] = slot rows of y in slot order, then the shared rows (gemm.hip)
+hipError_t launch_combine(const float* y, const float* ysh, const int32_t* idx, int T, int H,
+                          int E, int k, bool shared, float* out, const Ctx& c);
 hipError_t launch_x16(const float* x, int T, int H, char* ws, const WsLayout& L, const Ctx& c);
 hipError_t launch_reduce(const float* const* partials, int n, int64_t count, const float* res,
                          float* out, hipStream_t s);

@@ -29,6 +29,9 @@ constexpr int kRouterSplits = 8;   // split-K partial logits per expert at small
 // margin to fp16's 65504 at no cost in relative precision.
 constexpr float kHScale = 0.0625f;
 constexpr float kHUnscale = 16.0f;
+// MXFP4 prefill: tokens and h enter the block-scaled matrix cores as the sum
+// of this many MX-FP8 terms (e4m3 codes, an E8M0 scale per 32 values)
+constexpr int kMxTerms = 3;
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float float16v __attribute__((ext_vector_type(16)));
@@ -215,6 +218,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 // loads in the counter only make the compiler's own vmcnt waits stricter.
 __device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_off) {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(gptr), "s"(lds_off)
+                 : "m0");
+}
+
+// The same with one dword per lane: lane l's 4 bytes land at lds_off + 4 l.
+__device__ __forceinline__ void lds_dma4(const void* gptr, uint32_t lds_off) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
                  :
                  : "v"(gptr), "s"(lds_off)
                  : "m0");

@@ -36,7 +36,7 @@ def test_header_declares_the_boundary():
 def test_library_exports_every_declared_symbol(L):
     for fn in declared_functions():
         assert hasattr(L.lib, fn), fn
-    assert L.moe_abi_version() == 5
+    assert L.moe_abi_version() == 6
     assert L.moe_status_str(-3) == "workspace too small"
 
 
@@ -66,8 +66,12 @@ def test_workspace_bytes_host_only(L):
 
 
 def test_weight_format_is_checked(L):
-    # MXFP4 layers take the same workspace; an unknown format is an argument error
-    assert L.moe_workspace_bytes(desc(weight_format=1), 4096, 1) == L.moe_workspace_bytes(desc(), 4096, 1)
+    # MXFP4 layers keep tokens and h as three MX-FP8 terms (3 bytes per value
+    # plus scales) where K-quant layers keep fp16 (2 bytes); an unknown format
+    # is an argument error
+    kq = L.moe_workspace_bytes(desc(), 4096, 1)
+    mx = L.moe_workspace_bytes(desc(weight_format=1), 4096, 1)
+    assert kq < mx < kq + 4096 * 9 * 512 * 2 + 4096 * 2048 * 2
     assert L.moe_workspace_bytes(desc(weight_format=2), 1, 1) == 0
     assert raw_forward(L, desc(weight_format=2), 1) == -1
     assert raw_forward(L, desc(weight_format=-1), 1) == -1

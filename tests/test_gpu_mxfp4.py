@@ -23,6 +23,7 @@ if not torch.cuda.is_available():
     pytest.skip("needs a GPU", allow_module_level=True)
 
 import quantized_moe_transformer_amd as qm  # noqa: E402
+from quantized_moe_transformer_amd.layer import DeviceLayer  # noqa: E402
 from test_gpu_parity import (DEV, check_dequant_bitwise, check_layer, dev_layer,  # noqa: E402
                              gpu, gpu_dequant, rel_scale, run_router, run_shard, say)
 
@@ -129,3 +130,37 @@ def test_mx_bit_identical_reruns():
     b, _ = run_forward(dl, x, qm.MOE_PATH_MFMA)
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
     assert np.isfinite(a).all()
+
+
+@pytest.mark.parametrize("scales", [(100, 150), (40, 80), (116, 132)])
+@pytest.mark.parametrize("path,tol", [(qm.MOE_PATH_GEMV, GEMV_TOL), (qm.MOE_PATH_MFMA, MFMA_TOL)])
+def test_mx_wide_scale_bytes(scales, path, tol):
+    """E8M0 scale bytes far outside 114..128, the range in which the E2M1
+    weights would survive an fp16 weight stage exactly: (100, 150) reaches
+    weights of 6 * 2^23 (beyond fp16's 65504), (40, 80) weights of 2^-88
+    (below fp16's subnormals).  The fp32 GEMV decodes them exactly and the
+    block-scaled matrix cores apply them exactly; both paths against the
+    oracle at their tolerances (the ranges keep every intermediate inside
+    fp32's normal range)."""
+    shp = mi.LayerShape(H=512, E=8, k=2, I=256, Is=256, fmt=1, mx_scales=scales)
+    layer = mi.make_layer(shp, seed=61)
+    assert layer["gate"][:, :8].min() == scales[0] or layer["down"][:, :8].min() == scales[0]
+    x = mi.make_tokens(shp, 61, 70)
+    dl = DeviceLayer.from_shape(layer, shp)
+    ol = oracle.Layer.from_shape(layer, shp)
+    say(f"mx wide scales {scales} path={path}")
+    T = x.shape[0]
+    out = torch.full((T, shp.H), float("nan"), device=DEV)
+    used = qm.moe_layer_forward(dl.desc, gpu(x), T, out, dl.workspace(T), path=path)
+    torch.cuda.synchronize()
+    assert used == path
+    got = out.cpu().numpy()
+    ref = oracle.forward(ol, x)
+    assert np.isfinite(ref).all() and np.isfinite(got).all()
+    oi, _, _, logits = oracle.router(x, layer["router_w"], shp.k)
+    gi, _ = run_router(dl, x)
+    exact, _, wrong = topk_check(gi, oi, logits)
+    assert len(wrong) == 0
+    err = rel_err(got[exact], ref[exact])
+    say(f"  max|err|/RMS = {err:.3e}")
+    assert err <= tol
