@@ -172,7 +172,11 @@ size_t moe_workspace_bytes(const moe_layer_desc *desc, int32_t T, int32_t num_sh
 /*
  * Router: logits[t][e] = sum_h x[t][h] * router_w[h][e] to fp32 accuracy (for
  * T > 32 on the matrix cores with each operand split into two fp16 parts,
- * which requires |x| < 65504 and |router_w| < 64); the k largest
+ * which requires |x| < 65504 and |router_w| < 64: outside these limits the
+ * affected logits, and so the routing of those rows, are wrong, and no status
+ * says so, since the values are only on the device and no call synchronises;
+ * the grouped GEMM of K-quant layers also takes x as fp16 and has the same
+ * bound on |x|); the k largest
  * logits in descending order (ties to the lower expert index) become slots
  * 0..k-1 of topk_idx; topk_w[t][j] = softmax over all E logits of expert
  * topk_idx[t][j], renormalised over the k selected -- equal to the softmax of

@@ -15,6 +15,12 @@ class DeviceLayer:
     def __init__(self, arrays: Dict[str, np.ndarray], H: int, E: int, k: int, I: int, Is: int,
                  shared_weight: float = 1.0, device: str = "cuda", weight_format: int = 0):
         import torch
+        # the matrix-core router (more than 32 rows) splits 2^10 * router_w
+        # into two fp16 parts: it needs |router_w| < 64 (include/moe.h,
+        # router_topk); the host copy is checked once here, at upload
+        wr = arrays["router_w"]
+        if not np.all(np.abs(wr) < 64.0):
+            raise ValueError("router_w must be finite with |router_w| < 64")
         self.H, self.E, self.k, self.I, self.Is = H, E, k, I, Is
         self.weight_format = weight_format
         self.shared_weight = shared_weight

@@ -87,3 +87,18 @@ def test_mxfp4_blob_fields():
     assert layer["gate"].shape == (8, 128 * 256 // 256 * 144)
     assert layer["down"].shape == (8, 256 * 128 // 256 * 144)
     assert layer["sh_down"].shape == (256 * 128 // 256 * 144,)
+
+
+def test_device_layer_rejects_router_beyond_split_range():
+    # the upload checks the host router matrix against the matrix-core
+    # router's |router_w| < 64 before any device memory is touched
+    import pytest
+    from quantized_moe_transformer_amd.layer import DeviceLayer
+    layer = mi.make_layer(mi.TINY, 0)
+    bad = dict(layer, router_w=layer["router_w"].copy())
+    bad["router_w"][3, 1] = 64.0
+    with pytest.raises(ValueError):
+        DeviceLayer.from_shape(bad, mi.TINY, device="cpu")
+    bad["router_w"][3, 1] = np.nan
+    with pytest.raises(ValueError):
+        DeviceLayer.from_shape(bad, mi.TINY, device="cpu")
