@@ -147,12 +147,12 @@ struct BRegs {
 };
 
 // A stages hold kTM rows of kBK halves with no padding; the 16-byte chunk c
-// of row r sits at chunk position c ^ (r & 7), so the 32 rows that one MFMA
+// of row r sits at chunk position c ^ ((r >> 1) & 7), so the 32 rows that one MFMA
 // fragment read touches spread over all banks.
 // Token-row stages: the rows of step kk + kAStages - 1 are requested at the
 // start of step kk, into the stage that step kk - 1 read.
 constexpr int kAStages = 2;
-__device__ __forceinline__ int a_chunk(int r, int c) { return r * (kBK / 8) + (c ^ (r & 7)); }
+__device__ __forceinline__ int a_chunk(int r, int c) { return r * (kBK / 8) + (c ^ ((r >> 1) & 7)); }
 
 // wait until at most n later steps' token-row loads (MB per step) are in flight
 template <int MB>
@@ -385,7 +385,7 @@ __device__ __forceinline__ void gemm_consume(const GemmArgs& a, const TileInfo& 
     // global-to-LDS loads (no registers), into a ring of kAStages stages,
     // so their waits cover only these loads and the producers' waits only the
     // weight loads.  Thread tid's load i fills chunk slot q = tid + 256 i: row
-    // q >> 3, chunk position q & 7, i.e. logical chunk (q & 7) ^ (row & 7).  Rows
+    // q >> 3, chunk position q & 7, i.e. logical chunk (q & 7) ^ ((row >> 1) & 7).  Rows
     // past the tile's end re-read one of its rows (row r mod mcount): their
     // results are discarded, and every load is unconditional so each step
     // issues exactly MB of them per wave.
@@ -393,7 +393,7 @@ __device__ __forceinline__ void gemm_consume(const GemmArgs& a, const TileInfo& 
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
         const int q = tid + 256 * i;
-        const int r = q >> 3, c = (q & 7) ^ (r & 7);
+        const int r = q >> 3, c = (q & 7) ^ ((r >> 1) & 7);
         const int rv = r < mcount ? r : r % mcount;
         // MODE 0: the row's token, read here rather than from row_src so that
         // no barrier stands between the tile record and the first loads
@@ -431,7 +431,7 @@ __device__ __forceinline__ void gemm_consume(const GemmArgs& a, const TileInfo& 
         constexpr int kB1 = (MODE == 0 ? kTN / 2 : 32) * kLdsRow * 2;   // bytes from block bc0 to bc1
         half8 f[4][MB + 2];
         auto read_slice = [&](int ks) {
-            lds_read_rows<MB>(f[ks], sa + 16 * ((2 * ks + kh) ^ (nl & 7)));
+            lds_read_rows<MB>(f[ks], sa + 16 * ((2 * ks + kh) ^ ((nl >> 1) & 7)));
             lds_read_frag<0>(f[ks][MB], sb + 32 * ks);
             lds_read_frag<kB1>(f[ks][MB + 1], sb + 32 * ks);
         };

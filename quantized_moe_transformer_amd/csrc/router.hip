@@ -91,14 +91,14 @@ split_kernel(const float* __restrict__ x, _Float16* __restrict__ xh, _Float16* _
 // hi and lo parts of 64 token rows and of 128 router rows, 48 KB -- arrive by
 // direct global-to-LDS loads two steps ahead into a three-stage ring (twelve
 // 16-byte loads per thread per step).  Each row's eight 16-byte chunks sit
-// XOR-swizzled by the row index (chunk c at position c ^ (row & 7)).  Rows
+// XOR-swizzled by the row index (chunk c at position c ^ ((row >> 1) & 7)).  Rows
 // past T or E re-read the last valid row; their results are not written.
 constexpr int kRgStages = 3;
 constexpr int kRgStageHalves = 2 * (kRgT + kRgE) * kRgK;   // 48 KB
 constexpr int kRgDma = kRgStageHalves * 2 / 16 / 256;       // 12 loads per thread per step
 constexpr int kRgAChunks = 2 * kRgT * 8;                    // A hi + lo chunks of a stage
 
-__device__ __forceinline__ int rg_chunk(int row, int c) { return row * 8 + (c ^ (row & 7)); }
+__device__ __forceinline__ int rg_chunk(int row, int c) { return row * 8 + (c ^ ((row >> 1) & 7)); }
 
 __global__ void __launch_bounds__(256)
 router_gemm_kernel(const _Float16* __restrict__ xh, const _Float16* __restrict__ xl,
@@ -116,12 +116,12 @@ router_gemm_kernel(const _Float16* __restrict__ xh, const _Float16* __restrict__
     for (int j = 0; j < kRgDma; ++j) {
         const int q = (kRgDma * wave + j) * 64 + lane;
         if (q < kRgAChunks) {
-            const int part = q / (kRgT * 8), row = (q >> 3) & (kRgT - 1), c = (q & 7) ^ (row & 7);
+            const int part = q / (kRgT * 8), row = (q >> 3) & (kRgT - 1), c = (q & 7) ^ ((row >> 1) & 7);
             const int t = min(t0 + row, T - 1);
             src[j] = (part ? xl : xh) + (size_t)t * H + k0 + c * 8;
         } else {
             const int qb = q - kRgAChunks;
-            const int part = qb / (kRgE * 8), row = (qb >> 3) & (kRgE - 1), c = (qb & 7) ^ (row & 7);
+            const int part = qb / (kRgE * 8), row = (qb >> 3) & (kRgE - 1), c = (qb & 7) ^ ((row >> 1) & 7);
             const int e = min(e0 + row, E - 1);
             src[j] = (part ? wl : wh) + (size_t)e * H + k0 + c * 8;
         }
