@@ -214,8 +214,9 @@ int moe_layer_forward(const moe_layer_desc *desc, const float *x, int32_t T, flo
  * call allocates and frees nothing; the caller still passes x and out.
  *   Returns MOE_ETOOBIG, enqueuing nothing, when T rows need more workspace
  *   than the scratch holds (moe_workspace_bytes(desc, T, 1) >
- *   MOE_NOALLOC_SCRATCH_BYTES: above about 700 rows of the Qwen3.5-shaped
- *   layer; any T of the decode path fits).  Other errors as moe_layer_forward.
+ *   MOE_NOALLOC_SCRATCH_BYTES: above 1106 rows of the Qwen3.5-shaped layer
+ *   with K-quant weights, 913 with MXFP4; any T of the decode path fits).
+ *   Other errors as moe_layer_forward.
  *   Every call on one device shares that device's scratch and leaves its last
  *   contents there (no call needs any particular contents on entry): calls
  *   that overlap in time on one device -- on different streams, or from

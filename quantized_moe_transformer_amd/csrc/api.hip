@@ -198,8 +198,10 @@ WsLayout ws_layout(const moe_layer_desc& d, int T, int iloc) {
     } else {
         L.h16 = off;      off = align256(off + hrows * Iloc * 2);
     }
-    L.y = off;            off = align256(off + Tz * k * H * 4);
-    L.ysh = off;          off = align256(off + Tz * H * 4);
+    L.y = off;            off = align256(off + Tz * k * H * 2);
+    L.ysh = off;          off = align256(off + Tz * H * 2);
+    L.ysc = off;          off = align256(off + Tz * k * (H / 8));
+    L.yshsc = off;        off = align256(off + Tz * (H / 8));
     L.total = gemv_end > off ? gemv_end : off;
     return L;
 }

@@ -137,8 +137,10 @@ struct GemmArgs {
     int sb_rows;                    // MODE 1: every row's K range is whole superblocks
     _Float16* h_out;                // MODE 0
     int h_stride;
-    float* y;                       // MODE 1: [T*k][H]
-    float* ysh;                     // MODE 1: [T][H]
+    _Float16* y;                    // MODE 1: [T*k][H] (scaled fp16)
+    _Float16* ysh;                  // MODE 1: [T][H]
+    uint8_t* ysc;                   // MODE 1: [T*k][H/8] exponent bytes of y
+    uint8_t* yshsc;                 // MODE 1: [T][H/8] those of ysh
 };
 
 // Packed weights of one producer task (weight row, 16-byte half) for one step.
@@ -461,7 +463,7 @@ __device__ __forceinline__ void gemm_consume(const GemmArgs& a, const TileInfo& 
 // whole row segments.
 //   MODE 0: h = silu(gate) * up * 2^-4 as fp16, rows in sorted order.
 //   MODE 1: the slot's row (the shared expert: its own buffer) times the
-//   row's weight * 2^4, fp32.
+//   row's weight * 2^4, as scaled fp16 (store_rows_f16).
 template <int MODE, int MB>
 __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const TileInfo& ti, GemmLds& lds,
                                           const int32_t* row_src, const float* row_w,
@@ -502,17 +504,9 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const TileInfo&
                 }
             }
             __syncthreads();
-            // 32 rows x 256 floats = 2048 chunks of 4 floats, four per thread
-            float* dst = ti.is_sh ? a.ysh : a.y;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int q = tid + 512 * j;
-                const int r = q >> 6, c4 = q & 63;
-                const int m = 32 * i + r, o = ti.n0 + 4 * c4;
-                if (m < ti.mcount && o < a.H)
-                    *reinterpret_cast<float4*>(dst + (size_t)row_src[m] * a.H + o) =
-                        *reinterpret_cast<const float4*>(t + r * kPitch + 4 * c4);
-            }
+            store_rows_f16<kGemmThreads>(t, kPitch, ti.is_sh ? a.ysh : a.y,
+                                         ti.is_sh ? a.yshsc : a.ysc, row_src, 32 * i, ti.mcount,
+                                         ti.n0, a.H);
         }
         __syncthreads();   // the staging buffer is rewritten by the next block
     }
@@ -589,55 +583,71 @@ gemm_grouped_kernel(GemmArgs a) {
     }
 }
 
-// out[t] = ((y[t,0] + y[t,1]) + ... + y[t,k-1]) + ysh[t]; y rows already carry
-// their routing weight, ysh the shared weight.  Slots whose expert index is
-// out of range contribute nothing.
-// Every slot row of the token is requested before the first add (KMAX >= k
-// rows, streamed once: non-temporal), then added in slot order.
-__device__ __forceinline__ float4 ld_stream4(const float* p) {
-    typedef float f32x4 __attribute__((ext_vector_type(4)));
-    const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
-    return make_float4(v[0], v[1], v[2], v[3]);
+// out[t] = ((y[t,0] + y[t,1]) + ... + y[t,k-1]) + ysh[t] in fp32, each row
+// value its fp16 times the power-of-two scale of its 8 values (exact); y rows
+// already carry their routing weight, ysh the shared weight.  Slots whose
+// expert index is out of range contribute nothing.  One thread per 8 outputs:
+// every slot row's 16 bytes of the token are requested before the first add
+// (KMAX >= k rows, streamed once: non-temporal), then added in slot order.
+__device__ __forceinline__ void ld_stream8h(const _Float16* p, float (&f)[8]) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const float2v h = __builtin_convertvector(__builtin_bit_cast(half2v, (uint32_t)v[j]), float2v);
+        f[2 * j] = h[0];
+        f[2 * j + 1] = h[1];
+    }
 }
 
 template <int KMAX>
 __global__ void __launch_bounds__(256)
-combine_kernel(const float* __restrict__ y, const float* __restrict__ ysh,
+combine_kernel(const _Float16* __restrict__ y, const _Float16* __restrict__ ysh,
+               const uint8_t* __restrict__ ysc, const uint8_t* __restrict__ yshsc,
                const int32_t* __restrict__ idx, int T, int H, int E, int k, int has_shared,
                float* __restrict__ out) {
-    const int h4 = H / 4;
+    const int h8 = H / 8;
     const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= (size_t)T * h4) return;
-    const int t = (int)(i / h4), o4 = (int)(i % h4);
-    float4 v[KMAX];
+    if (i >= (size_t)T * h8) return;
+    const int t = (int)(i / h8), o8 = (int)(i % h8);
+    float v[KMAX][8], sc[KMAX];
     bool ok[KMAX];
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
         ok[j] = false;
+        sc[j] = 0.f;
         if (j < k) {
-            ok[j] = (unsigned)idx[(size_t)t * k + j] < (unsigned)E;
-            v[j] = ld_stream4(y + ((size_t)t * k + j) * H + 4 * o4);
+            const size_t s = (size_t)t * k + j;
+            ok[j] = (unsigned)idx[s] < (unsigned)E;
+            ld_stream8h(y + s * H + 8 * o8, v[j]);
+            sc[j] = pow2f((int)ysc[s * h8 + o8] - 127);
         }
     }
-    const float4 sh = has_shared ? ld_stream4(ysh + (size_t)t * H + 4 * o4)
-                                 : make_float4(0.f, 0.f, 0.f, 0.f);
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    float sh[8], shs = 0.f;
+    if (has_shared) {
+        ld_stream8h(ysh + (size_t)t * H + 8 * o8, sh);
+        shs = pow2f((int)yshsc[(size_t)t * h8 + o8] - 127);
+    } else {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) sh[c] = 0.f;
+    }
+    float acc[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] = 0.f;
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
         if (ok[j]) {   // a slot whose expert index is out of range adds nothing
-            acc.x += v[j].x;
-            acc.y += v[j].y;
-            acc.z += v[j].z;
-            acc.w += v[j].w;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) acc[c] += v[j][c] * sc[j];
         }
     }
     if (has_shared) {
-        acc.x += sh.x;
-        acc.y += sh.y;
-        acc.z += sh.z;
-        acc.w += sh.w;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[c] += sh[c] * shs;
     }
-    reinterpret_cast<float4*>(out + (size_t)t * H)[o4] = acc;
+    float4* o = reinterpret_cast<float4*>(out + (size_t)t * H + 8 * o8);
+    o[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    o[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
 }
 
 hipError_t launch_mfma(const moe_layer_desc& d, const float* x, int T, const int32_t* idx,
@@ -653,8 +663,10 @@ hipError_t launch_mfma(const moe_layer_desc& d, const float* x, int T, const int
     int32_t* tile_off = reinterpret_cast<int32_t*>(ws + L.tile_off);
     int32_t* perm = reinterpret_cast<int32_t*>(ws + L.perm);
     _Float16* h16 = reinterpret_cast<_Float16*>(ws + L.h16);
-    float* y = reinterpret_cast<float*>(ws + L.y);
-    float* ysh = reinterpret_cast<float*>(ws + L.ysh);
+    _Float16* y = reinterpret_cast<_Float16*>(ws + L.y);
+    _Float16* ysh = reinterpret_cast<_Float16*>(ws + L.ysh);
+    uint8_t* ysc = reinterpret_cast<uint8_t*>(ws + L.ysc);
+    uint8_t* yshsc = reinterpret_cast<uint8_t*>(ws + L.yshsc);
 
     if (!x16_ready) {
         hipError_t e = launch_x16(x, T, H, ws, L, c);
@@ -708,21 +720,24 @@ hipError_t launch_mfma(const moe_layer_desc& d, const float* x, int T, const int
     g2.sb_rows = (d.inter % kSbWeights == 0 && Iloc % kSbWeights == 0 && i0 % kSbWeights == 0) ? 1 : 0;
     g2.y = y;
     g2.ysh = ysh;
+    g2.ysc = ysc;
+    g2.yshsc = yshsc;
     launch_k(c, MOE_K_GEMM_DOWN, gemm_grouped_kernel<1>, dim3(max_tiles8 * g2.n_ntiles),
              dim3(kGemmThreads), 0, g2);
 
-    return launch_combine(y, ysh, idx, T, H, E, k, shared, out, c);
+    return launch_combine(y, ysh, ysc, yshsc, idx, T, H, E, k, shared, out, c);
 }
 
-hipError_t launch_combine(const float* y, const float* ysh, const int32_t* idx, int T, int H,
-                          int E, int k, bool shared, float* out, const Ctx& c) {
-    const size_t nc = (size_t)T * H / 4;
+hipError_t launch_combine(const _Float16* y, const _Float16* ysh, const uint8_t* ysc,
+                          const uint8_t* yshsc, const int32_t* idx, int T, int H, int E, int k,
+                          bool shared, float* out, const Ctx& c) {
+    const size_t nc = (size_t)T * H / 8;
     if (k <= 8)
         launch_k(c, MOE_K_COMBINE, combine_kernel<8>, dim3((unsigned)((nc + 255) / 256)), dim3(256),
-                 0, y, ysh, idx, T, H, E, k, shared ? 1 : 0, out);
+                 0, y, ysh, ysc, yshsc, idx, T, H, E, k, shared ? 1 : 0, out);
     else
         launch_k(c, MOE_K_COMBINE, combine_kernel<16>, dim3((unsigned)((nc + 255) / 256)), dim3(256),
-                 0, y, ysh, idx, T, H, E, k, shared ? 1 : 0, out);
+                 0, y, ysh, ysc, yshsc, idx, T, H, E, k, shared ? 1 : 0, out);
     return hipGetLastError();
 }
 

@@ -28,8 +28,10 @@ struct WsLayout {
     size_t tile_rec;      // int4 per row tile: group, first sorted row, rows, row offset in group
     size_t perm;          // int32 [T*k]
     size_t h16;           // fp16 [T*k + T][I_loc]
-    size_t y;             // float [T*k][H]
-    size_t ysh;           // float [T][H]
+    size_t y;             // fp16 [T*k][H]: per-slot expert rows, routing weight applied
+    size_t ysh;           // fp16 [T][H]: shared-expert rows, shared weight applied
+    size_t ysc;           // uint8 [T*k][H/8]: exponent byte of each 8 values of y
+    size_t yshsc;         // uint8 [T][H/8]: the same for ysh
     // grouped GEMM on MXFP4 weights (block-scaled matrix cores): tokens and h
     // as kMxTerms MX-FP8 terms (in place of x16 and h16)
     size_t mx_xq;         // e4m3 [kMxTerms][T][H]
@@ -91,8 +93,9 @@ hipError_t launch_mfma_mx(const moe_layer_desc& d, const float* x, int T, const 
                           const float* w, int i0, int iloc, float* out, char* ws,
                           const WsLayout& L, const Ctx& c);
 // out[t] = slot rows of y in slot order, then the shared rows (gemm.hip)
-hipError_t launch_combine(const float* y, const float* ysh, const int32_t* idx, int T, int H,
-                          int E, int k, bool shared, float* out, const Ctx& c);
+hipError_t launch_combine(const _Float16* y, const _Float16* ysh, const uint8_t* ysc,
+                          const uint8_t* yshsc, const int32_t* idx, int T, int H, int E, int k,
+                          bool shared, float* out, const Ctx& c);
 hipError_t launch_x16(const float* x, int T, int H, char* ws, const WsLayout& L, const Ctx& c);
 hipError_t launch_reduce(const float* const* partials, int n, int64_t count, const float* res,
                          float* out, hipStream_t s);

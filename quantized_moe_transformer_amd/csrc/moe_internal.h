@@ -109,6 +109,59 @@ __device__ __forceinline__ uint32_t pack_f16_rne(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((float2v){a, b}, half2v));
 }
 
+// Per-slot expert rows between the grouped down GEMM and the combine: fp16
+// values with one power-of-two scale per 8 consecutive values of a row, value
+// = fp16 * 2^e, e stored as the byte e + 127.  The scale takes the 8 values'
+// largest magnitude m to [2^14, 2^15) (m = f 2^E, f in [0.5, 1): e = E - 15,
+// at least -126 so that 2^e and 2^-e are normal floats); 0 or a non-finite m
+// gives e = 0.  Scaling by 2^-e is exact, so each value carries one fp16
+// rounding (nearest even) and cannot overflow; only 8 values whose largest
+// magnitude is below 2^-140 (an fp32 subnormal) keep fewer than fp16's 11 bits.
+__device__ __forceinline__ int yrow_exp(float m) {
+    if (!(m > 0.f) || !(m <= 3.402823466e38f)) return 0;
+    int E;
+    (void)__builtin_frexpf(m, &E);
+    const int e = E - 15;
+    return e < -126 ? -126 : e;   // E <= 128, so e <= 113
+}
+
+__device__ __forceinline__ float pow2f(int e) {   // 2^e for e in [-126, 127]
+    return __builtin_bit_cast(float, (uint32_t)(e + 127) << 23);
+}
+
+// The grouped GEMMs' down epilogue: 32 staged fp32 rows of [32][pitch] floats
+// (256 columns from n0) to scaled fp16 rows dst[row_src[m0 + r]][n0 ..] and
+// their exponent bytes dse[row_src[m0 + r]][n0 / 8 ..] (H / 8 per row): 1024
+// chunks of 8 values over the NTHREADS threads, one 16-byte store each.
+template <int NTHREADS>
+__device__ __forceinline__ void store_rows_f16(const float* t, int pitch, _Float16* dst,
+                                               uint8_t* dse, const int32_t* row_src, int m0,
+                                               int mcount, int n0, int H) {
+    static_assert(1024 % NTHREADS == 0, "whole chunks per thread");
+#pragma unroll
+    for (int j = 0; j < 1024 / NTHREADS; ++j) {
+        const int q = (int)threadIdx.x + NTHREADS * j;
+        const int r = q >> 5, c8 = q & 31;
+        const int m = m0 + r, o = n0 + 8 * c8;
+        if (m < mcount && o < H) {
+            const float4 u = *reinterpret_cast<const float4*>(t + r * pitch + 8 * c8);
+            const float4 v = *reinterpret_cast<const float4*>(t + r * pitch + 8 * c8 + 4);
+            const float mx = __builtin_fmaxf(
+                __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(u.x), __builtin_fabsf(u.y)),
+                                __builtin_fmaxf(__builtin_fabsf(u.z), __builtin_fabsf(u.w))),
+                __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(v.x), __builtin_fabsf(v.y)),
+                                __builtin_fmaxf(__builtin_fabsf(v.z), __builtin_fabsf(v.w))));
+            const int e = yrow_exp(mx);
+            const float inv = pow2f(-e);
+            const size_t row = (size_t)row_src[m];
+            *reinterpret_cast<uint4*>(dst + row * H + o) =
+                make_uint4(pack_f16_rne(u.x * inv, u.y * inv), pack_f16_rne(u.z * inv, u.w * inv),
+                           pack_f16_rne(v.x * inv, v.y * inv), pack_f16_rne(v.z * inv, v.w * inv));
+            dse[row * (H / 8) + o / 8] = (uint8_t)(e + 127);
+        }
+    }
+}
+
 // The 16-bit matrix-core operands of one 16-byte K-quant code piece: 16 codes
 // of sub-block 2c (low nibbles, elements 64c + 16hh + [0,16)) and 16 of
 // sub-block 2c+1 (high nibbles, elements 64c + 32 + 16hh + [0,16)), for the
