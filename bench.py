@@ -58,18 +58,18 @@ MX_TERMS = 3                    # MX-FP8 terms per token / h value on the MXFP4 
 # --copy-probe).  Keyed by the SHA-256 of the kernel's sources: when they change,
 # the counters no longer describe the kernel and traffic is reported as null.
 TRAFFIC = {
-    # decode T=1, 288 dispatches: FETCH 4751.4 KiB x 1.99980, WRITE 16.1 KiB x 1.0
-    "gemv_gateup": {"sources_sha256": "1a2aead47a400e21c45c8b1a87120e74c69d72231148bd03f0bcac7af52bcdb3",
-                    "fetch_bytes": 9729961, "write_bytes": 16448},
-    # prefill T=4096, 15 dispatches: FETCH 224666.3 KiB x 1.99980, WRITE 36864.0 KiB x 1.0
-    "gemm_gateup": {"sources_sha256": "fbf31bb999119bcf1a13a6ccf1acb7919a5233154dde93dbdc8bdbe6ede20d1a",
-                    "fetch_bytes": 460070485, "write_bytes": 37748736},
-    # MXFP4 decode T=1, 288 dispatches: FETCH 4756.7 KiB x 1.99980, WRITE 16.1 KiB x 1.0
-    "gemv_gateup_mx": {"sources_sha256": "1a2aead47a400e21c45c8b1a87120e74c69d72231148bd03f0bcac7af52bcdb3",
-                    "fetch_bytes": 9740726, "write_bytes": 16448},
-    # MXFP4 prefill T=4096, 15 dispatches: FETCH 224579.4 KiB x 1.99980, WRITE 36864.0 KiB x 1.0
-    "gemm_gateup_mx": {"sources_sha256": "fbf31bb999119bcf1a13a6ccf1acb7919a5233154dde93dbdc8bdbe6ede20d1a",
-                    "fetch_bytes": 459892643, "write_bytes": 37748736},
+    # decode T=1, 280 dispatches: FETCH 4752.4 KiB x 1.99980, WRITE 16.1 KiB x 1.0
+    "gemv_gateup": {"sources_sha256": "8361f2a89ce0277b7416ef83d49195169378c8cba01cabdf1148abc2aab6a521",
+                    "fetch_bytes": 9731927, "write_bytes": 16448},
+    # prefill T=4096, 18 dispatches: FETCH 225364.9 KiB x 1.99980, WRITE 36864.0 KiB x 1.0
+    "gemm_gateup": {"sources_sha256": "9151da38ab7382442f78c934c233aa92475c3f383bae18cab3a5fa02186bc6a7",
+                    "fetch_bytes": 461501216, "write_bytes": 37748736},
+    # MXFP4 decode T=1, 280 dispatches: FETCH 4756.8 KiB x 1.99980, WRITE 16.1 KiB x 1.0
+    "gemv_gateup_mx": {"sources_sha256": "8361f2a89ce0277b7416ef83d49195169378c8cba01cabdf1148abc2aab6a521",
+                    "fetch_bytes": 9740885, "write_bytes": 16448},
+    # MXFP4 prefill T=4096, 18 dispatches: FETCH 269597.8 KiB x 1.99980, WRITE 59904.9 KiB x 1.0
+    "gemm_gateup_mx": {"sources_sha256": "5d8962efcc52f516699fd2b0d09314e0487c9d80c3f3acac56b2dc4ea632537c",
+                    "fetch_bytes": 552081142, "write_bytes": 61342658},
 }
 FETCH_SIZE_FACTOR = 1.99980   # plain 256 MiB copy: true bytes read / FETCH_SIZE bytes
 WRITE_SIZE_FACTOR = 1.0
