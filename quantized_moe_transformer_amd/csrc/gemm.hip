@@ -137,8 +137,8 @@ struct GemmArgs {
     int sb_rows;                    // MODE 1: every row's K range is whole superblocks
     _Float16* h_out;                // MODE 0
     int h_stride;
-    _Float16* y;                    // MODE 1: [T*k][H] (scaled fp16)
-    _Float16* ysh;                  // MODE 1: [T][H]
+    int16_t* y;                     // MODE 1: [T*k][H] (16-bit block floating point)
+    int16_t* ysh;                   // MODE 1: [T][H]
     uint8_t* ysc;                   // MODE 1: [T*k][H/8] exponent bytes of y
     uint8_t* yshsc;                 // MODE 1: [T][H/8] those of ysh
 };
@@ -463,7 +463,7 @@ __device__ __forceinline__ void gemm_consume(const GemmArgs& a, const TileInfo& 
 // whole row segments.
 //   MODE 0: h = silu(gate) * up * 2^-4 as fp16, rows in sorted order.
 //   MODE 1: the slot's row (the shared expert: its own buffer) times the
-//   row's weight * 2^4, as scaled fp16 (store_rows_f16).
+//   row's weight * 2^4, as 16-bit block floating point (store_rows_q16).
 template <int MODE, int MB>
 __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const TileInfo& ti, GemmLds& lds,
                                           const int32_t* row_src, const float* row_w,
@@ -504,7 +504,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const TileInfo&
                 }
             }
             __syncthreads();
-            store_rows_f16<kGemmThreads>(t, kPitch, ti.is_sh ? a.ysh : a.y,
+            store_rows_q16<kGemmThreads>(t, kPitch, ti.is_sh ? a.ysh : a.y,
                                          ti.is_sh ? a.yshsc : a.ysc, row_src, 32 * i, ti.mcount,
                                          ti.n0, a.H);
         }
@@ -584,25 +584,31 @@ gemm_grouped_kernel(GemmArgs a) {
 }
 
 // out[t] = ((y[t,0] + y[t,1]) + ... + y[t,k-1]) + ysh[t] in fp32, each row
-// value its fp16 times the power-of-two scale of its 8 values (exact); y rows
-// already carry their routing weight, ysh the shared weight.  Slots whose
-// expert index is out of range contribute nothing.  One thread per 8 outputs:
-// every slot row's 16 bytes of the token are requested before the first add
-// (KMAX >= k rows, streamed once: non-temporal), then added in slot order.
-__device__ __forceinline__ void ld_stream8h(const _Float16* p, float (&f)[8]) {
+// value its int16 mantissa times its block's factor (store_rows_q16); y rows
+// already carry their routing weight, ysh the shared weight.
+// Slots whose expert index is out of range contribute nothing.  One thread per
+// 8 outputs: every slot row's 16 bytes of the token are requested before the
+// first add (KMAX >= k rows, streamed once: non-temporal), then added in slot
+// order.
+__device__ __forceinline__ void ld_stream8q(const int16_t* p, float (&f)[8]) {
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const float2v h = __builtin_convertvector(__builtin_bit_cast(half2v, (uint32_t)v[j]), float2v);
-        f[2 * j] = h[0];
-        f[2 * j + 1] = h[1];
+        const uint32_t w = v[j];
+        f[2 * j] = (float)(int)(int16_t)(w & 0xffffu);
+        f[2 * j + 1] = (float)((int)w >> 16);
     }
+}
+
+// a block's exponent byte -> the factor of its int16 mantissas
+__device__ __forceinline__ float yq_scale(int eb) {
+    return eb == kYNanByte ? __builtin_nanf("") : __builtin_ldexpf(kYInvQ, eb - 126);
 }
 
 template <int KMAX>
 __global__ void __launch_bounds__(256)
-combine_kernel(const _Float16* __restrict__ y, const _Float16* __restrict__ ysh,
+combine_kernel(const int16_t* __restrict__ y, const int16_t* __restrict__ ysh,
                const uint8_t* __restrict__ ysc, const uint8_t* __restrict__ yshsc,
                const int32_t* __restrict__ idx, int T, int H, int E, int k, int has_shared,
                float* __restrict__ out) {
@@ -619,14 +625,14 @@ combine_kernel(const _Float16* __restrict__ y, const _Float16* __restrict__ ysh,
         if (j < k) {
             const size_t s = (size_t)t * k + j;
             ok[j] = (unsigned)idx[s] < (unsigned)E;
-            ld_stream8h(y + s * H + 8 * o8, v[j]);
-            sc[j] = pow2f((int)ysc[s * h8 + o8] - 127);
+            ld_stream8q(y + s * H + 8 * o8, v[j]);
+            sc[j] = yq_scale(ysc[s * h8 + o8]);
         }
     }
     float sh[8], shs = 0.f;
     if (has_shared) {
-        ld_stream8h(ysh + (size_t)t * H + 8 * o8, sh);
-        shs = pow2f((int)yshsc[(size_t)t * h8 + o8] - 127);
+        ld_stream8q(ysh + (size_t)t * H + 8 * o8, sh);
+        shs = yq_scale(yshsc[(size_t)t * h8 + o8]);
     } else {
 #pragma unroll
         for (int c = 0; c < 8; ++c) sh[c] = 0.f;
@@ -663,8 +669,8 @@ hipError_t launch_mfma(const moe_layer_desc& d, const float* x, int T, const int
     int32_t* tile_off = reinterpret_cast<int32_t*>(ws + L.tile_off);
     int32_t* perm = reinterpret_cast<int32_t*>(ws + L.perm);
     _Float16* h16 = reinterpret_cast<_Float16*>(ws + L.h16);
-    _Float16* y = reinterpret_cast<_Float16*>(ws + L.y);
-    _Float16* ysh = reinterpret_cast<_Float16*>(ws + L.ysh);
+    int16_t* y = reinterpret_cast<int16_t*>(ws + L.y);
+    int16_t* ysh = reinterpret_cast<int16_t*>(ws + L.ysh);
     uint8_t* ysc = reinterpret_cast<uint8_t*>(ws + L.ysc);
     uint8_t* yshsc = reinterpret_cast<uint8_t*>(ws + L.yshsc);
 
@@ -728,7 +734,7 @@ hipError_t launch_mfma(const moe_layer_desc& d, const float* x, int T, const int
     return launch_combine(y, ysh, ysc, yshsc, idx, T, H, E, k, shared, out, c);
 }
 
-hipError_t launch_combine(const _Float16* y, const _Float16* ysh, const uint8_t* ysc,
+hipError_t launch_combine(const int16_t* y, const int16_t* ysh, const uint8_t* ysc,
                           const uint8_t* yshsc, const int32_t* idx, int T, int H, int E, int k,
                           bool shared, float* out, const Ctx& c) {
     const size_t nc = (size_t)T * H / 8;

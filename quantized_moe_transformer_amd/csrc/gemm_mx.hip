@@ -177,8 +177,8 @@ struct MxGemmArgs {
     uint8_t* hq;                    // MODE 0: h codes [NT][T*k + T][iloc]
     uint8_t* hs;                    // MODE 0: h scales [T*k + T][iloc/64][16]
     size_t h_term;
-    _Float16* y;                    // MODE 1: [T*k][H] (scaled fp16)
-    _Float16* ysh;                  // MODE 1: [T][H]
+    int16_t* y;                     // MODE 1: [T*k][H] (16-bit block floating point)
+    int16_t* ysh;                   // MODE 1: [T][H]
     uint8_t* ysc;                   // MODE 1: [T*k][H/8] exponent bytes of y
     uint8_t* yshsc;                 // MODE 1: [T][H/8] those of ysh
 };
@@ -450,7 +450,7 @@ __device__ __forceinline__ void mx_consume(const MxGemmArgs& a, const MxTileInfo
 //   MODE 0: h = silu(gate) * up (fp32), then NT-term MX-FP8 codes and scales
 //   of each (row, 32-column block), 4 threads per block.
 //   MODE 1: the slot's row (the shared expert: its own buffer) times the
-//   row's weight, as scaled fp16 (store_rows_f16).
+//   row's weight, as 16-bit block floating point (store_rows_q16).
 template <int MODE, int MB, int NT>
 __device__ __forceinline__ void mx_epilogue(const MxGemmArgs& a, const MxTileInfo& ti, MxLds& lds,
                                             const int32_t* row_src, const float* row_w,
@@ -493,7 +493,7 @@ __device__ __forceinline__ void mx_epilogue(const MxGemmArgs& a, const MxTileInf
                                    (n / 32) & 1, qt, codes, scales);
             }
         } else {
-            store_rows_f16<kMxThreads>(t, kPitch, ti.is_sh ? a.ysh : a.y,
+            store_rows_q16<kMxThreads>(t, kPitch, ti.is_sh ? a.ysh : a.y,
                                        ti.is_sh ? a.yshsc : a.ysc, row_src, 32 * i, ti.mcount,
                                        ti.n0, a.H);
         }
@@ -582,8 +582,8 @@ hipError_t launch_mfma_mx(const moe_layer_desc& d, const float* x, int T, const 
     int32_t* tile_off = reinterpret_cast<int32_t*>(ws + L.tile_off);
     int32_t* perm = reinterpret_cast<int32_t*>(ws + L.perm);
     int4* tile_rec = reinterpret_cast<int4*>(ws + L.tile_rec);
-    _Float16* y = reinterpret_cast<_Float16*>(ws + L.y);
-    _Float16* ysh = reinterpret_cast<_Float16*>(ws + L.ysh);
+    int16_t* y = reinterpret_cast<int16_t*>(ws + L.y);
+    int16_t* ysh = reinterpret_cast<int16_t*>(ws + L.ysh);
     uint8_t* ysc = reinterpret_cast<uint8_t*>(ws + L.ysc);
     uint8_t* yshsc = reinterpret_cast<uint8_t*>(ws + L.yshsc);
 

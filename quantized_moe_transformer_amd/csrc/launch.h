@@ -28,8 +28,9 @@ struct WsLayout {
     size_t tile_rec;      // int4 per row tile: group, first sorted row, rows, row offset in group
     size_t perm;          // int32 [T*k]
     size_t h16;           // fp16 [T*k + T][I_loc]
-    size_t y;             // fp16 [T*k][H]: per-slot expert rows, routing weight applied
-    size_t ysh;           // fp16 [T][H]: shared-expert rows, shared weight applied
+    size_t y;             // int16 [T*k][H]: per-slot expert rows (routing weight applied),
+                          // 16-bit block floating point (store_rows_q16)
+    size_t ysh;           // int16 [T][H]: shared-expert rows, shared weight applied
     size_t ysc;           // uint8 [T*k][H/8]: exponent byte of each 8 values of y
     size_t yshsc;         // uint8 [T][H/8]: the same for ysh
     // grouped GEMM on MXFP4 weights (block-scaled matrix cores): tokens and h
@@ -93,7 +94,7 @@ hipError_t launch_mfma_mx(const moe_layer_desc& d, const float* x, int T, const 
                           const float* w, int i0, int iloc, float* out, char* ws,
                           const WsLayout& L, const Ctx& c);
 // out[t] = slot rows of y in slot order, then the shared rows (gemm.hip)
-hipError_t launch_combine(const _Float16* y, const _Float16* ysh, const uint8_t* ysc,
+hipError_t launch_combine(const int16_t* y, const int16_t* ysh, const uint8_t* ysc,
                           const uint8_t* yshsc, const int32_t* idx, int T, int H, int E, int k,
                           bool shared, float* out, const Ctx& c);
 hipError_t launch_x16(const float* x, int T, int H, char* ws, const WsLayout& L, const Ctx& c);

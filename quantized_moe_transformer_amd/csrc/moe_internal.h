@@ -109,32 +109,27 @@ __device__ __forceinline__ uint32_t pack_f16_rne(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((float2v){a, b}, half2v));
 }
 
-// Per-slot expert rows between the grouped down GEMM and the combine: fp16
-// values with one power-of-two scale per 8 consecutive values of a row, value
-// = fp16 * 2^e, e stored as the byte e + 127.  The scale takes the 8 values'
-// largest magnitude m to [2^14, 2^15) (m = f 2^E, f in [0.5, 1): e = E - 15,
-// at least -126 so that 2^e and 2^-e are normal floats); 0 or a non-finite m
-// gives e = 0.  Scaling by 2^-e is exact, so each value carries one fp16
-// rounding (nearest even) and cannot overflow; only 8 values whose largest
-// magnitude is below 2^-140 (an fp32 subnormal) keep fewer than fp16's 11 bits.
-__device__ __forceinline__ int yrow_exp(float m) {
-    if (!(m > 0.f) || !(m <= 3.402823466e38f)) return 0;
-    int E;
-    (void)__builtin_frexpf(m, &E);
-    const int e = E - 15;
-    return e < -126 ? -126 : e;   // E <= 128, so e <= 113
-}
-
-__device__ __forceinline__ float pow2f(int e) {   // 2^e for e in [-126, 127]
-    return __builtin_bit_cast(float, (uint32_t)(e + 127) << 23);
-}
+// Per-slot expert rows between the grouped down GEMM and the combine: 16-bit
+// block floating point.  Each 8 consecutive values of a row share one byte
+// eb, the biased fp32 exponent of their largest magnitude m (at least 1), and
+// each value v is the int16 q = snorm16(v 2^(126 - eb)) (v_cvt_pknorm_i16_f32:
+// v 2^(126 - eb) lies in (-1, 1), times 32767, rounded to an integer), read
+// back as q 2^(eb - 126) / 32767.  m is at least half of 2^(eb - 126), so the
+// block's largest values keep 14 to 15 bits (absolute error about 2^-16 of
+// 2^(eb - 126), against fp16's 11 bits), with no range limit: only blocks
+// below fp32's normal range (eb = 0, taken as 1) lose bits, as fp32 itself
+// does.  A block holding an inf or NaN has eb = 255, zero mantissas, and
+// reads back as NaN.  m and eb come from an integer maximum of the values'
+// magnitude bits, which also orders inf and NaN above every finite value.
+constexpr int kYNanByte = 255;
+constexpr float kYInvQ = 1.0f / 32767.0f;
 
 // The grouped GEMMs' down epilogue: 32 staged fp32 rows of [32][pitch] floats
-// (256 columns from n0) to scaled fp16 rows dst[row_src[m0 + r]][n0 ..] and
-// their exponent bytes dse[row_src[m0 + r]][n0 / 8 ..] (H / 8 per row): 1024
-// chunks of 8 values over the NTHREADS threads, one 16-byte store each.
+// (256 columns from n0) to 16-bit rows dst[row_src[m0 + r]][n0 ..] and their
+// exponent bytes dse[row_src[m0 + r]][n0 / 8 ..] (H / 8 per row): 1024 chunks
+// of 8 values over the NTHREADS threads, one 16-byte store each.
 template <int NTHREADS>
-__device__ __forceinline__ void store_rows_f16(const float* t, int pitch, _Float16* dst,
+__device__ __forceinline__ void store_rows_q16(const float* t, int pitch, int16_t* dst,
                                                uint8_t* dse, const int32_t* row_src, int m0,
                                                int mcount, int n0, int H) {
     static_assert(1024 % NTHREADS == 0, "whole chunks per thread");
@@ -146,18 +141,27 @@ __device__ __forceinline__ void store_rows_f16(const float* t, int pitch, _Float
         if (m < mcount && o < H) {
             const float4 u = *reinterpret_cast<const float4*>(t + r * pitch + 8 * c8);
             const float4 v = *reinterpret_cast<const float4*>(t + r * pitch + 8 * c8 + 4);
-            const float mx = __builtin_fmaxf(
-                __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(u.x), __builtin_fabsf(u.y)),
-                                __builtin_fmaxf(__builtin_fabsf(u.z), __builtin_fabsf(u.w))),
-                __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(v.x), __builtin_fabsf(v.y)),
-                                __builtin_fmaxf(__builtin_fabsf(v.z), __builtin_fabsf(v.w))));
-            const int e = yrow_exp(mx);
-            const float inv = pow2f(-e);
+            const float f[8] = {u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};
+            uint32_t mb = 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t b = __builtin_bit_cast(uint32_t, f[i]) & 0x7fffffffu;
+                mb = mb > b ? mb : b;
+            }
+            int eb = (int)(mb >> 23);
+            const bool bad = eb == kYNanByte;
+            eb = eb < 1 ? 1 : eb;
+            const int sh = 126 - eb;
+            uint32_t w[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                w[i] = bad ? 0u
+                           : __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pknorm_i16(
+                                                              __builtin_ldexpf(f[2 * i], sh),
+                                                              __builtin_ldexpf(f[2 * i + 1], sh)));
             const size_t row = (size_t)row_src[m];
-            *reinterpret_cast<uint4*>(dst + row * H + o) =
-                make_uint4(pack_f16_rne(u.x * inv, u.y * inv), pack_f16_rne(u.z * inv, u.w * inv),
-                           pack_f16_rne(v.x * inv, v.y * inv), pack_f16_rne(v.z * inv, v.w * inv));
-            dse[row * (H / 8) + o / 8] = (uint8_t)(e + 127);
+            *reinterpret_cast<uint4*>(dst + row * H + o) = make_uint4(w[0], w[1], w[2], w[3]);
+            dse[row * (H / 8) + o / 8] = (uint8_t)eb;
         }
     }
 }
