@@ -419,42 +419,62 @@ __device__ __forceinline__ void gemm_consume(const GemmArgs& a, const TileInfo& 
     __syncthreads();              // the producers' first superblock fetch
     wait_a_steps<MB>(min(kAStages - 1, a.nk) - 1);   // step 0's rows landed
     __syncthreads();              // stage 0 ready
+    // The MFMAs of each step's last K slice run after the next barrier, from
+    // fragments already in registers (the stage they came from may then be
+    // overwritten): they cover the latency of the next step's first fragment
+    // reads, which otherwise leave the matrix core idle from the barrier to
+    // the first MFMA (several hundred cycles of a 2 500-cycle step in cycle
+    // stamps).  Only slice 0's reads go out before them: with slice 1's as
+    // well, the carried fragments no longer fit the 256 registers.
+    const int nl = lane & 31, kh = lane >> 5;
+    constexpr int kB1 = (MODE == 0 ? kTN / 2 : 32) * kLdsRow * 2;   // bytes from block bc0 to bc1
+    half8 ft[MB + 2];   // the previous step's last slice
+    auto mfma_slice = [&](const half8 (&g)[MB + 2]) {
+#pragma unroll
+        for (int i = 0; i < MB; ++i) {
+            acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(g[i], g[MB], acc[i][0], 0, 0, 0);
+            acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(g[i], g[MB + 1], acc[i][1], 0, 0, 0);
+        }
+    };
     for (int kk = 0; kk < a.nk; ++kk) {
         const int st = kk & 1;
-        // the rows of step kk + kAStages - 1 go to the stage that step kk - 1
-        // read (every wave left it at the last barrier)
-        if (kk + kAStages - 1 < a.nk) issue_a(kk + kAStages - 1);
         // fragments of K slice ks: f[ks][0..MB) token rows, f[ks][MB], f[ks][MB+1]
         // the two weight blocks; slice ks + 2's reads are issued before the
         // MFMAs of slice ks
-        const int nl = lane & 31, kh = lane >> 5;
         const uint32_t sa = (uint32_t)(uintptr_t)&lds.a[kk % kAStages][0] + 128 * nl;
         const uint32_t sb = (uint32_t)(uintptr_t)&lds.b[st][bc0 + nl][8 * kh];
-        constexpr int kB1 = (MODE == 0 ? kTN / 2 : 32) * kLdsRow * 2;   // bytes from block bc0 to bc1
         half8 f[4][MB + 2];
         auto read_slice = [&](int ks) {
             lds_read_rows<MB>(f[ks], sa + 16 * ((2 * ks + kh) ^ ((nl >> 1) & 7)));
             lds_read_frag<0>(f[ks][MB], sb + 32 * ks);
             lds_read_frag<kB1>(f[ks][MB + 1], sb + 32 * ks);
         };
+        // the rows of step kk + kAStages - 1 go to the stage that step kk - 1
+        // read (every wave left it at the last barrier)
+        if (kk + kAStages - 1 < a.nk) issue_a(kk + kAStages - 1);
         read_slice(0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (kk > 0) mfma_slice(ft);
+        __builtin_amdgcn_sched_barrier(0);
         read_slice(1);
 #pragma unroll
         for (int ks = 0; ks < kBK / 16; ++ks) {
-            if (ks > 0) __builtin_amdgcn_sched_barrier(0x6);
+            __builtin_amdgcn_sched_barrier(0x6);
             if (ks < 3) lds_wait_frags<MB + 2>(f[ks]);   // slice ks + 1 may still be in flight
             else lds_wait_frags<0>(f[ks]);
             if (ks < 2) read_slice(ks + 2);
+            if (ks < 3) {
+                mfma_slice(f[ks]);
+            } else {
 #pragma unroll
-            for (int i = 0; i < MB; ++i) {
-                acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f[ks][i], f[ks][MB], acc[i][0], 0, 0, 0);
-                acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f[ks][i], f[ks][MB + 1], acc[i][1], 0, 0, 0);
+                for (int i = 0; i < MB + 2; ++i) ft[i] = f[3][i];
             }
         }
         // step kk + 1's rows must have landed before the barrier
         wait_a_steps<MB>(min(kAStages - 2, a.nk - kk - 2));
         __syncthreads();
     }
+    mfma_slice(ft);   // the last step's last slice
 
 }
 
