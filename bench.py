@@ -59,17 +59,17 @@ MX_TERMS = 3                    # MX-FP8 terms per token / h value on the MXFP4 
 # the counters no longer describe the kernel and traffic is reported as null.
 TRAFFIC = {
     # decode T=1, 280 dispatches: FETCH 4752.4 KiB x 1.99980, WRITE 16.1 KiB x 1.0
-    "gemv_gateup": {"sources_sha256": "8361f2a89ce0277b7416ef83d49195169378c8cba01cabdf1148abc2aab6a521",
-                    "fetch_bytes": 9731927, "write_bytes": 16448},
-    # prefill T=4096, 18 dispatches: FETCH 225364.9 KiB x 1.99980, WRITE 36864.0 KiB x 1.0
-    "gemm_gateup": {"sources_sha256": "9151da38ab7382442f78c934c233aa92475c3f383bae18cab3a5fa02186bc6a7",
-                    "fetch_bytes": 461501216, "write_bytes": 37748736},
+    "gemv_gateup": {"sources_sha256": "4434d2cf17cbaf1fcb864471e21b143175bb8d0ca5accd2ab0f13c5186dcfd99",
+                    "fetch_bytes": 9731886, "write_bytes": 16448},
+    # prefill T=4096, 18 dispatches: FETCH 226199.8 KiB x 1.99980, WRITE 36864.0 KiB x 1.0
+    "gemm_gateup": {"sources_sha256": "3402e9c0b0c7815368f5726501af7902a8756224830f67a8cf0bcf9a9dc97a18",
+                    "fetch_bytes": 463210841, "write_bytes": 37748736},
     # MXFP4 decode T=1, 280 dispatches: FETCH 4756.8 KiB x 1.99980, WRITE 16.1 KiB x 1.0
-    "gemv_gateup_mx": {"sources_sha256": "8361f2a89ce0277b7416ef83d49195169378c8cba01cabdf1148abc2aab6a521",
-                    "fetch_bytes": 9740885, "write_bytes": 16448},
-    # MXFP4 prefill T=4096, 18 dispatches: FETCH 269597.8 KiB x 1.99980, WRITE 59904.9 KiB x 1.0
-    "gemm_gateup_mx": {"sources_sha256": "5d8962efcc52f516699fd2b0d09314e0487c9d80c3f3acac56b2dc4ea632537c",
-                    "fetch_bytes": 552081142, "write_bytes": 61342658},
+    "gemv_gateup_mx": {"sources_sha256": "4434d2cf17cbaf1fcb864471e21b143175bb8d0ca5accd2ab0f13c5186dcfd99",
+                    "fetch_bytes": 9740945, "write_bytes": 16448},
+    # MXFP4 prefill T=4096, 18 dispatches: FETCH 272663.4 KiB x 1.99980, WRITE 59905.1 KiB x 1.0
+    "gemm_gateup_mx": {"sources_sha256": "c061cd90155d652790c53cd36426ae8d0149105eced42466673dfc64ef85232e",
+                    "fetch_bytes": 558358886, "write_bytes": 61342811},
 }
 FETCH_SIZE_FACTOR = 1.99980   # plain 256 MiB copy: true bytes read / FETCH_SIZE bytes
 WRITE_SIZE_FACTOR = 1.0
@@ -88,6 +88,25 @@ def sources_sha(kernel):
         with open(os.path.join(ROOT, "quantized_moe_transformer_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
+
+
+# Matrix-core counters of the prefill gate/up GEMMs (profiles/gemm_*_prefill_T4096.md,
+# rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_* GRBM_GUI_ACTIVE),
+# keyed like TRAFFIC: mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x
+# GRBM_GUI_ACTIVE / 8 XCDs); executed_flops = MOPS x 512 (padded rows included).
+MFMA_COUNTERS = {
+    "gemm_gateup": {"sources_sha256": "3402e9c0b0c7815368f5726501af7902a8756224830f67a8cf0bcf9a9dc97a18",
+                    "mfma_busy": 0.3346, "executed_flops": 1.71262e+11},
+    "gemm_gateup_mx": {"sources_sha256": "c061cd90155d652790c53cd36426ae8d0149105eced42466673dfc64ef85232e",
+                    "mfma_busy": 0.3856, "executed_flops": 5.11772e+11},
+}
+
+
+def counters_for(kernel):
+    t = MFMA_COUNTERS.get(kernel)
+    if t is None or t["sources_sha256"] != sources_sha(kernel):
+        return None
+    return {k: v for k, v in t.items() if k != "sources_sha256"}
 
 
 def traffic_for(kernel):
@@ -518,7 +537,8 @@ def bench_prefill(args, torch, qm, mi, DeviceLayer, name="prefill4096", check_ro
         "roofline": roofline("gemm_mx_kernel<0>" if mx else "gemm_grouped_kernel<0>", "mfma",
                              flops_gu, gu_ms, "TFLOP/s", peak,
                              traffic_for("gemm_gateup_mx" if mx else "gemm_gateup"),
-                             {"median_launch_ms": kst["gemm_gateup"]["median_ms"],
+                             {"counters": counters_for("gemm_gateup_mx" if mx else "gemm_gateup"),
+                              "median_launch_ms": kst["gemm_gateup"]["median_ms"],
                               "min_launch_ms": kst["gemm_gateup"]["min_ms"], "launches": K}),
     }
     if mx:
