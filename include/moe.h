@@ -101,6 +101,14 @@ extern "C" {
 #define MOE_PATH_GEMV 1        /* fp32 dequant-GEMV, fp32 accumulation */
 #define MOE_PATH_MFMA 2        /* grouped GEMM on the matrix cores, fp32 accumulation: fp16
                                   operands (K-quant), block-scaled MX operands (MXFP4) */
+/*
+ * The MFMA path hands each routed expert's weighted output row to the slot-order
+ * combine as 16-bit block floating point: every 8 consecutive values share
+ * their largest magnitude's fp32 exponent and keep 14 to 15 bits each, with
+ * no range limit.  A group of 8 holding an inf or NaN reads back as 8 NaNs, so
+ * a non-finite value in one expert's output turns the token's 8 outputs of
+ * that column group to NaN (the GEMV path keeps fp32 rows throughout).
+ */
 
 /*
  * Layer description: plain values and device pointers, read during the call

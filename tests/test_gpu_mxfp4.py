@@ -164,3 +164,50 @@ def test_mx_wide_scale_bytes(scales, path, tol):
     err = rel_err(got[exact], ref[exact])
     say(f"  max|err|/RMS = {err:.3e}")
     assert err <= tol
+
+
+@pytest.mark.parametrize("path,tol", [(qm.MOE_PATH_GEMV, GEMV_TOL), (qm.MOE_PATH_MFMA, MFMA_TOL)])
+def test_mx_nan_scale_propagates(path, tol):
+    """E8M0 byte 255 is the format's NaN.  Give it to the first 32-weight
+    block of expert 0's down row 5: every token routed to expert 0 gets a NaN
+    in output feature 5 in the oracle.  The fp32 GEMV path must reproduce that
+    NaN pattern exactly.  The MFMA path carries the per-slot rows as 16-bit
+    block floating point, in which a block of 8 values holding a NaN reads
+    back as 8 NaNs: its NaNs must cover the oracle's and lie in the same rows
+    and 8-column groups.  Every other value matches at the path's tolerance."""
+    shp = mi.LayerShape(H=512, E=8, k=2, I=256, Is=256, fmt=1)
+    layer = mi.make_layer(shp, seed=62)
+    per_row = shp.I // 256                      # 144-byte superblocks per down row
+    down = layer["down"].copy()                 # [E][rows * per_row * 144] bytes
+    down[0, 5 * per_row * 144] = 255            # expert 0, row 5, scale of block 0
+    layer = dict(layer, down=down)
+    x = mi.make_tokens(shp, 62, 70)
+    dl = DeviceLayer.from_shape(layer, shp)
+    ol = oracle.Layer.from_shape(layer, shp)
+    say(f"mx NaN scale path={path}")
+    T = x.shape[0]
+    out = torch.zeros((T, shp.H), device=DEV)
+    used = qm.moe_layer_forward(dl.desc, gpu(x), T, out, dl.workspace(T), path=path)
+    torch.cuda.synchronize()
+    assert used == path
+    got = out.cpu().numpy()
+    ref = oracle.forward(ol, x)
+    oi, _, _, logits = oracle.router(x, layer["router_w"], shp.k)
+    gi, _ = run_router(dl, x)
+    exact, _, wrong = topk_check(gi, oi, logits)
+    assert len(wrong) == 0
+    nan_ref, nan_got = np.isnan(ref), np.isnan(got)
+    routed0 = (oi == 0).any(axis=1)
+    assert routed0.any() and (~routed0).any()
+    assert np.array_equal(nan_ref[:, 5], routed0) and nan_ref.sum() == routed0.sum()
+    if path == qm.MOE_PATH_GEMV:
+        assert np.array_equal(nan_got, nan_ref)
+    else:
+        assert (nan_got | ~nan_ref).all()                       # covers the oracle's NaNs
+        groups = np.repeat(nan_ref.reshape(T, -1, 8).any(axis=2), 8, axis=1)
+        assert (~nan_got | groups).all()                        # within their 8-column groups
+    fin = ~nan_ref & ~nan_got
+    assert np.isfinite(got[fin]).all()
+    err = float(np.abs(got[fin] - ref[fin]).max() / np.sqrt(np.mean(ref[fin] ** 2)))
+    say(f"  NaNs oracle {int(nan_ref.sum())}, GPU {int(nan_got.sum())}; finite max|err|/RMS = {err:.3e}")
+    assert err <= tol
