@@ -32,8 +32,9 @@
 // One producer and one consumer wave share each SIMD: the dequantisation
 // (VALU) of one wave runs beside the MFMAs of the other, which measured far
 // better than dequantising into MFMA operand registers in the MFMA wave
-// itself, where the two serialise.  The cost is LDS traffic: about 1.1 KB per
-// 32x32x16 MFMA, close to what the LDS delivers at the MFMA rate.
+// itself, where the two serialise.  The cost is a barrier per K step: the
+// consumers' fragment reads after each barrier, and the token rows, fetched
+// one step ahead, bound a step at about twice its MFMA time.
 //
 //   gateup (MODE 0): A = token rows of x16 gathered through the expert-sorted
 //     slot list, B = 128 gate rows + the matching 128 up rows (4-bit); each
