@@ -37,30 +37,31 @@ constexpr float kWrScale = 1024.0f, kLoScale = 2048.0f;
 constexpr int kRgT = 64, kRgE = 128, kRgK = 64;
 
 // One launch, two jobs.  Workgroups [0, nxb): x fp32 [T][H] -> hi (x16, also
-// the grouped GEMM's operand) and lo parts, four values per thread.
+// the grouped GEMM's operand) and lo parts, eight values (two 16-byte loads,
+// one 16-byte store per part) per thread.
 // Workgroups [nxb, nxb + nwb): the router matrix fp32 [H][E] -> 2^10 * (hi, lo)
 // parts transposed to [E][H], one 32 x 32 tile each (LDS transpose).  xl and
 // wr may be null (tokens only).
 __global__ void __launch_bounds__(256)
 split_kernel(const float* __restrict__ x, _Float16* __restrict__ xh, _Float16* __restrict__ xl,
-             size_t n4, int nxb, const float* __restrict__ wr, int H, int E,
+             size_t n8, int nxb, const float* __restrict__ wr, int H, int E,
              _Float16* __restrict__ wh, _Float16* __restrict__ wl) {
     __shared__ float tile[32][33];
     const int b = blockIdx.x;
     if (b < nxb) {
         const size_t i = (size_t)b * blockDim.x + threadIdx.x;
-        if (i >= n4) return;
-        const float4 v = reinterpret_cast<const float4*>(x)[i];
-        typedef _Float16 half4 __attribute__((ext_vector_type(4)));
-        half4 h, l;
-        const float f[4] = {v.x, v.y, v.z, v.w};
+        if (i >= n8) return;
+        const float4 v0 = reinterpret_cast<const float4*>(x)[2 * i];
+        const float4 v1 = reinterpret_cast<const float4*>(x)[2 * i + 1];
+        half8 h, l;
+        const float f[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < 8; ++j) {
             h[j] = (_Float16)f[j];
             l[j] = (_Float16)((f[j] - (float)h[j]) * kLoScale);
         }
-        reinterpret_cast<half4*>(xh)[i] = h;
-        if (xl) reinterpret_cast<half4*>(xl)[i] = l;
+        reinterpret_cast<half8*>(xh)[i] = h;
+        if (xl) reinterpret_cast<half8*>(xl)[i] = l;
         return;
     }
     const int wb = b - nxb, nhb = (H + 31) / 32;
@@ -220,9 +221,9 @@ hipError_t launch_router(const moe_layer_desc& d, const float* x, int T, int32_t
     _Float16* xl = reinterpret_cast<_Float16*>(ws + L.x_lo);
     _Float16* wh = reinterpret_cast<_Float16*>(ws + L.w_hi);
     _Float16* wl = reinterpret_cast<_Float16*>(ws + L.w_lo);
-    const size_t n4 = (size_t)T * H / 4;
-    const int nxb = (int)((n4 + 255) / 256), nwb = ((H + 31) / 32) * ((E + 31) / 32);
-    launch_k(c, MOE_K_X_F16, split_kernel, dim3(nxb + nwb), dim3(256), 0, x, xh, xl, n4, nxb,
+    const size_t n8 = (size_t)T * H / 8;   // H is a multiple of 256
+    const int nxb = (int)((n8 + 255) / 256), nwb = ((H + 31) / 32) * ((E + 31) / 32);
+    launch_k(c, MOE_K_X_F16, split_kernel, dim3(nxb + nwb), dim3(256), 0, x, xh, xl, n8, nxb,
              d.router_w, H, E, wh, wl);
     launch_k(c, MOE_K_ROUTER_MFMA, router_gemm_kernel,
              dim3((T + kRgT - 1) / kRgT, (E + kRgE - 1) / kRgE, kRgSplit), dim3(256), 0, xh, xl, wh,
@@ -234,10 +235,10 @@ hipError_t launch_router(const moe_layer_desc& d, const float* x, int T, int32_t
 
 // fp16 tokens for the grouped GEMM when the router did not already make them
 hipError_t launch_x16(const float* x, int T, int H, char* ws, const WsLayout& L, const Ctx& c) {
-    const size_t n4 = (size_t)T * H / 4;
-    const int nxb = (int)((n4 + 255) / 256);
+    const size_t n8 = (size_t)T * H / 8;
+    const int nxb = (int)((n8 + 255) / 256);
     launch_k(c, MOE_K_X_F16, split_kernel, dim3(nxb), dim3(256), 0, x,
-             reinterpret_cast<_Float16*>(ws + L.x16), (_Float16*)nullptr, n4, nxb,
+             reinterpret_cast<_Float16*>(ws + L.x16), (_Float16*)nullptr, n8, nxb,
              (const float*)nullptr, H, 0, (_Float16*)nullptr, (_Float16*)nullptr);
     return hipGetLastError();
 }
