@@ -155,7 +155,6 @@ struct BRegs {
 // Token-row stages: the rows of step kk + kAStages - 1 are requested at the
 // start of step kk, into the stage that step kk - 1 read.
 constexpr int kAStages = 2;
-__device__ __forceinline__ int a_chunk(int r, int c) { return r * (kBK / 8) + (c ^ ((r >> 1) & 7)); }
 
 // wait until at most n later steps' token-row loads (MB per step) are in flight
 template <int MB>
