@@ -146,7 +146,8 @@ def test_dequant_layer_matrices(name):
 @pytest.mark.parametrize("name,T,stream", [("tiny", 4, None), ("decode", 64, 7),
                                            ("decode_batched", 32, None),
                                            ("prefill512_zipf", 512, None),
-                                           ("prefill4096", 4096, None), ("prefill4096", 333, 3)])
+                                           ("prefill4096", 4096, None), ("prefill4096", 333, 3),
+                                           ("tiny", 131, 3)])
 def test_router_topk(name, T, stream):
     w, layer, dl, ol = dev_layer(name)
     x = mi.make_tokens(w.shape, w.seed, T, stream=w.x_stream if stream is None else stream,
