@@ -502,7 +502,7 @@ def bench_prefill(args, torch, qm, mi, DeviceLayer, name="prefill4096", check_ro
     assert set(used) == {qm.MOE_PATH_MFMA}, used
     eager_secs = time_steps(torch, step, K)
     dev_s, host_s = graph_time(torch, step, K)
-    names = ["x_f16", "x_mx", "router_mfma", "router_topk", "bucket_hist", "bucket_scan",
+    names = ["x_f16", "x_mx", "router_mfma", "router_topk", "bucket_hist",
              "bucket_scatter", "gemm_gateup", "gemm_down", "combine"]
     kst = {}
     kms = kernel_profile(torch, qm, lambda i, e: step(i, e), K, names, kst)

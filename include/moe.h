@@ -160,9 +160,9 @@ typedef struct moe_opts {
 #define MOE_K_DOWN_GEMV 4        /* decode: down + slot-order combine */
 #define MOE_K_X_F16 5            /* T > 32: tokens to fp16 hi/lo parts (and, when the router runs,
                                     the router matrix to fp16 hi/lo parts in the same launch) */
-#define MOE_K_BUCKET_HIST 6
-#define MOE_K_BUCKET_SCAN 7
-#define MOE_K_BUCKET_SCATTER 8
+#define MOE_K_BUCKET_HIST 6      /* more than 8192 slots: per-1024-slot expert counts */
+#define MOE_K_BUCKET_SCAN 7      /* not launched: the scan runs inside the sort (id kept) */
+#define MOE_K_BUCKET_SCATTER 8   /* expert offsets, tile list and the slot order by expert */
 #define MOE_K_GEMM_GATEUP 9      /* prefill: grouped GEMM gate/up + SwiGLU */
 #define MOE_K_GEMM_DOWN 10       /* prefill: grouped GEMM down */
 #define MOE_K_COMBINE 11         /* prefill: slot-order combine */
