@@ -398,9 +398,12 @@ def bench_layer_batches(args, torch, qm, mi, DeviceLayer, name, T, n_copies, K, 
 
 
 def bench_sharded(args, torch, qm, mi, DeviceLayer, name, T, n_copies, n_batches, K, W, label,
-                  check_rows):
+                  check_rows, two_streams):
     """The 256/256 shard mode as one step: router_topk once (the synchronised
-    decision), moe_layer_forward_shard(0, 2) and (1, 2), moe_reduce_partials."""
+    decision), moe_layer_forward_shard(0, 2) and (1, 2), moe_reduce_partials.
+    two_streams: shard 1 runs on a second stream, forked after the router and
+    joined before the reduce (the shard calls are independent, as on two
+    devices); else both run in order on one stream."""
     w = mi.WORKLOADS[name]
     shp = w.shape
     layer = mi.make_layer(shp, w.seed, zipf=w.zipf)
@@ -417,13 +420,21 @@ def bench_sharded(args, torch, qm, mi, DeviceLayer, name, T, n_copies, n_batches
     out = torch.empty((T, shp.H), device="cuda")
     used = []
 
+    side = torch.cuda.Stream() if two_streams else None
+
     def step(i, evs=None):
         c = copies[i % len(copies)]
         x = xd[(i // len(copies)) % n_batches]
         qm.router_topk(c.desc, x, T, idx, wts, ws_r)
+        main = torch.cuda.current_stream()
+        if side is not None:
+            side.wait_stream(main)
         for s in range(2):
-            used.append(qm.moe_layer_forward_shard(c.desc, x, T, idx, wts, s, 2, parts[s], ws[s],
-                                                   events=None if evs is None else evs[s]))
+            with torch.cuda.stream(main if s == 0 or side is None else side):
+                used.append(qm.moe_layer_forward_shard(c.desc, x, T, idx, wts, s, 2, parts[s],
+                                                       ws[s], events=None if evs is None else evs[s]))
+        if side is not None:
+            main.wait_stream(side)
         qm.moe_reduce_partials(parts, T * shp.H, out)
 
     for i in range(W):
@@ -443,10 +454,18 @@ def bench_sharded(args, torch, qm, mi, DeviceLayer, name, T, n_copies, n_batches
         slots = T * shp.k + T
         flops_gu = 2.0 * 2 * shp.H * (shp.I // 2) * slots
         flops = 3.0 * 2 * shp.H * shp.I * slots
-        rl = roofline("gemm_grouped_kernel<0> of shard 0 (gate/up + SwiGLU, I/2 = %d)" % (shp.I // 2),
-                      "mfma", flops_gu, kms[(0, "gemm_gateup")], "TFLOP/s", FP16_MFMA_PEAK_TFLOPS,
-                      extra={"median_launch_ms": kst[(0, "gemm_gateup")]["median_ms"],
-                             "min_launch_ms": kst[(0, "gemm_gateup")]["min_ms"]})
+        if two_streams:
+            # the shards' kernels overlap, so no single launch's duration is
+            # its own: the whole step carries the figure (a lower bound for
+            # the GEMMs, since the step also holds the router and the reduce)
+            rl = roofline("whole two-shard step (both shards' grouped GEMMs, concurrent)", "mfma",
+                          flops, dev_s * 1e3, "TFLOP/s", FP16_MFMA_PEAK_TFLOPS)
+        else:
+            rl = roofline("gemm_grouped_kernel<0> of shard 0 (gate/up + SwiGLU, I/2 = %d)"
+                          % (shp.I // 2), "mfma", flops_gu, kms[(0, "gemm_gateup")], "TFLOP/s",
+                          FP16_MFMA_PEAK_TFLOPS,
+                          extra={"median_launch_ms": kst[(0, "gemm_gateup")]["median_ms"],
+                                 "min_launch_ms": kst[(0, "gemm_gateup")]["min_ms"]})
         gemm_ms = sum(v for (c, n), v in kms.items() if n.startswith("gemm"))
         whole = {"expert_gflop": flops / 1e9,
                  "expert_mfma_frac": flops / (gemm_ms * 1e-3) / (FP16_MFMA_PEAK_TFLOPS * 1e12),
@@ -908,8 +927,10 @@ def main():
         c2s, checks["C2_sharded_T1"] = bench_sharded(
         args, torch, qm, mi, DeviceLayer, "decode_sharded", 1, args.copies, 64, args.steps,
         args.warmup, "sharded decode T=1: the same layer (seed 2), router_topk once, the 256/256 "
-        "shards as two moe_layer_forward_shard calls, moe_reduce_partials; 64-token pool, "
-        f"{args.copies} rotating weight copies, HIP graph of exactly `steps` steps", 64)
+        "shards as two moe_layer_forward_shard calls in order on one stream (two streams "
+        "measured slower at T=1), moe_reduce_partials; 64-token pool, "
+        f"{args.copies} rotating weight copies, HIP graph of exactly `steps` steps", 64,
+        two_streams=False)
     if want("batched_decode"):
         say("C2 batched decode T=32 ...")
         c2b, checks["C2_batched_T32"] = bench_layer_batches(
@@ -933,8 +954,9 @@ def main():
         c4s, checks["C4_sharded_T4096"] = bench_sharded(
             args, torch, qm, mi, DeviceLayer, "prefill4096", 4096, 2, 1, args.prefill_steps,
             args.prefill_warmup, "two-shard prefill T=4096: the same layer (seed 4), router_topk "
-            "once, the 256/256 shards as two moe_layer_forward_shard calls, moe_reduce_partials; "
-            "2 rotating weight copies, HIP graph of exactly `steps` steps", 256)
+            "once, the 256/256 shards as two moe_layer_forward_shard calls on two streams, "
+            "moe_reduce_partials; 2 rotating weight copies, HIP graph of exactly `steps` steps", 256,
+            two_streams=True)
     if not args.no_prefill and want("edges"):
         say("RMSNorm / residual at T=4096 ...")
         edges = bench_edges(torch, qm)
