@@ -584,14 +584,14 @@ def bench_continuum(args, torch, qm, mi, DeviceLayer):
     graphs over 4 weight copies and 4 token batches.  One JSON line per (T,
     path) on stdout: step time, tokens/s, algorithmic bytes (every distinct
     touched expert once, the shared expert, the router matrix, x and out) and
-    FLOPs, GB/s and GFLOP/s, and the path the automatic rule takes at that T."""
-    shp = mi.QWEN35_MOE
+    FLOPs, GB/s and GFLOP/s, and the path the automatic rule takes at that T.
+    --continuum-fmt 1 runs the same with MXFP4 expert weights."""
+    shp = mi.QWEN35_MOE_MX if args.continuum_fmt == 1 else mi.QWEN35_MOE
     seed = 2
     layer = mi.make_layer(shp, seed)
     base = DeviceLayer.from_shape(layer, shp)
     copies = [base] + [base.clone_weights() for _ in range(3)]
-    E_bytes = (2 * (shp.I * shp.H // 256) * mi.Q4K_SB_BYTES
-               + (shp.H * shp.I // 256) * mi.Q5K_SB_BYTES)
+    E_bytes = sum(expert_bytes(mi, shp))
     G = 8   # steps per graph: two rounds over the weight copies
     rows = []
     for T in args.continuum_t:
@@ -634,7 +634,8 @@ def bench_continuum(args, torch, qm, mi, DeviceLayer):
             secs = (time.perf_counter() - t0) / (n_rep * G)
             del g
             rows.append({
-                "T": T, "path": pname, "ms_per_step": secs * 1e3,
+                "T": T, "fmt": "mxfp4" if shp.fmt == 1 else "kquant", "path": pname,
+                "ms_per_step": secs * 1e3,
                 "tokens_per_s": T / secs,
                 "eager_ms_per_step": eager_s / eager_n * 1e3,
                 "distinct_experts": d_avg,
@@ -877,6 +878,8 @@ def main():
     ap.add_argument("--continuum", action="store_true",
                     help="only time both paths at T = 1 .. 512 (one JSON line per point)")
     ap.add_argument("--continuum-t", type=int, nargs="+", default=list(CONTINUUM_T))
+    ap.add_argument("--continuum-fmt", type=int, default=0, choices=[0, 1],
+                    help="expert weight format of the continuum: 0 K-quant, 1 MXFP4")
     ap.add_argument("--only", nargs="+", default=None, metavar="WORKLOAD",
                     choices=["decode", "sharded_decode", "batched_decode", "zipf_prefill",
                              "prefill", "sharded_prefill", "edges", "mxfp4_decode",

@@ -97,7 +97,8 @@ extern "C" {
 #define MOE_WFMT_MXFP4 1       /* MXFP4 gate, up and down */
 
 /* Compute paths (moe_opts.path). */
-#define MOE_PATH_AUTO 0        /* GEMV for T <= 14, grouped MFMA GEMM above (measured crossover) */
+#define MOE_PATH_AUTO 0        /* GEMV for T <= 17 (MXFP4: T <= 26), grouped MFMA GEMM above
+                                  (measured crossovers) */
 #define MOE_PATH_GEMV 1        /* fp32 dequant-GEMV, fp32 accumulation */
 #define MOE_PATH_MFMA 2        /* grouped GEMM on the matrix cores, fp32 accumulation: fp16
                                   operands (K-quant), block-scaled MX operands (MXFP4) */

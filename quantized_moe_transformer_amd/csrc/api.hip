@@ -234,15 +234,18 @@ static int check_desc(const moe_layer_desc* d) {
 }
 
 // Automatic path: the GEMV path up to this many token rows, the grouped GEMM
-// beyond.  Measured on the Qwen3.5-35B-A3B-shaped layer (uniform routing,
-// HIP-graph replay, one MI355X): GEMV 102 us vs GEMM 115 us at 12 rows, 133 us
-// vs 126 us at 16 rows; GEMV cost grows by about 7.5 us per row (each row
-// streams its own experts) while the GEMM reads each touched expert once.
-constexpr int kGemvMaxT = 14;
+// beyond, per weight format.  Measured on the Qwen3.5-35B-A3B-shaped layer
+// (uniform routing, HIP-graph replay, one MI355X): K-quant GEMV 122.9 us vs
+// GEMM 135.0 us at 16 rows, 138.1 vs 137.2 at 18, 150.4 vs 139.0 at 20;
+// MXFP4 159.0 vs 164.6 at 26 rows, 169.6 vs 165.5 at 28.  The GEMV cost grows
+// by about 6 us per row (each row streams its own experts) while the GEMM
+// reads each touched expert once per column tile.
+constexpr int kGemvMaxT = 17;     // K-quant
+constexpr int kGemvMaxTMx = 26;   // MXFP4
 
 static bool gemv_supports(int iloc) { return iloc >= 64 && iloc <= 2048 && iloc % 64 == 0; }
 
-static int choose_path(int T, int iloc, const moe_opts* o, int* path) {
+static int choose_path(int T, int iloc, int fmt, const moe_opts* o, int* path) {
     const int req = o ? o->path : MOE_PATH_AUTO;
     if (req == MOE_PATH_GEMV) {
         if (!gemv_supports(iloc)) return MOE_EUNSUPPORTED;
@@ -250,7 +253,8 @@ static int choose_path(int T, int iloc, const moe_opts* o, int* path) {
     } else if (req == MOE_PATH_MFMA) {
         *path = MOE_PATH_MFMA;
     } else if (req == MOE_PATH_AUTO) {
-        *path = (T <= kGemvMaxT && gemv_supports(iloc)) ? MOE_PATH_GEMV : MOE_PATH_MFMA;
+        const int tmax = fmt == MOE_WFMT_MXFP4 ? kGemvMaxTMx : kGemvMaxT;
+        *path = (T <= tmax && gemv_supports(iloc)) ? MOE_PATH_GEMV : MOE_PATH_MFMA;
     } else {
         return MOE_EINVAL;
     }
@@ -365,7 +369,7 @@ static int forward_common(const moe_layer_desc* desc, const float* x, int32_t T,
     int rc;
     if (T < 0) return MOE_EINVAL;
     int path = 0;
-    if ((rc = choose_path(T, iloc, opts, &path))) return rc;
+    if ((rc = choose_path(T, iloc, desc->weight_format, opts, &path))) return rc;
     if (opts && opts->path_used) *opts->path_used = path;
     if (T == 0) return MOE_OK;
     if (!x || !out || !ws || (!route && (!idx || !w))) return MOE_EINVAL;

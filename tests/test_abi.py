@@ -168,9 +168,14 @@ def test_empty_batch_is_a_no_op(L):
     assert L.lib.moe_dequant(None, 4, 0, 0, None, None) == L.MOE_OK
 
 
-def test_path_choice_reported(L):
-    d = desc()
-    for T, path, expect in [(1, 0, 1), (14, 0, 1), (15, 0, 2), (32, 0, 2), (1, 2, 2), (4096, 1, 1)]:
+@pytest.mark.parametrize("fmt,cases", [
+    (0, [(1, 0, 1), (17, 0, 1), (18, 0, 2), (32, 0, 2), (1, 2, 2), (4096, 1, 1)]),
+    (1, [(1, 0, 1), (26, 0, 1), (27, 0, 2), (4096, 0, 2), (1, 2, 2)]),
+])
+def test_path_choice_reported(L, fmt, cases):
+    # the automatic rule's crossover depends on the weight format
+    d = desc(weight_format=fmt)
+    for T, path, expect in cases:
         used = ctypes.c_int32(-1)
         o = L.moe_opts(path, ctypes.pointer(used), None, 0)
         # a too-small workspace stops the call after the path is chosen

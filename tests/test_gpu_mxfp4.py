@@ -68,6 +68,14 @@ def test_mx_layer(name, T, path, tol, stream):
         assert used == path
 
 
+def test_mx_auto_path_switch():
+    # MXFP4's automatic rule: GEMV up to 26 rows, the grouped GEMM from 27 rows on
+    _, used = check_layer("decode_mx", 26, qm.MOE_PATH_AUTO, GEMV_TOL, stream=6)
+    assert used == qm.MOE_PATH_GEMV
+    _, used = check_layer("decode_mx", 27, qm.MOE_PATH_AUTO, MFMA_TOL, stream=6)
+    assert used == qm.MOE_PATH_MFMA
+
+
 def test_mx_prefill_4096_all_rows():
     _, used = check_layer("prefill4096_mx", 4096, qm.MOE_PATH_AUTO, MFMA_TOL)
     assert used == qm.MOE_PATH_MFMA

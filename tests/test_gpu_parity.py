@@ -267,10 +267,10 @@ def test_gemv_batched_decode():
 
 
 def test_auto_path_switch():
-    # the automatic rule: GEMV up to 14 rows, the grouped GEMM from 15 rows on
-    _, used = check_layer("decode_batched", 14, qm.MOE_PATH_AUTO, GEMV_TOL, stream=6)
+    # the automatic rule: GEMV up to 17 rows, the grouped GEMM from 18 rows on
+    _, used = check_layer("decode_batched", 17, qm.MOE_PATH_AUTO, GEMV_TOL, stream=6)
     assert used == qm.MOE_PATH_GEMV
-    _, used = check_layer("decode_batched", 15, qm.MOE_PATH_AUTO, MFMA_TOL, stream=6)
+    _, used = check_layer("decode_batched", 18, qm.MOE_PATH_AUTO, MFMA_TOL, stream=6)
     assert used == qm.MOE_PATH_MFMA
 
 
