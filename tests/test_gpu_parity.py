@@ -465,6 +465,29 @@ def test_odd_expert_counts(E, k, T):
     assert rel_err(got[exact], oracle.forward(ol, x)[exact]) <= tol
 
 
+@pytest.mark.parametrize("T,path,tol", [(3, qm.MOE_PATH_GEMV, GEMV_TOL),
+                                         (40, qm.MOE_PATH_GEMV, GEMV_TOL),
+                                         (40, qm.MOE_PATH_MFMA, MFMA_TOL)])
+def test_max_experts_and_top_k(T, path, tol):
+    """The largest expert count and top-k the ABI takes (E = 1024, k = 16):
+    16 keys per lane in the top-k, 16 slots per token in the per-slot
+    buffers and the combine (its 16-slot form), 1024 bucketing groups."""
+    shp = mi.LayerShape(H=256, E=1024, k=16, I=128, Is=128)
+    layer = mi.make_layer(shp, seed=43)
+    x = mi.make_tokens(shp, 43, T)
+    dl = DeviceLayer.from_shape(layer, shp)
+    say(f"max experts E=1024 k=16 T={T} path={path}")
+    oi, ow, owd, logits = oracle.router(x, layer["router_w"], shp.k)
+    gi, gw = run_router(dl, x)
+    exact, exempt, wrong = topk_check(gi, oi, logits)
+    assert len(wrong) == 0
+    assert np.abs(gw[exact] - owd[exact]).max() <= 2e-5
+    got, used = run_forward(dl, x, path)
+    assert used == path
+    ol = oracle.Layer.from_shape(layer, shp)
+    assert rel_err(got[exact], oracle.forward(ol, x)[exact]) <= tol
+
+
 @pytest.mark.parametrize("E,k,Is", [(8, 8, 128), (1, 1, 0), (4, 3, 0)])
 @pytest.mark.parametrize("path,tol", [(qm.MOE_PATH_GEMV, GEMV_TOL), (qm.MOE_PATH_MFMA, MFMA_TOL)])
 @pytest.mark.parametrize("fmt", [0, 1])
