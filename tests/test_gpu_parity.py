@@ -468,15 +468,17 @@ def test_odd_expert_counts(E, k, T):
 @pytest.mark.parametrize("T,path,tol", [(3, qm.MOE_PATH_GEMV, GEMV_TOL),
                                          (40, qm.MOE_PATH_GEMV, GEMV_TOL),
                                          (40, qm.MOE_PATH_MFMA, MFMA_TOL)])
-def test_max_experts_and_top_k(T, path, tol):
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_max_experts_and_top_k(T, path, tol, fmt):
     """The largest expert count and top-k the ABI takes (E = 1024, k = 16):
     16 keys per lane in the top-k, 16 slots per token in the per-slot
-    buffers and the combine (its 16-slot form), 1024 bucketing groups."""
-    shp = mi.LayerShape(H=256, E=1024, k=16, I=128, Is=128)
+    buffers and the combine (its 16-slot form), 1024 bucketing groups; both
+    weight formats."""
+    shp = mi.LayerShape(H=256, E=1024, k=16, I=128, Is=128, fmt=fmt)
     layer = mi.make_layer(shp, seed=43)
     x = mi.make_tokens(shp, 43, T)
     dl = DeviceLayer.from_shape(layer, shp)
-    say(f"max experts E=1024 k=16 T={T} path={path}")
+    say(f"max experts E=1024 k=16 T={T} path={path} fmt={fmt}")
     oi, ow, owd, logits = oracle.router(x, layer["router_w"], shp.k)
     gi, gw = run_router(dl, x)
     exact, exempt, wrong = topk_check(gi, oi, logits)
