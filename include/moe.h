@@ -103,6 +103,13 @@ extern "C" {
 #define MOE_PATH_MFMA 2        /* grouped GEMM on the matrix cores, fp32 accumulation: fp16
                                   operands (K-quant), block-scaled MX operands (MXFP4) */
 /*
+ * The K-quant MFMA path rounds the tokens, the weights and h to fp16 once each.
+ * Its error against an exact evaluation depends on the layer: 2.9e-3 and
+ * 4.9e-3 of the output RMS on the Qwen3.5-shaped layer (T = 4096, and a Zipf
+ * batch of 512), but about 2e-2 on a layer as small as H = 256 with I = 64,
+ * where the tokens' rounding dominates.  MOE_PATH_GEMV keeps fp32 throughout.
+ */
+/*
  * The MFMA path hands each routed expert's weighted output row to the slot-order
  * combine as 16-bit block floating point: every 8 consecutive values share
  * their largest magnitude's fp32 exponent and keep 14 to 15 bits each, with

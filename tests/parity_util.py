@@ -16,6 +16,44 @@ def rel_err(got, ref):
     return float(np.abs(got - ref).max() / rms) if ref.size else 0.0
 
 
+def fp16_operand_reference(layer, shp, x, idx, w, sw=1.0):
+    """The K-quant layer with the MFMA path's operand roundings and nothing
+    else: tokens, the oracle's exact weights and h = silu(g) u * 2^-4 each
+    rounded to the nearest fp16 once, every product and sum in float64.
+    Separates what the fp16 operands cost from any defect of the kernels."""
+    import oracle
+    H, E, k, I, Is = shp.H, shp.E, shp.k, shp.I, shp.Is
+
+    def deq(name, bits, rows, cols):
+        return oracle.dequant(np.asarray(layer[name]).reshape(-1), bits).reshape(rows, cols)
+
+    def f16(a):
+        return np.asarray(a).astype(np.float16).astype(np.float64)
+
+    gate = [f16(deq("gate", 4, E * I, H)[e * I:(e + 1) * I]) for e in range(E)]
+    up = [f16(deq("up", 4, E * I, H)[e * I:(e + 1) * I]) for e in range(E)]
+    down = [f16(deq("down", 5, E * H, I)[e * H:(e + 1) * H]) for e in range(E)]
+
+    def ffn(g_w, u_w, d_w, xv):
+        g = g_w @ xv
+        u = u_w @ xv
+        h = f16(g / (1.0 + np.exp(-g)) * u * 2.0 ** -4)
+        return (d_w @ h) * 2.0 ** 4
+
+    sh = None
+    if Is:
+        sh = (f16(deq("sh_gate", 4, Is, H)), f16(deq("sh_up", 4, Is, H)), f16(deq("sh_down", 5, H, Is)))
+    xs = f16(x)
+    out = np.zeros((x.shape[0], H))
+    for t in range(x.shape[0]):
+        for j in range(k):
+            e = int(idx[t, j])
+            out[t] += float(w[t, j]) * ffn(gate[e], up[e], down[e], xs[t])
+        if sh is not None:
+            out[t] += sw * ffn(*sh, xs[t])
+    return out
+
+
 def topk_check(gpu_idx, ora_idx, ora_logits, gap=TOPK_GAP):
     """Classify rows: exact match, exempt (every differing slot is a swap
     between experts whose oracle logits differ by < gap), or wrong.
