@@ -20,19 +20,28 @@ def fp16_operand_reference(layer, shp, x, idx, w, sw=1.0):
     """The K-quant layer with the MFMA path's operand roundings and nothing
     else: tokens, the oracle's exact weights and h = silu(g) u * 2^-4 each
     rounded to the nearest fp16 once, every product and sum in float64.
-    Separates what the fp16 operands cost from any defect of the kernels."""
+    Separates what the fp16 operands cost from any defect of the kernels.
+    Only the experts that idx selects are decoded."""
     import oracle
-    H, E, k, I, Is = shp.H, shp.E, shp.k, shp.I, shp.Is
-
-    def deq(name, bits, rows, cols):
-        return oracle.dequant(np.asarray(layer[name]).reshape(-1), bits).reshape(rows, cols)
+    H, k, I, Is = shp.H, shp.k, shp.I, shp.Is
+    g_sb = I * H // 256 * 144     # bytes of one expert's gate (or up) matrix
+    d_sb = H * I // 256 * 176     # of its down matrix
 
     def f16(a):
         return np.asarray(a).astype(np.float16).astype(np.float64)
 
-    gate = [f16(deq("gate", 4, E * I, H)[e * I:(e + 1) * I]) for e in range(E)]
-    up = [f16(deq("up", 4, E * I, H)[e * I:(e + 1) * I]) for e in range(E)]
-    down = [f16(deq("down", 5, E * H, I)[e * H:(e + 1) * H]) for e in range(E)]
+    def deq(blob, bits, rows, cols):
+        return f16(oracle.dequant(np.asarray(blob).reshape(-1), bits).reshape(rows, cols))
+
+    cache = {}
+
+    def expert(e):
+        if e not in cache:
+            gb = np.asarray(layer["gate"]).reshape(-1)[e * g_sb:(e + 1) * g_sb]
+            ub = np.asarray(layer["up"]).reshape(-1)[e * g_sb:(e + 1) * g_sb]
+            db = np.asarray(layer["down"]).reshape(-1)[e * d_sb:(e + 1) * d_sb]
+            cache[e] = (deq(gb, 4, I, H), deq(ub, 4, I, H), deq(db, 5, H, I))
+        return cache[e]
 
     def ffn(g_w, u_w, d_w, xv):
         g = g_w @ xv
@@ -42,13 +51,13 @@ def fp16_operand_reference(layer, shp, x, idx, w, sw=1.0):
 
     sh = None
     if Is:
-        sh = (f16(deq("sh_gate", 4, Is, H)), f16(deq("sh_up", 4, Is, H)), f16(deq("sh_down", 5, H, Is)))
+        sh = (deq(layer["sh_gate"], 4, Is, H), deq(layer["sh_up"], 4, Is, H),
+              deq(layer["sh_down"], 5, H, Is))
     xs = f16(x)
     out = np.zeros((x.shape[0], H))
     for t in range(x.shape[0]):
         for j in range(k):
-            e = int(idx[t, j])
-            out[t] += float(w[t, j]) * ffn(gate[e], up[e], down[e], xs[t])
+            out[t] += float(w[t, j]) * ffn(*expert(int(idx[t, j])), xs[t])
         if sh is not None:
             out[t] += sw * ffn(*sh, xs[t])
     return out

@@ -282,6 +282,26 @@ def test_mfma_tiny_and_ragged():
     check_layer("decode", 67, qm.MOE_PATH_MFMA, MFMA_TOL, stream=9)
 
 
+@pytest.mark.parametrize("name,T,stream", [("tiny", 131, 3), ("decode", 16, 9),
+                                           ("prefill512_zipf", 24, 4)])
+def test_mfma_matches_fp16_operands(name, T, stream):
+    """The K-quant MFMA path against a float64 evaluation with the same fp16
+    roundings of tokens, weights and h and nothing else (the routing given,
+    so that both take the same experts): any kernel defect larger than the
+    16-bit slot rows' rounding shows at 1e-3 of the output RMS, ten times
+    tighter than the path's bar against the exact layer."""
+    w, layer, dl, ol = dev_layer(name)
+    x = mi.make_tokens(w.shape, w.seed, T, stream=stream, zipf=w.zipf)
+    oi, ow, owd, logits = oracle.router(x, layer["router_w"], w.shape.k)
+    say(f"fp16-operand reference {name} T={T}")
+    part, used = run_shard(dl, x, oi, owd.astype(np.float32), 0, 1, qm.MOE_PATH_MFMA)
+    assert used == qm.MOE_PATH_MFMA
+    ref16 = fp16_operand_reference(layer, w.shape, x, oi, owd.astype(np.float32))
+    err = rel_err(part.cpu().numpy(), ref16)
+    say(f"  max|err|/RMS against the fp16-operand reference = {err:.3e}")
+    assert err <= 1e-3
+
+
 def test_mfma_zipf_512():
     _, used = check_layer("prefill512_zipf", 512, qm.MOE_PATH_AUTO, MFMA_TOL)
     assert used == qm.MOE_PATH_MFMA
