@@ -70,14 +70,6 @@ constexpr int kBTasks = kTN * 2 / (64 * kProducers);   // 16-byte code pieces pe
 // row at k offsets 16*hh + [0,16) and 32 + 16*hh + [0,16).  The operands are
 // kq_piece_f16's: the round-to-nearest-even fp16 of the exact fp32 weight,
 // the same function the dequantisation test hook runs.
-// (x & m) | o in one v_and_or_b32 (the compiler splits it into an and and an
-// or when the constants are literals).
-__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t o) {
-    uint32_t r;
-    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(m), "v"(o));
-    return r;
-}
-
 template <bool HIGH>
 __device__ __forceinline__ void dequant_piece_to_lds(const SbHead& hd, const uint4& qs,
                                                      const uint4& qh, int c, int hh,

@@ -224,12 +224,6 @@ __device__ __forceinline__ float e2m1_f32(uint32_t n) {
     return __uint_as_float(__float_as_uint(mag) | ((n & 8u) << 28));
 }
 
-// Code of byte b (0..15) of a 16-byte piece held as 4 words: low nibble.
-__device__ __forceinline__ uint32_t piece_byte(const uint4& v, int b) {
-    const uint32_t w = b < 4 ? v.x : b < 8 ? v.y : b < 12 ? v.z : v.w;
-    return (w >> (8 * (b & 3))) & 0xffu;
-}
-
 // ---------------------------------------------------------------------------
 // Wave reductions (64 lanes), fixed butterfly order: deterministic
 // ---------------------------------------------------------------------------
