@@ -389,7 +389,13 @@ static int forward_common(const moe_layer_desc* desc, const float* x, int32_t T,
     if (route) {
         int32_t* ridx = reinterpret_cast<int32_t*>(wsp + L.idx);
         float* rw = reinterpret_cast<float*>(wsp + L.w);
-        if (launch_router(*desc, x, T, ridx, rw, wsp, L, c) != hipSuccess) return MOE_ELAUNCH;
+        // many slots: the top-k also makes the bucketing's per-block counts
+        int32_t* hb = bucket_self(T, desc->top_k, desc->n_experts)
+                          ? nullptr
+                          : reinterpret_cast<int32_t*>(wsp + L.bhist);
+        if (launch_router_hist(*desc, x, T, ridx, rw, wsp, L, c, hb) != hipSuccess)
+            return MOE_ELAUNCH;
+        c.hist_ready = hb != nullptr;
         idx = ridx;
         w = rw;
     }

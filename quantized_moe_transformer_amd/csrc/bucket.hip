@@ -19,7 +19,7 @@
 
 namespace moe {
 
-constexpr int kBucketBlock = 1024;   // slots (= threads) per block
+constexpr int kBucketBlock = kBucketSlots;   // slots (= threads) per block
 constexpr int kBucketWaves = kBucketBlock / 64;
 
 __global__ void __launch_bounds__(kBucketBlock)
@@ -178,22 +178,29 @@ bucket_sort_kernel(const int32_t* __restrict__ idx, int n, int nblk, int E, int 
     if (se >= 0) perm[wh[wave * E + se] + rank] = s;
 }
 
+bool bucket_self(int T, int k, int E) {
+    const int nblk = bucket_blocks(T, k);
+    return nblk <= kFusedMaxBlocks && (int64_t)nblk * E <= kFusedHist;
+}
+
 hipError_t launch_bucket(const int32_t* idx, int T, int k, int E, bool shared, int32_t* counts,
                          int32_t* offsets, int32_t* tile_off, int4* tile_rec, int32_t* perm,
                          int32_t* bhist, const Ctx& c) {
     const int n = T * k;
     const int nblk = bucket_blocks(T, k);
     // few slots: every workgroup counts all of them itself (one kernel); many:
-    // bucket_hist_kernel's per-block counts first
-    const bool self = nblk <= kFusedMaxBlocks && (int64_t)nblk * E <= kFusedHist;
+    // per-block counts first, from bucket_hist_kernel unless the router's
+    // top-k already made them
+    const bool self = bucket_self(T, k, E);
     const uint32_t wh_bytes = (uint32_t)(kBucketWaves * E * sizeof(int32_t));
     if (self) {
         launch_k(c, MOE_K_BUCKET_SCATTER, bucket_sort_kernel<true>, dim3(nblk), dim3(kBucketBlock),
                  (uint32_t)(nblk * E * sizeof(int32_t)) + wh_bytes, idx, n, nblk, E, T,
                  shared ? 1 : 0, (const int32_t*)nullptr, counts, offsets, tile_off, tile_rec, perm);
     } else {
-        launch_k(c, MOE_K_BUCKET_HIST, bucket_hist_kernel, dim3(nblk), dim3(kBucketBlock),
-                 (uint32_t)(E * sizeof(int32_t)), idx, n, E, bhist);
+        if (!c.hist_ready)
+            launch_k(c, MOE_K_BUCKET_HIST, bucket_hist_kernel, dim3(nblk), dim3(kBucketBlock),
+                     (uint32_t)(E * sizeof(int32_t)), idx, n, E, bhist);
         launch_k(c, MOE_K_BUCKET_SCATTER, bucket_sort_kernel<false>, dim3(nblk), dim3(kBucketBlock),
                  wh_bytes, idx, n, nblk, E, T, shared ? 1 : 0, (const int32_t*)bhist, counts,
                  offsets, tile_off, tile_rec, perm);

@@ -46,7 +46,11 @@ struct WsLayout {
 int router_splits(int T);
 // iloc: the intermediate rows per expert that the call computes (I, or a shard's)
 WsLayout ws_layout(const moe_layer_desc& d, int T, int iloc);
-inline int bucket_blocks(int T, int k) { return (T * k + 1023) / 1024; }
+constexpr int kBucketSlots = 1024;   // slots per bucketing block
+inline int bucket_blocks(int T, int k) { return (T * k + kBucketSlots - 1) / kBucketSlots; }
+// whether the bucketing counts the slots itself (few blocks) rather than
+// taking per-block counts from bucket_hist or the router's top-k
+bool bucket_self(int T, int k, int E);
 // upper bound on the grouped GEMM's row tiles: sum over experts of
 // ceil(count / kTileM) <= T*k / kTileM + E, plus the shared expert's
 inline int max_row_tiles(int T, int k, int E, bool shared) {
@@ -60,6 +64,7 @@ struct Ctx {
     hipStream_t s = nullptr;
     void** ev = nullptr;
     int n_ev = 0;
+    bool hist_ready = false;   // the router's top-k counted the slots into the bucketing's bhist
     hipEvent_t start(int id) const { return (ev && 2 * id + 1 < n_ev) ? (hipEvent_t)ev[2 * id] : nullptr; }
     hipEvent_t stop(int id) const { return (ev && 2 * id + 1 < n_ev) ? (hipEvent_t)ev[2 * id + 1] : nullptr; }
 };
@@ -76,6 +81,12 @@ inline void launch_k(const Ctx& c, int id, void (*kern)(KArgs...), dim3 grid, di
 
 hipError_t launch_router(const moe_layer_desc& d, const float* x, int T, int32_t* idx, float* w,
                          char* ws, const WsLayout& L, const Ctx& c);
+// the same; at T > kRouterSmallMaxT with bhist (else null) the top-k also
+// counts the slots per 1024-slot block and expert into bhist (zeroed first),
+// the bucketing's per-block histograms
+hipError_t launch_router_hist(const moe_layer_desc& d, const float* x, int T, int32_t* idx,
+                              float* w, char* ws, const WsLayout& L, const Ctx& c,
+                              int32_t* bhist);
 // route: run the router (and top-k) in the front kernel, writing L.idx / L.w
 // i0, iloc: intermediate rows [i0, i0 + iloc) of every expert (the shard)
 hipError_t launch_gemv(const moe_layer_desc& d, const float* x, int T, const int32_t* idx,

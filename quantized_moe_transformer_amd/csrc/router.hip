@@ -45,11 +45,14 @@ constexpr int kRgT = 64, kRgE = 128, kRgK = 64;
 __global__ void __launch_bounds__(256)
 split_kernel(const float* __restrict__ x, _Float16* __restrict__ xh, _Float16* __restrict__ xl,
              size_t n8, int nxb, const float* __restrict__ wr, int H, int E,
-             _Float16* __restrict__ wh, _Float16* __restrict__ wl) {
+             _Float16* __restrict__ wh, _Float16* __restrict__ wl, int32_t* __restrict__ zero,
+             size_t nzero) {
     __shared__ float tile[32][33];
     const int b = blockIdx.x;
     if (b < nxb) {
         const size_t i = (size_t)b * blockDim.x + threadIdx.x;
+        // the top-k's slot counts start from zero (zero may be null)
+        for (size_t z = i; z < nzero; z += (size_t)nxb * blockDim.x) zero[z] = 0;
         if (i >= n8) return;
         const float4 v0 = reinterpret_cast<const float4*>(x)[2 * i];
         const float4 v1 = reinterpret_cast<const float4*>(x)[2 * i + 1];
@@ -183,23 +186,31 @@ router_gemm_kernel(const _Float16* __restrict__ xh, const _Float16* __restrict__
         }
 }
 
-// Four tokens per workgroup, one wave each.
+// Four tokens per workgroup, one wave each.  With bhist (else null), lane j
+// also adds slot t*k + j to its block's count of its expert: the bucketing's
+// per-block histograms [T*k / kBucketSlots][E] (integer adds, in any order).
 __global__ void __launch_bounds__(256)
 router_topk_kernel(const float* __restrict__ part, int ks_n, int T, int E, int k,
-                   int32_t* __restrict__ idx, float* __restrict__ w) {
+                   int32_t* __restrict__ idx, float* __restrict__ w, int32_t* __restrict__ bhist) {
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
     int32_t* ir = idx + (size_t)t * k;
     float* wr = w + (size_t)t * k;
+    int e;
     if (ks_n == 1) {
-        if (E <= 256) wave_topk<4, 1>(part, E, k, t, ir, wr);
-        else wave_topk<16, 1>(part, E, k, t, ir, wr);
+        if (E <= 256) e = wave_topk<4, 1>(part, E, k, t, ir, wr);
+        else e = wave_topk<16, 1>(part, E, k, t, ir, wr);
     } else if (ks_n == kRgSplit) {
-        if (E <= 256) wave_topk<4, kRgSplit>(part, E, k, t, ir, wr);
-        else wave_topk<16, kRgSplit>(part, E, k, t, ir, wr);
+        if (E <= 256) e = wave_topk<4, kRgSplit>(part, E, k, t, ir, wr);
+        else e = wave_topk<16, kRgSplit>(part, E, k, t, ir, wr);
     } else {
-        if (E <= 256) wave_topk<4, kRouterSplits>(part, E, k, t, ir, wr);
-        else wave_topk<16, kRouterSplits>(part, E, k, t, ir, wr);
+        if (E <= 256) e = wave_topk<4, kRouterSplits>(part, E, k, t, ir, wr);
+        else e = wave_topk<16, kRouterSplits>(part, E, k, t, ir, wr);
+    }
+    const int lane = threadIdx.x & 63;
+    if (bhist != nullptr && lane < k && (unsigned)e < (unsigned)E) {
+        const int s = t * k + lane;
+        atomicAdd(&bhist[(size_t)(s / kBucketSlots) * E + e], 1);
     }
 }
 
@@ -208,13 +219,19 @@ hipError_t launch_router_small(const moe_layer_desc& d, const float* x, int T, c
 
 hipError_t launch_router(const moe_layer_desc& d, const float* x, int T, int32_t* idx, float* w,
                          char* ws, const WsLayout& L, const Ctx& c) {
+    return launch_router_hist(d, x, T, idx, w, ws, L, c, nullptr);
+}
+
+hipError_t launch_router_hist(const moe_layer_desc& d, const float* x, int T, int32_t* idx,
+                              float* w, char* ws, const WsLayout& L, const Ctx& c,
+                              int32_t* bhist) {
     const int H = d.hidden, E = d.n_experts;
     float* part = reinterpret_cast<float*>(ws + L.router_part);
     if (T <= kRouterSmallMaxT) {
         hipError_t e = launch_router_small(d, x, T, ws, L, c);
         if (e != hipSuccess) return e;
         launch_k(c, MOE_K_ROUTER_TOPK, router_topk_kernel, dim3((T + 3) / 4), dim3(256), 0, part,
-                 L.router_ks, T, E, d.top_k, idx, w);
+                 L.router_ks, T, E, d.top_k, idx, w, (int32_t*)nullptr);
         return hipGetLastError();
     }
     _Float16* xh = reinterpret_cast<_Float16*>(ws + L.x16);
@@ -223,13 +240,14 @@ hipError_t launch_router(const moe_layer_desc& d, const float* x, int T, int32_t
     _Float16* wl = reinterpret_cast<_Float16*>(ws + L.w_lo);
     const size_t n8 = (size_t)T * H / 8;   // H is a multiple of 256
     const int nxb = (int)((n8 + 255) / 256), nwb = ((H + 31) / 32) * ((E + 31) / 32);
+    const size_t nzero = bhist ? (size_t)bucket_blocks(T, d.top_k) * E : 0;
     launch_k(c, MOE_K_X_F16, split_kernel, dim3(nxb + nwb), dim3(256), 0, x, xh, xl, n8, nxb,
-             d.router_w, H, E, wh, wl);
+             d.router_w, H, E, wh, wl, bhist, nzero);
     launch_k(c, MOE_K_ROUTER_MFMA, router_gemm_kernel,
              dim3((T + kRgT - 1) / kRgT, (E + kRgE - 1) / kRgE, kRgSplit), dim3(256), 0, xh, xl, wh,
              wl, T, H, E, part);
     launch_k(c, MOE_K_ROUTER_TOPK, router_topk_kernel, dim3((T + 3) / 4), dim3(256), 0, part,
-             kRgSplit, T, E, d.top_k, idx, w);
+             kRgSplit, T, E, d.top_k, idx, w, bhist);
     return hipGetLastError();
 }
 
@@ -239,7 +257,8 @@ hipError_t launch_x16(const float* x, int T, int H, char* ws, const WsLayout& L,
     const int nxb = (int)((n8 + 255) / 256);
     launch_k(c, MOE_K_X_F16, split_kernel, dim3(nxb), dim3(256), 0, x,
              reinterpret_cast<_Float16*>(ws + L.x16), (_Float16*)nullptr, n8, nxb,
-             (const float*)nullptr, H, 0, (_Float16*)nullptr, (_Float16*)nullptr);
+             (const float*)nullptr, H, 0, (_Float16*)nullptr, (_Float16*)nullptr,
+             (int32_t*)nullptr, (size_t)0);
     return hipGetLastError();
 }
 
