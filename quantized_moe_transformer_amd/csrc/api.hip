@@ -390,7 +390,9 @@ static int forward_common(const moe_layer_desc* desc, const float* x, int32_t T,
         int32_t* ridx = reinterpret_cast<int32_t*>(wsp + L.idx);
         float* rw = reinterpret_cast<float*>(wsp + L.w);
         // many slots: the top-k also makes the bucketing's per-block counts
-        int32_t* hb = bucket_self(T, desc->top_k, desc->n_experts)
+        // (only the matrix-core router's top-k can; the few-row router never
+        // meets this case, since T <= kRouterSmallMaxT slots bucket in one block)
+        int32_t* hb = (T <= kRouterSmallMaxT || bucket_self(T, desc->top_k, desc->n_experts))
                           ? nullptr
                           : reinterpret_cast<int32_t*>(wsp + L.bhist);
         if (launch_router_hist(*desc, x, T, ridx, rw, wsp, L, c, hb) != hipSuccess)
