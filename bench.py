@@ -892,7 +892,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}): "
-              "this build has no multi-GPU path; the layer's shards run on one device.",
+              "the library has no multi-GPU path; the layer's shards run on one device.",
               file=sys.stderr)
         sys.exit(2)
 
