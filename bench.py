@@ -446,7 +446,9 @@ def bench_sharded(args, torch, qm, mi, DeviceLayer, name, T, n_copies, n_batches
     if path == qm.MOE_PATH_MFMA:
         names = ["gemm_gateup", "gemm_down", "combine"]
     else:
-        names = ["gemv_front", "gateup_gemv", "down_gemv"]
+        # with the routing given, a shard call is two kernels (the gate/up
+        # kernel also runs the shared expert; no front kernel)
+        names = ["gateup_gemv", "down_gemv"]
     kst = {}
     kms = kernel_profile_calls(torch, lambda i, e: step(i, e), min(K, 16), 2, names, kst)
     kms_flat = {f"shard{c}.{n}": v for (c, n), v in kms.items()}
@@ -471,12 +473,12 @@ def bench_sharded(args, torch, qm, mi, DeviceLayer, name, T, n_copies, n_batches
                  "expert_mfma_frac": flops / (gemm_ms * 1e-3) / (FP16_MFMA_PEAK_TFLOPS * 1e12),
                  "step_mfma_frac": flops / dev_s / (FP16_MFMA_PEAK_TFLOPS * 1e12)}
     else:
-        # the whole step (router_topk, two shards of three kernels, the reduce):
+        # the whole step (router_topk, two shards of two kernels, the reduce):
         # eager per-kernel events of these many small calls run slow (the GPU
         # idles between the host's calls), so the step's own graph time is
         # the basis
         layer_bytes = (shp.k + 1) * (gu + dn) + shp.H * shp.E * 4 + 3 * T * shp.H * 4
-        rl = roofline("whole sharded step (router_topk + 2 x 3 shard kernels + reduce)", "hbm",
+        rl = roofline("whole sharded step (router_topk + 2 x 2 shard kernels + reduce)", "hbm",
                       layer_bytes, dev_s * 1e3, "GB/s", HBM_PEAK_GBS)
         whole = {"layer_algorithmic_bytes": layer_bytes,
                  "layer_hbm_frac": layer_bytes / dev_s / (HBM_PEAK_GBS * 1e9)}

@@ -9,7 +9,9 @@
 //
 //   front   the router's split-K partial logits (many small XCD-grouped
 //           workgroups) and, side by side in the same grid, the shared
-//           expert's gate/up + SwiGLU, which needs no routing;
+//           expert's gate/up + SwiGLU, which needs no routing (with the
+//           routing given, as in the shard calls, there is no router work
+//           and the gate/up kernel takes the shared expert: two kernels);
 //   gateup  the first wave of every workgroup sums its token's partial logits
 //           in a fixed order and runs the top-k up to the workgroup's slot
 //           (the same selection in every workgroup of the token), then all
@@ -316,6 +318,7 @@ struct GemvArgs {
     int n_router_blocks;  // front kernel: router workgroups (0: none)
     int shared_rows_blocks;
     int n_shared_pad;     // front kernel: shared workgroups rounded up to kXcds
+    int sh_in_gateup;     // the gate/up kernel also runs the shared expert (slot k)
     float* out;
 };
 
@@ -457,11 +460,27 @@ gemv_front_kernel(GemvArgs a) {
                                      a.hbuf + (size_t)p * a.hstride);
 }
 
-// routed experts: grid (row blocks, T*k)
-template <int FMT, int LPR, int NSBL>
+// routed experts: grid (row blocks, T*k); SH (routing known before the
+// layer starts, so no router work in a front kernel, which is then not
+// launched): T more rows of workgroups for the shared expert as slot k of
+// each token
+template <int FMT, int LPR, int NSBL, bool SH>
 __global__ void __launch_bounds__(64 * kGuWaves)
 gemv_gateup_kernel(GemvArgs a) {
     const int q = blockIdx.y;
+    if constexpr (SH) {
+        if (q >= a.T * a.k) {
+            const int t = q - a.T * a.k;
+            const int rbase = (blockIdx.x * kGuWaves + (threadIdx.x >> 6)) * kGuSteps * (64 / LPR);
+            if (rbase >= a.iloc) return;
+            XRegs<LPR, NSBL> X;
+            X.load(a.x + (size_t)t * a.H);
+            // the shared expert has the routed width
+            gateup_rows<FMT, LPR, NSBL, kGuSteps>(a.sh_gate, a.sh_up, a.H, a.iloc, a.i0, X, rbase,
+                                                  a.hbuf + (size_t)(t * a.nslot + a.k) * a.hstride);
+            return;
+        }
+    }
     const int t = q / a.k, j = q % a.k;
     XRegs<LPR, NSBL> X;
     X.load(a.x + (size_t)t * a.H);   // independent of the routing: in flight during the top-k
@@ -651,13 +670,24 @@ template <int LPR, int NSBL>
 static void launch_gateup_t(const GemvArgs& a, const Ctx& c) {
     constexpr int rows_per_block = kGuWaves * kGuSteps * (64 / LPR);
     const int Iloc = a.iloc;
-    const dim3 grid((Iloc + rows_per_block - 1) / rows_per_block, a.T * a.k);
-    if (a.fmt == MOE_WFMT_MXFP4)
-        launch_k(c, MOE_K_GATEUP_GEMV, gemv_gateup_kernel<MOE_WFMT_MXFP4, LPR, NSBL>, grid,
-                 dim3(64 * kGuWaves), 0, a);
-    else
-        launch_k(c, MOE_K_GATEUP_GEMV, gemv_gateup_kernel<MOE_WFMT_KQUANT, LPR, NSBL>, grid,
-                 dim3(64 * kGuWaves), 0, a);
+    const dim3 grid((Iloc + rows_per_block - 1) / rows_per_block,
+                    a.T * a.k + (a.sh_in_gateup ? a.T : 0));
+    const dim3 block(64 * kGuWaves);
+    if (a.fmt == MOE_WFMT_MXFP4) {
+        if (a.sh_in_gateup)
+            launch_k(c, MOE_K_GATEUP_GEMV, gemv_gateup_kernel<MOE_WFMT_MXFP4, LPR, NSBL, true>,
+                     grid, block, 0, a);
+        else
+            launch_k(c, MOE_K_GATEUP_GEMV, gemv_gateup_kernel<MOE_WFMT_MXFP4, LPR, NSBL, false>,
+                     grid, block, 0, a);
+    } else {
+        if (a.sh_in_gateup)
+            launch_k(c, MOE_K_GATEUP_GEMV, gemv_gateup_kernel<MOE_WFMT_KQUANT, LPR, NSBL, true>,
+                     grid, block, 0, a);
+        else
+            launch_k(c, MOE_K_GATEUP_GEMV, gemv_gateup_kernel<MOE_WFMT_KQUANT, LPR, NSBL, false>,
+                     grid, block, 0, a);
+    }
 }
 
 #define MOE_DISPATCH_H(nsb, F, ...)                                  \
@@ -724,7 +754,11 @@ hipError_t launch_gemv(const moe_layer_desc& d, const float* x, int T, const int
         idx = a.idx_out;
         w = a.w_out;
     }
-    hipError_t e = launch_front(a, fused_route, d.shared_inter > 0, L, ws, c);
+    // with the routing known before the layer starts (given, or from the
+    // matrix-core router), the front kernel would hold only the shared
+    // expert's gate/up: the gate/up kernel takes it instead, one launch fewer
+    a.sh_in_gateup = d.shared_inter > 0 && !fused_route;
+    hipError_t e = launch_front(a, fused_route, d.shared_inter > 0 && fused_route, L, ws, c);
     if (e != hipSuccess) return e;
     a.route = fused_route ? 1 : 0;
     a.idx = idx;
