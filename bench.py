@@ -58,18 +58,18 @@ MX_TERMS = 3                    # MX-FP8 terms per token / h value on the MXFP4 
 # --copy-probe).  Keyed by the SHA-256 of the kernel's sources: when they change,
 # the counters no longer describe the kernel and traffic is reported as null.
 TRAFFIC = {
-    # decode T=1, 280 dispatches: FETCH 4752.4 KiB x 1.99980, WRITE 16.1 KiB x 1.0
-    "gemv_gateup": {"sources_sha256": "0d97fa90250343edb0851470f840c2f7fad1df6c6f47a1ebf7db35fd7cf8336d",
-                    "fetch_bytes": 9731985, "write_bytes": 16448},
-    # prefill T=4096, 18 dispatches: FETCH 226264.3 KiB x 1.99980, WRITE 36864.0 KiB x 1.0
+    # decode T=1, 280 dispatches: FETCH 4746.8 KiB x 1.99980, WRITE 16.1 KiB x 1.0
+    "gemv_gateup": {"sources_sha256": "5a13c6ff1b7f971e528e04773b95369a322fb4955fe95e4f540f33f3d8bd9d04",
+                    "fetch_bytes": 9720504, "write_bytes": 16448},
+    # prefill T=4096, 18 dispatches: FETCH 226219.0 KiB x 1.99980, WRITE 36864.0 KiB x 1.0
     "gemm_gateup": {"sources_sha256": "c7eed0e92b6ee3f0a0e6404fd3eb660b0b6ca8202873215bfdddb71dbc672a2d",
-                    "fetch_bytes": 463342930, "write_bytes": 37748736},
-    # MXFP4 decode T=1, 280 dispatches: FETCH 4756.6 KiB x 1.99980, WRITE 16.1 KiB x 1.0
-    "gemv_gateup_mx": {"sources_sha256": "0d97fa90250343edb0851470f840c2f7fad1df6c6f47a1ebf7db35fd7cf8336d",
-                    "fetch_bytes": 9740449, "write_bytes": 16448},
-    # MXFP4 prefill T=4096, 18 dispatches: FETCH 273400.5 KiB x 1.99980, WRITE 59906.8 KiB x 1.0
+                    "fetch_bytes": 463250154, "write_bytes": 37748736},
+    # MXFP4 decode T=1, 280 dispatches: FETCH 4756.5 KiB x 1.99980, WRITE 16.1 KiB x 1.0
+    "gemv_gateup_mx": {"sources_sha256": "5a13c6ff1b7f971e528e04773b95369a322fb4955fe95e4f540f33f3d8bd9d04",
+                    "fetch_bytes": 9740267, "write_bytes": 16448},
+    # MXFP4 prefill T=4096, 18 dispatches: FETCH 273324.5 KiB x 1.99980, WRITE 59904.6 KiB x 1.0
     "gemm_gateup_mx": {"sources_sha256": "191ec354f43f753bd83cb046438076d6b66c65bf3538ba930548a82810dbc029",
-                    "fetch_bytes": 559868253, "write_bytes": 61344533},
+                    "fetch_bytes": 559712642, "write_bytes": 61342299},
 }
 FETCH_SIZE_FACTOR = 1.99980   # plain 256 MiB copy: true bytes read / FETCH_SIZE bytes
 WRITE_SIZE_FACTOR = 1.0
@@ -96,9 +96,9 @@ def sources_sha(kernel):
 # GRBM_GUI_ACTIVE / 8 XCDs); executed_flops = MOPS x 512 (padded rows included).
 MFMA_COUNTERS = {
     "gemm_gateup": {"sources_sha256": "c7eed0e92b6ee3f0a0e6404fd3eb660b0b6ca8202873215bfdddb71dbc672a2d",
-                    "mfma_busy": 0.3368, "executed_flops": 1.71262e+11},
+                    "mfma_busy": 0.3358, "executed_flops": 1.71262e+11},
     "gemm_gateup_mx": {"sources_sha256": "191ec354f43f753bd83cb046438076d6b66c65bf3538ba930548a82810dbc029",
-                    "mfma_busy": 0.3863, "executed_flops": 5.11772e+11},
+                    "mfma_busy": 0.3835, "executed_flops": 5.11772e+11},
 }
 
 
@@ -313,7 +313,7 @@ def bench_decode(args, torch, qm, mi, DeviceLayer, name="decode"):
         "layer_hbm_frac_graph": layer_bytes / dev_s / (HBM_PEAK_GBS * 1e9),
         "layer_hbm_frac_kernels": layer_bytes / (sum(kms.values()) * 1e-3) / (HBM_PEAK_GBS * 1e9),
         "roofline": roofline(
-            "gemv_gateup_kernel<%s,64,1> (8 routed experts)" % ("MXFP4" if shp.fmt else "K-quant"),
+            "gemv_gateup_kernel<%s,64,1,false> (8 routed experts)" % ("MXFP4" if shp.fmt else "K-quant"),
             "hbm", gateup_bytes, kms["gateup_gemv"], "GB/s", HBM_PEAK_GBS,
             traffic_for("gemv_gateup_mx" if shp.fmt else "gemv_gateup"),
             {"median_launch_ms": kst["gateup_gemv"]["median_ms"],
