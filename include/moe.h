@@ -161,7 +161,9 @@ typedef struct moe_opts {
 } moe_opts;
 
 /* Kernel ids for moe_opts.kernel_events. */
-#define MOE_K_GEMV_FRONT 0       /* T <= 32: router partial logits; shared-expert gate/up */
+#define MOE_K_GEMV_FRONT 0       /* T <= 32: router partial logits; with them (GEMV path) the
+                                    shared-expert gate/up, which the gate/up kernel takes
+                                    when the routing is given */
 #define MOE_K_ROUTER_MFMA 1      /* T > 32: router logits on the matrix cores (split fp16, fp32-accurate) */
 #define MOE_K_ROUTER_TOPK 2      /* top-k + weights */
 #define MOE_K_GATEUP_GEMV 3      /* decode: top-k (when routing) + routed gate/up + SwiGLU */
