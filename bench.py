@@ -880,6 +880,9 @@ def main():
     ap.add_argument("--continuum", action="store_true",
                     help="only time both paths at T = 1 .. 512 (one JSON line per point)")
     ap.add_argument("--continuum-t", type=int, nargs="+", default=list(CONTINUUM_T))
+    ap.add_argument("--sharded-decode-streams", type=int, default=1, choices=[1, 2],
+                    help="C2 sharded decode: the two shard calls in order on one stream (1) or "
+                         "on two streams (2)")
     ap.add_argument("--continuum-fmt", type=int, default=0, choices=[0, 1],
                     help="expert weight format of the continuum: 0 K-quant, 1 MXFP4")
     ap.add_argument("--only", nargs="+", default=None, metavar="WORKLOAD",
@@ -932,10 +935,12 @@ def main():
         c2s, checks["C2_sharded_T1"] = bench_sharded(
         args, torch, qm, mi, DeviceLayer, "decode_sharded", 1, args.copies, 64, args.steps,
         args.warmup, "sharded decode T=1: the same layer (seed 2), router_topk once, the 256/256 "
-        "shards as two moe_layer_forward_shard calls in order on one stream (two streams "
-        "measured slower at T=1), moe_reduce_partials; 64-token pool, "
+        "shards as two moe_layer_forward_shard calls "
+        + ("in order on one stream (two streams measured slower at T=1)"
+           if args.sharded_decode_streams == 1 else "on two streams")
+        + ", moe_reduce_partials; 64-token pool, "
         f"{args.copies} rotating weight copies, HIP graph of exactly `steps` steps", 64,
-        two_streams=False)
+        two_streams=args.sharded_decode_streams == 2)
     if want("batched_decode"):
         say("C2 batched decode T=32 ...")
         c2b, checks["C2_batched_T32"] = bench_layer_batches(
