@@ -179,8 +179,7 @@ struct TileInfo {
 // Producers: (straight-line
 // code: the fragment reads of a 16-wide K slice are issued before its MFMAs).
 template <int MODE, int MB>
-__device__ __forceinline__ void gemm_produce(const GemmArgs& a, const TileInfo& ti, GemmLds& lds,
-                                          const int32_t* row_src, const float* row_w) {
+__device__ __forceinline__ void gemm_produce(const GemmArgs& a, const TileInfo& ti, GemmLds& lds) {
     constexpr int DSB = kQ5Bytes;   // bytes of a down superblock
     constexpr int kPD = PrefetchDistance<MODE>::v;
     const int tid = threadIdx.x;
@@ -367,7 +366,6 @@ __device__ __forceinline__ void gemm_produce(const GemmArgs& a, const TileInfo& 
 // Consumers: token rows into LDS, MFMAs into acc.
 template <int MODE, int MB>
 __device__ __forceinline__ void gemm_consume(const GemmArgs& a, const TileInfo& ti, GemmLds& lds,
-                                          const int32_t* row_src, const float* row_w,
                                              float16v (&acc)[MB][2]) {
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
@@ -534,9 +532,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileInfo& ti,
         acc[i][1] = float16v{};
     }
     if (threadIdx.x >> 6 >= kConsumers)
-        gemm_produce<MODE, MB>(a, ti, lds, row_src, row_w);
+        gemm_produce<MODE, MB>(a, ti, lds);
     else
-        gemm_consume<MODE, MB>(a, ti, lds, row_src, row_w, acc);
+        gemm_consume<MODE, MB>(a, ti, lds, acc);
     gemm_epilogue<MODE, MB>(a, ti, lds, row_src, row_w, acc);
 }
 

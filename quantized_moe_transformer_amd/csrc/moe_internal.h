@@ -267,19 +267,22 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 // against LDS reads of other stages with waits of its own; the caller waits
 // for these loads (wait_vmcnt) before any wave reads what they wrote.  Extra
 // loads in the counter only make the compiler's own vmcnt waits stricter.
+// The LDS address goes through m0, declared as an output of the asm (not a
+// clobber of a reserved register), so that the compiler keeps any value of
+// its own out of m0 across it.
 __device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_off) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                 :
-                 : "v"(gptr), "s"(lds_off)
-                 : "m0");
+    uint32_t m0v;
+    asm volatile("s_mov_b32 %0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                 : "={m0}"(m0v)
+                 : "v"(gptr), "s"(lds_off));
 }
 
 // The same with one dword per lane: lane l's 4 bytes land at lds_off + 4 l.
 __device__ __forceinline__ void lds_dma4(const void* gptr, uint32_t lds_off) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
-                 :
-                 : "v"(gptr), "s"(lds_off)
-                 : "m0");
+    uint32_t m0v;
+    asm volatile("s_mov_b32 %0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+                 : "={m0}"(m0v)
+                 : "v"(gptr), "s"(lds_off));
 }
 
 // s_waitcnt with only the vector-memory count bounded (<= 63)
