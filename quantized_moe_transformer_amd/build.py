@@ -19,6 +19,9 @@ FLAGS = [
     "-Wall", "-Wno-unused-function",
     # never emit packed fp32 arithmetic (v_pk_{add,mul,fma}_f32)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # leading scalar kernel arguments arrive preloaded in registers (kernels
+    # whose first argument is a struct are unaffected)
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
 ]
 
 

@@ -529,25 +529,41 @@ gemv_gateup_kernel(GemvArgs a) {
 constexpr int kDnPasses = 2;   // row passes per wave in the down kernel
 
 // Block: one wave per slot (nw = min(nslot, 16) waves, slot j on wave j % nw),
-// kDnPasses * (64 / lprd) output rows of one token.  A row's I_loc inputs are
-// I_loc / 32 lane tasks of 32 (a 16-byte code piece each); lprd, the lanes per
+// kDnPasses * (64 / LPRD) output rows of one token.  A row's I_loc inputs are
+// I_loc / 32 lane tasks of 32 (a 16-byte code piece each); LPRD, the lanes per
 // row, is that count rounded up to a power of two, the extra lanes adding 0.
-template <int FMT>
+// The routing and h pointers and the counts their addresses need come first
+// as scalar arguments, which the hardware preloads into registers: a wave's
+// first loads (the slot's expert and weight, its h) then wait for no
+// kernel-argument load.
+template <int FMT, int LPRD>
 __global__ void __launch_bounds__(1024)
-gemv_down_kernel(GemvArgs a, int lprd) {
+gemv_down_kernel(const int32_t* __restrict__ idx, const float* __restrict__ wts,
+                 const float* __restrict__ hbuf, int k, int nslot, int hstride, int iloc,
+                 GemvArgs a) {
     constexpr int SBB = FMT == MOE_WFMT_MXFP4 ? kMxBytes : kQ5Bytes;
+    constexpr int rs = 64 / LPRD;                 // rows per pass
     __shared__ float ys[17][kDnPasses * 64];
     __shared__ float s_wt[17];   // each slot's weight (0 for an invalid expert)
     const int t = blockIdx.y;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int nw = blockDim.x >> 6;
-    const int rs = 64 / lprd;                     // rows per pass
-    const int rslot = lane / lprd, task = lane % lprd;
-    const bool active = task < (a.iloc >> 5);
+    const int nw = nslot < 16 ? nslot : 16;       // the launch's waves (no argument load)
+    const int rslot = lane / LPRD, task = lane % LPRD;
+    const bool active = task < (iloc >> 5);
     const int cg = active ? task >> 1 : 0, hh = task & 1;
     const int obase = blockIdx.x * kDnPasses * rs;
     const int H = a.H;
-    for (int jv = wave; jv < a.nslot; jv += nw) {
+    // the routing reads of the wave's first slot go out first of all, from
+    // preloaded arguments only, so that they and the loads of the other
+    // arguments take one round trip together
+    const int jf = __builtin_amdgcn_readfirstlane(wave);
+    int ef = 0;
+    float wf = 0.f;
+    if (jf < k) {
+        ef = scalar_read(idx + (size_t)t * k + jf);
+        wf = scalar_read(wts + (size_t)t * k + jf);
+    }
+    for (int jv = wave; jv < nslot; jv += nw) {
         const int j = __builtin_amdgcn_readfirstlane(jv);   // wave-uniform
         // the routing reads first, then h (it does not depend on the
         // routing): the wait for the expert index covers only the routing
@@ -555,18 +571,23 @@ gemv_down_kernel(GemvArgs a, int lprd) {
         // issue order); the weight loads follow
         int e = 0;
         float wj = a.sw;
-        if (j < a.k) {
-            e = scalar_read(a.idx + (size_t)t * a.k + j);
-            wj = scalar_read(a.w + (size_t)t * a.k + j);
+        if (j < k) {
+            if (j == jf) {
+                e = ef;
+                wj = wf;
+            } else {
+                e = scalar_read(idx + (size_t)t * k + j);
+                wj = scalar_read(wts + (size_t)t * k + j);
+            }
         }
-        const float* hp = a.hbuf + (size_t)(t * a.nslot + j) * a.hstride + 64 * cg + 16 * hh;
+        const float* hp = hbuf + (size_t)(t * nslot + j) * hstride + 64 * cg + 16 * hh;
         float hl[16], hu[16];
         load16(hp, hl);
         load16(hp + 32, hu);
         const uint8_t* D;
         int Iexp;
         bool valid = true;
-        if (j < a.k) {
+        if (j < k) {
             valid = (unsigned)e < (unsigned)a.E;
             D = a.down + (size_t)(valid ? e : 0) * ((size_t)H * a.I / kSbWeights * SBB);
             Iexp = a.I;
@@ -605,7 +626,7 @@ gemv_down_kernel(GemvArgs a, int lprd) {
         for (int ps = 0; ps < kDnPasses; ++ps) {
             const float part =
                 active ? piece_dot_f<FMT, true>(hd[ps], qs[ps], qh[ps], cc[ps], hl, hu, sa, sb2) : 0.f;
-            const float y = wave_sum_group(part, lprd);
+            const float y = wave_sum_group(part, LPRD);
             if (task == 0) ys[j][ps * rs + rslot] = valid ? y : 0.f;
         }
     }
@@ -615,7 +636,7 @@ gemv_down_kernel(GemvArgs a, int lprd) {
         const int o = obase + r;
         if (o < H) {
             float acc = 0.f;
-            for (int j = 0; j < a.nslot; ++j) acc = __builtin_fmaf(s_wt[j], ys[j][r], acc);
+            for (int j = 0; j < nslot; ++j) acc = __builtin_fmaf(s_wt[j], ys[j][r], acc);
             a.out[(size_t)t * H + o] = acc;
         }
     }
@@ -733,6 +754,20 @@ hipError_t launch_router_small(const moe_layer_desc& d, const float* x, int T, c
 hipError_t launch_router(const moe_layer_desc& d, const float* x, int T, int32_t* idx, float* w,
                          char* ws, const WsLayout& L, const Ctx& c);   // router.hip
 
+template <int LPRD>
+static hipError_t launch_down_t(const GemvArgs& a, int T, const Ctx& c) {
+    constexpr int rows_per_block = kDnPasses * (64 / LPRD);
+    const int nw = a.nslot < 16 ? a.nslot : 16;
+    const dim3 grid2((a.H + rows_per_block - 1) / rows_per_block, T);
+    if (a.fmt == MOE_WFMT_MXFP4)
+        launch_k(c, MOE_K_DOWN_GEMV, gemv_down_kernel<MOE_WFMT_MXFP4, LPRD>, grid2, dim3(64 * nw),
+                 0, a.idx, a.w, a.hbuf, a.k, a.nslot, a.hstride, a.iloc, a);
+    else
+        launch_k(c, MOE_K_DOWN_GEMV, gemv_down_kernel<MOE_WFMT_KQUANT, LPRD>, grid2, dim3(64 * nw),
+                 0, a.idx, a.w, a.hbuf, a.k, a.nslot, a.hstride, a.iloc, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_gemv(const moe_layer_desc& d, const float* x, int T, const int32_t* idx,
                        const float* w, int i0, int iloc, float* out, char* ws,
                        const WsLayout& L, const Ctx& c, bool route) {
@@ -767,14 +802,15 @@ hipError_t launch_gemv(const moe_layer_desc& d, const float* x, int T, const int
     MOE_DISPATCH_H(nsb, launch_gateup_t, a, c);
     int lprd = 2;   // lanes per down row: Iloc / 32 rounded up to a power of two
     while (lprd < Iloc / 32) lprd *= 2;
-    const int rows_per_block = kDnPasses * (64 / lprd);
-    const int nw = a.nslot < 16 ? a.nslot : 16;
-    const dim3 grid2((d.hidden + rows_per_block - 1) / rows_per_block, T);
-    if (a.fmt == MOE_WFMT_MXFP4)
-        launch_k(c, MOE_K_DOWN_GEMV, gemv_down_kernel<MOE_WFMT_MXFP4>, grid2, dim3(64 * nw), 0, a, lprd);
-    else
-        launch_k(c, MOE_K_DOWN_GEMV, gemv_down_kernel<MOE_WFMT_KQUANT>, grid2, dim3(64 * nw), 0, a, lprd);
-    return hipGetLastError();
+    switch (lprd) {
+        case 2: return launch_down_t<2>(a, T, c);
+        case 4: return launch_down_t<4>(a, T, c);
+        case 8: return launch_down_t<8>(a, T, c);
+        case 16: return launch_down_t<16>(a, T, c);
+        case 32: return launch_down_t<32>(a, T, c);
+        case 64: return launch_down_t<64>(a, T, c);
+        default: return hipErrorInvalidValue;   // Iloc > 2048 (not on this path)
+    }
 }
 
 }  // namespace moe
