@@ -464,28 +464,34 @@ gemv_front_kernel(GemvArgs a) {
 // layer starts, so no router work in a front kernel, which is then not
 // launched): T more rows of workgroups for the shared expert as slot k of
 // each token
+// The pointers and counts that the first loads (activations, partial logits
+// or the given routing) need come first as scalar arguments, which the
+// hardware preloads into registers: those loads wait for no kernel-argument
+// load.
 template <int FMT, int LPR, int NSBL, bool SH>
 __global__ void __launch_bounds__(64 * kGuWaves)
-gemv_gateup_kernel(GemvArgs a) {
+gemv_gateup_kernel(const float* __restrict__ x, const float* __restrict__ part,
+                   const int32_t* __restrict__ idx, int k, int E, int H, int route, int T,
+                   GemvArgs a) {
     const int q = blockIdx.y;
     if constexpr (SH) {
-        if (q >= a.T * a.k) {
-            const int t = q - a.T * a.k;
+        if (q >= T * k) {
+            const int t = q - T * k;
             const int rbase = (blockIdx.x * kGuWaves + (threadIdx.x >> 6)) * kGuSteps * (64 / LPR);
             if (rbase >= a.iloc) return;
             XRegs<LPR, NSBL> X;
-            X.load(a.x + (size_t)t * a.H);
+            X.load(x + (size_t)t * H);
             // the shared expert has the routed width
-            gateup_rows<FMT, LPR, NSBL, kGuSteps>(a.sh_gate, a.sh_up, a.H, a.iloc, a.i0, X, rbase,
-                                                  a.hbuf + (size_t)(t * a.nslot + a.k) * a.hstride);
+            gateup_rows<FMT, LPR, NSBL, kGuSteps>(a.sh_gate, a.sh_up, H, a.iloc, a.i0, X, rbase,
+                                                  a.hbuf + (size_t)(t * a.nslot + k) * a.hstride);
             return;
         }
     }
-    const int t = q / a.k, j = q % a.k;
+    const int t = q / k, j = q % k;
     XRegs<LPR, NSBL> X;
-    X.load(a.x + (size_t)t * a.H);   // independent of the routing: in flight during the top-k
+    X.load(x + (size_t)t * H);   // independent of the routing: in flight during the top-k
     int e;
-    if (a.route) {
+    if (route) {
         // the first wave selects (stopping at slot j, whose expert lane j
         // holds) and hands the expert to the others through LDS; the first
         // wave of workgroup (0, t*k) fills all k slots and writes the
@@ -493,14 +499,14 @@ gemv_gateup_kernel(GemvArgs a) {
         __shared__ int s_e;
         if (threadIdx.x < 64) {
             if (blockIdx.x == 0 && j == 0) {
-                const int my_e = wave_topk<4, kRouterSplits>(a.part, a.E, a.k, t,
-                                                             a.idx_out + (size_t)t * a.k,
-                                                             a.w_out + (size_t)t * a.k);   // E <= 256
+                const int my_e = wave_topk<4, kRouterSplits>(part, E, k, t,
+                                                             a.idx_out + (size_t)t * k,
+                                                             a.w_out + (size_t)t * k);   // E <= 256
                 e = __builtin_amdgcn_readfirstlane(my_e);
             } else {
                 float my_l, top;
                 int my_e;
-                wave_topk_select<4, kRouterSplits>(a.part, a.E, j + 1, t, my_l, my_e, top);
+                wave_topk_select<4, kRouterSplits>(part, E, j + 1, t, my_l, my_e, top);
                 e = __builtin_amdgcn_readlane(my_e, j);
             }
             if (threadIdx.x == 0) s_e = e;
@@ -508,17 +514,17 @@ gemv_gateup_kernel(GemvArgs a) {
         __syncthreads();
         e = s_e;
     } else {
-        e = a.idx[(size_t)t * a.k + j];
+        e = idx[(size_t)t * k + j];
     }
-    if ((unsigned)e >= (unsigned)a.E) return;
-    const size_t mat = (size_t)a.I * a.H / kSbWeights * kQ4Bytes;   // MXFP4: the same size
+    if ((unsigned)e >= (unsigned)E) return;
+    const size_t mat = (size_t)a.I * H / kSbWeights * kQ4Bytes;   // MXFP4: the same size
     const int Iloc = a.iloc, i0 = a.i0;
     const int wave = threadIdx.x >> 6;
     constexpr int rows_per_wave = kGuSteps * (64 / LPR);
     const int rbase = (blockIdx.x * kGuWaves + wave) * rows_per_wave;
     if (rbase >= Iloc) return;
     const int p = t * a.nslot + j;
-    gateup_rows<FMT, LPR, NSBL, kGuSteps>(a.gate + (size_t)e * mat, a.up + (size_t)e * mat, a.H, Iloc,
+    gateup_rows<FMT, LPR, NSBL, kGuSteps>(a.gate + (size_t)e * mat, a.up + (size_t)e * mat, H, Iloc,
                                      i0, X, rbase, a.hbuf + (size_t)p * a.hstride);
 }
 
@@ -694,21 +700,17 @@ static void launch_gateup_t(const GemvArgs& a, const Ctx& c) {
     const dim3 grid((Iloc + rows_per_block - 1) / rows_per_block,
                     a.T * a.k + (a.sh_in_gateup ? a.T : 0));
     const dim3 block(64 * kGuWaves);
+#define MOE_GATEUP(F, S)                                                                        \
+    launch_k(c, MOE_K_GATEUP_GEMV, gemv_gateup_kernel<F, LPR, NSBL, S>, grid, block, 0, a.x,    \
+             (const float*)a.part, a.idx, a.k, a.E, a.H, a.route, a.T, a)
     if (a.fmt == MOE_WFMT_MXFP4) {
-        if (a.sh_in_gateup)
-            launch_k(c, MOE_K_GATEUP_GEMV, gemv_gateup_kernel<MOE_WFMT_MXFP4, LPR, NSBL, true>,
-                     grid, block, 0, a);
-        else
-            launch_k(c, MOE_K_GATEUP_GEMV, gemv_gateup_kernel<MOE_WFMT_MXFP4, LPR, NSBL, false>,
-                     grid, block, 0, a);
+        if (a.sh_in_gateup) MOE_GATEUP(MOE_WFMT_MXFP4, true);
+        else MOE_GATEUP(MOE_WFMT_MXFP4, false);
     } else {
-        if (a.sh_in_gateup)
-            launch_k(c, MOE_K_GATEUP_GEMV, gemv_gateup_kernel<MOE_WFMT_KQUANT, LPR, NSBL, true>,
-                     grid, block, 0, a);
-        else
-            launch_k(c, MOE_K_GATEUP_GEMV, gemv_gateup_kernel<MOE_WFMT_KQUANT, LPR, NSBL, false>,
-                     grid, block, 0, a);
+        if (a.sh_in_gateup) MOE_GATEUP(MOE_WFMT_KQUANT, true);
+        else MOE_GATEUP(MOE_WFMT_KQUANT, false);
     }
+#undef MOE_GATEUP
 }
 
 #define MOE_DISPATCH_H(nsb, F, ...)                                  \
