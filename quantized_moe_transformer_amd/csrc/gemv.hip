@@ -348,7 +348,8 @@ __host__ __device__ inline int router_blocks_per_tile(int E) {
 // g = tid / 2: rows g, g + G, ... of the split.  Each wave sums its 32 row
 // groups across its lanes, the four waves are added in LDS, in a fixed order.
 template <int TT, int NSB>
-__device__ __forceinline__ void router_role(const GemvArgs& a, int rb) {
+__device__ __forceinline__ void router_role(const GemvArgs& a, int rb, const float* router_w,
+                                            const float* x, int E, int H, int T) {
     constexpr int KS = kRouterSplits;
     static_assert(KS == kXcds, "one K split per XCD slot in the workgroup mapping");
     constexpr int ROWS = 32 * NSB;
@@ -356,7 +357,7 @@ __device__ __forceinline__ void router_role(const GemvArgs& a, int rb) {
     constexpr int RPT = ROWS / G;                // rows per thread
     __shared__ float xs[TT][ROWS];
     __shared__ float red[4][TT][kRtE];
-    const int nb = router_blocks_per_tile(a.E);
+    const int nb = router_blocks_per_tile(E);
     const int tb = rb / nb;
     const int u = rb % nb;
     const int w = u / kXcds;                     // index among the workgroups of its XCD
@@ -364,9 +365,9 @@ __device__ __forceinline__ void router_role(const GemvArgs& a, int rb) {
     const int pair = (w / (kRtLine / kRtE)) * kXcds + u % kXcds;   // (line group, split)
     const int ks = pair % KS;
     const int ec = (pair / KS) * (kRtLine / kRtE) + quarter;
-    if (ec * kRtE >= a.E) return;                // a quarter past the last expert
+    if (ec * kRtE >= E) return;                // a quarter past the last expert
     const int t0 = tb * TT;
-    const int nt = min(TT, a.T - t0);
+    const int nt = min(TT, T - t0);
     const int h0 = ks * ROWS;
     const int tid = threadIdx.x;
     const int q = tid & 1, g = tid >> 1;
@@ -378,11 +379,11 @@ __device__ __forceinline__ void router_role(const GemvArgs& a, int rb) {
         for (int r = 0; r < RPT; ++r)
 #pragma unroll
             for (int c = 0; c < 4; ++c) wv[r][c] = 0.f;
-    } else if ((a.E & 3) == 0 && e0 + 3 < a.E) {
+    } else if ((E & 3) == 0 && e0 + 3 < E) {
 #pragma unroll
         for (int r = 0; r < RPT; ++r) {
             const float4 f =
-                *reinterpret_cast<const float4*>(a.router_w + (size_t)(h0 + g + G * r) * a.E + e0);
+                *reinterpret_cast<const float4*>(router_w + (size_t)(h0 + g + G * r) * E + e0);
             wv[r][0] = f.x;
             wv[r][1] = f.y;
             wv[r][2] = f.z;
@@ -393,11 +394,11 @@ __device__ __forceinline__ void router_role(const GemvArgs& a, int rb) {
         for (int r = 0; r < RPT; ++r)
 #pragma unroll
             for (int c = 0; c < 4; ++c)
-                wv[r][c] = a.router_w[(size_t)(h0 + g + G * r) * a.E + min(e0 + c, a.E - 1)];
+                wv[r][c] = router_w[(size_t)(h0 + g + G * r) * E + min(e0 + c, E - 1)];
     }
     for (int i = tid; i < TT * ROWS; i += blockDim.x) {
         const int tt = i / ROWS, hh = i % ROWS;
-        xs[tt][hh] = tt < nt ? a.x[(size_t)(t0 + tt) * a.H + h0 + hh] : 0.f;
+        xs[tt][hh] = tt < nt ? x[(size_t)(t0 + tt) * H + h0 + hh] : 0.f;
     }
     __syncthreads();
     const int lane = tid & 63, wave = tid >> 6;
@@ -426,38 +427,42 @@ __device__ __forceinline__ void router_role(const GemvArgs& a, int rb) {
     if (tid < TT * kRtE) {
         const int tt = tid / kRtE, ee = tid % kRtE;
         const int eg = ec * kRtE + ee;
-        if (tt < nt && eg < a.E)
-            a.part[((size_t)(t0 + tt) * a.E + eg) * KS + ks] =
+        if (tt < nt && eg < E)
+            a.part[((size_t)(t0 + tt) * E + eg) * KS + ks] =
                 ((red[0][tt][ee] + red[1][tt][ee]) + red[2][tt][ee]) + red[3][tt][ee];
     }
 }
 
+// The pointers and counts that the first loads need come first as scalar
+// arguments, which the hardware preloads into registers.  The shared expert
+// runs here only when the layer routes its own rows (the whole layer, so its
+// rows start at 0).
 template <int FMT, int LPR, int NSBL, int TT>
 __global__ void __launch_bounds__(256)
-gemv_front_kernel(GemvArgs a) {
+gemv_front_kernel(const float* __restrict__ router_w, const float* __restrict__ x,
+                  const uint8_t* __restrict__ sh_gate, const uint8_t* __restrict__ sh_up, int E,
+                  int H, int T, int n_shared_pad, int shared_rows_blocks, int iloc, GemvArgs a) {
     // shared-expert workgroups first (each starts on a CU of its own), then
     // the router's, from a multiple of kXcds on
     const int b = blockIdx.x;
-    if (b >= a.n_shared_pad) {
-        router_role<TT, (LPR / 8) * NSBL>(a, b - a.n_shared_pad);
+    if (b >= n_shared_pad) {
+        router_role<TT, (LPR / 8) * NSBL>(a, b - n_shared_pad, router_w, x, E, H, T);
         return;
     }
     // shared expert: blocks per token = shared_rows_blocks, kShWaves waves each
     const int sb = b;
-    if (sb >= a.shared_rows_blocks * a.T) return;   // padding
-    const int t = sb / a.shared_rows_blocks;
-    const int rblk = sb % a.shared_rows_blocks;
-    const int Iloc = a.iloc, i0 = a.i0;   // the shared expert has the routed width
+    if (sb >= shared_rows_blocks * T) return;   // padding
+    const int t = sb / shared_rows_blocks;
+    const int rblk = sb % shared_rows_blocks;
     const int wave = threadIdx.x >> 6;
     if (wave >= kShWaves) return;
     constexpr int rows_per_wave = kShSteps * (64 / LPR);
     const int rbase = (rblk * kShWaves + wave) * rows_per_wave;
-    if (rbase >= Iloc) return;
-    const int p = t * a.nslot + a.k;
+    if (rbase >= iloc) return;   // the shared expert has the routed width
     XRegs<LPR, NSBL> X;
-    X.load(a.x + (size_t)t * a.H);
-    gateup_rows<FMT, LPR, NSBL, kShSteps>(a.sh_gate, a.sh_up, a.H, Iloc, i0, X, rbase,
-                                     a.hbuf + (size_t)p * a.hstride);
+    X.load(x + (size_t)t * H);
+    gateup_rows<FMT, LPR, NSBL, kShSteps>(sh_gate, sh_up, H, iloc, 0, X, rbase,
+                                          a.hbuf + (size_t)(t * a.nslot + a.k) * a.hstride);
 }
 
 // routed experts: grid (row blocks, T*k); SH (routing known before the
@@ -680,9 +685,13 @@ template <int FMT, int LPR, int NSBL>
 static void launch_front_f(const GemvArgs& a, int n_shared_blocks, const Ctx& c) {
     const dim3 grid(a.n_router_blocks + n_shared_blocks);
     if (a.T == 1)
-        launch_k(c, MOE_K_GEMV_FRONT, gemv_front_kernel<FMT, LPR, NSBL, 1>, grid, dim3(256), 0, a);
+        launch_k(c, MOE_K_GEMV_FRONT, gemv_front_kernel<FMT, LPR, NSBL, 1>, grid, dim3(256), 0,
+                 a.router_w, a.x, a.sh_gate, a.sh_up, a.E, a.H, a.T, a.n_shared_pad,
+                 a.shared_rows_blocks, a.iloc, a);
     else
-        launch_k(c, MOE_K_GEMV_FRONT, gemv_front_kernel<FMT, LPR, NSBL, 4>, grid, dim3(256), 0, a);
+        launch_k(c, MOE_K_GEMV_FRONT, gemv_front_kernel<FMT, LPR, NSBL, 4>, grid, dim3(256), 0,
+                 a.router_w, a.x, a.sh_gate, a.sh_up, a.E, a.H, a.T, a.n_shared_pad,
+                 a.shared_rows_blocks, a.iloc, a);
 }
 
 template <int LPR, int NSBL>
@@ -733,6 +742,9 @@ static hipError_t launch_front(GemvArgs& a, bool route, bool shared, const WsLay
     const int TT = a.T == 1 ? 1 : 4;
     a.n_router_blocks = route ? ((a.T + TT - 1) / TT) * router_blocks_per_tile(a.E) : 0;
     int n_shared = 0;
+    // the front kernel's shared role takes rows from 0 (it runs for the whole
+    // layer only; shard calls give their routing and use the gate/up kernel)
+    if (shared && a.i0 != 0) return hipErrorInvalidValue;
     if (shared) {
         const int rows_per_block = kShWaves * kShSteps * (64 / lanes_per_row(nsb));
         const int Iloc = a.iloc;
