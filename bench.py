@@ -58,18 +58,18 @@ MX_TERMS = 3                    # MX-FP8 terms per token / h value on the MXFP4 
 # --copy-probe).  Keyed by the SHA-256 of the kernel's sources: when they change,
 # the counters no longer describe the kernel and traffic is reported as null.
 TRAFFIC = {
-    # decode T=1, 280 dispatches: FETCH 4746.8 KiB x 1.99980, WRITE 16.1 KiB x 1.0
-    "gemv_gateup": {"sources_sha256": "5a13c6ff1b7f971e528e04773b95369a322fb4955fe95e4f540f33f3d8bd9d04",
-                    "fetch_bytes": 9720504, "write_bytes": 16448},
-    # prefill T=4096, 18 dispatches: FETCH 226219.0 KiB x 1.99980, WRITE 36864.0 KiB x 1.0
-    "gemm_gateup": {"sources_sha256": "c7eed0e92b6ee3f0a0e6404fd3eb660b0b6ca8202873215bfdddb71dbc672a2d",
-                    "fetch_bytes": 463250154, "write_bytes": 37748736},
-    # MXFP4 decode T=1, 280 dispatches: FETCH 4756.5 KiB x 1.99980, WRITE 16.1 KiB x 1.0
-    "gemv_gateup_mx": {"sources_sha256": "5a13c6ff1b7f971e528e04773b95369a322fb4955fe95e4f540f33f3d8bd9d04",
-                    "fetch_bytes": 9740267, "write_bytes": 16448},
-    # MXFP4 prefill T=4096, 18 dispatches: FETCH 273324.5 KiB x 1.99980, WRITE 59904.6 KiB x 1.0
-    "gemm_gateup_mx": {"sources_sha256": "191ec354f43f753bd83cb046438076d6b66c65bf3538ba930548a82810dbc029",
-                    "fetch_bytes": 559712642, "write_bytes": 61342299},
+    # decode T=1, 280 dispatches: FETCH 4754.0 KiB x 1.99980, WRITE 16.1 KiB x 1.0
+    "gemv_gateup": {"sources_sha256": "46667910a5c17fbd9a00eba92ea65908bcd4299e7148300d0037ff30eb420998",
+                    "fetch_bytes": 9735217, "write_bytes": 16448},
+    # prefill T=4096, 18 dispatches: FETCH 226169.4 KiB x 1.99980, WRITE 36864.0 KiB x 1.0
+    "gemm_gateup": {"sources_sha256": "534d73844496c7d887137977ef071bda57118cf947c222e2f139cfe319665ff2",
+                    "fetch_bytes": 463148539, "write_bytes": 37748736},
+    # MXFP4 decode T=1, 280 dispatches: FETCH 4757.5 KiB x 1.99980, WRITE 16.1 KiB x 1.0
+    "gemv_gateup_mx": {"sources_sha256": "46667910a5c17fbd9a00eba92ea65908bcd4299e7148300d0037ff30eb420998",
+                    "fetch_bytes": 9742290, "write_bytes": 16448},
+    # MXFP4 prefill T=4096, 18 dispatches: FETCH 271305.8 KiB x 1.99980, WRITE 59904.6 KiB x 1.0
+    "gemm_gateup_mx": {"sources_sha256": "b38ff33b1c664de6950f31fb11a9860100ad9ac7f1119d6633443d9a16d77e3e",
+                    "fetch_bytes": 555578677, "write_bytes": 61342272},
 }
 FETCH_SIZE_FACTOR = 1.99980   # plain 256 MiB copy: true bytes read / FETCH_SIZE bytes
 WRITE_SIZE_FACTOR = 1.0
@@ -95,10 +95,10 @@ def sources_sha(kernel):
 # keyed like TRAFFIC: mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x
 # GRBM_GUI_ACTIVE / 8 XCDs); executed_flops = MOPS x 512 (padded rows included).
 MFMA_COUNTERS = {
-    "gemm_gateup": {"sources_sha256": "c7eed0e92b6ee3f0a0e6404fd3eb660b0b6ca8202873215bfdddb71dbc672a2d",
-                    "mfma_busy": 0.3358, "executed_flops": 1.71262e+11},
-    "gemm_gateup_mx": {"sources_sha256": "191ec354f43f753bd83cb046438076d6b66c65bf3538ba930548a82810dbc029",
-                    "mfma_busy": 0.3835, "executed_flops": 5.11772e+11},
+    "gemm_gateup": {"sources_sha256": "534d73844496c7d887137977ef071bda57118cf947c222e2f139cfe319665ff2",
+                    "mfma_busy": 0.3357, "executed_flops": 1.71262e+11},
+    "gemm_gateup_mx": {"sources_sha256": "b38ff33b1c664de6950f31fb11a9860100ad9ac7f1119d6633443d9a16d77e3e",
+                    "mfma_busy": 0.3830, "executed_flops": 5.11772e+11},
 }
 
 
