@@ -396,7 +396,7 @@ __device__ __forceinline__ void router_role(const GemvArgs& a, int rb, const flo
             for (int c = 0; c < 4; ++c)
                 wv[r][c] = router_w[(size_t)(h0 + g + G * r) * E + min(e0 + c, E - 1)];
     }
-    for (int i = tid; i < TT * ROWS; i += blockDim.x) {
+    for (int i = tid; i < TT * ROWS; i += 256) {   // the front kernel's 256 threads
         const int tt = i / ROWS, hh = i % ROWS;
         xs[tt][hh] = tt < nt ? x[(size_t)(t0 + tt) * H + h0 + hh] : 0.f;
     }
@@ -437,11 +437,23 @@ __device__ __forceinline__ void router_role(const GemvArgs& a, int rb, const flo
 // arguments, which the hardware preloads into registers.  The shared expert
 // runs here only when the layer routes its own rows (the whole layer, so its
 // rows start at 0).
+// Small counts travel packed two to a register (16 bits each; k and the
+// slots per token 8 bits each), so that the preloaded arguments also hold
+// the pointers a workgroup needs last.
+__host__ __device__ inline uint32_t pack16(int lo, int hi) {
+    return (uint32_t)(lo & 0xffff) | ((uint32_t)hi << 16);
+}
+__device__ inline int lo16(uint32_t v) { return (int)(v & 0xffffu); }
+__device__ inline int hi16(uint32_t v) { return (int)(v >> 16); }
+
 template <int FMT, int LPR, int NSBL, int TT>
 __global__ void __launch_bounds__(256)
 gemv_front_kernel(const float* __restrict__ router_w, const float* __restrict__ x,
-                  const uint8_t* __restrict__ sh_gate, const uint8_t* __restrict__ sh_up, int E,
-                  int H, int T, int n_shared_pad, int shared_rows_blocks, int iloc, GemvArgs a) {
+                  const uint8_t* __restrict__ sh_gate, const uint8_t* __restrict__ sh_up,
+                  float* __restrict__ hbuf, uint32_t e_h, uint32_t t_pad, uint32_t rb_iloc,
+                  uint32_t k_nslot, GemvArgs a) {
+    const int E = lo16(e_h), H = hi16(e_h), T = lo16(t_pad), n_shared_pad = hi16(t_pad);
+    const int shared_rows_blocks = lo16(rb_iloc), iloc = hi16(rb_iloc);
     // shared-expert workgroups first (each starts on a CU of its own), then
     // the router's, from a multiple of kXcds on
     const int b = blockIdx.x;
@@ -461,34 +473,40 @@ gemv_front_kernel(const float* __restrict__ router_w, const float* __restrict__ 
     if (rbase >= iloc) return;   // the shared expert has the routed width
     XRegs<LPR, NSBL> X;
     X.load(x + (size_t)t * H);
+    // h of slot k (after the k routed slots) of token t; its rows are iloc wide
+    const int k = lo16(k_nslot), nslot = hi16(k_nslot);
     gateup_rows<FMT, LPR, NSBL, kShSteps>(sh_gate, sh_up, H, iloc, 0, X, rbase,
-                                          a.hbuf + (size_t)(t * a.nslot + a.k) * a.hstride);
+                                          hbuf + (size_t)(t * nslot + k) * iloc);
 }
 
 // routed experts: grid (row blocks, T*k); SH (routing known before the
 // layer starts, so no router work in a front kernel, which is then not
 // launched): T more rows of workgroups for the shared expert as slot k of
-// each token
-// The pointers and counts that the first loads (activations, partial logits
-// or the given routing) need come first as scalar arguments, which the
-// hardware preloads into registers: those loads wait for no kernel-argument
-// load.
-template <int FMT, int LPR, int NSBL, bool SH>
-__global__ void __launch_bounds__(64 * kGuWaves)
-gemv_gateup_kernel(const float* __restrict__ x, const float* __restrict__ part,
-                   const int32_t* __restrict__ idx, int k, int E, int H, int route, int T,
-                   GemvArgs a) {
+// each token.  The pointers and counts a workgroup needs -- for its first
+// loads (activations, partial logits or the given routing) and for its
+// weights and h row -- come in as preloaded kernel arguments, so no load
+// waits for a kernel-argument load.
+template <int FMT, int LPR, int NSBL, bool ROUTE, bool SH>
+__device__ __forceinline__ void gateup_body(const float* __restrict__ x,
+                                            const float* __restrict__ part,
+                                            const int32_t* __restrict__ idx,
+                                            const uint8_t* __restrict__ gate,
+                                            const uint8_t* __restrict__ up, float* __restrict__ hbuf,
+                                            int k, int nslot, int E, int H, int I, int iloc, int i0,
+                                            int T, const GemvArgs& a) {
     const int q = blockIdx.y;
+    const int wave = threadIdx.x >> 6;
+    constexpr int rows_per_wave = kGuSteps * (64 / LPR);
+    const int rbase = (blockIdx.x * kGuWaves + wave) * rows_per_wave;
     if constexpr (SH) {
         if (q >= T * k) {
             const int t = q - T * k;
-            const int rbase = (blockIdx.x * kGuWaves + (threadIdx.x >> 6)) * kGuSteps * (64 / LPR);
-            if (rbase >= a.iloc) return;
+            if (rbase >= iloc) return;
             XRegs<LPR, NSBL> X;
             X.load(x + (size_t)t * H);
             // the shared expert has the routed width
-            gateup_rows<FMT, LPR, NSBL, kGuSteps>(a.sh_gate, a.sh_up, H, a.iloc, a.i0, X, rbase,
-                                                  a.hbuf + (size_t)(t * a.nslot + k) * a.hstride);
+            gateup_rows<FMT, LPR, NSBL, kGuSteps>(a.sh_gate, a.sh_up, H, iloc, i0, X, rbase,
+                                                  hbuf + (size_t)(t * nslot + k) * iloc);
             return;
         }
     }
@@ -496,7 +514,7 @@ gemv_gateup_kernel(const float* __restrict__ x, const float* __restrict__ part,
     XRegs<LPR, NSBL> X;
     X.load(x + (size_t)t * H);   // independent of the routing: in flight during the top-k
     int e;
-    if (route) {
+    if constexpr (ROUTE) {
         // the first wave selects (stopping at slot j, whose expert lane j
         // holds) and hands the expert to the others through LDS; the first
         // wave of workgroup (0, t*k) fills all k slots and writes the
@@ -522,15 +540,33 @@ gemv_gateup_kernel(const float* __restrict__ x, const float* __restrict__ part,
         e = idx[(size_t)t * k + j];
     }
     if ((unsigned)e >= (unsigned)E) return;
-    const size_t mat = (size_t)a.I * H / kSbWeights * kQ4Bytes;   // MXFP4: the same size
-    const int Iloc = a.iloc, i0 = a.i0;
-    const int wave = threadIdx.x >> 6;
-    constexpr int rows_per_wave = kGuSteps * (64 / LPR);
-    const int rbase = (blockIdx.x * kGuWaves + wave) * rows_per_wave;
-    if (rbase >= Iloc) return;
-    const int p = t * a.nslot + j;
-    gateup_rows<FMT, LPR, NSBL, kGuSteps>(a.gate + (size_t)e * mat, a.up + (size_t)e * mat, H, Iloc,
-                                     i0, X, rbase, a.hbuf + (size_t)p * a.hstride);
+    if (rbase >= iloc) return;
+    const size_t mat = (size_t)I * H / kSbWeights * kQ4Bytes;   // MXFP4: the same size
+    gateup_rows<FMT, LPR, NSBL, kGuSteps>(gate + (size_t)e * mat, up + (size_t)e * mat, H, iloc,
+                                          i0, X, rbase, hbuf + (size_t)(t * nslot + j) * iloc);
+}
+
+// The layer routes its own rows: the top-k from the front kernel's partial
+// logits, for the whole layer (rows [0, I) of every expert).
+template <int FMT, int LPR, int NSBL>
+__global__ void __launch_bounds__(64 * kGuWaves)
+gemv_gateup_kernel(const float* __restrict__ x, const float* __restrict__ part,
+                   const uint8_t* __restrict__ gate, const uint8_t* __restrict__ up,
+                   float* __restrict__ hbuf, uint32_t k_nslot, uint32_t e_h, int I, GemvArgs a) {
+    gateup_body<FMT, LPR, NSBL, true, false>(x, part, nullptr, gate, up, hbuf, lo16(k_nslot),
+                                             hi16(k_nslot), lo16(e_h), hi16(e_h), I, I, 0, 0, a);
+}
+
+// The routing is given (shard and range calls, or the router ran first).
+template <int FMT, int LPR, int NSBL, bool SH>
+__global__ void __launch_bounds__(64 * kGuWaves)
+gemv_gateup_given_kernel(const int32_t* __restrict__ idx, const uint8_t* __restrict__ gate,
+                         const uint8_t* __restrict__ up, float* __restrict__ hbuf,
+                         uint32_t k_nslot, uint32_t e_h, uint32_t iloc_i0, int I, int T,
+                         GemvArgs a) {
+    gateup_body<FMT, LPR, NSBL, false, SH>(a.x, nullptr, idx, gate, up, hbuf, lo16(k_nslot),
+                                           hi16(k_nslot), lo16(e_h), hi16(e_h), I, lo16(iloc_i0),
+                                           hi16(iloc_i0), T, a);
 }
 
 // ---------------------------------------------------------------------------
@@ -684,14 +720,14 @@ static GemvArgs base_args(const moe_layer_desc& d, const float* x, int T, int i0
 template <int FMT, int LPR, int NSBL>
 static void launch_front_f(const GemvArgs& a, int n_shared_blocks, const Ctx& c) {
     const dim3 grid(a.n_router_blocks + n_shared_blocks);
+    const uint32_t e_h = pack16(a.E, a.H), t_pad = pack16(a.T, a.n_shared_pad);
+    const uint32_t rb_iloc = pack16(a.shared_rows_blocks, a.iloc), k_nslot = pack16(a.k, a.nslot);
     if (a.T == 1)
         launch_k(c, MOE_K_GEMV_FRONT, gemv_front_kernel<FMT, LPR, NSBL, 1>, grid, dim3(256), 0,
-                 a.router_w, a.x, a.sh_gate, a.sh_up, a.E, a.H, a.T, a.n_shared_pad,
-                 a.shared_rows_blocks, a.iloc, a);
+                 a.router_w, a.x, a.sh_gate, a.sh_up, a.hbuf, e_h, t_pad, rb_iloc, k_nslot, a);
     else
         launch_k(c, MOE_K_GEMV_FRONT, gemv_front_kernel<FMT, LPR, NSBL, 4>, grid, dim3(256), 0,
-                 a.router_w, a.x, a.sh_gate, a.sh_up, a.E, a.H, a.T, a.n_shared_pad,
-                 a.shared_rows_blocks, a.iloc, a);
+                 a.router_w, a.x, a.sh_gate, a.sh_up, a.hbuf, e_h, t_pad, rb_iloc, k_nslot, a);
 }
 
 template <int LPR, int NSBL>
@@ -703,15 +739,31 @@ static void launch_front_t(const GemvArgs& a, int n_shared_blocks, const Ctx& c)
 }
 
 template <int LPR, int NSBL>
-static void launch_gateup_t(const GemvArgs& a, const Ctx& c) {
+static hipError_t launch_gateup_t(const GemvArgs& a, const Ctx& c) {
     constexpr int rows_per_block = kGuWaves * kGuSteps * (64 / LPR);
     const int Iloc = a.iloc;
     const dim3 grid((Iloc + rows_per_block - 1) / rows_per_block,
                     a.T * a.k + (a.sh_in_gateup ? a.T : 0));
     const dim3 block(64 * kGuWaves);
-#define MOE_GATEUP(F, S)                                                                        \
-    launch_k(c, MOE_K_GATEUP_GEMV, gemv_gateup_kernel<F, LPR, NSBL, S>, grid, block, 0, a.x,    \
-             (const float*)a.part, a.idx, a.k, a.E, a.H, a.route, a.T, a)
+    const uint32_t k_nslot = pack16(a.k, a.nslot), e_h = pack16(a.E, a.H);
+    if (a.route) {
+        // the whole layer: rows [0, I) of every expert
+        if (a.i0 != 0 || a.iloc != a.I) return hipErrorInvalidValue;
+        if (a.fmt == MOE_WFMT_MXFP4)
+            launch_k(c, MOE_K_GATEUP_GEMV, gemv_gateup_kernel<MOE_WFMT_MXFP4, LPR, NSBL>, grid,
+                     block, 0, a.x, (const float*)a.part, a.gate, a.up, a.hbuf, k_nslot, e_h, a.I,
+                     a);
+        else
+            launch_k(c, MOE_K_GATEUP_GEMV, gemv_gateup_kernel<MOE_WFMT_KQUANT, LPR, NSBL>, grid,
+                     block, 0, a.x, (const float*)a.part, a.gate, a.up, a.hbuf, k_nslot, e_h, a.I,
+                     a);
+        return hipGetLastError();
+    }
+    if (a.i0 > 0xffff || a.iloc > 0xffff) return hipErrorInvalidValue;
+    const uint32_t iloc_i0 = pack16(a.iloc, a.i0);
+#define MOE_GATEUP(F, S)                                                                         \
+    launch_k(c, MOE_K_GATEUP_GEMV, gemv_gateup_given_kernel<F, LPR, NSBL, S>, grid, block, 0,    \
+             a.idx, a.gate, a.up, a.hbuf, k_nslot, e_h, iloc_i0, a.I, a.T, a)
     if (a.fmt == MOE_WFMT_MXFP4) {
         if (a.sh_in_gateup) MOE_GATEUP(MOE_WFMT_MXFP4, true);
         else MOE_GATEUP(MOE_WFMT_MXFP4, false);
@@ -720,6 +772,7 @@ static void launch_gateup_t(const GemvArgs& a, const Ctx& c) {
         else MOE_GATEUP(MOE_WFMT_KQUANT, false);
     }
 #undef MOE_GATEUP
+    return hipGetLastError();
 }
 
 #define MOE_DISPATCH_H(nsb, F, ...)                                  \
@@ -813,7 +866,16 @@ hipError_t launch_gemv(const moe_layer_desc& d, const float* x, int T, const int
     a.idx = idx;
     a.w = w;
     const int nsb = d.hidden / kSbWeights;
-    MOE_DISPATCH_H(nsb, launch_gateup_t, a, c);
+    hipError_t ge = hipSuccess;
+    switch (nsb) {
+        case 1: ge = launch_gateup_t<8, 1>(a, c); break;
+        case 2: ge = launch_gateup_t<16, 1>(a, c); break;
+        case 4: ge = launch_gateup_t<32, 1>(a, c); break;
+        case 8: ge = launch_gateup_t<64, 1>(a, c); break;
+        case 16: ge = launch_gateup_t<64, 2>(a, c); break;
+        default: return hipErrorInvalidValue;
+    }
+    if (ge != hipSuccess) return ge;
     int lprd = 2;   // lanes per down row: Iloc / 32 rounded up to a power of two
     while (lprd < Iloc / 32) lprd *= 2;
     switch (lprd) {
