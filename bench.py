@@ -58,18 +58,18 @@ MX_TERMS = 3                    # MX-FP8 terms per token / h value on the MXFP4 
 # --copy-probe).  Keyed by the SHA-256 of the kernel's sources: when they change,
 # the counters no longer describe the kernel and traffic is reported as null.
 TRAFFIC = {
-    # decode T=1, 280 dispatches: FETCH 4754.0 KiB x 1.99980, WRITE 16.1 KiB x 1.0
-    "gemv_gateup": {"sources_sha256": "46667910a5c17fbd9a00eba92ea65908bcd4299e7148300d0037ff30eb420998",
-                    "fetch_bytes": 9735217, "write_bytes": 16448},
-    # prefill T=4096, 18 dispatches: FETCH 226169.4 KiB x 1.99980, WRITE 36864.0 KiB x 1.0
+    # decode T=1, 280 dispatches: FETCH 4742.1 KiB x 1.99980, WRITE 16.1 KiB x 1.0
+    "gemv_gateup": {"sources_sha256": "ab97a693b3a11f1662f1a2bcf206fc385ed1ada85fb68a7c3b614e2450f7f202",
+                    "fetch_bytes": 9710787, "write_bytes": 16448},
+    # prefill T=4096, 18 dispatches: FETCH 226218.6 KiB x 1.99980, WRITE 36864.0 KiB x 1.0
     "gemm_gateup": {"sources_sha256": "534d73844496c7d887137977ef071bda57118cf947c222e2f139cfe319665ff2",
-                    "fetch_bytes": 463148539, "write_bytes": 37748736},
-    # MXFP4 decode T=1, 280 dispatches: FETCH 4757.5 KiB x 1.99980, WRITE 16.1 KiB x 1.0
-    "gemv_gateup_mx": {"sources_sha256": "46667910a5c17fbd9a00eba92ea65908bcd4299e7148300d0037ff30eb420998",
-                    "fetch_bytes": 9742290, "write_bytes": 16448},
-    # MXFP4 prefill T=4096, 18 dispatches: FETCH 271305.8 KiB x 1.99980, WRITE 59904.6 KiB x 1.0
+                    "fetch_bytes": 463249279, "write_bytes": 37748736},
+    # MXFP4 decode T=1, 280 dispatches: FETCH 4752.0 KiB x 1.99980, WRITE 16.1 KiB x 1.0
+    "gemv_gateup_mx": {"sources_sha256": "ab97a693b3a11f1662f1a2bcf206fc385ed1ada85fb68a7c3b614e2450f7f202",
+                    "fetch_bytes": 9731104, "write_bytes": 16448},
+    # MXFP4 prefill T=4096, 18 dispatches: FETCH 273389.4 KiB x 1.99980, WRITE 59904.9 KiB x 1.0
     "gemm_gateup_mx": {"sources_sha256": "b38ff33b1c664de6950f31fb11a9860100ad9ac7f1119d6633443d9a16d77e3e",
-                    "fetch_bytes": 555578677, "write_bytes": 61342272},
+                    "fetch_bytes": 559845485, "write_bytes": 61342612},
 }
 FETCH_SIZE_FACTOR = 1.99980   # plain 256 MiB copy: true bytes read / FETCH_SIZE bytes
 WRITE_SIZE_FACTOR = 1.0
@@ -96,9 +96,9 @@ def sources_sha(kernel):
 # GRBM_GUI_ACTIVE / 8 XCDs); executed_flops = MOPS x 512 (padded rows included).
 MFMA_COUNTERS = {
     "gemm_gateup": {"sources_sha256": "534d73844496c7d887137977ef071bda57118cf947c222e2f139cfe319665ff2",
-                    "mfma_busy": 0.3357, "executed_flops": 1.71262e+11},
+                    "mfma_busy": 0.3339, "executed_flops": 1.71262e+11},
     "gemm_gateup_mx": {"sources_sha256": "b38ff33b1c664de6950f31fb11a9860100ad9ac7f1119d6633443d9a16d77e3e",
-                    "mfma_busy": 0.3830, "executed_flops": 5.11772e+11},
+                    "mfma_busy": 0.3840, "executed_flops": 5.11772e+11},
 }
 
 
@@ -313,7 +313,7 @@ def bench_decode(args, torch, qm, mi, DeviceLayer, name="decode"):
         "layer_hbm_frac_graph": layer_bytes / dev_s / (HBM_PEAK_GBS * 1e9),
         "layer_hbm_frac_kernels": layer_bytes / (sum(kms.values()) * 1e-3) / (HBM_PEAK_GBS * 1e9),
         "roofline": roofline(
-            "gemv_gateup_kernel<%s,64,1,false> (8 routed experts)" % ("MXFP4" if shp.fmt else "K-quant"),
+            "gemv_gateup_kernel<%s,64,1> (8 routed experts)" % ("MXFP4" if shp.fmt else "K-quant"),
             "hbm", gateup_bytes, kms["gateup_gemv"], "GB/s", HBM_PEAK_GBS,
             traffic_for("gemv_gateup_mx" if shp.fmt else "gemv_gateup"),
             {"median_launch_ms": kst["gateup_gemv"]["median_ms"],
