@@ -437,9 +437,9 @@ __device__ __forceinline__ void router_role(const GemvArgs& a, int rb, const flo
 // arguments, which the hardware preloads into registers.  The shared expert
 // runs here only when the layer routes its own rows (the whole layer, so its
 // rows start at 0).
-// Small counts travel packed two to a register (16 bits each; k and the
-// slots per token 8 bits each), so that the preloaded arguments also hold
-// the pointers a workgroup needs last.
+// Small counts travel packed two to a register (16 bits each; the
+// launchers check the ranges), so that the preloaded arguments also hold the
+// pointers a workgroup needs last.
 __host__ __device__ inline uint32_t pack16(int lo, int hi) {
     return (uint32_t)(lo & 0xffff) | ((uint32_t)hi << 16);
 }
@@ -745,6 +745,8 @@ static hipError_t launch_gateup_t(const GemvArgs& a, const Ctx& c) {
     const dim3 grid((Iloc + rows_per_block - 1) / rows_per_block,
                     a.T * a.k + (a.sh_in_gateup ? a.T : 0));
     const dim3 block(64 * kGuWaves);
+    if (a.k > 0xffff || a.nslot > 0xffff || a.E > 0xffff || a.H > 0xffff)
+        return hipErrorInvalidValue;   // packed in 16 bits
     const uint32_t k_nslot = pack16(a.k, a.nslot), e_h = pack16(a.E, a.H);
     if (a.route) {
         // the whole layer: rows [0, I) of every expert
@@ -807,6 +809,10 @@ static hipError_t launch_front(GemvArgs& a, bool route, bool shared, const WsLay
     // router workgroups start at a multiple of kXcds (their XCD mapping)
     a.n_shared_pad = a.n_router_blocks > 0 ? (n_shared + kXcds - 1) / kXcds * kXcds : n_shared;
     if (a.n_router_blocks + n_shared == 0) return hipSuccess;
+    // the kernel takes these counts packed in 16 bits (it runs for T <= 32)
+    if (a.E > 0xffff || a.H > 0xffff || a.T > 0xffff || a.n_shared_pad > 0xffff ||
+        a.shared_rows_blocks > 0xffff || a.iloc > 0xffff || a.k > 0xffff || a.nslot > 0xffff)
+        return hipErrorInvalidValue;
     MOE_DISPATCH_H(nsb, launch_front_t, a, a.n_shared_pad, c);
     return hipGetLastError();
 }
