@@ -42,8 +42,9 @@ bucket_hist_kernel(const int32_t* __restrict__ idx, int n, int E, int32_t* __res
 // integer counts as bucket_hist_kernel, so that kernel is not launched), and
 // runs the exclusive scans over experts (integers: every workgroup gets the
 // same offsets).  Workgroup 0 also writes counts, offsets, tile_off and the
-// grouped GEMM's tile list (tiles of kTileM rows per expert, the shared
-// expert last as group E with all T rows).  Then each workgroup places its
+// grouped GEMM's tile list (tiles of kTileM rows per expert, then the shared
+// expert's as group E with all T rows, stored last tile first: the order in
+// which the GEMM's workgroups take them).  Then each workgroup places its
 // own slots: per-wave histograms -> per-wave bases, the rank of a slot among
 // equal experts inside its wave by a 64-step lane scan, perm[base + rank] = s.
 constexpr int kFusedHist = 8192;    // int32 entries of the LDS histogram (32 KB)
@@ -129,6 +130,12 @@ bucket_sort_kernel(const int32_t* __restrict__ idx, int n, int nblk, int E, int 
     st[e] = it;
     __syncthreads();
     if (b == 0) {
+        // row tile i (experts in order, then the shared expert) goes to record
+        // ntot - 1 - i: the grouped GEMM's workgroups take the records in
+        // order (the shared expert's, the largest, first) and read a record
+        // without waiting for the tile count
+        const int nsh = shared ? (T + kTileM - 1) / kTileM : 0;
+        const int ntot = st[kBucketBlock - 1] + nsh;
         if (e < E) {
             const int excl = ic - c;
             counts[e] = c;
@@ -136,17 +143,13 @@ bucket_sort_kernel(const int32_t* __restrict__ idx, int n, int nblk, int E, int 
             tile_off[e] = it - tiles;
             // the expert's row tiles: (group, first sorted row, rows, row offset)
             for (int j = 0; j < tiles; ++j)
-                tile_rec[it - tiles + j] = make_int4(e, excl + j * kTileM,
-                                                     min(kTileM, c - j * kTileM), j * kTileM);
+                tile_rec[ntot - 1 - (it - tiles + j)] =
+                    make_int4(e, excl + j * kTileM, min(kTileM, c - j * kTileM), j * kTileM);
         }
-        if (shared) {
-            // the shared expert (group E, all T rows in order) after the routed tiles
-            const int nsh = (T + kTileM - 1) / kTileM;
-            for (int j = tid; j < nsh; j += kBucketBlock)
-                tile_rec[st[kBucketBlock - 1] + j] =
-                    make_int4(E, sc[kBucketBlock - 1] + j * kTileM, min(kTileM, T - j * kTileM),
-                              j * kTileM);
-        }
+        // the shared expert (group E, all T rows in order) after the routed tiles
+        for (int j = tid; j < nsh; j += kBucketBlock)
+            tile_rec[nsh - 1 - j] = make_int4(E, sc[kBucketBlock - 1] + j * kTileM,
+                                              min(kTileM, T - j * kTileM), j * kTileM);
         if (e == E - 1) {
             offsets[E] = ic;
             offsets[E + 1] = ic + (shared ? T : 0);

@@ -538,25 +538,32 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileInfo& ti,
     gemm_epilogue<MODE, MB>(a, ti, lds, row_src, row_w, acc);
 }
 
+// tile_off, tile_rec, the packed counts (experts | column tiles << 16) and the
+// number of records come first as scalar arguments, which the hardware
+// preloads into registers: a workgroup reads the tile count and its record
+// at once, with no kernel-argument load before them.
 template <int MODE>
 __global__ void __launch_bounds__(kGemmThreads)
-gemm_grouped_kernel(GemmArgs a) {
+gemm_grouped_kernel(const int32_t* __restrict__ tile_off, const int4* __restrict__ tile_rec,
+                    uint32_t e_nt, int max_tiles, GemmArgs a) {
     __shared__ GemmLds lds;
     __shared__ int32_t row_src[kTM];     // MODE 0: token of each row; MODE 1: slot id
     __shared__ float row_w[kTM];         // MODE 1: routing weight * 2^4 of each row
 
-    const int ngroups = a.E + 1;
-    const int ntiles = a.tile_off[ngroups];
     // block -> (row tile, column tile): the column tiles of one row tile run
-    // on one XCD (blocks 8 apart), so its gathered rows are reused in L2; row
-    // tiles are taken in reverse (the shared expert's, the largest, first)
+    // on one XCD (blocks 8 apart), so its gathered rows are reused in L2; the
+    // records are stored in the order the row tiles are taken (the shared
+    // expert's, the largest, first)
     const int b = blockIdx.x;
-    const int nt = a.n_ntiles;
+    const int nt = hi16(e_nt);
     const int tile_raw = (b / (8 * nt)) * 8 + (b & 7);
     const int ntile = (b >> 3) % nt;
+    const int ntiles = tile_off[lo16(e_nt) + 1];
+    const int4 rec = tile_rec[min(tile_raw, max_tiles - 1)];   // written by the bucketing
+    // both loads in flight together: the record is needed in registers
+    // before the exit test (the compiler would otherwise load it after)
+    asm volatile("" ::"s"(rec.x), "s"(rec.y), "s"(rec.z), "s"(rec.w));
     if (tile_raw >= ntiles) return;
-    const int tile = ntiles - 1 - tile_raw;
-    const int4 rec = a.tile_rec[tile];   // written by the bucketing scan
     TileInfo ti;
     ti.g = rec.x;
     ti.is_sh = ti.g == a.E;
@@ -723,8 +730,10 @@ hipError_t launch_mfma(const moe_layer_desc& d, const float* x, int T, const int
     g1.nk = H / kBK;
     g1.h_out = h16;
     g1.h_stride = Iloc;
+    if (E > 0xffff || g1.n_ntiles > 0xffff) return hipErrorInvalidValue;   // packed in 16 bits
     launch_k(c, MOE_K_GEMM_GATEUP, gemm_grouped_kernel<0>, dim3(max_tiles8 * g1.n_ntiles),
-             dim3(kGemmThreads), 0, g1);
+             dim3(kGemmThreads), 0, (const int32_t*)tile_off, (const int4*)tile_rec,
+             pack16(E, g1.n_ntiles), max_tiles, g1);
 
     GemmArgs g2 = a;
     g2.a_src = h16;
@@ -738,8 +747,10 @@ hipError_t launch_mfma(const moe_layer_desc& d, const float* x, int T, const int
     g2.ysh = ysh;
     g2.ysc = ysc;
     g2.yshsc = yshsc;
+    if (g2.n_ntiles > 0xffff) return hipErrorInvalidValue;
     launch_k(c, MOE_K_GEMM_DOWN, gemm_grouped_kernel<1>, dim3(max_tiles8 * g2.n_ntiles),
-             dim3(kGemmThreads), 0, g2);
+             dim3(kGemmThreads), 0, (const int32_t*)tile_off, (const int4*)tile_rec,
+             pack16(E, g2.n_ntiles), max_tiles, g2);
 
     return launch_combine(y, ysh, ysc, yshsc, idx, T, H, E, k, shared, out, c);
 }

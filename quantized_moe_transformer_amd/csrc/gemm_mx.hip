@@ -517,24 +517,28 @@ __device__ __forceinline__ void mx_tile(const MxGemmArgs& a, const MxTileInfo& t
     mx_epilogue<MODE, MB, NT>(a, ti, lds, row_src, row_w, acc);
 }
 
+// tile_off, tile_rec, the packed counts (experts | column tiles << 16) and the
+// number of records come first as preloaded scalar arguments, as in the fp16
+// grouped GEMM.
 template <int MODE, int NT>
 __global__ void __launch_bounds__(kMxThreads)
-gemm_mx_kernel(MxGemmArgs a) {
+gemm_mx_kernel(const int32_t* __restrict__ tile_off, const int4* __restrict__ tile_rec,
+               uint32_t e_nt, int max_tiles, MxGemmArgs a) {
     __shared__ MxLds lds;
     int32_t* row_src = lds.row_src;
     float* row_w = lds.row_w;
 
-    const int ngroups = a.E + 1;
-    const int ntiles = a.tile_off[ngroups];
     // block -> (row tile, column tile) as in the fp16 grouped GEMM: the column
-    // tiles of one row tile run on one XCD; row tiles in reverse order
+    // tiles of one row tile run on one XCD; records in the order taken
     const int b = blockIdx.x;
-    const int nt = a.n_ntiles;
+    const int nt = hi16(e_nt);
     const int tile_raw = (b / (8 * nt)) * 8 + (b & 7);
     const int ntile = (b >> 3) % nt;
+    const int ntiles = tile_off[lo16(e_nt) + 1];
+    const int4 rec = tile_rec[min(tile_raw, max_tiles - 1)];
+    // both loads in flight together (the record in registers before the exit test)
+    asm volatile("" ::"s"(rec.x), "s"(rec.y), "s"(rec.z), "s"(rec.w));
     if (tile_raw >= ntiles) return;
-    const int tile = ntiles - 1 - tile_raw;
-    const int4 rec = a.tile_rec[tile];
     MxTileInfo ti;
     ti.g = rec.x;
     ti.is_sh = ti.g == a.E;
@@ -626,8 +630,10 @@ hipError_t launch_mfma_mx(const moe_layer_desc& d, const float* x, int T, const 
     g1.w_shared2 = d.sh_up_q;
     g1.n_ntiles = (iloc + kMxTN / 2 - 1) / (kMxTN / 2);
     g1.nk = H / kMxK;
+    if (E > 0xffff || g1.n_ntiles > 0xffff) return hipErrorInvalidValue;   // packed in 16 bits
     launch_k(c, MOE_K_GEMM_GATEUP, gemm_mx_kernel<0, kMxTerms>, dim3(max_tiles8 * g1.n_ntiles),
-             dim3(kMxThreads), 0, g1);
+             dim3(kMxThreads), 0, (const int32_t*)tile_off, (const int4*)tile_rec,
+             pack16(E, g1.n_ntiles), max_tiles, g1);
 
     MxGemmArgs g2 = a;
     g2.aq = hq;
@@ -642,8 +648,10 @@ hipError_t launch_mfma_mx(const moe_layer_desc& d, const float* x, int T, const 
     g2.ysh = ysh;
     g2.ysc = ysc;
     g2.yshsc = yshsc;
+    if (g2.n_ntiles > 0xffff) return hipErrorInvalidValue;
     launch_k(c, MOE_K_GEMM_DOWN, gemm_mx_kernel<1, kMxTerms>, dim3(max_tiles8 * g2.n_ntiles),
-             dim3(kMxThreads), 0, g2);
+             dim3(kMxThreads), 0, (const int32_t*)tile_off, (const int4*)tile_rec,
+             pack16(E, g2.n_ntiles), max_tiles, g2);
     return launch_combine(y, ysh, ysc, yshsc, idx, T, H, E, k, shared, out, c);
 }
 

@@ -437,15 +437,6 @@ __device__ __forceinline__ void router_role(const GemvArgs& a, int rb, const flo
 // arguments, which the hardware preloads into registers.  The shared expert
 // runs here only when the layer routes its own rows (the whole layer, so its
 // rows start at 0).
-// Small counts travel packed two to a register (16 bits each; the
-// launchers check the ranges), so that the preloaded arguments also hold the
-// pointers a workgroup needs last.
-__host__ __device__ inline uint32_t pack16(int lo, int hi) {
-    return (uint32_t)(lo & 0xffff) | ((uint32_t)hi << 16);
-}
-__device__ inline int lo16(uint32_t v) { return (int)(v & 0xffffu); }
-__device__ inline int hi16(uint32_t v) { return (int)(v >> 16); }
-
 template <int FMT, int LPR, int NSBL, int TT>
 __global__ void __launch_bounds__(256)
 gemv_front_kernel(const float* __restrict__ router_w, const float* __restrict__ x,

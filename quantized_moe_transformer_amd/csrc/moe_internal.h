@@ -262,6 +262,16 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     return (uint16_t)(u >> 16);
 }
 
+// Small counts travel to kernels packed two to a 32-bit argument (16 bits
+// each; the launchers check the ranges), so that the leading scalar
+// arguments, which the hardware preloads into registers (at most 14 dwords),
+// hold the pointers a workgroup needs on its critical path.
+__host__ __device__ inline uint32_t pack16(int lo, int hi) {
+    return (uint32_t)(lo & 0xffff) | ((uint32_t)hi << 16);
+}
+__device__ inline int lo16(uint32_t v) { return (int)(v & 0xffffu); }
+__device__ inline int hi16(uint32_t v) { return (int)(v >> 16); }
+
 // One 16-byte global-to-LDS load per lane: lane l's bytes land at LDS offset
 // lds_off + 16 l.  Written as asm so that the compiler does not order it
 // against LDS reads of other stages with waits of its own; the caller waits
