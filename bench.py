@@ -59,17 +59,17 @@ MX_TERMS = 3                    # MX-FP8 terms per token / h value on the MXFP4 
 # the counters no longer describe the kernel and traffic is reported as null.
 TRAFFIC = {
     # decode T=1, 280 dispatches: FETCH 4742.1 KiB x 1.99980, WRITE 16.1 KiB x 1.0
-    "gemv_gateup": {"sources_sha256": "ab97a693b3a11f1662f1a2bcf206fc385ed1ada85fb68a7c3b614e2450f7f202",
-                    "fetch_bytes": 9710787, "write_bytes": 16448},
-    # prefill T=4096, 18 dispatches: FETCH 226218.6 KiB x 1.99980, WRITE 36864.0 KiB x 1.0
-    "gemm_gateup": {"sources_sha256": "534d73844496c7d887137977ef071bda57118cf947c222e2f139cfe319665ff2",
-                    "fetch_bytes": 463249279, "write_bytes": 37748736},
-    # MXFP4 decode T=1, 280 dispatches: FETCH 4752.0 KiB x 1.99980, WRITE 16.1 KiB x 1.0
-    "gemv_gateup_mx": {"sources_sha256": "ab97a693b3a11f1662f1a2bcf206fc385ed1ada85fb68a7c3b614e2450f7f202",
-                    "fetch_bytes": 9731104, "write_bytes": 16448},
-    # MXFP4 prefill T=4096, 18 dispatches: FETCH 273389.4 KiB x 1.99980, WRITE 59904.9 KiB x 1.0
-    "gemm_gateup_mx": {"sources_sha256": "b38ff33b1c664de6950f31fb11a9860100ad9ac7f1119d6633443d9a16d77e3e",
-                    "fetch_bytes": 559845485, "write_bytes": 61342612},
+    "gemv_gateup": {"sources_sha256": "3484ee76d7d8624317574e6c94e1159e7075308b86b0a68b1d9a166cf634255a",
+                    "fetch_bytes": 9710765, "write_bytes": 16448},
+    # prefill T=4096, 18 dispatches: FETCH 226252.8 KiB x 1.99980, WRITE 36864.0 KiB x 1.0
+    "gemm_gateup": {"sources_sha256": "38c44c264ee3711088101b5964188bfb0a068286c3bf8ee0d684227a24fcfa10",
+                    "fetch_bytes": 463319423, "write_bytes": 37748736},
+    # MXFP4 decode T=1, 280 dispatches: FETCH 4752.3 KiB x 1.99980, WRITE 16.1 KiB x 1.0
+    "gemv_gateup_mx": {"sources_sha256": "3484ee76d7d8624317574e6c94e1159e7075308b86b0a68b1d9a166cf634255a",
+                    "fetch_bytes": 9731688, "write_bytes": 16448},
+    # MXFP4 prefill T=4096, 18 dispatches: FETCH 269575.9 KiB x 1.99980, WRITE 59905.6 KiB x 1.0
+    "gemm_gateup_mx": {"sources_sha256": "a23e786497430292dc59f05cc49339feebce277ef6f4fb50273feff6ae084548",
+                    "fetch_bytes": 552036176, "write_bytes": 61343321},
 }
 FETCH_SIZE_FACTOR = 1.99980   # plain 256 MiB copy: true bytes read / FETCH_SIZE bytes
 WRITE_SIZE_FACTOR = 1.0
@@ -95,10 +95,10 @@ def sources_sha(kernel):
 # keyed like TRAFFIC: mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x
 # GRBM_GUI_ACTIVE / 8 XCDs); executed_flops = MOPS x 512 (padded rows included).
 MFMA_COUNTERS = {
-    "gemm_gateup": {"sources_sha256": "534d73844496c7d887137977ef071bda57118cf947c222e2f139cfe319665ff2",
-                    "mfma_busy": 0.3339, "executed_flops": 1.71262e+11},
-    "gemm_gateup_mx": {"sources_sha256": "b38ff33b1c664de6950f31fb11a9860100ad9ac7f1119d6633443d9a16d77e3e",
-                    "mfma_busy": 0.3840, "executed_flops": 5.11772e+11},
+    "gemm_gateup": {"sources_sha256": "38c44c264ee3711088101b5964188bfb0a068286c3bf8ee0d684227a24fcfa10",
+                    "mfma_busy": 0.3349, "executed_flops": 1.71262e+11},
+    "gemm_gateup_mx": {"sources_sha256": "a23e786497430292dc59f05cc49339feebce277ef6f4fb50273feff6ae084548",
+                    "mfma_busy": 0.3860, "executed_flops": 5.11772e+11},
 }
 
 
