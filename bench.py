@@ -299,7 +299,8 @@ def bench_decode(args, torch, qm, mi, DeviceLayer, name="decode"):
     kms = kernel_profile(torch, qm, lambda i, e: step(i, e), nprof,
                          ["gemv_front", "gateup_gemv", "down_gemv"], kst)
     gu, dn = expert_bytes(mi, shp)
-    gateup_bytes = shp.k * gu + shp.H * 4 + shp.k * shp.I * 4
+    # the gate/up kernel streams the k routed experts and the shared one
+    gateup_bytes = (shp.k + 1) * gu + shp.H * 4 + (shp.k + 1) * shp.I * 4
     layer_bytes = (shp.k + 1) * (gu + dn) + shp.H * shp.E * 4   # K-quant: 19,202,048 B
     res = {
         "value": T / dev_s,
@@ -313,7 +314,8 @@ def bench_decode(args, torch, qm, mi, DeviceLayer, name="decode"):
         "layer_hbm_frac_graph": layer_bytes / dev_s / (HBM_PEAK_GBS * 1e9),
         "layer_hbm_frac_kernels": layer_bytes / (sum(kms.values()) * 1e-3) / (HBM_PEAK_GBS * 1e9),
         "roofline": roofline(
-            "gemv_gateup_kernel<%s,64,1> (8 routed experts)" % ("MXFP4" if shp.fmt else "K-quant"),
+            "gemv_gateup_kernel<%s,64,1,true> (8 routed experts and the shared one)"
+            % ("MXFP4" if shp.fmt else "K-quant"),
             "hbm", gateup_bytes, kms["gateup_gemv"], "GB/s", HBM_PEAK_GBS,
             traffic_for("gemv_gateup_mx" if shp.fmt else "gemv_gateup"),
             {"median_launch_ms": kst["gateup_gemv"]["median_ms"],
@@ -376,7 +378,7 @@ def bench_layer_batches(args, torch, qm, mi, DeviceLayer, name, T, n_copies, K, 
     else:
         names = ["gemv_front", "gateup_gemv", "down_gemv"]
         kms = kernel_profile(torch, qm, lambda i, e: step(i, e), min(K, 32), names)
-        gu_bytes = d_avg * gu + shp.H * 4 * T + T * shp.k * shp.I * 4
+        gu_bytes = (d_avg + 1) * gu + shp.H * 4 * T + T * (shp.k + 1) * shp.I * 4
         rl = roofline("gemv_gateup_kernel", "hbm", gu_bytes, kms["gateup_gemv"], "GB/s",
                       HBM_PEAK_GBS)
     qm.moe_layer_forward(base.desc, xd[0], T, out, ws)

@@ -8,14 +8,14 @@
 // layer runs as three kernels, each streaming its share of the bytes:
 //
 //   front   the router's split-K partial logits (many small XCD-grouped
-//           workgroups) and, side by side in the same grid, the shared
-//           expert's gate/up + SwiGLU, which needs no routing (with the
-//           routing given, as in the shard calls, there is no router work
-//           and the gate/up kernel takes the shared expert: two kernels);
-//   gateup  the first wave of every workgroup sums its token's partial logits
-//           in a fixed order and runs the top-k up to the workgroup's slot
-//           (the same selection in every workgroup of the token), then all
-//           four waves compute gate/up + SwiGLU of the routed expert's rows;
+//           workgroups; not launched when the routing is given, as in the
+//           shard calls: two kernels);
+//   gateup  the first wave of every routed workgroup sums its token's
+//           partial logits in a fixed order and runs the top-k up to the
+//           workgroup's slot (the same selection in every workgroup of the
+//           token), then all four waves compute gate/up + SwiGLU of the
+//           routed expert's rows; the shared expert's workgroups, which need
+//           no routing, stream its rows from the start;
 //   down    down projections, one wave per slot, slot results added in the
 //           selected-slot order with the shared expert last (page "CKE Zip:
 //           From Splitting Tokens To Splitting Qwen3.5 Weights", section "A
@@ -193,8 +193,6 @@ __device__ __forceinline__ float wave_sum_n(const float* v) {
 
 constexpr int kGuWaves = 4;   // waves per routed gate/up workgroup
 constexpr int kGuSteps = 2;   // row steps per wave (each step: gate row + up row)
-constexpr int kShWaves = 4;   // waves per shared-expert gate/up workgroup (front kernel)
-constexpr int kShSteps = 1;   // their row steps per wave
 
 // The activations under one lane's pieces (they do not depend on the expert).
 template <int LPR, int NSBL>
@@ -316,9 +314,6 @@ struct GemvArgs {
     int32_t* idx_out;     // ... and its first workgroup per token writes it here
     float* w_out;
     int n_router_blocks;  // front kernel: router workgroups (0: none)
-    int shared_rows_blocks;
-    int n_shared_pad;     // front kernel: shared workgroups rounded up to kXcds
-    int sh_in_gateup;     // the gate/up kernel also runs the shared expert (slot k)
     float* out;
 };
 
@@ -433,47 +428,20 @@ __device__ __forceinline__ void router_role(const GemvArgs& a, int rb, const flo
     }
 }
 
-// The pointers and counts that the first loads need come first as scalar
-// arguments, which the hardware preloads into registers.  The shared expert
-// runs here only when the layer routes its own rows (the whole layer, so its
-// rows start at 0).
-template <int FMT, int LPR, int NSBL, int TT>
+// Router partial logits (T <= kRouterSmallMaxT).  The pointers and counts
+// its loads need come first as scalar arguments, which the hardware preloads
+// into registers.
+template <int LPR, int NSBL, int TT>
 __global__ void __launch_bounds__(256)
-gemv_front_kernel(const float* __restrict__ router_w, const float* __restrict__ x,
-                  const uint8_t* __restrict__ sh_gate, const uint8_t* __restrict__ sh_up,
-                  float* __restrict__ hbuf, uint32_t e_h, uint32_t t_pad, uint32_t rb_iloc,
-                  uint32_t k_nslot, GemvArgs a) {
-    const int E = lo16(e_h), H = hi16(e_h), T = lo16(t_pad), n_shared_pad = hi16(t_pad);
-    const int shared_rows_blocks = lo16(rb_iloc), iloc = hi16(rb_iloc);
-    // shared-expert workgroups first (each starts on a CU of its own), then
-    // the router's, from a multiple of kXcds on
-    const int b = blockIdx.x;
-    if (b >= n_shared_pad) {
-        router_role<TT, (LPR / 8) * NSBL>(a, b - n_shared_pad, router_w, x, E, H, T);
-        return;
-    }
-    // shared expert: blocks per token = shared_rows_blocks, kShWaves waves each
-    const int sb = b;
-    if (sb >= shared_rows_blocks * T) return;   // padding
-    const int t = sb / shared_rows_blocks;
-    const int rblk = sb % shared_rows_blocks;
-    const int wave = threadIdx.x >> 6;
-    if (wave >= kShWaves) return;
-    constexpr int rows_per_wave = kShSteps * (64 / LPR);
-    const int rbase = (rblk * kShWaves + wave) * rows_per_wave;
-    if (rbase >= iloc) return;   // the shared expert has the routed width
-    XRegs<LPR, NSBL> X;
-    X.load(x + (size_t)t * H);
-    // h of slot k (after the k routed slots) of token t; its rows are iloc wide
-    const int k = lo16(k_nslot), nslot = hi16(k_nslot);
-    gateup_rows<FMT, LPR, NSBL, kShSteps>(sh_gate, sh_up, H, iloc, 0, X, rbase,
-                                          hbuf + (size_t)(t * nslot + k) * iloc);
+gemv_front_kernel(const float* __restrict__ router_w, const float* __restrict__ x, uint32_t e_h,
+                  int T, GemvArgs a) {
+    router_role<TT, (LPR / 8) * NSBL>(a, blockIdx.x, router_w, x, lo16(e_h), hi16(e_h), T);
 }
 
-// routed experts: grid (row blocks, T*k); SH (routing known before the
-// layer starts, so no router work in a front kernel, which is then not
-// launched): T more rows of workgroups for the shared expert as slot k of
-// each token.  The pointers and counts a workgroup needs -- for its first
+// routed experts: grid (row blocks, T*k); SH (the layer has a shared
+// expert): T more rows of workgroups for the shared expert as slot k of each
+// token, which need no routing and start streaming at once.  The pointers and
+// counts a workgroup needs -- for its first
 // loads (activations, partial logits or the given routing) and for its
 // weights and h row -- come in as preloaded kernel arguments, so no load
 // waits for a kernel-argument load.
@@ -539,13 +507,14 @@ __device__ __forceinline__ void gateup_body(const float* __restrict__ x,
 
 // The layer routes its own rows: the top-k from the front kernel's partial
 // logits, for the whole layer (rows [0, I) of every expert).
-template <int FMT, int LPR, int NSBL>
+template <int FMT, int LPR, int NSBL, bool SH>
 __global__ void __launch_bounds__(64 * kGuWaves)
 gemv_gateup_kernel(const float* __restrict__ x, const float* __restrict__ part,
                    const uint8_t* __restrict__ gate, const uint8_t* __restrict__ up,
-                   float* __restrict__ hbuf, uint32_t k_nslot, uint32_t e_h, int I, GemvArgs a) {
-    gateup_body<FMT, LPR, NSBL, true, false>(x, part, nullptr, gate, up, hbuf, lo16(k_nslot),
-                                             hi16(k_nslot), lo16(e_h), hi16(e_h), I, I, 0, 0, a);
+                   float* __restrict__ hbuf, uint32_t k_nslot, uint32_t e_h, int I, int T,
+                   GemvArgs a) {
+    gateup_body<FMT, LPR, NSBL, true, SH>(x, part, nullptr, gate, up, hbuf, lo16(k_nslot),
+                                          hi16(k_nslot), lo16(e_h), hi16(e_h), I, I, 0, T, a);
 }
 
 // The routing is given (shard and range calls, or the router ran first).
@@ -708,33 +677,24 @@ static GemvArgs base_args(const moe_layer_desc& d, const float* x, int T, int i0
     return a;
 }
 
-template <int FMT, int LPR, int NSBL>
-static void launch_front_f(const GemvArgs& a, int n_shared_blocks, const Ctx& c) {
-    const dim3 grid(a.n_router_blocks + n_shared_blocks);
-    const uint32_t e_h = pack16(a.E, a.H), t_pad = pack16(a.T, a.n_shared_pad);
-    const uint32_t rb_iloc = pack16(a.shared_rows_blocks, a.iloc), k_nslot = pack16(a.k, a.nslot);
-    if (a.T == 1)
-        launch_k(c, MOE_K_GEMV_FRONT, gemv_front_kernel<FMT, LPR, NSBL, 1>, grid, dim3(256), 0,
-                 a.router_w, a.x, a.sh_gate, a.sh_up, a.hbuf, e_h, t_pad, rb_iloc, k_nslot, a);
-    else
-        launch_k(c, MOE_K_GEMV_FRONT, gemv_front_kernel<FMT, LPR, NSBL, 4>, grid, dim3(256), 0,
-                 a.router_w, a.x, a.sh_gate, a.sh_up, a.hbuf, e_h, t_pad, rb_iloc, k_nslot, a);
-}
-
 template <int LPR, int NSBL>
-static void launch_front_t(const GemvArgs& a, int n_shared_blocks, const Ctx& c) {
-    if (a.fmt == MOE_WFMT_MXFP4)
-        launch_front_f<MOE_WFMT_MXFP4, LPR, NSBL>(a, n_shared_blocks, c);
+static void launch_front_t(const GemvArgs& a, const Ctx& c) {
+    const dim3 grid(a.n_router_blocks);
+    const uint32_t e_h = pack16(a.E, a.H);
+    if (a.T == 1)
+        launch_k(c, MOE_K_GEMV_FRONT, gemv_front_kernel<LPR, NSBL, 1>, grid, dim3(256), 0,
+                 a.router_w, a.x, e_h, a.T, a);
     else
-        launch_front_f<MOE_WFMT_KQUANT, LPR, NSBL>(a, n_shared_blocks, c);
+        launch_k(c, MOE_K_GEMV_FRONT, gemv_front_kernel<LPR, NSBL, 4>, grid, dim3(256), 0,
+                 a.router_w, a.x, e_h, a.T, a);
 }
 
 template <int LPR, int NSBL>
 static hipError_t launch_gateup_t(const GemvArgs& a, const Ctx& c) {
     constexpr int rows_per_block = kGuWaves * kGuSteps * (64 / LPR);
     const int Iloc = a.iloc;
-    const dim3 grid((Iloc + rows_per_block - 1) / rows_per_block,
-                    a.T * a.k + (a.sh_in_gateup ? a.T : 0));
+    const bool sh = a.nslot > a.k;   // a shared expert: slot k of each token
+    const dim3 grid((Iloc + rows_per_block - 1) / rows_per_block, a.T * a.k + (sh ? a.T : 0));
     const dim3 block(64 * kGuWaves);
     if (a.k > 0xffff || a.nslot > 0xffff || a.E > 0xffff || a.H > 0xffff)
         return hipErrorInvalidValue;   // packed in 16 bits
@@ -742,14 +702,17 @@ static hipError_t launch_gateup_t(const GemvArgs& a, const Ctx& c) {
     if (a.route) {
         // the whole layer: rows [0, I) of every expert
         if (a.i0 != 0 || a.iloc != a.I) return hipErrorInvalidValue;
-        if (a.fmt == MOE_WFMT_MXFP4)
-            launch_k(c, MOE_K_GATEUP_GEMV, gemv_gateup_kernel<MOE_WFMT_MXFP4, LPR, NSBL>, grid,
-                     block, 0, a.x, (const float*)a.part, a.gate, a.up, a.hbuf, k_nslot, e_h, a.I,
-                     a);
-        else
-            launch_k(c, MOE_K_GATEUP_GEMV, gemv_gateup_kernel<MOE_WFMT_KQUANT, LPR, NSBL>, grid,
-                     block, 0, a.x, (const float*)a.part, a.gate, a.up, a.hbuf, k_nslot, e_h, a.I,
-                     a);
+#define MOE_GATEUP_R(F, S)                                                                       \
+    launch_k(c, MOE_K_GATEUP_GEMV, gemv_gateup_kernel<F, LPR, NSBL, S>, grid, block, 0, a.x,     \
+             (const float*)a.part, a.gate, a.up, a.hbuf, k_nslot, e_h, a.I, a.T, a)
+        if (a.fmt == MOE_WFMT_MXFP4) {
+            if (sh) MOE_GATEUP_R(MOE_WFMT_MXFP4, true);
+            else MOE_GATEUP_R(MOE_WFMT_MXFP4, false);
+        } else {
+            if (sh) MOE_GATEUP_R(MOE_WFMT_KQUANT, true);
+            else MOE_GATEUP_R(MOE_WFMT_KQUANT, false);
+        }
+#undef MOE_GATEUP_R
         return hipGetLastError();
     }
     if (a.i0 > 0xffff || a.iloc > 0xffff) return hipErrorInvalidValue;
@@ -758,10 +721,10 @@ static hipError_t launch_gateup_t(const GemvArgs& a, const Ctx& c) {
     launch_k(c, MOE_K_GATEUP_GEMV, gemv_gateup_given_kernel<F, LPR, NSBL, S>, grid, block, 0,    \
              a.idx, a.gate, a.up, a.hbuf, k_nslot, e_h, iloc_i0, a.I, a.T, a)
     if (a.fmt == MOE_WFMT_MXFP4) {
-        if (a.sh_in_gateup) MOE_GATEUP(MOE_WFMT_MXFP4, true);
+        if (sh) MOE_GATEUP(MOE_WFMT_MXFP4, true);
         else MOE_GATEUP(MOE_WFMT_MXFP4, false);
     } else {
-        if (a.sh_in_gateup) MOE_GATEUP(MOE_WFMT_KQUANT, true);
+        if (sh) MOE_GATEUP(MOE_WFMT_KQUANT, true);
         else MOE_GATEUP(MOE_WFMT_KQUANT, false);
     }
 #undef MOE_GATEUP
@@ -778,33 +741,14 @@ static hipError_t launch_gateup_t(const GemvArgs& a, const Ctx& c) {
         default: return hipErrorInvalidValue;                        \
     }
 
-static int lanes_per_row(int nsb) { return nsb >= 8 ? 64 : 8 * nsb; }
-
-// Front kernel: router partials (T <= kRouterSmallMaxT) and/or the shared expert's gate/up.
-static hipError_t launch_front(GemvArgs& a, bool route, bool shared, const WsLayout& L, char* ws,
-                               const Ctx& c) {
+// Front kernel: router partial logits (T <= kRouterSmallMaxT).
+static hipError_t launch_front(GemvArgs& a, const WsLayout& L, char* ws, const Ctx& c) {
     const int nsb = a.H / kSbWeights;
     a.part = reinterpret_cast<float*>(ws + L.router_part);
     const int TT = a.T == 1 ? 1 : 4;
-    a.n_router_blocks = route ? ((a.T + TT - 1) / TT) * router_blocks_per_tile(a.E) : 0;
-    int n_shared = 0;
-    // the front kernel's shared role takes rows from 0 (it runs for the whole
-    // layer only; shard calls give their routing and use the gate/up kernel)
-    if (shared && a.i0 != 0) return hipErrorInvalidValue;
-    if (shared) {
-        const int rows_per_block = kShWaves * kShSteps * (64 / lanes_per_row(nsb));
-        const int Iloc = a.iloc;
-        a.shared_rows_blocks = (Iloc + rows_per_block - 1) / rows_per_block;
-        n_shared = a.shared_rows_blocks * a.T;
-    }
-    // router workgroups start at a multiple of kXcds (their XCD mapping)
-    a.n_shared_pad = a.n_router_blocks > 0 ? (n_shared + kXcds - 1) / kXcds * kXcds : n_shared;
-    if (a.n_router_blocks + n_shared == 0) return hipSuccess;
-    // the kernel takes these counts packed in 16 bits (it runs for T <= 32)
-    if (a.E > 0xffff || a.H > 0xffff || a.T > 0xffff || a.n_shared_pad > 0xffff ||
-        a.shared_rows_blocks > 0xffff || a.iloc > 0xffff || a.k > 0xffff || a.nslot > 0xffff)
-        return hipErrorInvalidValue;
-    MOE_DISPATCH_H(nsb, launch_front_t, a, a.n_shared_pad, c);
+    a.n_router_blocks = ((a.T + TT - 1) / TT) * router_blocks_per_tile(a.E);
+    if (a.E > 0xffff || a.H > 0xffff) return hipErrorInvalidValue;   // packed in 16 bits
+    MOE_DISPATCH_H(nsb, launch_front_t, a, c);
     return hipGetLastError();
 }
 
@@ -812,7 +756,7 @@ static hipError_t launch_front(GemvArgs& a, bool route, bool shared, const WsLay
 hipError_t launch_router_small(const moe_layer_desc& d, const float* x, int T, char* ws,
                                const WsLayout& L, const Ctx& c) {
     GemvArgs a = base_args(d, x, T, 0, 1);
-    return launch_front(a, true, false, L, ws, c);
+    return launch_front(a, L, ws, c);
 }
 
 hipError_t launch_router(const moe_layer_desc& d, const float* x, int T, int32_t* idx, float* w,
@@ -853,12 +797,14 @@ hipError_t launch_gemv(const moe_layer_desc& d, const float* x, int T, const int
         idx = a.idx_out;
         w = a.w_out;
     }
-    // with the routing known before the layer starts (given, or from the
-    // matrix-core router), the front kernel would hold only the shared
-    // expert's gate/up: the gate/up kernel takes it instead, one launch fewer
-    a.sh_in_gateup = d.shared_inter > 0 && !fused_route;
-    hipError_t e = launch_front(a, fused_route, d.shared_inter > 0 && fused_route, L, ws, c);
-    if (e != hipSuccess) return e;
+    // the front kernel: the router's partial logits, when this call routes
+    // its own rows here (the gate/up kernel then runs the top-k)
+    if (fused_route) {
+        hipError_t e = launch_front(a, L, ws, c);
+        if (e != hipSuccess) return e;
+    } else {
+        a.part = reinterpret_cast<float*>(ws + L.router_part);
+    }
     a.route = fused_route ? 1 : 0;
     a.idx = idx;
     a.w = w;
