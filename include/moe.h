@@ -161,12 +161,11 @@ typedef struct moe_opts {
 } moe_opts;
 
 /* Kernel ids for moe_opts.kernel_events. */
-#define MOE_K_GEMV_FRONT 0       /* T <= 32: router partial logits; with them (GEMV path) the
-                                    shared-expert gate/up, which the gate/up kernel takes
-                                    when the routing is given */
+#define MOE_K_GEMV_FRONT 0       /* T <= 32: router partial logits */
 #define MOE_K_ROUTER_MFMA 1      /* T > 32: router logits on the matrix cores (split fp16, fp32-accurate) */
 #define MOE_K_ROUTER_TOPK 2      /* top-k + weights */
-#define MOE_K_GATEUP_GEMV 3      /* decode: top-k (when routing) + routed gate/up + SwiGLU */
+#define MOE_K_GATEUP_GEMV 3      /* decode: top-k (when routing) + routed and shared gate/up
+                                    + SwiGLU */
 #define MOE_K_DOWN_GEMV 4        /* decode: down + slot-order combine */
 #define MOE_K_X_F16 5            /* T > 32: tokens to fp16 hi/lo parts (and, when the router runs,
                                     the router matrix to fp16 hi/lo parts in the same launch) */
