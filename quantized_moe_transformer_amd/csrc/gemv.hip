@@ -256,6 +256,10 @@ __device__ __forceinline__ void gateup_rows(const uint8_t* __restrict__ G,
             hu[st][it] = load_head_f<FMT>(us);
         }
     }
+    // every weight load goes out before the first wait: left free, the
+    // scheduler interleaves waits and decoding with these loads (it did so
+    // for the short MXFP4 decode), which serialises their round trips
+    __builtin_amdgcn_sched_barrier(0);
     X.sums();
     float (&xl)[NSBL][16] = X.xl;
     float (&xh)[NSBL][16] = X.xh;
@@ -463,6 +467,10 @@ __device__ __forceinline__ void gateup_body(const float* __restrict__ x,
             if (rbase >= iloc) return;
             XRegs<LPR, NSBL> X;
             X.load(x + (size_t)t * H);
+            // the activation loads go out first: left free, the scheduler
+            // may wait for the weights and decode them before it issues
+            // these read-only loads (a memory clobber does not hold them)
+            __builtin_amdgcn_sched_barrier(0);
             // the shared expert has the routed width
             gateup_rows<FMT, LPR, NSBL, kGuSteps>(a.sh_gate, a.sh_up, H, iloc, i0, X, rbase,
                                                   hbuf + (size_t)(t * nslot + k) * iloc);
