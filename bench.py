@@ -58,18 +58,18 @@ MX_TERMS = 3                    # MX-FP8 terms per token / h value on the MXFP4 
 # --copy-probe).  Keyed by the SHA-256 of the kernel's sources: when they change,
 # the counters no longer describe the kernel and traffic is reported as null.
 TRAFFIC = {
-    # decode T=1, 280 dispatches: FETCH 5356.6 KiB x 1.99980, WRITE 18.1 KiB x 1.0
-    "gemv_gateup": {"sources_sha256": "997ae3f89bde57a2e36d6aa535a2c542004368042b3c28f271bdd108ef42a040",
-                    "fetch_bytes": 10969307, "write_bytes": 18509},
-    # prefill T=4096, 18 dispatches: FETCH 226145.3 KiB x 1.99980, WRITE 36864.0 KiB x 1.0
+    # decode T=1, 280 dispatches: FETCH 5354.9 KiB x 1.99980, WRITE 18.1 KiB x 1.0
+    "gemv_gateup": {"sources_sha256": "5998a7c213106d780440f3ee6e36c8c233fe7cba407271d831836f2c0f104a38",
+                    "fetch_bytes": 10965762, "write_bytes": 18525},
+    # prefill T=4096, 18 dispatches: FETCH 226190.0 KiB x 1.99980, WRITE 36864.0 KiB x 1.0
     "gemm_gateup": {"sources_sha256": "38c44c264ee3711088101b5964188bfb0a068286c3bf8ee0d684227a24fcfa10",
-                    "fetch_bytes": 463099314, "write_bytes": 37748736},
+                    "fetch_bytes": 463190704, "write_bytes": 37748736},
     # MXFP4 decode T=1, 280 dispatches: FETCH 5370.2 KiB x 1.99980, WRITE 18.1 KiB x 1.0
-    "gemv_gateup_mx": {"sources_sha256": "997ae3f89bde57a2e36d6aa535a2c542004368042b3c28f271bdd108ef42a040",
-                    "fetch_bytes": 10996979, "write_bytes": 18496},
-    # MXFP4 prefill T=4096, 18 dispatches: FETCH 269671.6 KiB x 1.99980, WRITE 59904.9 KiB x 1.0
+    "gemv_gateup_mx": {"sources_sha256": "5998a7c213106d780440f3ee6e36c8c233fe7cba407271d831836f2c0f104a38",
+                    "fetch_bytes": 10997025, "write_bytes": 18496},
+    # MXFP4 prefill T=4096, 18 dispatches: FETCH 269645.6 KiB x 1.99980, WRITE 59905.2 KiB x 1.0
     "gemm_gateup_mx": {"sources_sha256": "a23e786497430292dc59f05cc49339feebce277ef6f4fb50273feff6ae084548",
-                    "fetch_bytes": 552232273, "write_bytes": 61342658},
+                    "fetch_bytes": 552178931, "write_bytes": 61342976},
 }
 FETCH_SIZE_FACTOR = 1.99980   # plain 256 MiB copy: true bytes read / FETCH_SIZE bytes
 WRITE_SIZE_FACTOR = 1.0
@@ -96,9 +96,9 @@ def sources_sha(kernel):
 # GRBM_GUI_ACTIVE / 8 XCDs); executed_flops = MOPS x 512 (padded rows included).
 MFMA_COUNTERS = {
     "gemm_gateup": {"sources_sha256": "38c44c264ee3711088101b5964188bfb0a068286c3bf8ee0d684227a24fcfa10",
-                    "mfma_busy": 0.3366, "executed_flops": 1.71262e+11},
+                    "mfma_busy": 0.3365, "executed_flops": 1.71262e+11},
     "gemm_gateup_mx": {"sources_sha256": "a23e786497430292dc59f05cc49339feebce277ef6f4fb50273feff6ae084548",
-                    "mfma_busy": 0.3851, "executed_flops": 5.11772e+11},
+                    "mfma_busy": 0.3866, "executed_flops": 5.11772e+11},
 }
 
 

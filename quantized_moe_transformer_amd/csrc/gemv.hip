@@ -347,8 +347,9 @@ __host__ __device__ inline int router_blocks_per_tile(int E) {
 // g = tid / 2: rows g, g + G, ... of the split.  Each wave sums its 32 row
 // groups across its lanes, the four waves are added in LDS, in a fixed order.
 template <int TT, int NSB>
-__device__ __forceinline__ void router_role(const GemvArgs& a, int rb, const float* router_w,
-                                            const float* x, int E, int H, int T) {
+__device__ __forceinline__ void router_role(float* __restrict__ part, int rb,
+                                            const float* router_w, const float* x, int E, int H,
+                                            int T) {
     constexpr int KS = kRouterSplits;
     static_assert(KS == kXcds, "one K split per XCD slot in the workgroup mapping");
     constexpr int ROWS = 32 * NSB;
@@ -427,19 +428,21 @@ __device__ __forceinline__ void router_role(const GemvArgs& a, int rb, const flo
         const int tt = tid / kRtE, ee = tid % kRtE;
         const int eg = ec * kRtE + ee;
         if (tt < nt && eg < E)
-            a.part[((size_t)(t0 + tt) * E + eg) * KS + ks] =
+            part[((size_t)(t0 + tt) * E + eg) * KS + ks] =
                 ((red[0][tt][ee] + red[1][tt][ee]) + red[2][tt][ee]) + red[3][tt][ee];
     }
 }
 
-// Router partial logits (T <= kRouterSmallMaxT).  The pointers and counts
-// its loads need come first as scalar arguments, which the hardware preloads
-// into registers.
+// Router partial logits (T <= kRouterSmallMaxT).  Every argument is a
+// scalar one that the hardware preloads into registers (8 dwords): no
+// argument load, and so no wait for one, sits between the router's loads
+// and its store (a wait for LDS before a barrier also waits for any scalar
+// load in flight).
 template <int LPR, int NSBL, int TT>
 __global__ void __launch_bounds__(256)
-gemv_front_kernel(const float* __restrict__ router_w, const float* __restrict__ x, uint32_t e_h,
-                  int T, GemvArgs a) {
-    router_role<TT, (LPR / 8) * NSBL>(a, blockIdx.x, router_w, x, lo16(e_h), hi16(e_h), T);
+gemv_front_kernel(const float* __restrict__ router_w, const float* __restrict__ x,
+                  float* __restrict__ part, uint32_t e_h, int T) {
+    router_role<TT, (LPR / 8) * NSBL>(part, blockIdx.x, router_w, x, lo16(e_h), hi16(e_h), T);
 }
 
 // routed experts: grid (row blocks, T*k); SH (the layer has a shared
@@ -691,10 +694,10 @@ static void launch_front_t(const GemvArgs& a, const Ctx& c) {
     const uint32_t e_h = pack16(a.E, a.H);
     if (a.T == 1)
         launch_k(c, MOE_K_GEMV_FRONT, gemv_front_kernel<LPR, NSBL, 1>, grid, dim3(256), 0,
-                 a.router_w, a.x, e_h, a.T, a);
+                 a.router_w, a.x, a.part, e_h, a.T);
     else
         launch_k(c, MOE_K_GEMV_FRONT, gemv_front_kernel<LPR, NSBL, 4>, grid, dim3(256), 0,
-                 a.router_w, a.x, e_h, a.T, a);
+                 a.router_w, a.x, a.part, e_h, a.T);
 }
 
 template <int LPR, int NSBL>
