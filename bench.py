@@ -58,18 +58,18 @@ MX_TERMS = 3                    # MX-FP8 terms per token / h value on the MXFP4 
 # --copy-probe).  Keyed by the SHA-256 of the kernel's sources: when they change,
 # the counters no longer describe the kernel and traffic is reported as null.
 TRAFFIC = {
-    # decode T=1, 280 dispatches: FETCH 5354.9 KiB x 1.99980, WRITE 18.1 KiB x 1.0
-    "gemv_gateup": {"sources_sha256": "5998a7c213106d780440f3ee6e36c8c233fe7cba407271d831836f2c0f104a38",
-                    "fetch_bytes": 10965762, "write_bytes": 18525},
-    # prefill T=4096, 18 dispatches: FETCH 226190.0 KiB x 1.99980, WRITE 36864.0 KiB x 1.0
+    # decode T=1, 280 dispatches: FETCH 5347.0 KiB x 1.99980, WRITE 18.1 KiB x 1.0
+    "gemv_gateup": {"sources_sha256": "a0156ea4c49fe8856b2acbbfad167349df54fdecc42435744e4987386e9269e3",
+                    "fetch_bytes": 10949472, "write_bytes": 18505},
+    # prefill T=4096, 18 dispatches: FETCH 226176.6 KiB x 1.99980, WRITE 36864.0 KiB x 1.0
     "gemm_gateup": {"sources_sha256": "38c44c264ee3711088101b5964188bfb0a068286c3bf8ee0d684227a24fcfa10",
-                    "fetch_bytes": 463190704, "write_bytes": 37748736},
-    # MXFP4 decode T=1, 280 dispatches: FETCH 5370.2 KiB x 1.99980, WRITE 18.1 KiB x 1.0
-    "gemv_gateup_mx": {"sources_sha256": "5998a7c213106d780440f3ee6e36c8c233fe7cba407271d831836f2c0f104a38",
-                    "fetch_bytes": 10997025, "write_bytes": 18496},
-    # MXFP4 prefill T=4096, 18 dispatches: FETCH 269645.6 KiB x 1.99980, WRITE 59905.2 KiB x 1.0
+                    "fetch_bytes": 463163407, "write_bytes": 37748736},
+    # MXFP4 decode T=1, 280 dispatches: FETCH 5365.6 KiB x 1.99980, WRITE 18.1 KiB x 1.0
+    "gemv_gateup_mx": {"sources_sha256": "a0156ea4c49fe8856b2acbbfad167349df54fdecc42435744e4987386e9269e3",
+                    "fetch_bytes": 10987668, "write_bytes": 18496},
+    # MXFP4 prefill T=4096, 18 dispatches: FETCH 269652.6 KiB x 1.99980, WRITE 59906.3 KiB x 1.0
     "gemm_gateup_mx": {"sources_sha256": "a23e786497430292dc59f05cc49339feebce277ef6f4fb50273feff6ae084548",
-                    "fetch_bytes": 552178931, "write_bytes": 61342976},
+                    "fetch_bytes": 552193244, "write_bytes": 61344089},
 }
 FETCH_SIZE_FACTOR = 1.99980   # plain 256 MiB copy: true bytes read / FETCH_SIZE bytes
 WRITE_SIZE_FACTOR = 1.0
@@ -96,9 +96,9 @@ def sources_sha(kernel):
 # GRBM_GUI_ACTIVE / 8 XCDs); executed_flops = MOPS x 512 (padded rows included).
 MFMA_COUNTERS = {
     "gemm_gateup": {"sources_sha256": "38c44c264ee3711088101b5964188bfb0a068286c3bf8ee0d684227a24fcfa10",
-                    "mfma_busy": 0.3365, "executed_flops": 1.71262e+11},
+                    "mfma_busy": 0.3374, "executed_flops": 1.71262e+11},
     "gemm_gateup_mx": {"sources_sha256": "a23e786497430292dc59f05cc49339feebce277ef6f4fb50273feff6ae084548",
-                    "mfma_busy": 0.3866, "executed_flops": 5.11772e+11},
+                    "mfma_busy": 0.3852, "executed_flops": 5.11772e+11},
 }
 
 

@@ -317,7 +317,6 @@ struct GemvArgs {
     int route;            // gateup computes the top-k from `part` ...
     int32_t* idx_out;     // ... and its first workgroup per token writes it here
     float* w_out;
-    int n_router_blocks;  // front kernel: router workgroups (0: none)
     float* out;
 };
 
@@ -347,7 +346,7 @@ __host__ __device__ inline int router_blocks_per_tile(int E) {
 // g = tid / 2: rows g, g + G, ... of the split.  Each wave sums its 32 row
 // groups across its lanes, the four waves are added in LDS, in a fixed order.
 template <int TT, int NSB>
-__device__ __forceinline__ void router_role(float* __restrict__ part, int rb,
+__device__ __forceinline__ void router_role(float* __restrict__ part, int tb, int u,
                                             const float* router_w, const float* x, int E, int H,
                                             int T) {
     constexpr int KS = kRouterSplits;
@@ -357,9 +356,8 @@ __device__ __forceinline__ void router_role(float* __restrict__ part, int rb,
     constexpr int RPT = ROWS / G;                // rows per thread
     __shared__ float xs[TT][ROWS];
     __shared__ float red[4][TT][kRtE];
-    const int nb = router_blocks_per_tile(E);
-    const int tb = rb / nb;
-    const int u = rb % nb;
+    // tb: the token tile; u: the workgroup within it (the tile's count of
+    // workgroups is a multiple of kXcds, so u % kXcds is the XCD slot)
     const int w = u / kXcds;                     // index among the workgroups of its XCD
     const int quarter = w % (kRtLine / kRtE);
     const int pair = (w / (kRtLine / kRtE)) * kXcds + u % kXcds;   // (line group, split)
@@ -442,12 +440,14 @@ template <int LPR, int NSBL, int TT>
 __global__ void __launch_bounds__(256)
 gemv_front_kernel(const float* __restrict__ router_w, const float* __restrict__ x,
                   float* __restrict__ part, uint32_t e_h, int T) {
-    router_role<TT, (LPR / 8) * NSBL>(part, blockIdx.x, router_w, x, lo16(e_h), hi16(e_h), T);
+    router_role<TT, (LPR / 8) * NSBL>(part, blockIdx.y, blockIdx.x, router_w, x, lo16(e_h),
+                                      hi16(e_h), T);
 }
 
-// routed experts: grid (row blocks, T*k); SH (the layer has a shared
-// expert): T more rows of workgroups for the shared expert as slot k of each
-// token, which need no routing and start streaming at once.  The pointers and
+// grid (row blocks, k + SH, T): slot j of token t, the slot and the token
+// read from the block index with no division; SH (the layer has a shared
+// expert): slot k is the shared expert's, which needs no routing and starts
+// streaming at once.  The pointers and
 // counts a workgroup needs -- for its first
 // loads (activations, partial logits or the given routing) and for its
 // weights and h row -- come in as preloaded kernel arguments, so no load
@@ -460,13 +460,12 @@ __device__ __forceinline__ void gateup_body(const float* __restrict__ x,
                                             const uint8_t* __restrict__ up, float* __restrict__ hbuf,
                                             int k, int nslot, int E, int H, int I, int iloc, int i0,
                                             int T, const GemvArgs& a) {
-    const int q = blockIdx.y;
+    const int j = blockIdx.y, t = blockIdx.z;   // slot j of token t
     const int wave = threadIdx.x >> 6;
     constexpr int rows_per_wave = kGuSteps * (64 / LPR);
     const int rbase = (blockIdx.x * kGuWaves + wave) * rows_per_wave;
     if constexpr (SH) {
-        if (q >= T * k) {
-            const int t = q - T * k;
+        if (j >= k) {
             if (rbase >= iloc) return;
             XRegs<LPR, NSBL> X;
             X.load(x + (size_t)t * H);
@@ -480,14 +479,13 @@ __device__ __forceinline__ void gateup_body(const float* __restrict__ x,
             return;
         }
     }
-    const int t = q / k, j = q % k;
     XRegs<LPR, NSBL> X;
     X.load(x + (size_t)t * H);   // independent of the routing: in flight during the top-k
     int e;
     if constexpr (ROUTE) {
         // the first wave selects (stopping at slot j, whose expert lane j
         // holds) and hands the expert to the others through LDS; the first
-        // wave of workgroup (0, t*k) fills all k slots and writes the
+        // wave of workgroup (0, 0, t) fills all k slots and writes the
         // token's routing
         __shared__ int s_e;
         if (threadIdx.x < 64) {
@@ -690,7 +688,8 @@ static GemvArgs base_args(const moe_layer_desc& d, const float* x, int T, int i0
 
 template <int LPR, int NSBL>
 static void launch_front_t(const GemvArgs& a, const Ctx& c) {
-    const dim3 grid(a.n_router_blocks);
+    const int TT = a.T == 1 ? 1 : 4;   // tokens per workgroup
+    const dim3 grid(router_blocks_per_tile(a.E), (a.T + TT - 1) / TT);
     const uint32_t e_h = pack16(a.E, a.H);
     if (a.T == 1)
         launch_k(c, MOE_K_GEMV_FRONT, gemv_front_kernel<LPR, NSBL, 1>, grid, dim3(256), 0,
@@ -705,7 +704,7 @@ static hipError_t launch_gateup_t(const GemvArgs& a, const Ctx& c) {
     constexpr int rows_per_block = kGuWaves * kGuSteps * (64 / LPR);
     const int Iloc = a.iloc;
     const bool sh = a.nslot > a.k;   // a shared expert: slot k of each token
-    const dim3 grid((Iloc + rows_per_block - 1) / rows_per_block, a.T * a.k + (sh ? a.T : 0));
+    const dim3 grid((Iloc + rows_per_block - 1) / rows_per_block, a.k + (sh ? 1 : 0), a.T);
     const dim3 block(64 * kGuWaves);
     if (a.k > 0xffff || a.nslot > 0xffff || a.E > 0xffff || a.H > 0xffff)
         return hipErrorInvalidValue;   // packed in 16 bits
@@ -756,8 +755,6 @@ static hipError_t launch_gateup_t(const GemvArgs& a, const Ctx& c) {
 static hipError_t launch_front(GemvArgs& a, const WsLayout& L, char* ws, const Ctx& c) {
     const int nsb = a.H / kSbWeights;
     a.part = reinterpret_cast<float*>(ws + L.router_part);
-    const int TT = a.T == 1 ? 1 : 4;
-    a.n_router_blocks = ((a.T + TT - 1) / TT) * router_blocks_per_tile(a.E);
     if (a.E > 0xffff || a.H > 0xffff) return hipErrorInvalidValue;   // packed in 16 bits
     MOE_DISPATCH_H(nsb, launch_front_t, a, c);
     return hipGetLastError();
